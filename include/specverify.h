@@ -1,0 +1,181 @@
+/*
+ * specverify.h -- C ABI of libspecverify, the speculative-sampling verify
+ * step on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (DistillSpec, Zhou et al., ICLR 2024, Appendix A.3,
+ * Algorithm A.1 "Speculative decoding step", lossless: lenience eps = 1; the
+ * same rule as summarised from Leviathan et al. on "How speculative decoding
+ * lets a small model draft and a large one check"):
+ *
+ *   For each sequence b with gamma_b draft tokens x_0..x_{gamma_b - 1}:
+ *     p_i = softmax(target logits row i / T_b),  i = 0..gamma_b
+ *     q_i = softmax(draft  logits row i / T_b),  i = 0..gamma_b - 1
+ *     r_i ~ U(0, 1];  n = first i with r_i > p_i(x_i) / q_i(x_i), else gamma_b
+ *     next token ~ norm(max(0, p_n - q_n))  if n < gamma_b
+ *                ~ p_{gamma_b}              if n == gamma_b
+ *   Greedy sequences (T_b == 0) accept x_i while it equals argmax p_i and
+ *   emit argmax p_n ("Speculative Decoding and Distillation" notes,
+ *   Practical considerations: greedy acceptance is exact match). The
+ *   temperature softmax is the one in the same notes, Part 2 "Loss (Hinton)",
+ *   with one T shared by target and draft.
+ *   The caller appends x_0..x_{n-1} and the next token: at least one and at
+ *   most gamma_b + 1 tokens per call and sequence.
+ *
+ * Uniforms: Philox4x32-10 (Salmon et al., SC'11) with key = seed and counter
+ * (row lo, row hi, i, 0), row = philox_row_offset + b. Word 0 of block i is
+ * r_i; word 1 of block n is the uniform of the final draw. A word w becomes
+ * ((w >> 8) + 1) * 2^-24, in (0, 1]. The final draw is the inverse CDF in
+ * index order: the smallest v with u * C_{V-1} <= C_v. Argmax ties resolve to
+ * the lowest index.
+ *
+ * Layout (every tensor pointer below is a DEVICE pointer, caller-owned):
+ *   target_logits  [sum_b (gamma_b + 1), V] row-major, row stride V, packed by
+ *                  sequence: sequence b's rows start at sum_{b'<b}(gamma_b'+1)
+ *   draft_logits   [sum_b gamma_b, V], sequence b's rows at sum_{b'<b} gamma_b'
+ *   draft_tokens   [sum_b gamma_b] int32, same packing as the draft rows
+ *   gamma_per_row  [B] int32 in [0, max_gamma]
+ *   temperature    [B] float32: > 0 sampling, == 0 greedy
+ *   out_n_accepted [B] int32, out_next_token [B] int32
+ * Both logit tensors share one dtype (bf16 or fp32). -inf logits are legal
+ * (masked tokens).
+ *
+ * Asynchrony: every entry point that takes a stream only enqueues work on it
+ * and returns; results are valid after the stream is synchronised. Nothing
+ * allocates device memory: scratch space is the caller's workspace, sized by
+ * specv_workspace_bytes(). Calls that share a workspace must not overlap.
+ *
+ * Errors:
+ *   - argument errors (null pointers, sizes out of range, row totals that
+ *     cannot match, misaligned logits, workspace too small) return a status
+ *     before anything is enqueued;
+ *   - a failed launch returns SPECV_ERR_HIP;
+ *   - data errors found on the device give that sequence (-1, -1) and set a
+ *     bit in the status word at byte offset 0 of the workspace: a gamma_b
+ *     outside [0, max_gamma] or gammas that disagree with the row totals
+ *     (every sequence gets (-1, -1)); T_b NaN, negative or +inf; a draft token
+ *     outside [0, V); a needed row with NaN or +inf or no finite logit
+ *     (needed rows: all target rows; draft rows only of sampling sequences).
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPECV_MAX_GAMMA 63
+
+typedef enum { SPECV_F32 = 0, SPECV_BF16 = 1 } specv_dtype_t;
+
+typedef enum {
+  SPECV_OK = 0,
+  SPECV_ERR_INVALID_ARGUMENT = 1,
+  SPECV_ERR_WORKSPACE = 2,
+  SPECV_ERR_HIP = 3,
+  SPECV_ERR_UNSUPPORTED = 4
+} specv_status_t;
+
+/* Device status word: uint32 at byte offset 0 of the workspace after a call. */
+#define SPECV_WORKSPACE_STATUS_OFFSET 0
+#define SPECV_DEV_SEQ_ERROR 1u    /* at least one sequence got (-1, -1)        */
+#define SPECV_DEV_LAYOUT_ERROR 2u /* gammas out of range or row totals differ  */
+
+/* Host struct describing one call. */
+typedef struct {
+  int32_t batch;               /* B >= 0 (B == 0: nothing to do)             */
+  int32_t vocab;               /* V >= 1                                     */
+  int32_t max_gamma;           /* 0 <= max_gamma <= SPECV_MAX_GAMMA          */
+  specv_dtype_t dtype;         /* dtype of both logit tensors                */
+  int64_t total_target_rows;   /* sum_b (gamma_b + 1) == total_draft_rows + B */
+  int64_t total_draft_rows;    /* sum_b gamma_b <= B * max_gamma             */
+} specv_shape_t;
+
+/* Bytes of device workspace specv_verify needs for `shape`; 0 if the shape
+ * is invalid (a valid shape always needs at least 256 bytes). */
+size_t specv_workspace_bytes(const specv_shape_t* shape);
+
+/* The verify step (DistillSpec Algorithm A.1, eps = 1), all sequences at
+ * once. `workspace` is a device buffer of at least specv_workspace_bytes()
+ * bytes, 256-byte aligned; its contents need no initialisation. */
+specv_status_t specv_verify(const specv_shape_t* shape, const void* target_logits,
+                            const void* draft_logits, const int32_t* draft_tokens,
+                            const int32_t* gamma_per_row, const float* temperature,
+                            uint64_t seed, uint64_t philox_row_offset,
+                            int32_t* out_n_accepted, int32_t* out_next_token,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Same as specv_verify with the uniforms given instead of drawn: r is
+ * [B, max_gamma] float32 (r_i of sequence b at r[b * max_gamma + i]) and u is
+ * [B] float32, device pointers. Values are used as given (expected in
+ * (0, 1]). Decouples the random stream from the accept/draw logic. */
+specv_status_t specv_verify_with_uniforms(const specv_shape_t* shape, const void* target_logits,
+                                          const void* draft_logits, const int32_t* draft_tokens,
+                                          const int32_t* gamma_per_row, const float* temperature,
+                                          const float* r, const float* u,
+                                          int32_t* out_n_accepted, int32_t* out_next_token,
+                                          void* workspace, size_t workspace_bytes,
+                                          hipStream_t stream);
+
+/* Stages of one call, in launch order. */
+#define SPECV_STAGE_PLAN 0      /* offsets of the packed rows              */
+#define SPECV_STAGE_ROWSTATS 1  /* pass 1: max, sum of exp, argmax per row */
+#define SPECV_STAGE_ACCEPT 2    /* ratios, uniforms, accepted count        */
+#define SPECV_STAGE_RESIDUAL 3  /* pass 2: weight mass per chunk           */
+#define SPECV_STAGE_DRAW 4      /* inverse-CDF draw of the next token      */
+#define SPECV_NUM_STAGES 5
+
+/* specv_verify that also records events[2 s] before and events[2 s + 1]
+ * after stage s on `stream` (events: 2 * SPECV_NUM_STAGES hipEvent_t created
+ * by the caller, or NULL). For timing the stages of a call. */
+specv_status_t specv_verify_profiled(const specv_shape_t* shape, const void* target_logits,
+                                     const void* draft_logits, const int32_t* draft_tokens,
+                                     const int32_t* gamma_per_row, const float* temperature,
+                                     uint64_t seed, uint64_t philox_row_offset,
+                                     int32_t* out_n_accepted, int32_t* out_next_token,
+                                     void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream, hipEvent_t* events);
+
+/* Row statistics of pass 1, merged per row (the values specv_verify uses):
+ * m = max z, s = sum_v exp((z_v - m) / T_b) (float64; NaN for rows of greedy
+ * sequences and for rows with NaN/+inf), arg = argmax z (lowest index).
+ * Outputs are device arrays of total_target_rows / total_draft_rows entries;
+ * draft rows of greedy sequences are not read: m = NaN, s = NaN, arg = -1. */
+specv_status_t specv_row_stats(const specv_shape_t* shape, const void* target_logits,
+                               const void* draft_logits, const int32_t* gamma_per_row,
+                               const float* temperature, float* out_target_max,
+                               double* out_target_sum, int32_t* out_target_argmax,
+                               float* out_draft_max, double* out_draft_sum,
+                               int32_t* out_draft_argmax, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
+/* Temperature-softmax probabilities of selected rows, as the final draw
+ * evaluates them: rows[k] >= 0 selects target row rows[k], rows[k] < 0
+ * selects draft row -rows[k] - 1 (device int64 array of n_rows entries);
+ * out_probs is [n_rows, V] float32. The row's sequence must be sampling. */
+specv_status_t specv_softmax_rows(const specv_shape_t* shape, const void* target_logits,
+                                  const void* draft_logits, const int32_t* gamma_per_row,
+                                  const float* temperature, const int64_t* rows, int64_t n_rows,
+                                  float* out_probs, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+
+/* Raw Philox4x32-10 blocks of the device generator: out[4k..4k+4) for key =
+ * seed and counter ctr[4k..4k+4) (device arrays, n blocks). */
+specv_status_t specv_philox4x32_10(uint64_t seed, const uint32_t* ctr, uint32_t* out, int64_t n,
+                                   hipStream_t stream);
+
+/* Plain device copy of `bytes` bytes (16-byte aligned pointers): a
+ * calibration kernel for memory counters and copy bandwidth. */
+specv_status_t specv_copy_bytes(void* dst, const void* src, size_t bytes, hipStream_t stream);
+
+const char* specv_status_string(specv_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

@@ -1,0 +1,188 @@
+"""ctypes wrapper around the CPU oracle (oracle/specv_oracle.c).
+
+TEST INFRASTRUCTURE. Only the test suite, ``__graft_entry__.smoke()`` and the
+benchmark's ``cpu_baseline`` leg may import this package. The HIP library and
+its Python binding never import it and never fall back to it.
+
+Every function takes numpy arrays in the packed layout of the verify step:
+target logits ``[sum(gamma_b + 1), V]``, draft logits ``[sum(gamma_b), V]``
+(bf16 stored as uint16 bit patterns, or float32), draft tokens
+``[sum(gamma_b)]`` int32, ``gamma[B]`` int32, ``temperature[B]`` float32.
+"""
+import ctypes
+import os
+from dataclasses import dataclass
+from pathlib import Path
+
+import numpy as np
+
+from . import build as _build
+
+F32, BF16 = 0, 1
+NEAR_TIE = 1e-6
+
+MUTANT_NONE = 0
+MUTANT_RESIDUAL_IS_P = 1
+MUTANT_RESIDUAL_IS_Q = 2
+MUTANT_N_PLUS_ONE = 3
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not _build.LIBRARY.exists():
+        _build.build()
+    lib = ctypes.CDLL(str(_build.LIBRARY))
+    P = ctypes.c_void_p
+    i64, u64 = ctypes.c_int64, ctypes.c_uint64
+    lib.oracle_verify.restype = ctypes.c_int
+    lib.oracle_verify.argtypes = [i64, i64, i64, ctypes.c_int, i64, i64, P, P, P, P, P,
+                                  u64, u64, P, P, P, P, P, P, P, P, ctypes.c_int]
+    lib.oracle_row_stats.restype = None
+    lib.oracle_row_stats.argtypes = [P, ctypes.c_int, i64, i64, P, P, P, P, P]
+    lib.oracle_softmax_row.restype = None
+    lib.oracle_softmax_row.argtypes = [P, ctypes.c_int, i64, i64, ctypes.c_float, P]
+    lib.oracle_philox_blocks.restype = None
+    lib.oracle_philox_blocks.argtypes = [u64, P, P, i64]
+    lib.oracle_uniform24.restype = ctypes.c_double
+    lib.oracle_uniform24.argtypes = [ctypes.c_uint32]
+    lib.oracle_uniform24_many.restype = None
+    lib.oracle_uniform24_many.argtypes = [P, P, i64]
+    lib.oracle_decode_bf16.restype = None
+    lib.oracle_decode_bf16.argtypes = [P, P, i64]
+    lib.oracle_set_mutant.restype = None
+    lib.oracle_set_mutant.argtypes = [ctypes.c_int]
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.uint16:
+        return BF16
+    if a.dtype == np.float32:
+        return F32
+    raise TypeError("logits must be uint16 (bf16 bits) or float32, got %s" % a.dtype)
+
+
+def default_threads() -> int:
+    n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+@dataclass
+class VerifyResult:
+    n: np.ndarray          # [B] int32 accepted counts, -1 on a data error
+    next_token: np.ndarray  # [B] int32 emitted token, -1 on a data error
+    margin: np.ndarray     # [B] float64 smallest relative decision margin
+    near_tie: np.ndarray   # [B] bool, margin < 1e-6
+    ratio: np.ndarray      # [B, max_gamma] float64 p_i(x_i)/q_i(x_i) (NaN if not reached)
+    resmass: np.ndarray    # [B] float64 total weight of the final draw (NaN if greedy)
+    layout_ok: bool
+
+
+def verify(target, draft, tokens, gamma, temperature, *, vocab, max_gamma, seed=0,
+           row_offset=0, r=None, u=None, nthreads=None) -> VerifyResult:
+    """Run the oracle over every sequence. ``r`` ([B, max_gamma] float32) and
+    ``u`` ([B] float32) inject the uniforms instead of drawing them from
+    Philox4x32-10."""
+    lib = _load()
+    gamma = np.ascontiguousarray(gamma, dtype=np.int32)
+    B = int(gamma.shape[0])
+    target = np.ascontiguousarray(target)
+    draft = np.ascontiguousarray(draft)
+    if draft.size and draft.dtype != target.dtype:
+        raise TypeError("target and draft logits must share a dtype")
+    tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+    temperature = np.ascontiguousarray(temperature, dtype=np.float32)
+    tt = target.size // vocab
+    td = draft.size // vocab if vocab else 0
+    out_n = np.empty(B, np.int32)
+    out_next = np.empty(B, np.int32)
+    margin = np.empty(B, np.float64)
+    near = np.empty(B, np.uint8)
+    ratio = np.full((B, max(max_gamma, 1)), np.nan, np.float64)
+    resmass = np.full(B, np.nan, np.float64)
+    if r is not None:
+        r = np.ascontiguousarray(r, dtype=np.float32).reshape(B, max_gamma)
+    if u is not None:
+        u = np.ascontiguousarray(u, dtype=np.float32).reshape(B)
+    code = lib.oracle_verify(B, vocab, max_gamma, _dtype_code(target), tt, td, _ptr(target),
+                             _ptr(draft), _ptr(tokens), _ptr(gamma), _ptr(temperature),
+                             int(seed), int(row_offset), _ptr(r), _ptr(u), _ptr(out_n),
+                             _ptr(out_next), _ptr(margin), _ptr(near), _ptr(ratio),
+                             _ptr(resmass), int(nthreads or default_threads()))
+    return VerifyResult(out_n, out_next, margin, near.astype(bool),
+                        ratio[:, :max_gamma], resmass, code == 0)
+
+
+def row_stats(logits, vocab, temperature_per_row):
+    """(m, S, argmax, valid) per row; S is NaN where the row's T is 0."""
+    lib = _load()
+    logits = np.ascontiguousarray(logits)
+    rows = logits.size // vocab
+    T = np.ascontiguousarray(temperature_per_row, dtype=np.float32).reshape(rows)
+    m = np.empty(rows, np.float64)
+    s = np.empty(rows, np.float64)
+    a = np.empty(rows, np.int32)
+    ok = np.empty(rows, np.uint8)
+    lib.oracle_row_stats(_ptr(logits), _dtype_code(logits), rows, vocab, _ptr(T), _ptr(m),
+                         _ptr(s), _ptr(a), _ptr(ok))
+    return m, s, a, ok.astype(bool)
+
+
+def softmax_row(logits, vocab, row, T):
+    lib = _load()
+    logits = np.ascontiguousarray(logits)
+    out = np.empty(vocab, np.float64)
+    lib.oracle_softmax_row(_ptr(logits), _dtype_code(logits), vocab, int(row), float(T),
+                           _ptr(out))
+    return out
+
+
+def philox_blocks(seed, counters):
+    """Philox4x32-10 blocks for counters [k, 4] uint32 -> [k, 4] uint32."""
+    lib = _load()
+    ctr = np.ascontiguousarray(counters, dtype=np.uint32).reshape(-1, 4)
+    out = np.empty_like(ctr)
+    lib.oracle_philox_blocks(int(seed), _ptr(ctr), _ptr(out), ctr.shape[0])
+    return out
+
+
+def uniform24(words):
+    """U(w) = ((w >> 8) + 1) * 2^-24 for every 32-bit word."""
+    lib = _load()
+    w = np.ascontiguousarray(words, dtype=np.uint32).ravel()
+    out = np.empty(w.shape, np.float64)
+    lib.oracle_uniform24_many(_ptr(w), _ptr(out), w.size)
+    return out
+
+
+def decode_bf16(bits):
+    lib = _load()
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    out = np.empty(bits.shape, np.float64)
+    lib.oracle_decode_bf16(_ptr(bits), _ptr(out), bits.size)
+    return out
+
+
+class mutant:
+    """Context manager that plants one known mistake in the oracle (negative
+    controls for the statistical tests)."""
+
+    def __init__(self, which: int):
+        self.which = which
+
+    def __enter__(self):
+        _load().oracle_set_mutant(self.which)
+        return self
+
+    def __exit__(self, *exc):
+        _load().oracle_set_mutant(MUTANT_NONE)
+        return False

@@ -1,0 +1,495 @@
+/*
+ * specv_oracle.c -- plain CPU oracle for the speculative-sampling verify step.
+ *
+ * TEST INFRASTRUCTURE. Only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg may load or call this library. The product path (the HIP
+ * library) never links, imports or falls back to it, and this file shares no
+ * source, header or constant table with it.
+ *
+ * What it computes, and where the method is defined:
+ *   - DistillSpec (Zhou et al., ICLR 2024), Appendix A.3, Algorithm A.1
+ *     "Speculative decoding step", with lenience eps = 1 (lossless): compute
+ *     the ratios p_i(x_i)/q_i(x_i), draw one uniform per draft position, take
+ *     n = the first position whose uniform exceeds its ratio (gamma if none),
+ *     then draw one more token from norm(max(0, p_n - q_n)) when n < gamma,
+ *     or from p_gamma when every draft was accepted.
+ *   - The same step as summarised from Leviathan, Kalman and Matias on
+ *     "How speculative decoding lets a small model draft and a large one
+ *     check" (1-indexed form of the same rule), and in prose in the study
+ *     notes "Speculative Decoding and Distillation", Part 1, steps 3-5.
+ *   - Temperature softmax sigma_T(z)_i = exp(z_i/T) / sum_j exp(z_j/T), the
+ *     same T for the target and the draft rows: "Speculative Decoding and
+ *     Distillation", Part 2 "Loss (Hinton)".
+ *   - Greedy verification (T = 0) is exact match against argmax p:
+ *     "Speculative Decoding and Distillation", Practical considerations
+ *     ("Greedy vs sampling"); DISCO (arXiv 2405.04304) section 3 describes
+ *     the same as rejection sampling at zero temperature.
+ *
+ * Precision: every probability, ratio and cumulative sum is float64. Inputs
+ * (bf16 or fp32 logits, fp32 temperatures) convert to float64 exactly.
+ *
+ * Readings where the pages leave a step open (all restated in the design
+ * notes of the repository):
+ *   - uniforms come from Philox4x32-10 (Salmon, Moraes, Dror and Shaw,
+ *     "Parallel Random Numbers: As Easy as 1, 2, 3", SC'11), key = seed,
+ *     counter = (row lo, row hi, position, 0) with row = row_offset + b;
+ *     word 0 gives r_i, word 1 at position n gives the final-draw uniform u;
+ *   - a 32-bit word w maps to U(w) = ((w >> 8) + 1) * 2^-24, in (0, 1];
+ *   - reject iff r_i > ratio_i (equality accepts); q_i(x_i) = 0 gives an
+ *     infinite ratio (accept);
+ *   - the final draw is the inverse CDF in index order: the smallest v with
+ *     u * C_{V-1} <= C_v, C the inclusive prefix sum of the weights; if the
+ *     residual mass is exactly 0 the weights fall back to p_n;
+ *   - greedy argmax ties resolve to the lowest index, on the raw logits;
+ *   - a sequence whose needed rows hold NaN or +inf, or hold no finite logit,
+ *     or whose tokens fall outside [0, V), or whose T is NaN, negative or
+ *     +inf, yields (n, token) = (-1, -1); a gamma outside [0, max_gamma], or
+ *     row totals that disagree with the gammas, make every sequence (-1, -1).
+ *
+ * Parity pins: see the test suite (Philox against rocRAND's implementation,
+ * softmax against torch float64, injected-uniform hand cases, quadrature
+ * over the uniforms on tiny inputs, and chi-square tests of the output law).
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_F32 0
+#define ORACLE_BF16 1
+
+#define ORACLE_NEAR_TIE 1e-6
+
+/* Negative controls for the statistical tests: each value plants one known
+ * mistake so that the tests can show they would catch it. 0 = correct. */
+#define MUTANT_NONE 0
+#define MUTANT_RESIDUAL_IS_P 1 /* residual replaced by p_n            */
+#define MUTANT_RESIDUAL_IS_Q 2 /* residual replaced by q_n            */
+#define MUTANT_N_PLUS_ONE 3    /* accepted count off by one (capped)  */
+static int g_mutant = MUTANT_NONE;
+
+void oracle_set_mutant(int m) { g_mutant = m; }
+
+/* ------------------------------------------------------------------ */
+/* Philox4x32-10 (Salmon et al., SC'11): 10 rounds of the 4x32 S-box.  */
+/* Each round multiplies words 0 and 2 by the two Philox constants,    */
+/* mixes the high halves with words 1 and 3 and the round key, and the */
+/* key advances by the two Weyl constants between rounds.              */
+/* ------------------------------------------------------------------ */
+void oracle_philox4x32_10(uint64_t seed, const uint32_t ctr_in[4], uint32_t out[4]) {
+  const uint32_t mul_a = 0xD2511F53u, mul_b = 0xCD9E8D57u;
+  const uint32_t weyl_a = 0x9E3779B9u, weyl_b = 0xBB67AE85u;
+  uint32_t key_a = (uint32_t)seed, key_b = (uint32_t)(seed >> 32);
+  uint32_t x0 = ctr_in[0], x1 = ctr_in[1], x2 = ctr_in[2], x3 = ctr_in[3];
+  for (int round = 0; round < 10; ++round) {
+    uint64_t prod_a = (uint64_t)mul_a * (uint64_t)x0;
+    uint64_t prod_b = (uint64_t)mul_b * (uint64_t)x2;
+    uint32_t y0 = (uint32_t)(prod_b >> 32) ^ x1 ^ key_a;
+    uint32_t y1 = (uint32_t)prod_b;
+    uint32_t y2 = (uint32_t)(prod_a >> 32) ^ x3 ^ key_b;
+    uint32_t y3 = (uint32_t)prod_a;
+    x0 = y0; x1 = y1; x2 = y2; x3 = y3;
+    key_a += weyl_a;
+    key_b += weyl_b;
+  }
+  out[0] = x0; out[1] = x1; out[2] = x2; out[3] = x3;
+}
+
+/* U(w) = ((w >> 8) + 1) / 2^24: 24 random bits, in (0, 1], exact in fp32. */
+double oracle_uniform24(uint32_t w) { return (double)((w >> 8) + 1u) / 16777216.0; }
+
+void oracle_uniform24_many(const uint32_t* w, double* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_uniform24(w[i]);
+}
+
+/* The two uniforms the step uses for sequence row `row` and position `pos`. */
+static void draw_uniforms(uint64_t seed, uint64_t row, uint32_t pos, double* r_word0,
+                          double* u_word1) {
+  uint32_t ctr[4] = {(uint32_t)row, (uint32_t)(row >> 32), pos, 0u};
+  uint32_t w[4];
+  oracle_philox4x32_10(seed, ctr, w);
+  if (r_word0) *r_word0 = oracle_uniform24(w[0]);
+  if (u_word1) *u_word1 = oracle_uniform24(w[1]);
+}
+
+/* ------------------------------------------------------------------ */
+/* Input decoding: bf16 is the top half of an IEEE binary32.           */
+/* ------------------------------------------------------------------ */
+static double bf16_to_double(uint16_t h) {
+  uint32_t bits = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+void oracle_decode_bf16(const uint16_t* in, double* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = bf16_to_double(in[i]);
+}
+
+/* Copy row `row` of a [rows, V] logit matrix into z[0..V) as float64. */
+static void load_row(const void* base, int dtype, int64_t V, int64_t row, double* z) {
+  if (dtype == ORACLE_BF16) {
+    const uint16_t* p = (const uint16_t*)base + row * V;
+    for (int64_t v = 0; v < V; ++v) z[v] = bf16_to_double(p[v]);
+  } else {
+    const float* p = (const float*)base + row * V;
+    for (int64_t v = 0; v < V; ++v) z[v] = (double)p[v];
+  }
+}
+
+/* A row is usable when it has no NaN, no +inf and at least one finite value
+ * (-inf marks a masked token of probability 0). */
+static int row_is_valid(const double* z, int64_t V) {
+  int any_finite = 0;
+  for (int64_t v = 0; v < V; ++v) {
+    if (isnan(z[v])) return 0;
+    if (isinf(z[v]) && z[v] > 0) return 0;
+    if (isfinite(z[v])) any_finite = 1;
+  }
+  return any_finite;
+}
+
+/* argmax over raw logits, lowest index on ties. */
+static int64_t row_argmax(const double* z, int64_t V) {
+  int64_t best = 0;
+  for (int64_t v = 1; v < V; ++v)
+    if (z[v] > z[best]) best = v;
+  return best;
+}
+
+/* Temperature softmax: m = max z, S = sum exp((z - m)/T) in index order,
+ * p_v = exp((z_v - m)/T) / S. Writes p when p != NULL. */
+static void row_softmax(const double* z, int64_t V, double T, double* m_out, double* s_out,
+                        double* p) {
+  double m = -INFINITY;
+  for (int64_t v = 0; v < V; ++v)
+    if (z[v] > m) m = z[v];
+  double s = 0.0;
+  for (int64_t v = 0; v < V; ++v) s += exp((z[v] - m) / T);
+  if (p)
+    for (int64_t v = 0; v < V; ++v) p[v] = exp((z[v] - m) / T) / s;
+  if (m_out) *m_out = m;
+  if (s_out) *s_out = s;
+}
+
+/* ------------------------------------------------------------------ */
+/* The verify step.                                                    */
+/* ------------------------------------------------------------------ */
+typedef struct {
+  int64_t batch, vocab, max_gamma;
+  int dtype;
+  int64_t total_target_rows, total_draft_rows;
+  const void* target;
+  const void* draft;
+  const int32_t* tokens;
+  const int32_t* gamma;
+  const float* temperature;
+  uint64_t seed, row_offset;
+  const float* inj_r; /* [batch * max_gamma] or NULL: injected r_i      */
+  const float* inj_u; /* [batch] or NULL: injected final-draw uniforms  */
+  int32_t* out_n;
+  int32_t* out_next;
+  double* out_margin;  /* [batch] or NULL */
+  uint8_t* out_near;   /* [batch] or NULL */
+  double* out_ratio;   /* [batch * max_gamma] or NULL: p_i(x_i)/q_i(x_i) */
+  double* out_resmass; /* [batch] or NULL: total weight of the final draw */
+  const int64_t* toff;
+  const int64_t* doff;
+  int layout_ok;
+  int nthreads;
+} job_t;
+
+typedef struct {
+  double* z;  /* V   */
+  double* zq; /* V   */
+  double* p;  /* V   */
+  double* q;  /* V   */
+  double* w;  /* V   */
+} scratch_t;
+
+static void set_result(const job_t* J, int64_t b, int32_t n, int32_t next, double margin) {
+  J->out_n[b] = n;
+  J->out_next[b] = next;
+  if (J->out_margin) J->out_margin[b] = margin;
+  if (J->out_near) J->out_near[b] = (uint8_t)(margin < ORACLE_NEAR_TIE);
+}
+
+/* Inverse-CDF draw in index order over weights w[0..V): the smallest v with
+ * t <= C_v where t = u * C_{V-1}. Returns -1 when the total is 0. */
+static int64_t inverse_cdf(const double* w, int64_t V, double u, double* margin, double* total_out) {
+  double total = 0.0;
+  for (int64_t v = 0; v < V; ++v) total += w[v];
+  if (total_out) *total_out = total;
+  if (!(total > 0.0)) return -1;
+  double t = u * total;
+  double c = 0.0, prev = 0.0;
+  for (int64_t v = 0; v < V; ++v) {
+    prev = c;
+    c += w[v];
+    if (t <= c) {
+      double lo = t - prev, hi = c - t;
+      *margin = (lo < hi ? lo : hi) / total;
+      return v;
+    }
+  }
+  /* Unreachable in exact arithmetic (t <= total); rounding could leave t a
+   * hair above the last prefix: take the last token of positive weight. */
+  for (int64_t v = V - 1; v >= 0; --v)
+    if (w[v] > 0.0) {
+      *margin = 0.0;
+      return v;
+    }
+  return -1;
+}
+
+static void verify_sequence(const job_t* J, int64_t b, scratch_t* S) {
+  const int64_t V = J->vocab;
+  if (!J->layout_ok) {
+    set_result(J, b, -1, -1, INFINITY);
+    return;
+  }
+  const int64_t g = J->gamma[b];
+  const double T = (double)J->temperature[b];
+  const int64_t t0 = J->toff[b], d0 = J->doff[b];
+  if (isnan(T) || T < 0.0 || isinf(T)) {
+    set_result(J, b, -1, -1, INFINITY);
+    return;
+  }
+  for (int64_t i = 0; i < g; ++i) {
+    int32_t x = J->tokens[d0 + i];
+    if (x < 0 || x >= V) {
+      set_result(J, b, -1, -1, INFINITY);
+      return;
+    }
+  }
+
+  if (T == 0.0) {
+    /* Greedy: accept while the draft token equals the target argmax; emit
+     * argmax of the first disagreeing (or the bonus) target row. Every
+     * target row is checked for validity; draft rows are not read. */
+    int64_t n = g, next = -1;
+    int64_t first_bad = -1;
+    for (int64_t i = 0; i <= g; ++i) {
+      load_row(J->target, J->dtype, V, t0 + i, S->z);
+      if (!row_is_valid(S->z, V)) {
+        first_bad = i;
+        break;
+      }
+      int64_t a = row_argmax(S->z, V);
+      if (i < g && n == g && J->tokens[d0 + i] != a) n = i;
+      if (i == n && next < 0) next = a;
+    }
+    if (first_bad >= 0) {
+      set_result(J, b, -1, -1, INFINITY);
+      return;
+    }
+    if (g_mutant == MUTANT_N_PLUS_ONE && n < g) {
+      n = n + 1;
+      load_row(J->target, J->dtype, V, t0 + n, S->z);
+      next = row_argmax(S->z, V);
+    }
+    set_result(J, b, (int32_t)n, (int32_t)next, INFINITY);
+    return;
+  }
+
+  /* Sampling. Validate every needed row first (target 0..g, draft 0..g-1). */
+  for (int64_t i = 0; i <= g; ++i) {
+    load_row(J->target, J->dtype, V, t0 + i, S->z);
+    if (!row_is_valid(S->z, V)) {
+      set_result(J, b, -1, -1, INFINITY);
+      return;
+    }
+  }
+  for (int64_t i = 0; i < g; ++i) {
+    load_row(J->draft, J->dtype, V, d0 + i, S->z);
+    if (!row_is_valid(S->z, V)) {
+      set_result(J, b, -1, -1, INFINITY);
+      return;
+    }
+  }
+
+  const uint64_t philox_row = J->row_offset + (uint64_t)b;
+  double margin = INFINITY;
+
+  /* Accept walk (Algorithm A.1 steps 5-7): ratio_i = p_i(x_i)/q_i(x_i),
+   * reject at the first i with r_i > ratio_i. */
+  int64_t n = g;
+  for (int64_t i = 0; i < g; ++i) {
+    const int32_t x = J->tokens[d0 + i];
+    double mp, sp, mq, sq;
+    load_row(J->target, J->dtype, V, t0 + i, S->z);
+    row_softmax(S->z, V, T, &mp, &sp, NULL);
+    const double p_x = exp((S->z[x] - mp) / T) / sp;
+    load_row(J->draft, J->dtype, V, d0 + i, S->zq);
+    row_softmax(S->zq, V, T, &mq, &sq, NULL);
+    const double q_x = exp((S->zq[x] - mq) / T) / sq;
+    const double ratio = (q_x == 0.0) ? INFINITY : p_x / q_x;
+    if (J->out_ratio) J->out_ratio[b * J->max_gamma + i] = ratio;
+    double r;
+    if (J->inj_r)
+      r = (double)J->inj_r[b * J->max_gamma + i];
+    else
+      draw_uniforms(J->seed, philox_row, (uint32_t)i, &r, NULL);
+    if (isfinite(ratio)) {
+      double mg = fabs(r - ratio) / ratio;
+      if (mg < margin) margin = mg;
+    }
+    if (r > ratio) {
+      n = i;
+      break;
+    }
+  }
+  if (g_mutant == MUTANT_N_PLUS_ONE && n < g) n = n + 1;
+
+  /* Final draw (Algorithm A.1 steps 8-11). */
+  double u;
+  if (J->inj_u)
+    u = (double)J->inj_u[b];
+  else
+    draw_uniforms(J->seed, philox_row, (uint32_t)n, NULL, &u);
+
+  load_row(J->target, J->dtype, V, t0 + n, S->z);
+  row_softmax(S->z, V, T, NULL, NULL, S->p);
+  if (n < g && g_mutant != MUTANT_RESIDUAL_IS_P) {
+    load_row(J->draft, J->dtype, V, d0 + n, S->zq);
+    row_softmax(S->zq, V, T, NULL, NULL, S->q);
+    for (int64_t v = 0; v < V; ++v) {
+      double d = S->p[v] - S->q[v];
+      S->w[v] = d > 0.0 ? d : 0.0;
+    }
+    if (g_mutant == MUTANT_RESIDUAL_IS_Q)
+      for (int64_t v = 0; v < V; ++v) S->w[v] = S->q[v];
+  } else {
+    for (int64_t v = 0; v < V; ++v) S->w[v] = S->p[v];
+  }
+  double draw_margin = INFINITY, total = 0.0;
+  int64_t tok = inverse_cdf(S->w, V, u, &draw_margin, &total);
+  if (tok < 0) {
+    /* The residual has no mass (p_n == q_n up to rounding): draw from p_n. */
+    tok = inverse_cdf(S->p, V, u, &draw_margin, &total);
+  }
+  if (J->out_resmass) J->out_resmass[b] = total;
+  if (draw_margin < margin) margin = draw_margin;
+  set_result(J, b, (int32_t)n, (int32_t)tok, margin);
+}
+
+typedef struct {
+  const job_t* J;
+  int tid;
+} worker_arg_t;
+
+static void* worker(void* arg) {
+  worker_arg_t* A = (worker_arg_t*)arg;
+  const job_t* J = A->J;
+  scratch_t S;
+  size_t bytes = (size_t)J->vocab * sizeof(double);
+  S.z = (double*)malloc(bytes);
+  S.zq = (double*)malloc(bytes);
+  S.p = (double*)malloc(bytes);
+  S.q = (double*)malloc(bytes);
+  S.w = (double*)malloc(bytes);
+  for (int64_t b = A->tid; b < J->batch; b += J->nthreads) verify_sequence(J, b, &S);
+  free(S.z); free(S.zq); free(S.p); free(S.q); free(S.w);
+  return NULL;
+}
+
+/* Packed ragged layout: target rows of sequence b start at
+ * toff[b] = sum_{b' < b} (gamma_b' + 1), draft rows at doff[b] = sum gamma_b'. */
+static int plan_offsets(job_t* J, int64_t* toff, int64_t* doff) {
+  int64_t st = 0, sd = 0;
+  int ok = 1;
+  for (int64_t b = 0; b < J->batch; ++b) {
+    int64_t g = J->gamma[b];
+    if (g < 0 || g > J->max_gamma) ok = 0;
+    toff[b] = st;
+    doff[b] = sd;
+    if (g < 0) g = 0;
+    st += g + 1;
+    sd += g;
+  }
+  if (st != J->total_target_rows || sd != J->total_draft_rows) ok = 0;
+  return ok;
+}
+
+static int run_job(job_t* J) {
+  int64_t* toff = (int64_t*)malloc((size_t)(J->batch + 1) * sizeof(int64_t));
+  int64_t* doff = (int64_t*)malloc((size_t)(J->batch + 1) * sizeof(int64_t));
+  J->layout_ok = plan_offsets(J, toff, doff);
+  J->toff = toff;
+  J->doff = doff;
+  int nt = J->nthreads < 1 ? 1 : J->nthreads;
+  if (nt > J->batch) nt = (int)(J->batch > 0 ? J->batch : 1);
+  J->nthreads = nt;
+  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nt);
+  worker_arg_t* args = (worker_arg_t*)malloc(sizeof(worker_arg_t) * (size_t)nt);
+  for (int t = 0; t < nt; ++t) {
+    args[t].J = J;
+    args[t].tid = t;
+    pthread_create(&th[t], NULL, worker, &args[t]);
+  }
+  for (int t = 0; t < nt; ++t) pthread_join(th[t], NULL);
+  free(th); free(args); free(toff); free(doff);
+  return J->layout_ok ? 0 : 1;
+}
+
+/* Returns 0 when the layout is consistent, 1 when every sequence was given
+ * (-1, -1) because a gamma or a row total was out of range. */
+int oracle_verify(int64_t batch, int64_t vocab, int64_t max_gamma, int dtype,
+                  int64_t total_target_rows, int64_t total_draft_rows, const void* target,
+                  const void* draft, const int32_t* tokens, const int32_t* gamma,
+                  const float* temperature, uint64_t seed, uint64_t row_offset,
+                  const float* inj_r, const float* inj_u, int32_t* out_n, int32_t* out_next,
+                  double* out_margin, uint8_t* out_near, double* out_ratio, double* out_resmass,
+                  int nthreads) {
+  job_t J;
+  memset(&J, 0, sizeof J);
+  J.batch = batch; J.vocab = vocab; J.max_gamma = max_gamma; J.dtype = dtype;
+  J.total_target_rows = total_target_rows; J.total_draft_rows = total_draft_rows;
+  J.target = target; J.draft = draft; J.tokens = tokens; J.gamma = gamma;
+  J.temperature = temperature; J.seed = seed; J.row_offset = row_offset;
+  J.inj_r = inj_r; J.inj_u = inj_u;
+  J.out_n = out_n; J.out_next = out_next; J.out_margin = out_margin; J.out_near = out_near;
+  J.out_ratio = out_ratio; J.out_resmass = out_resmass;
+  J.nthreads = nthreads;
+  return run_job(&J);
+}
+
+/* Per-row statistics of rows [0, rows) of one logit matrix at temperature
+ * T_row[r]: m (max), S (sum exp((z - m)/T), NaN when T_row[r] == 0), the
+ * argmax (lowest index) and a validity flag. */
+void oracle_row_stats(const void* logits, int dtype, int64_t rows, int64_t vocab,
+                      const float* T_row, double* out_m, double* out_s, int32_t* out_arg,
+                      uint8_t* out_valid) {
+  double* z = (double*)malloc((size_t)vocab * sizeof(double));
+  for (int64_t r = 0; r < rows; ++r) {
+    load_row(logits, dtype, vocab, r, z);
+    out_valid[r] = (uint8_t)row_is_valid(z, vocab);
+    out_arg[r] = (int32_t)row_argmax(z, vocab);
+    const double T = (double)T_row[r];
+    if (T > 0.0) {
+      row_softmax(z, vocab, T, &out_m[r], &out_s[r], NULL);
+    } else {
+      double m = -INFINITY;
+      for (int64_t v = 0; v < vocab; ++v)
+        if (z[v] > m) m = z[v];
+      out_m[r] = m;
+      out_s[r] = NAN;
+    }
+  }
+  free(z);
+}
+
+/* Probabilities p_v = exp((z_v - m)/T)/S of one row. */
+void oracle_softmax_row(const void* logits, int dtype, int64_t vocab, int64_t row, float T,
+                        double* out_p) {
+  double* z = (double*)malloc((size_t)vocab * sizeof(double));
+  load_row(logits, dtype, vocab, row, z);
+  row_softmax(z, vocab, (double)T, NULL, NULL, out_p);
+  free(z);
+}
+
+/* Batched Philox blocks: out[4k..4k+4) = Philox4x32-10(seed, ctr[4k..4k+4)). */
+void oracle_philox_blocks(uint64_t seed, const uint32_t* ctr, uint32_t* out, int64_t count) {
+  for (int64_t k = 0; k < count; ++k) oracle_philox4x32_10(seed, ctr + 4 * k, out + 4 * k);
+}
