@@ -1,0 +1,208 @@
+// device.hpp -- wave-level building blocks of libspecverify's kernels (gfx950).
+//
+// Everything here is device code for CDNA4: 64-lane wavefronts, raw v_exp_f32,
+// cross-lane exchange with __shfl_xor / __shfl_up (ds_swizzle / DPP / bpermute,
+// no LDS storage), ballots as 64-bit masks.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace specv {
+
+constexpr int kWave = 64;
+constexpr int kBlock = 256;                     // 4 waves per workgroup
+constexpr int kWavesPerBlock = kBlock / kWave;  // each wave is an independent work item
+
+enum : int { kF32 = 0, kBF16 = 1 };
+
+// Device status word bits (mirrored in the public header).
+constexpr uint32_t kSeqError = 1u;
+constexpr uint32_t kLayoutError = 2u;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float ninf() { return -__builtin_huge_valf(); }
+__device__ __forceinline__ float pinf() { return __builtin_huge_valf(); }
+
+// bf16 is the upper half of an IEEE binary32: widening is exact.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// 2^x on the transcendental unit (v_exp_f32). Results below the smallest
+// normal flush to 0; -inf -> 0; NaN -> NaN.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// log2(e) / T in fp32: exp((z - m) / T) = 2^((z - m) * k). Every kernel that
+// evaluates a softmax at temperature T derives k through this one function.
+__device__ __forceinline__ float temp_scale(float T) {
+  return (float)(1.4426950408889634074 / (double)T);
+}
+
+// Reference point of a row or chunk with maximum m: rk = fl32(m * k), or 0
+// for an all-masked (-inf) span. Terms are 2^(fl32(z k - rk)), so the same
+// rk appears in a row's sum and in every probability taken from it, and its
+// rounding cancels between them.
+__device__ __forceinline__ float ref_point(float m, float k) { return (m == ninf()) ? 0.f : m * k; }
+
+// Factor that moves a sum taken relative to maximum m onto the reference of
+// maximum mn >= m; 0 for an all-masked sum (keeps NaN payloads: NaN * 0).
+__device__ __forceinline__ double rescale64(float m, float mn, float k) {
+  if (m == ninf()) return 0.0;
+  return exp2((double)(m * k) - (double)ref_point(mn, k));
+}
+
+template <int DT>
+__device__ __forceinline__ float load_logit(const void* base, int64_t idx) {
+  if constexpr (DT == kBF16) {
+    const uint16_t h = static_cast<const uint16_t*>(base)[idx];
+    return __uint_as_float((uint32_t)h << 16);
+  } else {
+    return static_cast<const float*>(base)[idx];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Tiles: what one wave reads per loop iteration from a row chunk starting at
+// element e0. Each lane owns NE elements, in increasing index order within
+// the lane and across iterations (the argmax tie rule relies on it).
+//   bf16, vector path: 4 x 16-byte loads per lane = 32 elements; one wave
+//                      instruction covers 1 KiB of contiguous row.
+//   fp32, vector path: 4 x 16-byte loads per lane = 16 elements.
+//   scalar path (rows not 16-byte aligned): 16 strided 2- or 4-byte loads.
+// ---------------------------------------------------------------------------
+template <int DT, bool VEC>
+struct Tile {
+  static constexpr int NE = (VEC && DT == kBF16) ? 32 : 16;
+  static constexpr int EPI = kWave * NE;  // elements per wave iteration
+  static constexpr int VE = (DT == kBF16) ? 8 : 4;  // elements per 16-byte vector
+
+  // Element index of slot j of lane `lane` in iteration `it`.
+  __device__ static __forceinline__ int64_t index(int64_t e0, int it, int lane, int j) {
+    if constexpr (VEC) {
+      const int64_t vec = (int64_t)(it * 4 + j / VE) * kWave + lane;
+      return e0 + vec * VE + (j % VE);
+    } else {
+      return e0 + (int64_t)(it * NE + j) * kWave + lane;
+    }
+  }
+
+  // Load iteration `it`; slots at or past e1 read as -inf when MASK.
+  template <bool MASK>
+  __device__ static __forceinline__ void load(const void* row, int64_t e0, int64_t e1, int it,
+                                              int lane, float (&z)[NE]) {
+    if constexpr (VEC) {
+      const u32x4* p = reinterpret_cast<const u32x4*>(
+          static_cast<const char*>(row) + e0 * (DT == kBF16 ? 2 : 4));
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t vec = (int64_t)(it * 4 + u) * kWave + lane;
+        u32x4 q;
+        if (MASK && e0 + vec * VE >= e1) {
+          constexpr uint32_t kNegInf = (DT == kBF16) ? 0xff80ff80u : 0xff800000u;  // -inf
+          q = u32x4{kNegInf, kNegInf, kNegInf, kNegInf};
+        } else {
+          q = __builtin_nontemporal_load(p + vec);
+        }
+        if constexpr (DT == kBF16) {
+          z[u * 8 + 0] = bf16_lo(q.x); z[u * 8 + 1] = bf16_hi(q.x);
+          z[u * 8 + 2] = bf16_lo(q.y); z[u * 8 + 3] = bf16_hi(q.y);
+          z[u * 8 + 4] = bf16_lo(q.z); z[u * 8 + 5] = bf16_hi(q.z);
+          z[u * 8 + 6] = bf16_lo(q.w); z[u * 8 + 7] = bf16_hi(q.w);
+        } else {
+          z[u * 4 + 0] = __uint_as_float(q.x); z[u * 4 + 1] = __uint_as_float(q.y);
+          z[u * 4 + 2] = __uint_as_float(q.z); z[u * 4 + 3] = __uint_as_float(q.w);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NE; ++j) {
+        const int64_t idx = e0 + (int64_t)(it * NE + j) * kWave + lane;
+        z[j] = (MASK && idx >= e1) ? ninf() : load_logit<DT>(row, idx);
+      }
+    }
+  }
+};
+
+// Pairwise (tree) sum of N floats, N a power of two: fixed order, log2(N)
+// rounding levels.
+template <int N>
+__device__ __forceinline__ float tree_sum(float (&e)[N]) {
+#pragma unroll
+  for (int w = N / 2; w >= 1; w >>= 1) {
+#pragma unroll
+    for (int j = 0; j < w; ++j) e[j] += e[j + w];
+  }
+  return e[0];
+}
+
+template <int N>
+__device__ __forceinline__ float tile_max(const float (&z)[N]) {
+  float g = z[0];
+#pragma unroll
+  for (int j = 1; j < N; ++j) g = fmaxf(g, z[j]);
+  return g;
+}
+
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int off = kWave / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// Inclusive prefix sum across the wave (lane order).
+__device__ __forceinline__ double wave_inclusive_scan(double v, int lane) {
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const double o = __shfl_up(v, off, kWave);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+
+__device__ __forceinline__ int first_lane(uint64_t mask) { return __ffsll((long long)mask) - 1; }
+
+__device__ __forceinline__ int64_t wave_uniform(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds; each round
+// multiplies counter words 0 and 2 by the two Philox multipliers, folds the
+// high halves into words 1 and 3 with the round key, and the key advances by
+// the two Weyl increments after every round.
+// ---------------------------------------------------------------------------
+struct PhiloxBlock {
+  uint32_t w0, w1, w2, w3;
+};
+
+__device__ __forceinline__ PhiloxBlock philox4x32_10(uint64_t seed, uint32_t c0, uint32_t c1,
+                                                     uint32_t c2, uint32_t c3) {
+  constexpr uint32_t kMulA = 0xD2511F53u, kMulB = 0xCD9E8D57u;
+  constexpr uint32_t kWeylA = 0x9E3779B9u, kWeylB = 0xBB67AE85u;
+  uint32_t ka = (uint32_t)seed, kb = (uint32_t)(seed >> 32);
+#pragma unroll
+  for (int round = 0; round < 10; ++round) {
+    const uint32_t hi_a = __umulhi(kMulA, c0), lo_a = kMulA * c0;
+    const uint32_t hi_b = __umulhi(kMulB, c2), lo_b = kMulB * c2;
+    c0 = hi_b ^ c1 ^ ka;
+    c1 = lo_b;
+    c2 = hi_a ^ c3 ^ kb;
+    c3 = lo_a;
+    ka += kWeylA;
+    kb += kWeylB;
+  }
+  return PhiloxBlock{c0, c1, c2, c3};
+}
+
+// 24 random bits -> (0, 1]: ((w >> 8) + 1) * 2^-24, exact in fp32.
+__device__ __forceinline__ float uniform24(uint32_t w) {
+  return (float)((w >> 8) + 1u) * 5.9604644775390625e-08f;
+}
+
+}  // namespace specv

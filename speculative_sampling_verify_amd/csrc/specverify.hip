@@ -1,0 +1,433 @@
+// specverify.hip -- host side of libspecverify: argument checks, workspace
+// carve-up and kernel launches on the caller's stream. The C ABI is declared
+// in include/specverify.h.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "kernels.hpp"
+#include "specverify.h"
+
+using namespace specv;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kK1ChunkBytes = 32768;  // pass-1 work item: 32 KiB of one row
+constexpr int kDrawStep = kBlock * 8; // elements per workgroup scan step of the draw
+constexpr int64_t kTargetMassItems = 2048;  // pass-2 waves to aim for (8 per CU)
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Plan {
+  int dt;
+  int64_t B, V, max_gamma, tt, td;
+  int64_t esz;
+  int chunks1, chunk1_elems;
+  int chunks3, chunk3_elems;
+  size_t off_toff, off_doff, off_tmap, off_dmap, off_tparts, off_dparts, off_sel, off_mass;
+  size_t bytes;
+};
+
+bool shape_ok(const specv_shape_t* s) {
+  if (!s) return false;
+  if (s->batch < 0 || s->vocab < 1 || s->max_gamma < 0 || s->max_gamma > SPECV_MAX_GAMMA) return false;
+  if (s->dtype != SPECV_F32 && s->dtype != SPECV_BF16) return false;
+  if (s->total_draft_rows < 0 || s->total_target_rows < 0) return false;
+  if (s->total_target_rows != s->total_draft_rows + s->batch) return false;
+  if (s->total_draft_rows > (int64_t)s->batch * s->max_gamma) return false;
+  // packed element offsets must fit int64 comfortably
+  if (s->total_target_rows > ((int64_t)1 << 40) / s->vocab) return false;
+  return true;
+}
+
+void make_plan(const specv_shape_t* s, Plan* p) {
+  p->dt = (s->dtype == SPECV_BF16) ? kBF16 : kF32;
+  p->B = s->batch;
+  p->V = s->vocab;
+  p->max_gamma = s->max_gamma;
+  p->tt = s->total_target_rows;
+  p->td = s->total_draft_rows;
+  p->esz = (p->dt == kBF16) ? 2 : 4;
+  // pass 1: 32 KiB chunks (16384 bf16 / 8192 fp32 elements), a multiple of
+  // every tile's elements-per-iteration
+  p->chunk1_elems = (int)(kK1ChunkBytes / p->esz);
+  p->chunks1 = (int)((p->V + p->chunk1_elems - 1) / p->chunk1_elems);
+  // pass 2: enough chunks per sequence to give ~2048 waves in total
+  int64_t c3 = (kTargetMassItems + p->B - 1) / (p->B > 0 ? p->B : 1);
+  const int64_t max_c3 = (p->V + kDrawStep - 1) / kDrawStep;
+  c3 = c3 < 1 ? 1 : (c3 > max_c3 ? max_c3 : c3);
+  int64_t ch3 = (p->V + c3 - 1) / c3;
+  ch3 = (ch3 + kDrawStep - 1) / kDrawStep * kDrawStep;
+  p->chunk3_elems = (int)ch3;
+  p->chunks3 = (int)((p->V + ch3 - 1) / ch3);
+  size_t off = kAlign;  // [0, 256): status word
+  p->off_toff = off; off = align_up(off + (size_t)(p->B + 1) * 8);
+  p->off_doff = off; off = align_up(off + (size_t)(p->B + 1) * 8);
+  p->off_tmap = off; off = align_up(off + (size_t)p->tt * 4);
+  p->off_dmap = off; off = align_up(off + (size_t)p->td * 4);
+  p->off_tparts = off; off = align_up(off + (size_t)p->tt * p->chunks1 * sizeof(RowPart));
+  p->off_dparts = off; off = align_up(off + (size_t)p->td * p->chunks1 * sizeof(RowPart));
+  p->off_sel = off; off = align_up(off + (size_t)p->B * sizeof(Select));
+  p->off_mass = off; off = align_up(off + (size_t)p->B * p->chunks3 * sizeof(double));
+  p->bytes = off;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+struct Call {
+  const specv_shape_t* shape;
+  const void* target;
+  const void* draft;
+  const int32_t* tokens;
+  const int32_t* gamma;
+  const float* temperature;
+  uint64_t seed, row_offset;
+  const float* inj_r;
+  const float* inj_u;
+  int32_t* out_n;
+  int32_t* out_next;
+  void* ws;
+  size_t ws_bytes;
+  hipStream_t stream;
+  hipEvent_t* events;
+};
+
+specv_status_t check_common(const specv_shape_t* shape, const void* target, const void* draft,
+                            const int32_t* gamma, const float* temperature, void* ws,
+                            size_t ws_bytes, Plan* p) {
+  if (!shape_ok(shape)) return SPECV_ERR_INVALID_ARGUMENT;
+  make_plan(shape, p);
+  if (p->B == 0) return SPECV_OK;
+  if (!gamma || !temperature) return SPECV_ERR_INVALID_ARGUMENT;
+  if (!target) return SPECV_ERR_INVALID_ARGUMENT;
+  if (p->td > 0 && !draft) return SPECV_ERR_INVALID_ARGUMENT;
+  if (!aligned(target, (size_t)p->esz) || (draft && !aligned(draft, (size_t)p->esz)))
+    return SPECV_ERR_INVALID_ARGUMENT;
+  if (!ws || ws_bytes < p->bytes || !aligned(ws, kAlign)) return SPECV_ERR_WORKSPACE;
+  return SPECV_OK;
+}
+
+bool vector_path(const Plan& p, const void* target, const void* draft) {
+  return (p.V * p.esz) % 16 == 0 && aligned(target, 16) && (!draft || aligned(draft, 16));
+}
+
+inline specv_status_t launched() {
+  return hipGetLastError() == hipSuccess ? SPECV_OK : SPECV_ERR_HIP;
+}
+
+inline void mark(hipEvent_t* ev, int idx, hipStream_t s) {
+  if (ev) (void)hipEventRecord(ev[idx], s);
+}
+
+inline unsigned blocks_for(int64_t waves) {
+  return (unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock);
+}
+
+specv_status_t launch_plan(const Plan& p, const int32_t* gamma, void* ws, hipStream_t st) {
+  PlanArgs a;
+  a.gamma = gamma;
+  a.toff = at<int64_t>(ws, p.off_toff);
+  a.doff = at<int64_t>(ws, p.off_doff);
+  a.tmap = at<int32_t>(ws, p.off_tmap);
+  a.dmap = at<int32_t>(ws, p.off_dmap);
+  a.status = at<uint32_t>(ws, 0);
+  a.total_t = p.tt;
+  a.total_d = p.td;
+  a.B = (int32_t)p.B;
+  a.max_gamma = (int32_t)p.max_gamma;
+  hipLaunchKernelGGL(k0_plan, dim3(1), dim3(1024), 0, st, a);
+  return launched();
+}
+
+specv_status_t launch_row_stats(const Plan& p, bool vec, const void* target, const void* draft,
+                                const float* temperature, void* ws, hipStream_t st) {
+  RowStatsArgs a;
+  a.target = target;
+  a.draft = draft;
+  a.temperature = temperature;
+  a.tmap = at<int32_t>(ws, p.off_tmap);
+  a.dmap = at<int32_t>(ws, p.off_dmap);
+  a.tparts = at<RowPart>(ws, p.off_tparts);
+  a.dparts = at<RowPart>(ws, p.off_dparts);
+  a.status = at<uint32_t>(ws, 0);
+  a.total_t = p.tt;
+  a.total_d = p.td;
+  a.V = p.V;
+  a.B = (int32_t)p.B;
+  a.chunks = p.chunks1;
+  a.chunk_elems = p.chunk1_elems;
+  const int64_t waves = (p.tt + p.td) * p.chunks1;
+  if (waves == 0) return SPECV_OK;
+  const dim3 grid(blocks_for(waves)), block(kBlock);
+  if (p.dt == kBF16) {
+    if (vec) hipLaunchKernelGGL((k1_row_stats<kBF16, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k1_row_stats<kBF16, false>), grid, block, 0, st, a);
+  } else {
+    if (vec) hipLaunchKernelGGL((k1_row_stats<kF32, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k1_row_stats<kF32, false>), grid, block, 0, st, a);
+  }
+  return launched();
+}
+
+specv_status_t launch_accept(const Plan& p, const Call& c) {
+  AcceptArgs a;
+  a.target = c.target;
+  a.draft = c.draft;
+  a.tokens = c.tokens;
+  a.gamma = c.gamma;
+  a.temperature = c.temperature;
+  a.toff = at<int64_t>(c.ws, p.off_toff);
+  a.doff = at<int64_t>(c.ws, p.off_doff);
+  a.tparts = at<RowPart>(c.ws, p.off_tparts);
+  a.dparts = at<RowPart>(c.ws, p.off_dparts);
+  a.status = at<uint32_t>(c.ws, 0);
+  a.sel = at<Select>(c.ws, p.off_sel);
+  a.out_n = c.out_n;
+  a.out_next = c.out_next;
+  a.inj_r = c.inj_r;
+  a.inj_u = c.inj_u;
+  a.seed = c.seed;
+  a.row_offset = c.row_offset;
+  a.V = p.V;
+  a.B = (int32_t)p.B;
+  a.max_gamma = (int32_t)p.max_gamma;
+  a.chunks = p.chunks1;
+  const dim3 grid(blocks_for(p.B)), block(kBlock);
+  if (p.dt == kBF16) hipLaunchKernelGGL((k2_accept<kBF16>), grid, block, 0, c.stream, a);
+  else hipLaunchKernelGGL((k2_accept<kF32>), grid, block, 0, c.stream, a);
+  return launched();
+}
+
+DrawArgs draw_args(const Plan& p, const Call& c) {
+  DrawArgs a;
+  a.target = c.target;
+  a.draft = c.draft;
+  a.sel = at<Select>(c.ws, p.off_sel);
+  a.mass = at<double>(c.ws, p.off_mass);
+  a.out_next = c.out_next;
+  a.V = p.V;
+  a.B = (int32_t)p.B;
+  a.chunks3 = p.chunks3;
+  a.chunk3_elems = p.chunk3_elems;
+  return a;
+}
+
+specv_status_t launch_mass(const Plan& p, bool vec, const Call& c) {
+  const DrawArgs a = draw_args(p, c);
+  const dim3 grid(blocks_for(p.B * p.chunks3)), block(kBlock);
+  if (p.dt == kBF16) {
+    if (vec) hipLaunchKernelGGL((k3_mass<kBF16, true>), grid, block, 0, c.stream, a);
+    else hipLaunchKernelGGL((k3_mass<kBF16, false>), grid, block, 0, c.stream, a);
+  } else {
+    if (vec) hipLaunchKernelGGL((k3_mass<kF32, true>), grid, block, 0, c.stream, a);
+    else hipLaunchKernelGGL((k3_mass<kF32, false>), grid, block, 0, c.stream, a);
+  }
+  return launched();
+}
+
+specv_status_t launch_draw(const Plan& p, const Call& c) {
+  const DrawArgs a = draw_args(p, c);
+  const dim3 grid((unsigned)p.B), block(kBlock);
+  if (p.dt == kBF16) hipLaunchKernelGGL((k3_draw<kBF16>), grid, block, 0, c.stream, a);
+  else hipLaunchKernelGGL((k3_draw<kF32>), grid, block, 0, c.stream, a);
+  return launched();
+}
+
+specv_status_t run(const Call& c) {
+  Plan p;
+  specv_status_t st = check_common(c.shape, c.target, c.draft, c.gamma, c.temperature, c.ws,
+                                   c.ws_bytes, &p);
+  if (st != SPECV_OK || p.B == 0) return st;
+  if (!c.out_n || !c.out_next) return SPECV_ERR_INVALID_ARGUMENT;
+  if (p.td > 0 && !c.tokens) return SPECV_ERR_INVALID_ARGUMENT;
+  if ((c.inj_r == nullptr) != (c.inj_u == nullptr)) return SPECV_ERR_INVALID_ARGUMENT;
+  const bool vec = vector_path(p, c.target, c.draft);
+  mark(c.events, 2 * SPECV_STAGE_PLAN, c.stream);
+  if ((st = launch_plan(p, c.gamma, c.ws, c.stream)) != SPECV_OK) return st;
+  mark(c.events, 2 * SPECV_STAGE_PLAN + 1, c.stream);
+  mark(c.events, 2 * SPECV_STAGE_ROWSTATS, c.stream);
+  if ((st = launch_row_stats(p, vec, c.target, c.draft, c.temperature, c.ws, c.stream)) != SPECV_OK)
+    return st;
+  mark(c.events, 2 * SPECV_STAGE_ROWSTATS + 1, c.stream);
+  mark(c.events, 2 * SPECV_STAGE_ACCEPT, c.stream);
+  if ((st = launch_accept(p, c)) != SPECV_OK) return st;
+  mark(c.events, 2 * SPECV_STAGE_ACCEPT + 1, c.stream);
+  mark(c.events, 2 * SPECV_STAGE_RESIDUAL, c.stream);
+  if ((st = launch_mass(p, vec, c)) != SPECV_OK) return st;
+  mark(c.events, 2 * SPECV_STAGE_RESIDUAL + 1, c.stream);
+  mark(c.events, 2 * SPECV_STAGE_DRAW, c.stream);
+  if ((st = launch_draw(p, c)) != SPECV_OK) return st;
+  mark(c.events, 2 * SPECV_STAGE_DRAW + 1, c.stream);
+  return SPECV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t specv_workspace_bytes(const specv_shape_t* shape) {
+  if (!shape_ok(shape)) return 0;
+  Plan p;
+  make_plan(shape, &p);
+  return p.bytes;
+}
+
+specv_status_t specv_verify(const specv_shape_t* shape, const void* target_logits,
+                            const void* draft_logits, const int32_t* draft_tokens,
+                            const int32_t* gamma_per_row, const float* temperature,
+                            uint64_t seed, uint64_t philox_row_offset,
+                            int32_t* out_n_accepted, int32_t* out_next_token,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Call c{shape, target_logits, draft_logits, draft_tokens, gamma_per_row, temperature,
+         seed, philox_row_offset, nullptr, nullptr, out_n_accepted, out_next_token,
+         workspace, workspace_bytes, stream, nullptr};
+  return run(c);
+}
+
+specv_status_t specv_verify_profiled(const specv_shape_t* shape, const void* target_logits,
+                                     const void* draft_logits, const int32_t* draft_tokens,
+                                     const int32_t* gamma_per_row, const float* temperature,
+                                     uint64_t seed, uint64_t philox_row_offset,
+                                     int32_t* out_n_accepted, int32_t* out_next_token,
+                                     void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream, hipEvent_t* events) {
+  Call c{shape, target_logits, draft_logits, draft_tokens, gamma_per_row, temperature,
+         seed, philox_row_offset, nullptr, nullptr, out_n_accepted, out_next_token,
+         workspace, workspace_bytes, stream, events};
+  return run(c);
+}
+
+specv_status_t specv_verify_with_uniforms(const specv_shape_t* shape, const void* target_logits,
+                                          const void* draft_logits, const int32_t* draft_tokens,
+                                          const int32_t* gamma_per_row, const float* temperature,
+                                          const float* r, const float* u,
+                                          int32_t* out_n_accepted, int32_t* out_next_token,
+                                          void* workspace, size_t workspace_bytes,
+                                          hipStream_t stream) {
+  if (!u || (!r && shape && shape->max_gamma > 0 && shape->batch > 0))
+    return SPECV_ERR_INVALID_ARGUMENT;
+  // with max_gamma == 0 there are no r entries; any non-null pointer will do
+  Call c{shape, target_logits, draft_logits, draft_tokens, gamma_per_row, temperature,
+         0, 0, r ? r : u, u, out_n_accepted, out_next_token,
+         workspace, workspace_bytes, stream, nullptr};
+  return run(c);
+}
+
+specv_status_t specv_row_stats(const specv_shape_t* shape, const void* target_logits,
+                               const void* draft_logits, const int32_t* gamma_per_row,
+                               const float* temperature, float* out_target_max,
+                               double* out_target_sum, int32_t* out_target_argmax,
+                               float* out_draft_max, double* out_draft_sum,
+                               int32_t* out_draft_argmax, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  Plan p;
+  specv_status_t st = check_common(shape, target_logits, draft_logits, gamma_per_row, temperature,
+                                   workspace, workspace_bytes, &p);
+  if (st != SPECV_OK || p.B == 0) return st;
+  if (!out_target_max || !out_target_sum || !out_target_argmax) return SPECV_ERR_INVALID_ARGUMENT;
+  if (p.td > 0 && (!out_draft_max || !out_draft_sum || !out_draft_argmax))
+    return SPECV_ERR_INVALID_ARGUMENT;
+  const bool vec = vector_path(p, target_logits, draft_logits);
+  if ((st = launch_plan(p, gamma_per_row, workspace, stream)) != SPECV_OK) return st;
+  if ((st = launch_row_stats(p, vec, target_logits, draft_logits, temperature, workspace, stream)) !=
+      SPECV_OK)
+    return st;
+  MergeArgs a;
+  a.tparts = at<RowPart>(workspace, p.off_tparts);
+  a.dparts = at<RowPart>(workspace, p.off_dparts);
+  a.tmap = at<int32_t>(workspace, p.off_tmap);
+  a.dmap = at<int32_t>(workspace, p.off_dmap);
+  a.temperature = temperature;
+  a.status = at<uint32_t>(workspace, 0);
+  a.out_tm = out_target_max;
+  a.out_ts = out_target_sum;
+  a.out_ta = out_target_argmax;
+  a.out_dm = out_draft_max;
+  a.out_ds = out_draft_sum;
+  a.out_da = out_draft_argmax;
+  a.total_t = p.tt;
+  a.total_d = p.td;
+  a.B = (int32_t)p.B;
+  a.chunks = p.chunks1;
+  const int64_t rows = p.tt + p.td;
+  hipLaunchKernelGGL(k_merge_rows, dim3((unsigned)((rows + kBlock - 1) / kBlock)), dim3(kBlock), 0,
+                     stream, a);
+  return launched();
+}
+
+specv_status_t specv_softmax_rows(const specv_shape_t* shape, const void* target_logits,
+                                  const void* draft_logits, const int32_t* gamma_per_row,
+                                  const float* temperature, const int64_t* rows, int64_t n_rows,
+                                  float* out_probs, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+  Plan p;
+  specv_status_t st = check_common(shape, target_logits, draft_logits, gamma_per_row, temperature,
+                                   workspace, workspace_bytes, &p);
+  if (st != SPECV_OK || p.B == 0 || n_rows == 0) return st;
+  if (n_rows < 0 || n_rows > 65535 || !rows || !out_probs) return SPECV_ERR_INVALID_ARGUMENT;
+  const bool vec = vector_path(p, target_logits, draft_logits);
+  if ((st = launch_plan(p, gamma_per_row, workspace, stream)) != SPECV_OK) return st;
+  if ((st = launch_row_stats(p, vec, target_logits, draft_logits, temperature, workspace, stream)) !=
+      SPECV_OK)
+    return st;
+  ProbArgs a;
+  a.target = target_logits;
+  a.draft = draft_logits;
+  a.tparts = at<RowPart>(workspace, p.off_tparts);
+  a.dparts = at<RowPart>(workspace, p.off_dparts);
+  a.tmap = at<int32_t>(workspace, p.off_tmap);
+  a.dmap = at<int32_t>(workspace, p.off_dmap);
+  a.temperature = temperature;
+  a.rows = rows;
+  a.out = out_probs;
+  a.V = p.V;
+  a.n_rows = n_rows;
+  a.total_t = p.tt;
+  a.total_d = p.td;
+  a.B = (int32_t)p.B;
+  a.chunks = p.chunks1;
+  const dim3 grid((unsigned)((p.V + 2047) / 2048), (unsigned)n_rows);
+  if (p.dt == kBF16) hipLaunchKernelGGL((k_softmax_rows<kBF16>), grid, dim3(kBlock), 0, stream, a);
+  else hipLaunchKernelGGL((k_softmax_rows<kF32>), grid, dim3(kBlock), 0, stream, a);
+  return launched();
+}
+
+specv_status_t specv_philox4x32_10(uint64_t seed, const uint32_t* ctr, uint32_t* out, int64_t n,
+                                   hipStream_t stream) {
+  if (n < 0 || (n > 0 && (!ctr || !out))) return SPECV_ERR_INVALID_ARGUMENT;
+  if (n == 0) return SPECV_OK;
+  hipLaunchKernelGGL(k_philox, dim3((unsigned)((n + kBlock - 1) / kBlock)), dim3(kBlock), 0, stream,
+                     seed, ctr, out, n);
+  return launched();
+}
+
+specv_status_t specv_copy_bytes(void* dst, const void* src, size_t bytes, hipStream_t stream) {
+  if (bytes == 0) return SPECV_OK;
+  if (!dst || !src || bytes % 16 != 0 || !aligned(dst, 16) || !aligned(src, 16))
+    return SPECV_ERR_INVALID_ARGUMENT;
+  const int64_t n16 = (int64_t)(bytes / 16);
+  int64_t blocks = (n16 + kBlock - 1) / kBlock;
+  if (blocks > 256 * 64) blocks = 256 * 64;
+  hipLaunchKernelGGL(k_copy, dim3((unsigned)blocks), dim3(kBlock), 0, stream,
+                     static_cast<u32x4*>(dst), static_cast<const u32x4*>(src), n16);
+  return launched();
+}
+
+const char* specv_status_string(specv_status_t status) {
+  switch (status) {
+    case SPECV_OK: return "ok";
+    case SPECV_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case SPECV_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case SPECV_ERR_HIP: return "HIP launch failed";
+    case SPECV_ERR_UNSUPPORTED: return "unsupported";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"
