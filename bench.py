@@ -1,0 +1,243 @@
+"""Benchmark of the speculative-sampling verify step on one MI355X.
+
+One step = one specv_verify call (all stages: plan, pass-1 row statistics,
+accept, residual mass, draw) over one batch of synthetic input already
+resident in HBM. Default workload: the T5-XXL-like setting (gamma = 5,
+V = 32128, bf16 logits, T = 1) with 2,000 rounds batched as independent
+sequences into one call. Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                  [--no-cpu-baseline] [--copy-calibration BYTES]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+import numpy as np
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+METRIC = "verified (gamma+1)xV rows/sec and achieved HBM GB/s vs MI355X peak, 1 GPU"
+HBM_PEAK_GBPS = 8000.0
+MALL_BYTES = 256 << 20
+WORKLOADS = {
+    # name: (generator kwargs, description)
+    "t5xxl_like": (dict(rounds=2000), "T5-XXL-like: 2000 rounds x (gamma=5, V=32128, bf16), T=1"),
+    "t5xxl_like_greedy": (dict(rounds=2000, greedy=True),
+                          "T5-XXL-like greedy: 2000 rounds x (gamma=5, V=32128, bf16), T=0"),
+    "serving_b64": (dict(), "batched serving: B=64, gamma=7, V=128256, bf16, T=0.7"),
+    "ragged_b256": (dict(), "ragged lookahead: B=256, gamma_b~U{1..16}, V=152064, bf16, T=1"),
+    "large_vocab": (dict(), "large vocab: B=128, gamma=8, V=256000, fp32, odd rows greedy"),
+}
+KERNEL_SOURCES = ["speculative_sampling_verify_amd/csrc/kernels.hpp",
+                  "speculative_sampling_verify_amd/csrc/device.hpp",
+                  "speculative_sampling_verify_amd/csrc/specverify.hip"]
+
+
+def kernel_sha() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update((ROOT / f).read_bytes())
+    return h.hexdigest()[:16]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def make_inputs(name):
+    import synth
+    base = name[:-7] if name.endswith("_greedy") else name
+    kw, desc = WORKLOADS[name]
+    return getattr(synth, base)(**kw), desc
+
+
+def cpu_baseline(x, gpu_n, gpu_next, budget_s=12.0):
+    """The oracle as it stands, on the host's cores, over repeated passes of
+    the same step's sequences (bounded by a time budget)."""
+    import oracle
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    passes, res = 0, None
+    while True:
+        res = oracle.verify(x.target, x.draft, x.tokens, x.gamma, x.temperature, vocab=x.vocab,
+                            max_gamma=x.max_gamma, seed=x.seed, row_offset=x.row_offset,
+                            nthreads=threads)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or el / passes * (passes + 1) > 2.5 * budget_s:
+            break
+    rows = passes * x.total_target_rows
+    mism = (gpu_n != res.n) | (gpu_next != res.next_token)
+    return {"value": rows / el, "unit": "verified target rows/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "%d pass(es) over the step's %d sequences (%d target rows each pass), %.1f s"
+                      % (passes, x.batch, x.total_target_rows, el),
+            "parity_vs_gpu": {"sequences": int(x.batch), "mismatches": int(mism.sum()),
+                              "unexplained": int((mism & ~res.near_tie).sum()),
+                              "near_ties": int(res.near_tie.sum())}}
+
+
+def load_traffic(workload, sha):
+    f = ROOT / "profiles" / ("traffic_%s.json" % workload)
+    if not f.exists():
+        return None
+    rec = json.loads(f.read_text())
+    if rec.get("kernel_sha") != sha:
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="t5xxl_like", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0,
+                    help="run only a plain device copy of this many bytes (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the verify step is built and timed on a single "
+              "MI355X; --gpus %d is not supported." % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import speculative_sampling_verify_amd as svx
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.copy_calibration:
+        n = args.copy_calibration // 16 * 16
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(max(1, args.steps)):
+            svx.specv_copy_bytes(dst, src)
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(10):
+            svx.specv_copy_bytes(dst, src)
+        e.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / 10
+        print(json.dumps({"copy_bytes": n, "ms": ms, "gbps": 2 * n / ms / 1e6}))
+        return
+
+    t_gen = time.perf_counter()
+    x, desc = make_inputs(args.workload)
+    log("[bench] generated %s in %.1f s (B=%d, target rows=%d, draft rows=%d)"
+        % (args.workload, time.perf_counter() - t_gen, x.batch, x.total_target_rows,
+           x.total_draft_rows))
+    base = svx.from_inputs(x, dev)
+    set_bytes = sum(t.numel() * t.element_size() for t in (base["target"], base["draft"]))
+    # distinct copies so that the bytes read between reuses of one set exceed
+    # the 256 MB memory-attached last-level cache several times over
+    n_sets = max(2, int(np.ceil(4 * MALL_BYTES / max(1, set_bytes))))
+    sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(n_sets - 1)]
+    shape = svx._shape_of(base["target"], base["draft"], base["gamma"], x.max_gamma)
+    ws = svx.workspace_for(shape, dev)
+    out_n = torch.empty(x.batch, dtype=torch.int32, device=dev)
+    out_next = torch.empty(x.batch, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, events=None):
+        s = sets[i % n_sets]
+        if events is None:
+            svx.specv_verify(s["target"], s["draft"], s["draft_tokens"], s["gamma"],
+                             s["temperature"], max_gamma=x.max_gamma, seed=x.seed,
+                             philox_row_offset=x.row_offset, out_n=out_n, out_next=out_next,
+                             workspace=ws, stream=stream)
+        else:
+            svx.specv_verify_profiled(s["target"], s["draft"], s["draft_tokens"], s["gamma"],
+                                      s["temperature"], events, max_gamma=x.max_gamma,
+                                      seed=x.seed, philox_row_offset=x.row_offset, out_n=out_n,
+                                      out_next=out_next, workspace=ws, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # Timed region: K steps. The library records one HIP event pair around
+    # its pass-1 kernel (k1_row_stats) in every step, on the stream it
+    # launches on; everything else runs uninstrumented.
+    K = args.steps
+    k1_stage = svx.STAGES.index("row_stats")
+    k1_events = [svx.StageEvents(stages=(k1_stage,)) for _ in range(K)]
+    t_start, t_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(K):
+        step(i, k1_events[i])
+    t_stop.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_stop) / K
+    k1_ms = float(np.mean([ev.elapsed_ms(k1_stage) for ev in k1_events]))
+
+    # Diagnostics outside the timed region: the same steps with no events at
+    # all, and with an event pair around every stage.
+    t_start.record(stream)
+    for i in range(K):
+        step(i)
+    t_stop.record(stream)
+    torch.cuda.synchronize()
+    ms_step_plain = t_start.elapsed_time(t_stop) / K
+    all_events = [svx.StageEvents() for _ in range(K)]
+    for i in range(K):
+        step(i, all_events[i])
+    torch.cuda.synchronize()
+    stage_ms = {name: float(np.mean([ev.elapsed_ms(si) for ev in all_events]))
+                for si, name in enumerate(svx.STAGES)}
+
+    n_host = out_n.cpu().numpy()
+    next_host = out_next.cpu().numpy()
+    pass1 = x.pass1_bytes()
+    rows_per_step = x.total_target_rows
+    emitted = int(np.sum(n_host[n_host >= 0] + 1))
+    achieved = pass1 / (k1_ms * 1e-3) / 1e9
+    sha = kernel_sha()
+    result = {
+        "metric": METRIC,
+        "value": rows_per_step / (ms_step * 1e-3),
+        "unit": "verified target rows/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": desc, "batch": x.batch, "gamma": int(x.gamma.max()),
+                   "vocab": x.vocab, "logits": x.dtype,
+                   "temperature": sorted(set(float(t) for t in x.temperature))},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": load_traffic(args.workload, sha),
+                     "kernel": "k1_row_stats", "algorithmic_bytes_per_launch": pass1,
+                     "avg_launch_ms": k1_ms},
+        "step_gbps": pass1 / (ms_step * 1e-3) / 1e9,
+        "step_frac_of_peak": pass1 / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "ms_per_step_uninstrumented": ms_step_plain,
+        "stage_ms_instrumented": stage_ms,
+        "emitted_tokens_per_s": emitted / (ms_step * 1e-3),
+        "sequences_per_s": x.batch / (ms_step * 1e-3),
+        "rotating_input_sets": n_sets,
+        "kernel_sha": sha,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on the host")
+        result["cpu_baseline"] = cpu_baseline(x, n_host, next_host)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

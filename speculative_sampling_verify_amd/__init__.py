@@ -250,12 +250,13 @@ def specv_copy_bytes(dst, src, stream=None):
 
 
 class StageEvents:
-    """2 * len(STAGES) HIP events for specv_verify_profiled (created through
-    the HIP runtime so they live on the stream the library launches on)."""
+    """2 * len(STAGES) HIP event slots for specv_verify_profiled (created
+    through the HIP runtime). Only the stages listed get events; the other
+    slots stay NULL and are not recorded."""
 
     _hip = None
 
-    def __init__(self):
+    def __init__(self, stages=None):
         if StageEvents._hip is None:
             h = ctypes.CDLL("libamdhip64.so")
             h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
@@ -266,7 +267,8 @@ class StageEvents:
             StageEvents._hip = h
         n = 2 * len(STAGES)
         self.array = (ctypes.c_void_p * n)()
-        for i in range(n):
+        wanted = range(len(STAGES)) if stages is None else stages
+        for i in [2 * st + h for st in wanted for h in (0, 1)]:
             ev = ctypes.c_void_p()
             if StageEvents._hip.hipEventCreate(ctypes.byref(ev)) != 0:
                 raise SpecvError("hipEventCreate failed")

@@ -71,12 +71,19 @@ __device__ __forceinline__ float load_logit(const void* base, int64_t idx) {
 //                      instruction covers 1 KiB of contiguous row.
 //   fp32, vector path: 4 x 16-byte loads per lane = 16 elements.
 //   scalar path (rows not 16-byte aligned): 16 strided 2- or 4-byte loads.
+// A tile is loaded raw (RD dwords per lane) and widened to fp32 separately,
+// so a kernel can issue the next tile's loads before it works on this one.
 // ---------------------------------------------------------------------------
 template <int DT, bool VEC>
 struct Tile {
   static constexpr int NE = (VEC && DT == kBF16) ? 32 : 16;
   static constexpr int EPI = kWave * NE;  // elements per wave iteration
   static constexpr int VE = (DT == kBF16) ? 8 : 4;  // elements per 16-byte vector
+  static constexpr int RD = VEC ? 16 : NE;           // raw dwords per lane
+
+  struct Raw {
+    uint32_t d[RD];
+  };
 
   // Element index of slot j of lane `lane` in iteration `it`.
   __device__ static __forceinline__ int64_t index(int64_t e0, int it, int lane, int j) {
@@ -88,40 +95,65 @@ struct Tile {
     }
   }
 
-  // Load iteration `it`; slots at or past e1 read as -inf when MASK.
+  // Raw load of iteration `it`; slots at or past e1 read as -inf when MASK.
   template <bool MASK>
-  __device__ static __forceinline__ void load(const void* row, int64_t e0, int64_t e1, int it,
-                                              int lane, float (&z)[NE]) {
+  __device__ static __forceinline__ void load_raw(const void* row, int64_t e0, int64_t e1, int it,
+                                                  int lane, Raw& r) {
     if constexpr (VEC) {
       const u32x4* p = reinterpret_cast<const u32x4*>(
           static_cast<const char*>(row) + e0 * (DT == kBF16 ? 2 : 4));
+      constexpr uint32_t kNegInf = (DT == kBF16) ? 0xff80ff80u : 0xff800000u;  // -inf
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int64_t vec = (int64_t)(it * 4 + u) * kWave + lane;
         u32x4 q;
-        if (MASK && e0 + vec * VE >= e1) {
-          constexpr uint32_t kNegInf = (DT == kBF16) ? 0xff80ff80u : 0xff800000u;  // -inf
+        if (MASK && e0 + vec * VE >= e1)
           q = u32x4{kNegInf, kNegInf, kNegInf, kNegInf};
-        } else {
+        else
           q = __builtin_nontemporal_load(p + vec);
-        }
-        if constexpr (DT == kBF16) {
-          z[u * 8 + 0] = bf16_lo(q.x); z[u * 8 + 1] = bf16_hi(q.x);
-          z[u * 8 + 2] = bf16_lo(q.y); z[u * 8 + 3] = bf16_hi(q.y);
-          z[u * 8 + 4] = bf16_lo(q.z); z[u * 8 + 5] = bf16_hi(q.z);
-          z[u * 8 + 6] = bf16_lo(q.w); z[u * 8 + 7] = bf16_hi(q.w);
-        } else {
-          z[u * 4 + 0] = __uint_as_float(q.x); z[u * 4 + 1] = __uint_as_float(q.y);
-          z[u * 4 + 2] = __uint_as_float(q.z); z[u * 4 + 3] = __uint_as_float(q.w);
-        }
+        r.d[4 * u + 0] = q.x; r.d[4 * u + 1] = q.y; r.d[4 * u + 2] = q.z; r.d[4 * u + 3] = q.w;
       }
     } else {
 #pragma unroll
       for (int j = 0; j < NE; ++j) {
         const int64_t idx = e0 + (int64_t)(it * NE + j) * kWave + lane;
-        z[j] = (MASK && idx >= e1) ? ninf() : load_logit<DT>(row, idx);
+        float v;
+        if (MASK && idx >= e1)
+          v = ninf();
+        else if constexpr (DT == kBF16)
+          v = __uint_as_float((uint32_t)__builtin_nontemporal_load(static_cast<const uint16_t*>(row) + idx) << 16);
+        else
+          v = __builtin_nontemporal_load(static_cast<const float*>(row) + idx);
+        r.d[j] = __float_as_uint(v);
       }
     }
+  }
+
+  __device__ static __forceinline__ void load_raw(const void* row, int64_t e0, int64_t e1, int it,
+                                                  int n_full, int lane, Raw& r) {
+    if (it < n_full) load_raw<false>(row, e0, e1, it, lane, r);
+    else load_raw<true>(row, e0, e1, it, lane, r);
+  }
+
+  __device__ static __forceinline__ void widen(const Raw& r, float (&z)[NE]) {
+    if constexpr (VEC && DT == kBF16) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        z[2 * q] = bf16_lo(r.d[q]);
+        z[2 * q + 1] = bf16_hi(r.d[q]);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < NE; ++q) z[q] = __uint_as_float(r.d[q]);
+    }
+  }
+
+  template <bool MASK>
+  __device__ static __forceinline__ void load(const void* row, int64_t e0, int64_t e1, int it,
+                                              int lane, float (&z)[NE]) {
+    Raw r;
+    load_raw<MASK>(row, e0, e1, it, lane, r);
+    widen(r, z);
   }
 };
 
@@ -143,6 +175,18 @@ __device__ __forceinline__ float tile_max(const float (&z)[N]) {
 #pragma unroll
   for (int j = 1; j < N; ++j) g = fmaxf(g, z[j]);
   return g;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = kWave / 2; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+__device__ __forceinline__ int wave_min(int v) {
+#pragma unroll
+  for (int off = kWave / 2; off >= 1; off >>= 1) v = min(v, __shfl_xor(v, off, kWave));
+  return v;
 }
 
 __device__ __forceinline__ double wave_sum(double v) {

@@ -45,18 +45,23 @@ struct Select {
   double u;
 };
 
+// Per-row temperature scale written by k0_plan: k = log2(e)/T_b > 0 for a
+// sampling sequence, 0 for a greedy one, -1 for an invalid temperature.
 struct PlanArgs {
   const int32_t* gamma;
+  const float* temperature;
   int64_t* toff;
   int64_t* doff;
-  int32_t* tmap;
-  int32_t* dmap;
+  float* tk;
+  float* dk;
   uint32_t* status;
   int64_t total_t, total_d;
   int32_t B, max_gamma;
 };
 
 // One workgroup of 1024 threads: thread t owns a contiguous run of sequences.
+// Writes the packed row offsets, the per-row temperature scale, and the
+// status word (layout error or 0).
 __global__ __launch_bounds__(1024) void k0_plan(PlanArgs a) {
   __shared__ int64_t sh_t[16], sh_d[16];
   __shared__ int sh_bad[16];
@@ -102,9 +107,11 @@ __global__ __launch_bounds__(1024) void k0_plan(PlanArgs a) {
     const int64_t gg = g < 0 ? 0 : g;
     a.toff[b] = t;
     a.doff[b] = d;
+    const float T = a.temperature[b];
+    const float kk = (T > 0.f && T < pinf()) ? temp_scale(T) : (T == 0.f ? 0.f : -1.f);
     const int64_t tend = min(t + gg + 1, a.total_t), dend = min(d + gg, a.total_d);
-    for (int64_t j = t; j < tend; ++j) a.tmap[j] = b;
-    for (int64_t j = d; j < dend; ++j) a.dmap[j] = b;
+    for (int64_t j = t; j < tend; ++j) a.tk[j] = kk;
+    for (int64_t j = d; j < dend; ++j) a.dk[j] = kk;
     t += gg + 1;
     d += gg;
   }
@@ -117,9 +124,8 @@ __global__ __launch_bounds__(1024) void k0_plan(PlanArgs a) {
 struct RowStatsArgs {
   const void* target;
   const void* draft;
-  const float* temperature;
-  const int32_t* tmap;
-  const int32_t* dmap;
+  const float* tk;
+  const float* dk;
   RowPart* tparts;
   RowPart* dparts;
   const uint32_t* status;
@@ -127,133 +133,118 @@ struct RowStatsArgs {
   int32_t B, chunks, chunk_elems;
 };
 
-// Online (max, sum) over one chunk for a sampling row. Per element: widen,
-// max, one fma and one v_exp_f32 into a pairwise sum; the running sum is
-// float64 and is rescaled only when the lane's maximum grows.
-template <int DT, bool VEC>
-__device__ __forceinline__ RowPart chunk_stats_sampling(const void* row, int64_t e0, int64_t e1,
-                                                        float k, int lane) {
+// Pass-1 loop over one (row, chunk), double-buffered: the loads of tile it+1
+// are in flight while tile it is processed. `a` holds tile 0 on entry (the
+// caller issues it before its metadata lookups).
+//
+// Sampling rows: online (max, sum). Per element: widen, max (v_max3), one fma
+// and one v_exp_f32 into a pairwise sum; the per-lane running sum is float64,
+// rescaled only when the lane's maximum grows. Greedy rows: max, argmax and
+// a NaN/+inf check only. For the argmax (greedy rows, or WITH_ARG) a lane
+// remembers the tile where its maximum last grew and re-reads that one tile
+// at the end.
+template <int DT, bool VEC, bool SAMPLING, bool WITH_ARG>
+__device__ __forceinline__ RowPart chunk_pass(const void* row, int64_t e0, int64_t e1, int n_full,
+                                              int n_iter, float k, int lane,
+                                              typename Tile<DT, VEC>::Raw& a) {
   using TL = Tile<DT, VEC>;
+  using Raw = typename TL::Raw;
   constexpr int NE = TL::NE;
-  const int64_t n = e1 - e0;
-  const int n_full = (int)(n / TL::EPI), n_iter = (int)((n + TL::EPI - 1) / TL::EPI);
+  constexpr bool ARG = WITH_ARG || !SAMPLING;
   float m = ninf(), rk = 0.f;
   double s = 0.0;
-  int best = -1;
-  float z[NE];
-  auto step = [&](int it) {
-    const float g = tile_max(z);
-    if (g > m) best = it;
-    const float mn = fmaxf(m, g);
-    const float rkn = ref_point(mn, k);
-    const float sc = (m == ninf()) ? 0.f : exp2_hw(rk - rkn);
-    float e[NE];
-#pragma unroll
-    for (int j = 0; j < NE; ++j) e[j] = exp2_hw(__builtin_fmaf(z[j], k, -rkn));
-    const float acc = tree_sum(e);
-    s = __builtin_fma(s, (double)sc, (double)acc);
-    m = mn;
-    rk = rkn;
-  };
-  for (int it = 0; it < n_full; ++it) {
-    TL::template load<false>(row, e0, e1, it, lane, z);
-    step(it);
-  }
-  if (n_full < n_iter) {
-    TL::template load<true>(row, e0, e1, n_full, lane, z);
-    step(n_full);
-  }
-  // the lane's lowest index attaining m: re-read the one tile where m appeared
-  int arg = INT32_MAX;
-  if (best >= 0) {
-    TL::template load<true>(row, e0, e1, best, lane, z);
-#pragma unroll
-    for (int j = NE - 1; j >= 0; --j)
-      if (z[j] == m) arg = (int)TL::index(e0, best, lane, j);
-  }
-#pragma unroll
-  for (int off = kWave / 2; off >= 1; off >>= 1) {
-    const float m2 = __shfl_xor(m, off, kWave);
-    const double s2 = __shfl_xor(s, off, kWave);
-    const int a2 = __shfl_xor(arg, off, kWave);
-    const float mn = fmaxf(m, m2);
-    s = s * rescale64(m, mn, k) + s2 * rescale64(m2, mn, k);
-    arg = (m2 > m) ? a2 : ((m2 == m) ? min(arg, a2) : arg);
-    m = mn;
-  }
-  return RowPart{s, m, arg};
-}
-
-// Max and argmax only (greedy rows); s = NaN if any logit is NaN or +inf.
-template <int DT, bool VEC>
-__device__ __forceinline__ RowPart chunk_stats_greedy(const void* row, int64_t e0, int64_t e1,
-                                                      int lane) {
-  using TL = Tile<DT, VEC>;
-  constexpr int NE = TL::NE;
-  const int64_t n = e1 - e0;
-  const int n_full = (int)(n / TL::EPI), n_iter = (int)((n + TL::EPI - 1) / TL::EPI);
-  float m = ninf();
-  int best = -1;
   bool bad = false;
-  float z[NE];
-  auto step = [&](int it) {
+  int best = -1;
+  auto process = [&](const Raw& raw, int it) {
+    float z[NE];
+    TL::widen(raw, z);
     const float g = tile_max(z);
+    if constexpr (ARG) best = (g > m) ? it : best;
+    if constexpr (SAMPLING) {
+      const float mn = fmaxf(m, g);
+      const float rkn = ref_point(mn, k);
+      const float sc = (m == ninf()) ? 0.f : exp2_hw(rk - rkn);
+      float e[NE];
 #pragma unroll
-    for (int j = 0; j < NE; ++j) bad |= !(z[j] < pinf());
-    if (g > m) best = it;
-    m = fmaxf(m, g);
+      for (int j = 0; j < NE; ++j) e[j] = exp2_hw(__builtin_fmaf(z[j], k, -rkn));
+      const float acc = tree_sum(e);
+      s = __builtin_fma(s, (double)sc, (double)acc);
+      m = mn;
+      rk = rkn;
+    } else {
+#pragma unroll
+      for (int j = 0; j < NE; ++j) bad |= !(z[j] < pinf());
+      m = fmaxf(m, g);
+    }
   };
-  for (int it = 0; it < n_full; ++it) {
-    TL::template load<false>(row, e0, e1, it, lane, z);
-    step(it);
+  Raw b;
+  for (int it = 0; it < n_iter; it += 2) {
+    if (it + 1 < n_iter) TL::load_raw(row, e0, e1, it + 1, n_full, lane, b);
+    process(a, it);
+    if (it + 1 >= n_iter) break;
+    if (it + 2 < n_iter) TL::load_raw(row, e0, e1, it + 2, n_full, lane, a);
+    process(b, it + 1);
   }
-  if (n_full < n_iter) {
-    TL::template load<true>(row, e0, e1, n_full, lane, z);
-    step(n_full);
+  // wave merge: maximum first, then one rescale per lane and a float64 sum
+  const float M = wave_max(m);
+  double S;
+  if constexpr (SAMPLING) {
+    const double f = (m == ninf()) ? 0.0 : exp2((double)(m * k) - (double)ref_point(M, k));
+    S = wave_sum(s * f);
+  } else {
+    S = (ballot(bad) != 0) ? __builtin_nan("") : 0.0;
   }
   int arg = INT32_MAX;
-  if (best >= 0) {
-    TL::template load<true>(row, e0, e1, best, lane, z);
+  if constexpr (ARG) {
+    if (best >= 0 && m == M) {
+      float z[NE];
+      TL::template load<true>(row, e0, e1, best, lane, z);
 #pragma unroll
-    for (int j = NE - 1; j >= 0; --j)
-      if (z[j] == m) arg = (int)TL::index(e0, best, lane, j);
+      for (int j = NE - 1; j >= 0; --j)
+        if (z[j] == m) arg = (int)TL::index(e0, best, lane, j);
+    }
+    arg = wave_min(arg);
   }
-#pragma unroll
-  for (int off = kWave / 2; off >= 1; off >>= 1) {
-    const float m2 = __shfl_xor(m, off, kWave);
-    const int a2 = __shfl_xor(arg, off, kWave);
-    arg = (m2 > m) ? a2 : ((m2 == m) ? min(arg, a2) : arg);
-    m = fmaxf(m, m2);
-  }
-  const bool any_bad = ballot(bad) != 0;
-  return RowPart{any_bad ? __builtin_nan("") : 0.0, m, arg};
+  return RowPart{S, M, arg};
 }
 
-template <int DT, bool VEC>
+template <int DT, bool VEC, bool WITH_ARG>
 __global__ __launch_bounds__(kBlock) void k1_row_stats(RowStatsArgs a) {
+  using TL = Tile<DT, VEC>;
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t item = wave_uniform((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
   const int64_t rows = a.total_t + a.total_d;
   if (item >= rows * a.chunks) return;
-  if (a.status[0] & kLayoutError) return;
   const int64_t r = item / a.chunks;
   const int c = (int)(item - r * a.chunks);
   const bool is_draft = r >= a.total_t;
   const int64_t j = is_draft ? r - a.total_t : r;
-  int b = is_draft ? a.dmap[j] : a.tmap[j];
-  b = min(max(b, 0), a.B - 1);
-  const float T = a.temperature[b];
-  const bool sampling = T > 0.f && T < pinf();
-  if (is_draft && !sampling) return;  // greedy sequences never read draft rows
   constexpr int64_t esz = (DT == kBF16) ? 2 : 4;
   const void* row = static_cast<const char*>(is_draft ? a.draft : a.target) + j * a.V * esz;
   const int64_t e0 = (int64_t)c * a.chunk_elems;
   const int64_t e1 = min(a.V, e0 + a.chunk_elems);
+  const int64_t n = e1 - e0;
+  const int n_full = (int)(n / TL::EPI), n_iter = (int)((n + TL::EPI - 1) / TL::EPI);
+  // Target rows are always read: tile 0 is in flight while the row's scale
+  // and the status word are looked up. Draft rows are read only for sampling
+  // sequences, so their scale comes first.
+  typename TL::Raw first;
+  float k;
+  if (is_draft) {
+    k = a.dk[j];
+    if (!(k > 0.f)) return;  // greedy (or invalid) sequence: draft row not needed
+    TL::load_raw(row, e0, e1, 0, n_full, lane, first);
+  } else {
+    TL::load_raw(row, e0, e1, 0, n_full, lane, first);
+    k = a.tk[j];
+    if (!(k >= 0.f)) return;  // invalid temperature: the sequence fails in k2_accept
+  }
+  if (a.status[0] & kLayoutError) return;
   RowPart out;
-  if (sampling)
-    out = chunk_stats_sampling<DT, VEC>(row, e0, e1, temp_scale(T), lane);
+  if (k > 0.f)
+    out = chunk_pass<DT, VEC, true, WITH_ARG>(row, e0, e1, n_full, n_iter, k, lane, first);
   else
-    out = chunk_stats_greedy<DT, VEC>(row, e0, e1, lane);
+    out = chunk_pass<DT, VEC, false, true>(row, e0, e1, n_full, n_iter, 0.f, lane, first);
   if (lane == 0) (is_draft ? a.dparts : a.tparts)[j * a.chunks + c] = out;
 }
 
@@ -431,21 +422,28 @@ __device__ __forceinline__ Weights make_weights(const Select& s, bool force_bonu
   return w;
 }
 
+constexpr int kSub = 1024;  // elements per sub-block of the final draw
+
 struct DrawArgs {
   const void* target;
   const void* draft;
   const Select* sel;
-  double* mass;       // [B, chunks3]
+  double* sub;        // [B, nsub] weight mass of each 1024-element sub-block
   int32_t* out_next;
   int64_t V;
-  int32_t B, chunks3, chunk3_elems;
+  int32_t B, chunks3, chunk3_elems, nsub;
 };
 
-// Pass 2: weight mass of one chunk of the selected row pair.
+// Pass 2: weight mass of one chunk of the selected row pair, written per
+// 1024-element sub-block so that the draw only has to scan one sub-block.
+// A tile (EPI = 1024 or 2048 elements) holds one or two sub-blocks: in the
+// bf16 vector tile, slots 0..15 of every lane lie in the first 1024 elements.
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kBlock) void k3_mass(DrawArgs a) {
   using TL = Tile<DT, VEC>;
   constexpr int NE = TL::NE;
+  constexpr int SUBS = TL::EPI / kSub;  // sub-blocks per tile (1 or 2)
+  constexpr int PER = NE / SUBS;        // slots per lane per sub-block
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t item = wave_uniform((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
   if (item >= (int64_t)a.B * a.chunks3) return;
@@ -458,24 +456,35 @@ __global__ __launch_bounds__(kBlock) void k3_mass(DrawArgs a) {
   const void* trow = static_cast<const char*>(a.target) + s.trow * a.V * esz;
   const void* drow = W.residual ? static_cast<const char*>(a.draft) + s.drow * a.V * esz : nullptr;
   const int64_t e0 = (int64_t)c * a.chunk3_elems, e1 = min(a.V, e0 + a.chunk3_elems);
-  const int64_t n = max((int64_t)0, e1 - e0);
+  const int64_t n = e1 - e0;
   const int n_full = (int)(n / TL::EPI), n_iter = (int)((n + TL::EPI - 1) / TL::EPI);
-  double acc = 0.0;
-  float zt[NE], zd[NE], w[NE];
+  double* out = a.sub + b * a.nsub;
+  typename TL::Raw rt, rd;
+  float w[NE];
   for (int it = 0; it < n_iter; ++it) {
-    if (it < n_full) {
-      TL::template load<false>(trow, e0, e1, it, lane, zt);
-      if (W.residual) TL::template load<false>(drow, e0, e1, it, lane, zd);
+    TL::load_raw(trow, e0, e1, it, n_full, lane, rt);
+    if (W.residual) TL::load_raw(drow, e0, e1, it, n_full, lane, rd);
+    if constexpr (VEC && DT == kBF16) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        w[2 * q] = W(bf16_lo(rt.d[q]), W.residual ? bf16_lo(rd.d[q]) : 0.f);
+        w[2 * q + 1] = W(bf16_hi(rt.d[q]), W.residual ? bf16_hi(rd.d[q]) : 0.f);
+      }
     } else {
-      TL::template load<true>(trow, e0, e1, it, lane, zt);
-      if (W.residual) TL::template load<true>(drow, e0, e1, it, lane, zd);
+#pragma unroll
+      for (int q = 0; q < NE; ++q)
+        w[q] = W(__uint_as_float(rt.d[q]), W.residual ? __uint_as_float(rd.d[q]) : 0.f);
     }
 #pragma unroll
-    for (int j = 0; j < NE; ++j) w[j] = W(zt[j], W.residual ? zd[j] : 0.f);
-    acc += (double)tree_sum(w);
+    for (int h = 0; h < SUBS; ++h) {
+      float part[PER];
+#pragma unroll
+      for (int j = 0; j < PER; ++j) part[j] = w[h * PER + j];
+      const double m = wave_sum((double)tree_sum(part));
+      const int64_t sb = (e0 + (int64_t)it * TL::EPI) / kSub + h;
+      if (lane == 0 && sb < a.nsub) out[sb] = m;
+    }
   }
-  acc = wave_sum(acc);
-  if (lane == 0) a.mass[item] = acc;
 }
 
 // Inverse-CDF search inside [lo, hi) of the selected row: the smallest v with
@@ -493,6 +502,7 @@ __device__ int block_draw(const void* trow, const void* drow, const Weights& W, 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int64_t last_pos = -1;
   int token = -1;
+  __syncthreads();  // shared state of a previous call is no longer read
   for (int64_t e = lo; e < hi; e += (int64_t)kBlock * 8) {
     const int64_t my = e + (int64_t)tid * 8;
     float w[8];
@@ -542,6 +552,7 @@ __device__ int block_draw(const void* trow, const void* drow, const Weights& W, 
       }
       __syncthreads();
       token = sh_tok;
+      __syncthreads();
       break;
     }
     base += step_total;
@@ -562,58 +573,103 @@ __device__ int block_draw(const void* trow, const void* drow, const Weights& W, 
   return token;
 }
 
+// Workgroup inclusive scan of the sequence's sub-block masses, in passes of
+// kBlock entries with a carry. With t < 0 it only returns the total mass (the
+// inclusive prefix through the last entry); with t >= 0 it returns the first
+// sub-block whose inclusive prefix reaches t, with that prefix's exclusive
+// part in *base (-1 if none). Both modes perform the same additions in the
+// same order, so a t <= total always finds its sub-block.
+__device__ int64_t scan_subs(const double* sub, int64_t nsub, double t, double* base,
+                             double* total) {
+  __shared__ double sh_w[kWavesPerBlock];
+  __shared__ int sh_first[kWavesPerBlock];
+  __shared__ double sh_carry, sh_base;
+  __shared__ int64_t sh_hit;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __syncthreads();  // every thread is done with the shared state of a previous call
+  if (tid == 0) {
+    sh_carry = 0.0;
+    sh_hit = -1;
+  }
+  __syncthreads();
+  for (int64_t p = 0; p < nsub; p += kBlock) {
+    const int64_t i = p + tid;
+    const double v = (i < nsub) ? sub[i] : 0.0;
+    double incl = wave_inclusive_scan(v, lane);
+    if (lane == 63) sh_w[wave] = incl;
+    __syncthreads();
+    double wb = sh_carry;
+    for (int q = 0; q < wave; ++q) wb += sh_w[q];
+    incl += wb;  // inclusive prefix through entry i
+    const double prev = __shfl_up(incl, 1, kWave);
+    const double excl = (lane == 0) ? wb : prev;
+    const uint64_t m = ballot(t >= 0.0 && i < nsub && incl >= t);
+    if (lane == 0) sh_first[wave] = m ? first_lane(m) : 64;
+    __syncthreads();
+    int owner = -1;
+    for (int q = 0; q < kWavesPerBlock; ++q)
+      if (sh_first[q] < 64) { owner = q * 64 + sh_first[q]; break; }
+    if (owner >= 0) {
+      if (tid == owner) {
+        sh_hit = i;
+        sh_base = excl;
+      }
+      __syncthreads();
+      if (base) *base = sh_base;
+      const int64_t hit = sh_hit;
+      __syncthreads();
+      return hit;
+    }
+    if (tid == kBlock - 1) sh_carry = incl;  // entries past nsub add exact zeros
+    __syncthreads();
+  }
+  if (total) *total = sh_carry;
+  __syncthreads();  // sh_carry has been read by every thread before it can be reset
+  return -1;
+}
+
 template <int DT>
 __global__ __launch_bounds__(kBlock) void k3_draw(DrawArgs a) {
   const int64_t b = blockIdx.x;
   if (b >= a.B) return;
   const Select s = a.sel[b];
   if (s.mode == kModeNone) return;
-  __shared__ double sh_base, sh_t;
-  __shared__ int sh_chunk;
-  const double* mass = a.mass + b * a.chunks3;
-  if (threadIdx.x == 0) {
-    double tot = 0.0;
-    for (int c = 0; c < a.chunks3; ++c) tot += mass[c];
-    int chunk = -1;
-    double base = 0.0, t = 0.0;
-    if (tot > 0.0) {
-      t = s.u * tot;
-      double cum = 0.0;
-      int lastnz = -1;
-      for (int c = 0; c < a.chunks3; ++c) {
-        if (mass[c] > 0.0) lastnz = c;
-        if (t <= cum + mass[c] && mass[c] > 0.0) { chunk = c; break; }
-        cum += mass[c];
-      }
-      if (chunk < 0) {  // rounding: t above the last prefix
-        chunk = lastnz;
-        cum = 0.0;
-        for (int c = 0; c < chunk; ++c) cum += mass[c];
-      }
-      base = cum;
-    }
-    sh_chunk = chunk;
-    sh_base = base;
-    sh_t = t;
-  }
-  __syncthreads();
   constexpr int64_t esz = (DT == kBF16) ? 2 : 4;
   const void* trow = static_cast<const char*>(a.target) + s.trow * a.V * esz;
   const void* drow = (s.mode == kModeResidual) ? static_cast<const char*>(a.draft) + s.drow * a.V * esz : nullptr;
+  const double* sub = a.sub + b * a.nsub;
+  double total = 0.0;
+  scan_subs(sub, a.nsub, -1.0, nullptr, &total);
   int token;
-  if (sh_chunk >= 0) {
+  if (total > 0.0) {
+    const double t = s.u * total;  // u in (0, 1]: t <= total
+    double base = 0.0;
+    const int64_t hit = scan_subs(sub, a.nsub, t, &base, nullptr);
     const Weights W = make_weights(s, false);
-    const int64_t lo = (int64_t)sh_chunk * a.chunk3_elems, hi = min(a.V, lo + a.chunk3_elems);
-    int64_t last_pos = -1;
-    token = block_draw<DT>(trow, drow, W, lo, hi, sh_base, sh_t, nullptr, &last_pos);
+    int64_t sb = hit, last_pos = -1;
+    if (sb < 0) {  // unreachable for t <= total; kept as a guard
+      sb = a.nsub - 1;
+      base = 0.0;
+    }
+    const int64_t lo = sb * kSub, hi = min(a.V, lo + kSub);
+    token = block_draw<DT>(trow, drow, W, lo, hi, base, t, nullptr, &last_pos);
     if (token < 0) token = (int)last_pos;
+    if (token < 0) {  // the chosen sub-block holds no weight (rounding): last positive token
+      int64_t lp = -1;
+      for (int64_t q = a.nsub - 1; q >= 0 && lp < 0; --q) {
+        if (!(sub[q] > 0.0)) continue;
+        block_draw<DT>(trow, drow, W, q * kSub, min(a.V, (q + 1) * kSub), 0.0,
+                       __builtin_huge_val(), nullptr, &lp);
+      }
+      token = (int)lp;
+    }
   } else {
     // The residual has no mass in fp32 (p_n == q_n to rounding): draw from p_n.
     const Weights W = make_weights(s, true);
-    double total = 0.0;
+    double tot = 0.0;
     int64_t last_pos = -1;
-    block_draw<DT>(trow, nullptr, W, 0, a.V, 0.0, __builtin_huge_val(), &total, &last_pos);
-    token = block_draw<DT>(trow, nullptr, W, 0, a.V, 0.0, s.u * total, nullptr, &last_pos);
+    block_draw<DT>(trow, nullptr, W, 0, a.V, 0.0, __builtin_huge_val(), &tot, &last_pos);
+    token = block_draw<DT>(trow, nullptr, W, 0, a.V, 0.0, s.u * tot, nullptr, &last_pos);
     if (token < 0) token = (int)last_pos;
   }
   if (threadIdx.x == 0) a.out_next[b] = token;
@@ -624,9 +680,8 @@ __global__ __launch_bounds__(kBlock) void k3_draw(DrawArgs a) {
 struct MergeArgs {
   const RowPart* tparts;
   const RowPart* dparts;
-  const int32_t* tmap;
-  const int32_t* dmap;
-  const float* temperature;
+  const float* tk;
+  const float* dk;
   const uint32_t* status;
   float* out_tm;
   double* out_ts;
@@ -653,16 +708,15 @@ __global__ __launch_bounds__(kBlock) void k_merge_rows(MergeArgs a) {
     oa[j] = -1;
     return;
   }
-  const int b = min(max(is_draft ? a.dmap[j] : a.tmap[j], 0), a.B - 1);
-  const float T = a.temperature[b];
-  const bool sampling = T > 0.f && T < pinf();
-  if (is_draft && !sampling) {
+  const float kk = is_draft ? a.dk[j] : a.tk[j];
+  const bool sampling = kk > 0.f;
+  if ((is_draft && !sampling) || !(kk >= 0.f)) {
     om[j] = __builtin_nanf("");
     os[j] = __builtin_nan("");
     oa[j] = -1;
     return;
   }
-  const float k = sampling ? temp_scale(T) : 0.f;
+  const float k = sampling ? kk : 0.f;
   const RowStat st = merge_row((is_draft ? a.dparts : a.tparts) + j * a.chunks, a.chunks, k, sampling);
   om[j] = st.m;
   // re-reference the sum from fl32(m k) to m k exactly: sum 2^((z - m) k)
@@ -676,9 +730,8 @@ struct ProbArgs {
   const void* draft;
   const RowPart* tparts;
   const RowPart* dparts;
-  const int32_t* tmap;
-  const int32_t* dmap;
-  const float* temperature;
+  const float* tk;
+  const float* dk;
   const int64_t* rows;
   float* out;
   int64_t V, n_rows, total_t, total_d;
@@ -701,9 +754,7 @@ __global__ __launch_bounds__(kBlock) void k_softmax_rows(ProbArgs a) {
     }
     return;
   }
-  const int b = min(max(is_draft ? a.dmap[j] : a.tmap[j], 0), a.B - 1);
-  const float T = a.temperature[b];
-  const float k = temp_scale(T);
+  const float k = is_draft ? a.dk[j] : a.tk[j];
   const RowStat st = merge_row((is_draft ? a.dparts : a.tparts) + j * a.chunks, a.chunks, k, true);
   Select s{};
   s.mode = kModeBonus;

@@ -25,7 +25,8 @@ struct Plan {
   int64_t esz;
   int chunks1, chunk1_elems;
   int chunks3, chunk3_elems;
-  size_t off_toff, off_doff, off_tmap, off_dmap, off_tparts, off_dparts, off_sel, off_mass;
+  int64_t nsub;
+  size_t off_toff, off_doff, off_tk, off_dk, off_tparts, off_dparts, off_sel, off_sub;
   size_t bytes;
 };
 
@@ -64,12 +65,13 @@ void make_plan(const specv_shape_t* s, Plan* p) {
   size_t off = kAlign;  // [0, 256): status word
   p->off_toff = off; off = align_up(off + (size_t)(p->B + 1) * 8);
   p->off_doff = off; off = align_up(off + (size_t)(p->B + 1) * 8);
-  p->off_tmap = off; off = align_up(off + (size_t)p->tt * 4);
-  p->off_dmap = off; off = align_up(off + (size_t)p->td * 4);
+  p->off_tk = off; off = align_up(off + (size_t)p->tt * 4);
+  p->off_dk = off; off = align_up(off + (size_t)p->td * 4);
   p->off_tparts = off; off = align_up(off + (size_t)p->tt * p->chunks1 * sizeof(RowPart));
   p->off_dparts = off; off = align_up(off + (size_t)p->td * p->chunks1 * sizeof(RowPart));
   p->off_sel = off; off = align_up(off + (size_t)p->B * sizeof(Select));
-  p->off_mass = off; off = align_up(off + (size_t)p->B * p->chunks3 * sizeof(double));
+  p->nsub = (p->V + kSub - 1) / kSub;
+  p->off_sub = off; off = align_up(off + (size_t)p->B * p->nsub * sizeof(double));
   p->bytes = off;
 }
 
@@ -122,20 +124,22 @@ inline specv_status_t launched() {
 }
 
 inline void mark(hipEvent_t* ev, int idx, hipStream_t s) {
-  if (ev) (void)hipEventRecord(ev[idx], s);
+  if (ev && ev[idx]) (void)hipEventRecord(ev[idx], s);
 }
 
 inline unsigned blocks_for(int64_t waves) {
   return (unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock);
 }
 
-specv_status_t launch_plan(const Plan& p, const int32_t* gamma, void* ws, hipStream_t st) {
+specv_status_t launch_plan(const Plan& p, const int32_t* gamma, const float* temperature, void* ws,
+                           hipStream_t st) {
   PlanArgs a;
   a.gamma = gamma;
+  a.temperature = temperature;
   a.toff = at<int64_t>(ws, p.off_toff);
   a.doff = at<int64_t>(ws, p.off_doff);
-  a.tmap = at<int32_t>(ws, p.off_tmap);
-  a.dmap = at<int32_t>(ws, p.off_dmap);
+  a.tk = at<float>(ws, p.off_tk);
+  a.dk = at<float>(ws, p.off_dk);
   a.status = at<uint32_t>(ws, 0);
   a.total_t = p.tt;
   a.total_d = p.td;
@@ -146,13 +150,12 @@ specv_status_t launch_plan(const Plan& p, const int32_t* gamma, void* ws, hipStr
 }
 
 specv_status_t launch_row_stats(const Plan& p, bool vec, const void* target, const void* draft,
-                                const float* temperature, void* ws, hipStream_t st) {
+                                void* ws, hipStream_t st, bool with_argmax = false) {
   RowStatsArgs a;
   a.target = target;
   a.draft = draft;
-  a.temperature = temperature;
-  a.tmap = at<int32_t>(ws, p.off_tmap);
-  a.dmap = at<int32_t>(ws, p.off_dmap);
+  a.tk = at<float>(ws, p.off_tk);
+  a.dk = at<float>(ws, p.off_dk);
   a.tparts = at<RowPart>(ws, p.off_tparts);
   a.dparts = at<RowPart>(ws, p.off_dparts);
   a.status = at<uint32_t>(ws, 0);
@@ -165,12 +168,23 @@ specv_status_t launch_row_stats(const Plan& p, bool vec, const void* target, con
   const int64_t waves = (p.tt + p.td) * p.chunks1;
   if (waves == 0) return SPECV_OK;
   const dim3 grid(blocks_for(waves)), block(kBlock);
-  if (p.dt == kBF16) {
-    if (vec) hipLaunchKernelGGL((k1_row_stats<kBF16, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((k1_row_stats<kBF16, false>), grid, block, 0, st, a);
+  // specv_verify needs no argmax of sampling rows; the diagnostics export does
+  if (with_argmax) {
+    if (p.dt == kBF16) {
+      if (vec) hipLaunchKernelGGL((k1_row_stats<kBF16, true, true>), grid, block, 0, st, a);
+      else hipLaunchKernelGGL((k1_row_stats<kBF16, false, true>), grid, block, 0, st, a);
+    } else {
+      if (vec) hipLaunchKernelGGL((k1_row_stats<kF32, true, true>), grid, block, 0, st, a);
+      else hipLaunchKernelGGL((k1_row_stats<kF32, false, true>), grid, block, 0, st, a);
+    }
   } else {
-    if (vec) hipLaunchKernelGGL((k1_row_stats<kF32, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((k1_row_stats<kF32, false>), grid, block, 0, st, a);
+    if (p.dt == kBF16) {
+      if (vec) hipLaunchKernelGGL((k1_row_stats<kBF16, true, false>), grid, block, 0, st, a);
+      else hipLaunchKernelGGL((k1_row_stats<kBF16, false, false>), grid, block, 0, st, a);
+    } else {
+      if (vec) hipLaunchKernelGGL((k1_row_stats<kF32, true, false>), grid, block, 0, st, a);
+      else hipLaunchKernelGGL((k1_row_stats<kF32, false, false>), grid, block, 0, st, a);
+    }
   }
   return launched();
 }
@@ -209,12 +223,13 @@ DrawArgs draw_args(const Plan& p, const Call& c) {
   a.target = c.target;
   a.draft = c.draft;
   a.sel = at<Select>(c.ws, p.off_sel);
-  a.mass = at<double>(c.ws, p.off_mass);
+  a.sub = at<double>(c.ws, p.off_sub);
   a.out_next = c.out_next;
   a.V = p.V;
   a.B = (int32_t)p.B;
   a.chunks3 = p.chunks3;
   a.chunk3_elems = p.chunk3_elems;
+  a.nsub = (int32_t)p.nsub;
   return a;
 }
 
@@ -249,10 +264,10 @@ specv_status_t run(const Call& c) {
   if ((c.inj_r == nullptr) != (c.inj_u == nullptr)) return SPECV_ERR_INVALID_ARGUMENT;
   const bool vec = vector_path(p, c.target, c.draft);
   mark(c.events, 2 * SPECV_STAGE_PLAN, c.stream);
-  if ((st = launch_plan(p, c.gamma, c.ws, c.stream)) != SPECV_OK) return st;
+  if ((st = launch_plan(p, c.gamma, c.temperature, c.ws, c.stream)) != SPECV_OK) return st;
   mark(c.events, 2 * SPECV_STAGE_PLAN + 1, c.stream);
   mark(c.events, 2 * SPECV_STAGE_ROWSTATS, c.stream);
-  if ((st = launch_row_stats(p, vec, c.target, c.draft, c.temperature, c.ws, c.stream)) != SPECV_OK)
+  if ((st = launch_row_stats(p, vec, c.target, c.draft, c.ws, c.stream)) != SPECV_OK)
     return st;
   mark(c.events, 2 * SPECV_STAGE_ROWSTATS + 1, c.stream);
   mark(c.events, 2 * SPECV_STAGE_ACCEPT, c.stream);
@@ -334,16 +349,15 @@ specv_status_t specv_row_stats(const specv_shape_t* shape, const void* target_lo
   if (p.td > 0 && (!out_draft_max || !out_draft_sum || !out_draft_argmax))
     return SPECV_ERR_INVALID_ARGUMENT;
   const bool vec = vector_path(p, target_logits, draft_logits);
-  if ((st = launch_plan(p, gamma_per_row, workspace, stream)) != SPECV_OK) return st;
-  if ((st = launch_row_stats(p, vec, target_logits, draft_logits, temperature, workspace, stream)) !=
+  if ((st = launch_plan(p, gamma_per_row, temperature, workspace, stream)) != SPECV_OK) return st;
+  if ((st = launch_row_stats(p, vec, target_logits, draft_logits, workspace, stream, true)) !=
       SPECV_OK)
     return st;
   MergeArgs a;
   a.tparts = at<RowPart>(workspace, p.off_tparts);
   a.dparts = at<RowPart>(workspace, p.off_dparts);
-  a.tmap = at<int32_t>(workspace, p.off_tmap);
-  a.dmap = at<int32_t>(workspace, p.off_dmap);
-  a.temperature = temperature;
+  a.tk = at<float>(workspace, p.off_tk);
+  a.dk = at<float>(workspace, p.off_dk);
   a.status = at<uint32_t>(workspace, 0);
   a.out_tm = out_target_max;
   a.out_ts = out_target_sum;
@@ -372,18 +386,16 @@ specv_status_t specv_softmax_rows(const specv_shape_t* shape, const void* target
   if (st != SPECV_OK || p.B == 0 || n_rows == 0) return st;
   if (n_rows < 0 || n_rows > 65535 || !rows || !out_probs) return SPECV_ERR_INVALID_ARGUMENT;
   const bool vec = vector_path(p, target_logits, draft_logits);
-  if ((st = launch_plan(p, gamma_per_row, workspace, stream)) != SPECV_OK) return st;
-  if ((st = launch_row_stats(p, vec, target_logits, draft_logits, temperature, workspace, stream)) !=
-      SPECV_OK)
+  if ((st = launch_plan(p, gamma_per_row, temperature, workspace, stream)) != SPECV_OK) return st;
+  if ((st = launch_row_stats(p, vec, target_logits, draft_logits, workspace, stream)) != SPECV_OK)
     return st;
   ProbArgs a;
   a.target = target_logits;
   a.draft = draft_logits;
   a.tparts = at<RowPart>(workspace, p.off_tparts);
   a.dparts = at<RowPart>(workspace, p.off_dparts);
-  a.tmap = at<int32_t>(workspace, p.off_tmap);
-  a.dmap = at<int32_t>(workspace, p.off_dmap);
-  a.temperature = temperature;
+  a.tk = at<float>(workspace, p.off_tk);
+  a.dk = at<float>(workspace, p.off_dk);
   a.rows = rows;
   a.out = out_probs;
   a.V = p.V;
