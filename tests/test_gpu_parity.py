@@ -1,7 +1,7 @@
 """GPU parity: libspecverify (through its C ABI) against the CPU oracle on the
 same seeded inputs and the same Philox stream.
 
-Bar (north star of the verify step): accepted counts and emitted tokens are
+Bar: accepted counts and emitted tokens are
 bit-exact on every sequence that is not a near-tie (a decisive uniform within
 1e-6 relative of its threshold or of an inverse-CDF boundary; the oracle
 flags them and they are counted); probabilities within 1e-5 absolute; row
