@@ -121,17 +121,17 @@ specv_status_t specv_verify_with_uniforms(const specv_shape_t* shape, const void
                                           void* workspace, size_t workspace_bytes,
                                           hipStream_t stream);
 
-/* Stages of one call, in launch order. */
-#define SPECV_STAGE_PLAN 0      /* offsets of the packed rows              */
-#define SPECV_STAGE_ROWSTATS 1  /* pass 1: max, sum of exp, argmax per row */
-#define SPECV_STAGE_ACCEPT 2    /* ratios, uniforms, accepted count        */
-#define SPECV_STAGE_RESIDUAL 3  /* pass 2: weight mass per chunk           */
-#define SPECV_STAGE_DRAW 4      /* inverse-CDF draw of the next token      */
-#define SPECV_NUM_STAGES 5
+/* Stages of one call, in launch order (one kernel each). */
+#define SPECV_STAGE_PLAN 0        /* offsets of the packed rows, per-row T scale */
+#define SPECV_STAGE_ROWSTATS 1    /* pass 1: max, sum of exp (argmax) per row    */
+#define SPECV_STAGE_ACCEPT_MASS 2 /* ratios, uniforms, n; pass 2 weight masses   */
+#define SPECV_STAGE_DRAW 3        /* inverse-CDF draw of the next token          */
+#define SPECV_NUM_STAGES 4
 
 /* specv_verify that also records events[2 s] before and events[2 s + 1]
  * after stage s on `stream` (events: 2 * SPECV_NUM_STAGES hipEvent_t created
- * by the caller, or NULL). For timing the stages of a call. */
+ * by the caller, or NULL; a NULL entry is skipped). For timing the stages of
+ * a call. */
 specv_status_t specv_verify_profiled(const specv_shape_t* shape, const void* target_logits,
                                      const void* draft_logits, const int32_t* draft_tokens,
                                      const int32_t* gamma_per_row, const float* temperature,

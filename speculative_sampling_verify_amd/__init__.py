@@ -19,7 +19,7 @@ SPECV_F32, SPECV_BF16 = 0, 1
 SPECV_MAX_GAMMA = 63
 SPECV_DEV_SEQ_ERROR = 1
 SPECV_DEV_LAYOUT_ERROR = 2
-STAGES = ("plan", "row_stats", "accept", "residual_mass", "draw")
+STAGES = ("plan", "row_stats", "accept_and_mass", "draw")
 
 if not LIBRARY.exists():
     raise ImportError("libspecverify.so is not built (run __graft_entry__.build() or "

@@ -7,15 +7,15 @@
 //                  streamed once with 16-byte non-temporal loads; each wave
 //                  owns one (row, chunk) and keeps (max, sum of 2^(z k - rk),
 //                  argmax) in registers, reduced across the wave by shuffles.
-//   k2_accept      one wave per sequence, one lane per draft position: merges
-//                  the chunk statistics, gathers p_i(x_i) and q_i(x_i), draws
-//                  r_i from Philox, and takes the first rejection by ballot.
-//                  Greedy sequences finish here (argmax match).
-//   k3_mass        pass 2 over the one selected row pair of each sampling
-//                  sequence: weight mass max(0, p - q) (or p) per chunk.
-//   k3_draw        one workgroup per sampling sequence: picks the chunk that
-//                  holds u * total, then an LDS-assisted workgroup prefix scan
-//                  inside it finds the token (inverse CDF in index order).
+//   k3_accept_mass the accept step (one wave per sequence, one lane per draft
+//                  position: merge the chunk statistics, gather p_i(x_i) and
+//                  q_i(x_i), draw r_i from Philox, first rejection by ballot;
+//                  greedy sequences finish here) fused with pass 2 over the
+//                  one selected row pair of each sampling sequence: weight
+//                  mass max(0, p - q) or p per 1024-element sub-block.
+//   k4_draw        one wave per sampling sequence picks the sub-block that
+//                  holds u * total and a wave prefix scan inside it finds the
+//                  token (inverse CDF in index order).
 #pragma once
 
 #include "device.hpp"
@@ -31,7 +31,7 @@ struct RowPart {
   int32_t arg;
 };
 
-// What the final draw of one sampling sequence needs (written by k2_accept).
+// What the final draw of one sampling sequence needs (written by the accept step).
 enum : int32_t { kModeNone = 0, kModeResidual = 1, kModeBonus = 2 };
 struct Select {
   int32_t mode;
@@ -61,24 +61,33 @@ struct PlanArgs {
 
 // One workgroup of 1024 threads: thread t owns a contiguous run of sequences.
 // Writes the packed row offsets, the per-row temperature scale, and the
-// status word (layout error or 0).
+// status word (layout error or 0). Runs of up to kPlanKeep sequences per
+// thread stay in registers between the scan and the writes.
+constexpr int kPlanKeep = 4;
+
 __global__ __launch_bounds__(1024) void k0_plan(PlanArgs a) {
   __shared__ int64_t sh_t[16], sh_d[16];
   __shared__ int sh_bad[16];
-  __shared__ int64_t sh_tot_t, sh_tot_d;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int per = (a.B + 1023) / 1024;
   const int lo = min(a.B, tid * per), hi = min(a.B, lo + per);
+  int32_t keep_g[kPlanKeep];
+  float keep_k[kPlanKeep];
   int64_t st = 0, sd = 0;
   int bad = 0;
   for (int b = lo; b < hi; ++b) {
     const int32_t g = a.gamma[b];
+    const float T = a.temperature[b];
     bad |= (g < 0 || g > a.max_gamma);
     const int64_t gg = g < 0 ? 0 : g;
     st += gg + 1;
     sd += gg;
+    if (b - lo < kPlanKeep) {
+      keep_g[b - lo] = g;
+      keep_k[b - lo] = (T > 0.f && T < pinf()) ? temp_scale(T) : (T == 0.f ? 0.f : -1.f);
+    }
   }
-  // workgroup exclusive scan of (st, sd)
+  // workgroup exclusive scan of (st, sd): waves, then the 16 wave totals
   int64_t it = st, id = sd;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -88,27 +97,34 @@ __global__ __launch_bounds__(1024) void k0_plan(PlanArgs a) {
   const int wbad = __any(bad) ? 1 : 0;
   if (lane == 63) { sh_t[wave] = it; sh_d[wave] = id; sh_bad[wave] = wbad; }
   __syncthreads();
+  int64_t wt = 0, wd = 0, tot_t = 0, tot_d = 0;
+  int anybad = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) {
+    if (w < wave) { wt += sh_t[w]; wd += sh_d[w]; }
+    tot_t += sh_t[w];
+    tot_d += sh_d[w];
+    anybad |= sh_bad[w];
+  }
   if (tid == 0) {
-    int64_t ct = 0, cd = 0;
-    int ab = 0;
-    for (int w = 0; w < 16; ++w) {
-      const int64_t t = sh_t[w], d = sh_d[w];
-      sh_t[w] = ct; sh_d[w] = cd;
-      ct += t; cd += d; ab |= sh_bad[w];
-    }
-    sh_tot_t = ct; sh_tot_d = cd;
-    const bool layout_bad = ab || ct != a.total_t || cd != a.total_d;
+    const bool layout_bad = anybad || tot_t != a.total_t || tot_d != a.total_d;
     a.status[0] = layout_bad ? kLayoutError : 0u;
   }
-  __syncthreads();
-  int64_t t = sh_t[wave] + it - st, d = sh_d[wave] + id - sd;
+  int64_t t = wt + it - st, d = wd + id - sd;
   for (int b = lo; b < hi; ++b) {
-    const int32_t g = a.gamma[b];
+    int32_t g;
+    float kk;
+    if (b - lo < kPlanKeep) {
+      g = keep_g[b - lo];
+      kk = keep_k[b - lo];
+    } else {
+      g = a.gamma[b];
+      const float T = a.temperature[b];
+      kk = (T > 0.f && T < pinf()) ? temp_scale(T) : (T == 0.f ? 0.f : -1.f);
+    }
     const int64_t gg = g < 0 ? 0 : g;
     a.toff[b] = t;
     a.doff[b] = d;
-    const float T = a.temperature[b];
-    const float kk = (T > 0.f && T < pinf()) ? temp_scale(T) : (T == 0.f ? 0.f : -1.f);
     const int64_t tend = min(t + gg + 1, a.total_t), dend = min(d + gg, a.total_d);
     for (int64_t j = t; j < tend; ++j) a.tk[j] = kk;
     for (int64_t j = d; j < dend; ++j) a.dk[j] = kk;
@@ -116,8 +132,8 @@ __global__ __launch_bounds__(1024) void k0_plan(PlanArgs a) {
     d += gg;
   }
   if (tid == 1023) {
-    a.toff[a.B] = sh_tot_t;
-    a.doff[a.B] = sh_tot_d;
+    a.toff[a.B] = tot_t;
+    a.doff[a.B] = tot_d;
   }
 }
 
@@ -237,7 +253,7 @@ __global__ __launch_bounds__(kBlock) void k1_row_stats(RowStatsArgs a) {
   } else {
     TL::load_raw(row, e0, e1, 0, n_full, lane, first);
     k = a.tk[j];
-    if (!(k >= 0.f)) return;  // invalid temperature: the sequence fails in k2_accept
+    if (!(k >= 0.f)) return;  // invalid temperature: the accept step fails the sequence
   }
   if (a.status[0] & kLayoutError) return;
   RowPart out;
@@ -258,14 +274,35 @@ struct RowStat {
 };
 
 __device__ __forceinline__ RowStat merge_row(const RowPart* p, int chunks, float k, bool sampling) {
+  // Chunks in index order, four loads in flight at a time: a running maximum
+  // (the first chunk attaining it gives the argmax), the running sum moved
+  // onto the new maximum's reference when it grows, and each group's terms
+  // moved onto the group's maximum; the float64 exp2 evaluations of a group
+  // are independent of each other.
   float M = ninf();
-  for (int c = 0; c < chunks; ++c) M = fmaxf(M, p[c].m);
-  int32_t arg = INT32_MAX;
   double S = 0.0;
-  for (int c = 0; c < chunks; ++c) {
-    const RowPart q = p[c];
-    if (q.m == M && arg == INT32_MAX) arg = q.arg;
-    S += sampling ? q.s * rescale64(q.m, M, k) : q.s;
+  int32_t arg = INT32_MAX;
+  for (int c0 = 0; c0 < chunks; c0 += 4) {
+    RowPart q[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      q[u] = (c0 + u < chunks) ? p[c0 + u] : RowPart{0.0, ninf(), INT32_MAX};
+    float mg = M;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (q[u].m > mg) arg = q[u].arg;
+      mg = fmaxf(mg, q[u].m);
+    }
+    if (sampling) {
+      double add = 0.0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) add += q[u].s * rescale64(q[u].m, mg, k);
+      S = S * rescale64(M, mg, k) + add;
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) S += q[u].s;
+    }
+    M = mg;
   }
   RowStat st;
   st.s = S;
@@ -297,34 +334,30 @@ struct AcceptArgs {
   int32_t B, max_gamma, chunks;
 };
 
-// One wave per sequence; lane i owns draft position i and target row i.
+// The accept step of one sequence, by one wave; lane i owns draft position i
+// and target row i. Returns the selection for the final draw (kModeNone for
+// greedy and failed sequences, which are finished here). With `write` the
+// wave also stores n (and the token of a greedy or failed sequence), the
+// selection, and the status bit of a data error.
 template <int DT>
-__global__ __launch_bounds__(kBlock) void k2_accept(AcceptArgs a) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int64_t b = wave_uniform((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
-  if (b >= a.B) return;
-  Select* sel = a.sel + b;
-  auto fail = [&]() {
-    if (lane == 0) {
-      a.out_n[b] = -1;
-      a.out_next[b] = -1;
-      sel->mode = kModeNone;
-      atomicOr(a.status, kSeqError);
+__device__ Select accept_sequence(const AcceptArgs& a, int64_t b, int lane, bool write) {
+  Select s{};
+  s.mode = kModeNone;
+  auto finish = [&](int n, int next, bool error) {
+    if (write && lane == 0) {
+      a.out_n[b] = n;
+      a.out_next[b] = next;
+      a.sel[b] = s;
+      if (error) atomicOr(a.status, kSeqError);
     }
+    return s;
   };
-  if (a.status[0] & kLayoutError) {
-    if (lane == 0) {
-      a.out_n[b] = -1;
-      a.out_next[b] = -1;
-      sel->mode = kModeNone;
-    }
-    return;
-  }
+  if (a.status[0] & kLayoutError) return finish(-1, -1, false);
   const int g = a.gamma[b];
   const float T = a.temperature[b];
   const bool greedy = (T == 0.f);
   const bool sampling = (T > 0.f) && (T < pinf());
-  if (!greedy && !sampling) { fail(); return; }
+  if (!greedy && !sampling) return finish(-1, -1, true);
   const int64_t t0 = a.toff[b], d0 = a.doff[b];
   const float k = sampling ? temp_scale(T) : 0.f;
   RowStat st_t{}, st_d{};
@@ -342,18 +375,12 @@ __global__ __launch_bounds__(kBlock) void k2_accept(AcceptArgs a) {
       bad |= !st_d.valid;
     }
   }
-  if (ballot(bad) != 0) { fail(); return; }
+  if (ballot(bad) != 0) return finish(-1, -1, true);
 
   if (greedy) {
     const uint64_t rej = ballot(lane < g && x != st_t.arg);
     const int n = rej ? first_lane(rej) : g;
-    const int next = __shfl(st_t.arg, n, kWave);
-    if (lane == 0) {
-      a.out_n[b] = n;
-      a.out_next[b] = next;
-      sel->mode = kModeNone;
-    }
-    return;
+    return finish(n, __shfl(st_t.arg, n, kWave), false);
   }
 
   // Sampling: block (row, i) of Philox gives r_i (word 0) and the uniform of
@@ -376,27 +403,22 @@ __global__ __launch_bounds__(kBlock) void k2_accept(AcceptArgs a) {
   }
   const uint64_t mask = ballot(rej);
   const int n = mask ? first_lane(mask) : g;
-  const double un = __shfl(u, n, kWave);
-  const float rkT = __shfl(st_t.rk, n, kWave);
-  const double sT = __shfl(st_t.s, n, kWave);
-  const float rkD = __shfl(st_d.rk, n, kWave);
-  const double sD = __shfl(st_d.s, n, kWave);
-  if (lane == 0) {
-    Select s;
-    s.mode = (n < g) ? kModeResidual : kModeBonus;
-    s.n = n;
-    s.trow = t0 + n;
-    s.drow = (n < g) ? d0 + n : -1;
-    s.k = k;
-    s.rkT = rkT;
-    s.rkD = rkD;
-    s.pad = 0;
-    s.sT = sT;
-    s.sD = sD;
-    s.u = un;
-    *sel = s;
+  s.mode = (n < g) ? kModeResidual : kModeBonus;
+  s.n = n;
+  s.trow = t0 + n;
+  s.drow = (n < g) ? d0 + n : -1;
+  s.k = k;
+  s.rkT = __shfl(st_t.rk, n, kWave);
+  s.rkD = __shfl(st_d.rk, n, kWave);
+  s.pad = 0;
+  s.sT = __shfl(st_t.s, n, kWave);
+  s.sD = __shfl(st_d.s, n, kWave);
+  s.u = __shfl(u, n, kWave);
+  if (write && lane == 0) {
     a.out_n[b] = n;
+    a.sel[b] = s;
   }
+  return s;
 }
 
 // Weight of one token in the final draw: max(0, p - q) or p, in fp32.
@@ -434,12 +456,169 @@ struct DrawArgs {
   int32_t B, chunks3, chunk3_elems, nsub;
 };
 
-// Pass 2: weight mass of one chunk of the selected row pair, written per
-// 1024-element sub-block so that the draw only has to scan one sub-block.
-// A tile (EPI = 1024 or 2048 elements) holds one or two sub-blocks: in the
-// bf16 vector tile, slots 0..15 of every lane lie in the first 1024 elements.
+// Wave-level inclusive scan of a sequence's sub-block masses in passes of 64
+// entries with a carry. t < 0: returns -1 and the total (the inclusive prefix
+// through the last entry; entries past nsub add exact zeros). t >= 0: returns
+// the first entry whose inclusive prefix reaches t and its exclusive prefix
+// in *base. Both modes make the same additions in the same order, so any
+// t <= total finds an entry.
+__device__ int64_t wave_scan_subs(const double* sub, int64_t nsub, double t, int lane, double* base,
+                                  double* total) {
+  double carry = 0.0;
+  for (int64_t p = 0; p < nsub; p += kWave) {
+    const int64_t i = p + lane;
+    const double v = (i < nsub) ? sub[i] : 0.0;
+    const double incl = wave_inclusive_scan(v, lane) + carry;
+    const double prev = __shfl_up(incl, 1, kWave);
+    const double excl = (lane == 0) ? carry : prev;
+    if (t >= 0.0) {
+      const uint64_t m = ballot(i < nsub && incl >= t);
+      if (m) {
+        const int L = first_lane(m);
+        if (base) *base = __shfl(excl, L, kWave);
+        return p + L;
+      }
+    }
+    carry = __shfl(incl, kWave - 1, kWave);
+  }
+  if (total) *total = carry;
+  return -1;
+}
+
+// Sixteen consecutive logits [lo, lo + 16) of a row as fp32 (slots at or past
+// V read -inf). Vector path: lo is a multiple of 16 elements and rows are
+// 16-byte aligned, so a lane's run is 2 (bf16) or 4 (fp32) aligned 16-byte
+// vectors, each entirely inside or entirely past the row.
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kBlock) void k3_mass(DrawArgs a) {
+__device__ __forceinline__ void load16(const void* row, int64_t lo, int64_t V, float (&z)[16]) {
+  if constexpr (VEC) {
+    constexpr int VE = (DT == kBF16) ? 8 : 4;
+    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const char*>(row) + lo * (DT == kBF16 ? 2 : 4));
+#pragma unroll
+    for (int u = 0; u < 16 / VE; ++u) {
+      u32x4 q = (lo + u * VE < V) ? p[u] : u32x4{0xff800000u, 0xff800000u, 0xff800000u, 0xff800000u};
+      if constexpr (DT == kBF16) {
+        if (!(lo + u * VE < V)) q = u32x4{0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};
+        z[u * 8 + 0] = bf16_lo(q.x); z[u * 8 + 1] = bf16_hi(q.x);
+        z[u * 8 + 2] = bf16_lo(q.y); z[u * 8 + 3] = bf16_hi(q.y);
+        z[u * 8 + 4] = bf16_lo(q.z); z[u * 8 + 5] = bf16_hi(q.z);
+        z[u * 8 + 6] = bf16_lo(q.w); z[u * 8 + 7] = bf16_hi(q.w);
+      } else {
+        z[u * 4 + 0] = __uint_as_float(q.x); z[u * 4 + 1] = __uint_as_float(q.y);
+        z[u * 4 + 2] = __uint_as_float(q.z); z[u * 4 + 3] = __uint_as_float(q.w);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) z[j] = (lo + j < V) ? load_logit<DT>(row, lo + j) : ninf();
+  }
+}
+
+// Inverse-CDF walk over sub-blocks [sb0, sb1) of the selected row, starting
+// from prefix `carry`: lane l owns elements [sb*1024 + 16 l, +16) in index
+// order; a wave inclusive scan of the lane sums finds the lane whose run
+// reaches t, and that lane walks its 16 weights. Returns the token, or -1 if
+// t is not reached (with t < 0: always), the final prefix in *total and the
+// last element of positive weight in *last.
+template <int DT, bool VEC>
+__device__ int wave_draw(const void* trow, const void* drow, const Weights& W, int64_t V,
+                         int64_t sb0, int64_t sb1, double carry, double t, int lane,
+                         double* total, int64_t* last) {
+  int64_t lastpos = -1;
+  for (int64_t sb = sb0; sb < sb1; ++sb) {
+    const int64_t lo = sb * kSub + (int64_t)lane * 16;
+    float w[16], zt[16], zd[16];
+    load16<DT, VEC>(trow, lo, V, zt);
+    if (W.residual) load16<DT, VEC>(drow, lo, V, zd);
+    double ls = 0.0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      w[j] = W(zt[j], W.residual ? zd[j] : 0.f);
+      if (w[j] > 0.f) lastpos = lo + j;
+      ls += (double)w[j];
+    }
+    const double incl = wave_inclusive_scan(ls, lane) + carry;
+    const double prev = __shfl_up(incl, 1, kWave);
+    const double excl = (lane == 0) ? carry : prev;
+    if (t >= 0.0) {
+      const uint64_t m = ballot(incl >= t);
+      if (m) {
+        const int L = first_lane(m);
+        int tok = -1;
+        if (lane == L) {
+          double cum = excl;
+          int64_t lp = -1;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            cum += (double)w[j];
+            if (w[j] > 0.f) lp = lo + j;
+            if (tok < 0 && w[j] > 0.f && t <= cum) tok = (int)(lo + j);
+          }
+          if (tok < 0) tok = (int)lp;  // rounding: stay inside the run that reached t
+        }
+        return __shfl(tok, L, kWave);
+      }
+    }
+    carry = __shfl(incl, kWave - 1, kWave);
+  }
+  if (total) *total = carry;
+  if (last) {
+    long long lp = lastpos;
+#pragma unroll
+    for (int off = kWave / 2; off >= 1; off >>= 1) lp = max(lp, (long long)__shfl_xor(lp, off, kWave));
+    *last = lp;
+  }
+  return -1;
+}
+
+// The final draw of sequence b by one wave: picks the sub-block that holds
+// u * total from the pass-2 masses, then walks that sub-block.
+template <int DT, bool VEC>
+__device__ int draw_token(const DrawArgs& a, int64_t b, const Select& s, int lane) {
+  constexpr int64_t esz = (DT == kBF16) ? 2 : 4;
+  const void* trow = static_cast<const char*>(a.target) + s.trow * a.V * esz;
+  const void* drow = (s.mode == kModeResidual) ? static_cast<const char*>(a.draft) + s.drow * a.V * esz : nullptr;
+  const double* sub = a.sub + b * a.nsub;
+  double total = 0.0;
+  wave_scan_subs(sub, a.nsub, -1.0, lane, nullptr, &total);
+  int token = -1;
+  if (total > 0.0) {
+    const double t = s.u * total;  // u in (0, 1]: t <= total
+    const Weights W = make_weights(s, false);
+    double base = 0.0;
+    const int64_t sb = wave_scan_subs(sub, a.nsub, t, lane, &base, nullptr);
+    int64_t last = -1;
+    if (sb >= 0) {
+      token = wave_draw<DT, VEC>(trow, drow, W, a.V, sb, sb + 1, base, t, lane, nullptr, &last);
+      if (token < 0) token = (int)last;
+    }
+    for (int64_t q = a.nsub - 1; token < 0 && q >= 0; --q) {
+      // rounding left t past every prefix: the last token of positive weight
+      if (!(sub[q] > 0.0)) continue;
+      wave_draw<DT, VEC>(trow, drow, W, a.V, q, q + 1, 0.0, -1.0, lane, nullptr, &last);
+      token = (int)last;
+    }
+  } else {
+    // The residual has no mass in fp32 (p_n == q_n to rounding): draw from p_n.
+    const Weights W = make_weights(s, true);
+    double tot = 0.0;
+    int64_t last = -1;
+    wave_draw<DT, VEC>(trow, nullptr, W, a.V, 0, a.nsub, 0.0, -1.0, lane, &tot, &last);
+    token = wave_draw<DT, VEC>(trow, nullptr, W, a.V, 0, a.nsub, 0.0, s.u * tot, lane, nullptr, nullptr);
+    if (token < 0) token = (int)last;
+  }
+  return token;
+}
+
+// Accept step and pass 2 in one launch: wave (b, c) first runs the accept
+// step of sequence b (every wave of b computes the same, wave c == 0 stores
+// it), then, for a sampling sequence, the weight mass max(0, p - q) (or p)
+// of chunk c of the selected row pair, written per 1024-element sub-block so
+// that the draw only has to scan one sub-block. A tile (EPI = 1024 or 2048
+// elements) holds one or two sub-blocks: in the bf16 vector tile, slots
+// 0..15 of every lane lie in the first 1024 elements.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kBlock) void k3_accept_mass(AcceptArgs acc, DrawArgs a) {
   using TL = Tile<DT, VEC>;
   constexpr int NE = TL::NE;
   constexpr int SUBS = TL::EPI / kSub;  // sub-blocks per tile (1 or 2)
@@ -449,7 +628,7 @@ __global__ __launch_bounds__(kBlock) void k3_mass(DrawArgs a) {
   if (item >= (int64_t)a.B * a.chunks3) return;
   const int64_t b = item / a.chunks3;
   const int c = (int)(item - b * a.chunks3);
-  const Select s = a.sel[b];
+  const Select s = accept_sequence<DT>(acc, b, lane, c == 0);
   if (s.mode == kModeNone) return;
   const Weights W = make_weights(s, false);
   constexpr int64_t esz = (DT == kBF16) ? 2 : 4;
@@ -487,192 +666,17 @@ __global__ __launch_bounds__(kBlock) void k3_mass(DrawArgs a) {
   }
 }
 
-// Inverse-CDF search inside [lo, hi) of the selected row: the smallest v with
-// t <= base + sum_{lo <= v' <= v} w_v'. Every thread owns 8 consecutive
-// elements per step; a workgroup inclusive scan (wave shuffles + LDS across
-// waves) locates the owning thread, which walks its 8 elements. Returns -1 if
-// rounding leaves t above the range's total (caller falls back).
-template <int DT>
-__device__ int block_draw(const void* trow, const void* drow, const Weights& W, int64_t lo,
-                          int64_t hi, double base, double t, double* total_out,
-                          int64_t* last_pos_out) {
-  __shared__ double sh_wave[kWavesPerBlock];
-  __shared__ int sh_found[kWavesPerBlock];
-  __shared__ int sh_tok;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int64_t last_pos = -1;
-  int token = -1;
-  __syncthreads();  // shared state of a previous call is no longer read
-  for (int64_t e = lo; e < hi; e += (int64_t)kBlock * 8) {
-    const int64_t my = e + (int64_t)tid * 8;
-    float w[8];
-    double ts = 0.0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int64_t v = my + j;
-      float wv = 0.f;
-      if (v < hi) {
-        const float zT = load_logit<DT>(trow, v);
-        const float zD = W.residual ? load_logit<DT>(drow, v) : 0.f;
-        wv = W(zT, zD);
-      }
-      w[j] = wv;
-      if (wv > 0.f) last_pos = v;
-      ts += (double)wv;
-    }
-    double incl = wave_inclusive_scan(ts, lane);
-    if (lane == 63) sh_wave[wave] = incl;
-    __syncthreads();
-    double wbase = 0.0, step_total = 0.0;
-    for (int q = 0; q < kWavesPerBlock; ++q) {
-      if (q < wave) wbase += sh_wave[q];
-      step_total += sh_wave[q];
-    }
-    incl += wbase;
-    const double excl = incl - ts;
-    const uint64_t m = ballot(base + incl >= t);
-    if (lane == 0) sh_found[wave] = m ? first_lane(m) : 64;
-    if (tid == 0) sh_tok = -1;
-    __syncthreads();
-    int owner = -1;
-    for (int q = 0; q < kWavesPerBlock; ++q)
-      if (sh_found[q] < 64) { owner = q * 64 + sh_found[q]; break; }
-    if (owner >= 0) {
-      if (tid == owner) {
-        double c = base + excl;
-        int tok = -1;
-        int64_t lastpos_here = -1;
-        for (int j = 0; j < 8; ++j) {
-          c += (double)w[j];
-          if (w[j] > 0.f) lastpos_here = my + j;
-          if (t <= c && tok < 0 && w[j] > 0.f) tok = (int)(my + j);
-        }
-        if (tok < 0) tok = (int)lastpos_here;  // rounding: stay inside the owning run
-        sh_tok = tok;
-      }
-      __syncthreads();
-      token = sh_tok;
-      __syncthreads();
-      break;
-    }
-    base += step_total;
-    __syncthreads();
-  }
-  // block-wide last positive element (rounding fallback of the caller)
-  __shared__ long long sh_last[kWavesPerBlock];
-  long long lp = last_pos;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) lp = max(lp, (long long)__shfl_xor(lp, off, 64));
-  if (lane == 0) sh_last[wave] = lp;
-  __syncthreads();
-  long long best = -1;
-  for (int q = 0; q < kWavesPerBlock; ++q) best = max(best, sh_last[q]);
-  if (last_pos_out) *last_pos_out = best;
-  if (total_out) *total_out = base;
-  __syncthreads();
-  return token;
-}
-
-// Workgroup inclusive scan of the sequence's sub-block masses, in passes of
-// kBlock entries with a carry. With t < 0 it only returns the total mass (the
-// inclusive prefix through the last entry); with t >= 0 it returns the first
-// sub-block whose inclusive prefix reaches t, with that prefix's exclusive
-// part in *base (-1 if none). Both modes perform the same additions in the
-// same order, so a t <= total always finds its sub-block.
-__device__ int64_t scan_subs(const double* sub, int64_t nsub, double t, double* base,
-                             double* total) {
-  __shared__ double sh_w[kWavesPerBlock];
-  __shared__ int sh_first[kWavesPerBlock];
-  __shared__ double sh_carry, sh_base;
-  __shared__ int64_t sh_hit;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  __syncthreads();  // every thread is done with the shared state of a previous call
-  if (tid == 0) {
-    sh_carry = 0.0;
-    sh_hit = -1;
-  }
-  __syncthreads();
-  for (int64_t p = 0; p < nsub; p += kBlock) {
-    const int64_t i = p + tid;
-    const double v = (i < nsub) ? sub[i] : 0.0;
-    double incl = wave_inclusive_scan(v, lane);
-    if (lane == 63) sh_w[wave] = incl;
-    __syncthreads();
-    double wb = sh_carry;
-    for (int q = 0; q < wave; ++q) wb += sh_w[q];
-    incl += wb;  // inclusive prefix through entry i
-    const double prev = __shfl_up(incl, 1, kWave);
-    const double excl = (lane == 0) ? wb : prev;
-    const uint64_t m = ballot(t >= 0.0 && i < nsub && incl >= t);
-    if (lane == 0) sh_first[wave] = m ? first_lane(m) : 64;
-    __syncthreads();
-    int owner = -1;
-    for (int q = 0; q < kWavesPerBlock; ++q)
-      if (sh_first[q] < 64) { owner = q * 64 + sh_first[q]; break; }
-    if (owner >= 0) {
-      if (tid == owner) {
-        sh_hit = i;
-        sh_base = excl;
-      }
-      __syncthreads();
-      if (base) *base = sh_base;
-      const int64_t hit = sh_hit;
-      __syncthreads();
-      return hit;
-    }
-    if (tid == kBlock - 1) sh_carry = incl;  // entries past nsub add exact zeros
-    __syncthreads();
-  }
-  if (total) *total = sh_carry;
-  __syncthreads();  // sh_carry has been read by every thread before it can be reset
-  return -1;
-}
-
-template <int DT>
-__global__ __launch_bounds__(kBlock) void k3_draw(DrawArgs a) {
-  const int64_t b = blockIdx.x;
+// The final draw: one wave per sampling sequence, in its own launch (the
+// kernel boundary orders every pass-2 store before the draw's reads).
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kBlock) void k4_draw(DrawArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t b = wave_uniform((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
   if (b >= a.B) return;
   const Select s = a.sel[b];
   if (s.mode == kModeNone) return;
-  constexpr int64_t esz = (DT == kBF16) ? 2 : 4;
-  const void* trow = static_cast<const char*>(a.target) + s.trow * a.V * esz;
-  const void* drow = (s.mode == kModeResidual) ? static_cast<const char*>(a.draft) + s.drow * a.V * esz : nullptr;
-  const double* sub = a.sub + b * a.nsub;
-  double total = 0.0;
-  scan_subs(sub, a.nsub, -1.0, nullptr, &total);
-  int token;
-  if (total > 0.0) {
-    const double t = s.u * total;  // u in (0, 1]: t <= total
-    double base = 0.0;
-    const int64_t hit = scan_subs(sub, a.nsub, t, &base, nullptr);
-    const Weights W = make_weights(s, false);
-    int64_t sb = hit, last_pos = -1;
-    if (sb < 0) {  // unreachable for t <= total; kept as a guard
-      sb = a.nsub - 1;
-      base = 0.0;
-    }
-    const int64_t lo = sb * kSub, hi = min(a.V, lo + kSub);
-    token = block_draw<DT>(trow, drow, W, lo, hi, base, t, nullptr, &last_pos);
-    if (token < 0) token = (int)last_pos;
-    if (token < 0) {  // the chosen sub-block holds no weight (rounding): last positive token
-      int64_t lp = -1;
-      for (int64_t q = a.nsub - 1; q >= 0 && lp < 0; --q) {
-        if (!(sub[q] > 0.0)) continue;
-        block_draw<DT>(trow, drow, W, q * kSub, min(a.V, (q + 1) * kSub), 0.0,
-                       __builtin_huge_val(), nullptr, &lp);
-      }
-      token = (int)lp;
-    }
-  } else {
-    // The residual has no mass in fp32 (p_n == q_n to rounding): draw from p_n.
-    const Weights W = make_weights(s, true);
-    double tot = 0.0;
-    int64_t last_pos = -1;
-    block_draw<DT>(trow, nullptr, W, 0, a.V, 0.0, __builtin_huge_val(), &tot, &last_pos);
-    token = block_draw<DT>(trow, nullptr, W, 0, a.V, 0.0, s.u * tot, nullptr, &last_pos);
-    if (token < 0) token = (int)last_pos;
-  }
-  if (threadIdx.x == 0) a.out_next[b] = token;
+  const int token = draw_token<DT, VEC>(a, b, s, lane);
+  if (lane == 0) a.out_next[b] = token;
 }
 
 // ----------------------------- test exports --------------------------------

@@ -13,9 +13,17 @@ using namespace specv;
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr int kK1ChunkBytes = 32768;  // pass-1 work item: 32 KiB of one row
+// Tuning constants (measured on MI355X; see the design notes).
+#ifndef SPECV_K1_CHUNK_BYTES
+#define SPECV_K1_CHUNK_BYTES 65536
+#endif
+#ifndef SPECV_MASS_WAVES
+#define SPECV_MASS_WAVES 8192
+#endif
+constexpr int kK1ChunkBytes = SPECV_K1_CHUNK_BYTES;  // pass-1 work item: bytes of one row (at least)
+constexpr int64_t kMaxChunks1 = 16;                  // pass-1 chunks per row (at most)
 constexpr int kDrawStep = kBlock * 8; // elements per workgroup scan step of the draw
-constexpr int64_t kTargetMassItems = 2048;  // pass-2 waves to aim for (8 per CU)
+constexpr int64_t kTargetMassItems = SPECV_MASS_WAVES;  // pass-2 waves to aim for
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -50,11 +58,16 @@ void make_plan(const specv_shape_t* s, Plan* p) {
   p->tt = s->total_target_rows;
   p->td = s->total_draft_rows;
   p->esz = (p->dt == kBF16) ? 2 : 4;
-  // pass 1: 32 KiB chunks (16384 bf16 / 8192 fp32 elements), a multiple of
-  // every tile's elements-per-iteration
-  p->chunk1_elems = (int)(kK1ChunkBytes / p->esz);
-  p->chunks1 = (int)((p->V + p->chunk1_elems - 1) / p->chunk1_elems);
-  // pass 2: enough chunks per sequence to give ~2048 waves in total
+  // pass 1: 64 KiB chunks (32768 bf16 / 16384 fp32 elements), widened for
+  // long rows so that a row has at most 16 chunks to merge; always a multiple
+  // of 2048 elements (every tile's elements-per-iteration divides it). Fewer
+  // chunks per row shorten the accept step's merge.
+  int64_t ch1 = kK1ChunkBytes / p->esz;
+  const int64_t wide = ((p->V + kMaxChunks1 - 1) / kMaxChunks1 + 2047) / 2048 * 2048;
+  if (wide > ch1) ch1 = wide;
+  p->chunk1_elems = (int)ch1;
+  p->chunks1 = (int)((p->V + ch1 - 1) / ch1);
+  // pass 2: enough chunks per sequence to give about kTargetMassItems waves
   int64_t c3 = (kTargetMassItems + p->B - 1) / (p->B > 0 ? p->B : 1);
   const int64_t max_c3 = (p->V + kDrawStep - 1) / kDrawStep;
   c3 = c3 < 1 ? 1 : (c3 > max_c3 ? max_c3 : c3);
@@ -189,7 +202,7 @@ specv_status_t launch_row_stats(const Plan& p, bool vec, const void* target, con
   return launched();
 }
 
-specv_status_t launch_accept(const Plan& p, const Call& c) {
+AcceptArgs accept_args(const Plan& p, const Call& c) {
   AcceptArgs a;
   a.target = c.target;
   a.draft = c.draft;
@@ -212,10 +225,7 @@ specv_status_t launch_accept(const Plan& p, const Call& c) {
   a.B = (int32_t)p.B;
   a.max_gamma = (int32_t)p.max_gamma;
   a.chunks = p.chunks1;
-  const dim3 grid(blocks_for(p.B)), block(kBlock);
-  if (p.dt == kBF16) hipLaunchKernelGGL((k2_accept<kBF16>), grid, block, 0, c.stream, a);
-  else hipLaunchKernelGGL((k2_accept<kF32>), grid, block, 0, c.stream, a);
-  return launched();
+  return a;
 }
 
 DrawArgs draw_args(const Plan& p, const Call& c) {
@@ -233,24 +243,30 @@ DrawArgs draw_args(const Plan& p, const Call& c) {
   return a;
 }
 
-specv_status_t launch_mass(const Plan& p, bool vec, const Call& c) {
+specv_status_t launch_accept_mass(const Plan& p, bool vec, const Call& c) {
+  const AcceptArgs acc = accept_args(p, c);
   const DrawArgs a = draw_args(p, c);
   const dim3 grid(blocks_for(p.B * p.chunks3)), block(kBlock);
   if (p.dt == kBF16) {
-    if (vec) hipLaunchKernelGGL((k3_mass<kBF16, true>), grid, block, 0, c.stream, a);
-    else hipLaunchKernelGGL((k3_mass<kBF16, false>), grid, block, 0, c.stream, a);
+    if (vec) hipLaunchKernelGGL((k3_accept_mass<kBF16, true>), grid, block, 0, c.stream, acc, a);
+    else hipLaunchKernelGGL((k3_accept_mass<kBF16, false>), grid, block, 0, c.stream, acc, a);
   } else {
-    if (vec) hipLaunchKernelGGL((k3_mass<kF32, true>), grid, block, 0, c.stream, a);
-    else hipLaunchKernelGGL((k3_mass<kF32, false>), grid, block, 0, c.stream, a);
+    if (vec) hipLaunchKernelGGL((k3_accept_mass<kF32, true>), grid, block, 0, c.stream, acc, a);
+    else hipLaunchKernelGGL((k3_accept_mass<kF32, false>), grid, block, 0, c.stream, acc, a);
   }
   return launched();
 }
 
-specv_status_t launch_draw(const Plan& p, const Call& c) {
+specv_status_t launch_draw(const Plan& p, bool vec, const Call& c) {
   const DrawArgs a = draw_args(p, c);
-  const dim3 grid((unsigned)p.B), block(kBlock);
-  if (p.dt == kBF16) hipLaunchKernelGGL((k3_draw<kBF16>), grid, block, 0, c.stream, a);
-  else hipLaunchKernelGGL((k3_draw<kF32>), grid, block, 0, c.stream, a);
+  const dim3 grid(blocks_for(p.B)), block(kBlock);
+  if (p.dt == kBF16) {
+    if (vec) hipLaunchKernelGGL((k4_draw<kBF16, true>), grid, block, 0, c.stream, a);
+    else hipLaunchKernelGGL((k4_draw<kBF16, false>), grid, block, 0, c.stream, a);
+  } else {
+    if (vec) hipLaunchKernelGGL((k4_draw<kF32, true>), grid, block, 0, c.stream, a);
+    else hipLaunchKernelGGL((k4_draw<kF32, false>), grid, block, 0, c.stream, a);
+  }
   return launched();
 }
 
@@ -270,14 +286,11 @@ specv_status_t run(const Call& c) {
   if ((st = launch_row_stats(p, vec, c.target, c.draft, c.ws, c.stream)) != SPECV_OK)
     return st;
   mark(c.events, 2 * SPECV_STAGE_ROWSTATS + 1, c.stream);
-  mark(c.events, 2 * SPECV_STAGE_ACCEPT, c.stream);
-  if ((st = launch_accept(p, c)) != SPECV_OK) return st;
-  mark(c.events, 2 * SPECV_STAGE_ACCEPT + 1, c.stream);
-  mark(c.events, 2 * SPECV_STAGE_RESIDUAL, c.stream);
-  if ((st = launch_mass(p, vec, c)) != SPECV_OK) return st;
-  mark(c.events, 2 * SPECV_STAGE_RESIDUAL + 1, c.stream);
+  mark(c.events, 2 * SPECV_STAGE_ACCEPT_MASS, c.stream);
+  if ((st = launch_accept_mass(p, vec, c)) != SPECV_OK) return st;
+  mark(c.events, 2 * SPECV_STAGE_ACCEPT_MASS + 1, c.stream);
   mark(c.events, 2 * SPECV_STAGE_DRAW, c.stream);
-  if ((st = launch_draw(p, c)) != SPECV_OK) return st;
+  if ((st = launch_draw(p, vec, c)) != SPECV_OK) return st;
   mark(c.events, 2 * SPECV_STAGE_DRAW + 1, c.stream);
   return SPECV_OK;
 }
