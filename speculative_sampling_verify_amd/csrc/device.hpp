@@ -53,6 +53,12 @@ __device__ __forceinline__ double rescale64(float m, float mn, float k) {
   return exp2((double)(m * k) - (double)ref_point(mn, k));
 }
 
+// The same factor from v_exp_f32 (within 1 ulp; exactly 1 when m == mn).
+__device__ __forceinline__ float rescale32(float m, float mn, float k) {
+  if (m == ninf()) return 0.f;
+  return exp2_hw(m * k - ref_point(mn, k));
+}
+
 template <int DT>
 __device__ __forceinline__ float load_logit(const void* base, int64_t idx) {
   if constexpr (DT == kBF16) {

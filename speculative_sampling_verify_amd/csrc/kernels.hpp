@@ -22,7 +22,7 @@
 
 namespace specv {
 
-// Statistics of one (row, chunk): s = sum over the chunk of
+// Statistics of one (row, chunk): s = sum over the chunk's elements of
 // 2^(fl32(z k - ref_point(m, k))) (sampling rows) or 0/NaN (greedy rows, NaN
 // flags a NaN/+inf logit); m = max; arg = lowest index attaining m.
 struct RowPart {
@@ -146,21 +146,34 @@ struct RowStatsArgs {
   RowPart* dparts;
   const uint32_t* status;
   int64_t total_t, total_d, V;
-  int32_t B, chunks, chunk_elems;
+  int32_t B, chunks;
 };
 
 // Pass-1 loop over one (row, chunk), double-buffered: the loads of tile it+1
-// are in flight while tile it is processed. `a` holds tile 0 on entry (the
-// caller issues it before its metadata lookups).
+// are in flight while tile it is processed. A row is cut into tiles of EPI
+// elements; chunk c of a row with C chunks is the tiles t = c, c + C, c + 2C,
+// ..., so the C waves of a row read neighbouring tiles at about the same time
+// (DRAM locality of the concurrently active waves). Within a lane, element
+// indices grow with the iteration. `a` holds tile c on entry (the caller
+// issues it before its metadata lookups).
 //
 // Sampling rows: online (max, sum). Per element: widen, max (v_max3), one fma
 // and one v_exp_f32 into a pairwise sum; the per-lane running sum is float64,
 // rescaled only when the lane's maximum grows. Greedy rows: max, argmax and
 // a NaN/+inf check only. For the argmax (greedy rows, or WITH_ARG) a lane
-// remembers the tile where its maximum last grew and re-reads that one tile
-// at the end.
+// remembers the iteration where its maximum last grew and re-reads that one
+// tile at the end.
+template <int DT, bool VEC>
+__device__ __forceinline__ void load_tile(const void* row, int64_t V, int64_t t, int lane,
+                                          typename Tile<DT, VEC>::Raw& r) {
+  using TL = Tile<DT, VEC>;
+  const int64_t e0 = t * TL::EPI;
+  if (e0 + TL::EPI <= V) TL::template load_raw<false>(row, e0, V, 0, lane, r);
+  else TL::template load_raw<true>(row, e0, V, 0, lane, r);
+}
+
 template <int DT, bool VEC, bool SAMPLING, bool WITH_ARG>
-__device__ __forceinline__ RowPart chunk_pass(const void* row, int64_t e0, int64_t e1, int n_full,
+__device__ __forceinline__ RowPart chunk_pass(const void* row, int64_t V, int c, int chunks,
                                               int n_iter, float k, int lane,
                                               typename Tile<DT, VEC>::Raw& a) {
   using TL = Tile<DT, VEC>;
@@ -193,12 +206,13 @@ __device__ __forceinline__ RowPart chunk_pass(const void* row, int64_t e0, int64
       m = fmaxf(m, g);
     }
   };
+  auto tile_of = [&](int it) { return (int64_t)c + (int64_t)it * chunks; };
   Raw b;
   for (int it = 0; it < n_iter; it += 2) {
-    if (it + 1 < n_iter) TL::load_raw(row, e0, e1, it + 1, n_full, lane, b);
+    if (it + 1 < n_iter) load_tile<DT, VEC>(row, V, tile_of(it + 1), lane, b);
     process(a, it);
     if (it + 1 >= n_iter) break;
-    if (it + 2 < n_iter) TL::load_raw(row, e0, e1, it + 2, n_full, lane, a);
+    if (it + 2 < n_iter) load_tile<DT, VEC>(row, V, tile_of(it + 2), lane, a);
     process(b, it + 1);
   }
   // wave merge: maximum first, then one rescale per lane and a float64 sum
@@ -213,11 +227,12 @@ __device__ __forceinline__ RowPart chunk_pass(const void* row, int64_t e0, int64
   int arg = INT32_MAX;
   if constexpr (ARG) {
     if (best >= 0 && m == M) {
+      const int64_t e0 = tile_of(best) * TL::EPI;
       float z[NE];
-      TL::template load<true>(row, e0, e1, best, lane, z);
+      TL::template load<true>(row, e0, V, 0, lane, z);
 #pragma unroll
       for (int j = NE - 1; j >= 0; --j)
-        if (z[j] == m) arg = (int)TL::index(e0, best, lane, j);
+        if (z[j] == m) arg = (int)TL::index(e0, 0, lane, j);
     }
     arg = wave_min(arg);
   }
@@ -237,11 +252,9 @@ __global__ __launch_bounds__(kBlock) void k1_row_stats(RowStatsArgs a) {
   const int64_t j = is_draft ? r - a.total_t : r;
   constexpr int64_t esz = (DT == kBF16) ? 2 : 4;
   const void* row = static_cast<const char*>(is_draft ? a.draft : a.target) + j * a.V * esz;
-  const int64_t e0 = (int64_t)c * a.chunk_elems;
-  const int64_t e1 = min(a.V, e0 + a.chunk_elems);
-  const int64_t n = e1 - e0;
-  const int n_full = (int)(n / TL::EPI), n_iter = (int)((n + TL::EPI - 1) / TL::EPI);
-  // Target rows are always read: tile 0 is in flight while the row's scale
+  const int64_t tiles = (a.V + TL::EPI - 1) / TL::EPI;  // >= chunks
+  const int n_iter = (int)((tiles - c + a.chunks - 1) / a.chunks);
+  // Target rows are always read: tile c is in flight while the row's scale
   // and the status word are looked up. Draft rows are read only for sampling
   // sequences, so their scale comes first.
   typename TL::Raw first;
@@ -249,18 +262,18 @@ __global__ __launch_bounds__(kBlock) void k1_row_stats(RowStatsArgs a) {
   if (is_draft) {
     k = a.dk[j];
     if (!(k > 0.f)) return;  // greedy (or invalid) sequence: draft row not needed
-    TL::load_raw(row, e0, e1, 0, n_full, lane, first);
+    load_tile<DT, VEC>(row, a.V, c, lane, first);
   } else {
-    TL::load_raw(row, e0, e1, 0, n_full, lane, first);
+    load_tile<DT, VEC>(row, a.V, c, lane, first);
     k = a.tk[j];
     if (!(k >= 0.f)) return;  // invalid temperature: the accept step fails the sequence
   }
   if (a.status[0] & kLayoutError) return;
   RowPart out;
   if (k > 0.f)
-    out = chunk_pass<DT, VEC, true, WITH_ARG>(row, e0, e1, n_full, n_iter, k, lane, first);
+    out = chunk_pass<DT, VEC, true, WITH_ARG>(row, a.V, c, a.chunks, n_iter, k, lane, first);
   else
-    out = chunk_pass<DT, VEC, false, true>(row, e0, e1, n_full, n_iter, 0.f, lane, first);
+    out = chunk_pass<DT, VEC, false, true>(row, a.V, c, a.chunks, n_iter, 0.f, lane, first);
   if (lane == 0) (is_draft ? a.dparts : a.tparts)[j * a.chunks + c] = out;
 }
 
@@ -274,11 +287,12 @@ struct RowStat {
 };
 
 __device__ __forceinline__ RowStat merge_row(const RowPart* p, int chunks, float k, bool sampling) {
-  // Chunks in index order, four loads in flight at a time: a running maximum
-  // (the first chunk attaining it gives the argmax), the running sum moved
-  // onto the new maximum's reference when it grows, and each group's terms
-  // moved onto the group's maximum; the float64 exp2 evaluations of a group
-  // are independent of each other.
+  // Chunks in order, four loads in flight at a time: a running maximum (the
+  // lowest index attaining it gives the argmax), the running sum moved onto
+  // the new maximum's reference when it grows, and each group's terms moved
+  // onto the group's maximum. The factors come from v_exp_f32 (within 1 ulp);
+  // the chunk that holds the maximum gets exactly 1, so the error only
+  // touches the other chunks' share of the sum, as in the in-chunk rescales.
   float M = ninf();
   double S = 0.0;
   int32_t arg = INT32_MAX;
@@ -290,14 +304,16 @@ __device__ __forceinline__ RowStat merge_row(const RowPart* p, int chunks, float
     float mg = M;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
+      // chunks interleave tiles: on equal maxima keep the lowest index
       if (q[u].m > mg) arg = q[u].arg;
+      else if (q[u].m == mg) arg = min(arg, q[u].arg);
       mg = fmaxf(mg, q[u].m);
     }
     if (sampling) {
       double add = 0.0;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) add += q[u].s * rescale64(q[u].m, mg, k);
-      S = S * rescale64(M, mg, k) + add;
+      for (int u = 0; u < 4; ++u) add += q[u].s * (double)rescale32(q[u].m, mg, k);
+      S = S * (double)rescale32(M, mg, k) + add;
     } else {
 #pragma unroll
       for (int u = 0; u < 4; ++u) S += q[u].s;

@@ -14,13 +14,13 @@ namespace {
 
 constexpr size_t kAlign = 256;
 // Tuning constants (measured on MI355X; see the design notes).
-#ifndef SPECV_K1_CHUNK_BYTES
-#define SPECV_K1_CHUNK_BYTES 65536
+#ifndef SPECV_K1_CHUNK_ELEMS
+#define SPECV_K1_CHUNK_ELEMS 16384
 #endif
 #ifndef SPECV_MASS_WAVES
 #define SPECV_MASS_WAVES 8192
 #endif
-constexpr int kK1ChunkBytes = SPECV_K1_CHUNK_BYTES;  // pass-1 work item: bytes of one row (at least)
+constexpr int64_t kK1ChunkElems = SPECV_K1_CHUNK_ELEMS;  // pass-1 work item: elements of one row
 constexpr int64_t kMaxChunks1 = 16;                  // pass-1 chunks per row (at most)
 constexpr int kDrawStep = kBlock * 8; // elements per workgroup scan step of the draw
 constexpr int64_t kTargetMassItems = SPECV_MASS_WAVES;  // pass-2 waves to aim for
@@ -31,7 +31,7 @@ struct Plan {
   int dt;
   int64_t B, V, max_gamma, tt, td;
   int64_t esz;
-  int chunks1, chunk1_elems;
+  int chunks1;
   int chunks3, chunk3_elems;
   int64_t nsub;
   size_t off_toff, off_doff, off_tk, off_dk, off_tparts, off_dparts, off_sel, off_sub;
@@ -58,15 +58,12 @@ void make_plan(const specv_shape_t* s, Plan* p) {
   p->tt = s->total_target_rows;
   p->td = s->total_draft_rows;
   p->esz = (p->dt == kBF16) ? 2 : 4;
-  // pass 1: 64 KiB chunks (32768 bf16 / 16384 fp32 elements), widened for
-  // long rows so that a row has at most 16 chunks to merge; always a multiple
-  // of 2048 elements (every tile's elements-per-iteration divides it). Fewer
-  // chunks per row shorten the accept step's merge.
-  int64_t ch1 = kK1ChunkBytes / p->esz;
-  const int64_t wide = ((p->V + kMaxChunks1 - 1) / kMaxChunks1 + 2047) / 2048 * 2048;
-  if (wide > ch1) ch1 = wide;
-  p->chunk1_elems = (int)ch1;
-  p->chunks1 = (int)((p->V + ch1 - 1) / ch1);
+  // pass 1: about kK1ChunkElems elements per (row, chunk) work item, at most
+  // 16 chunks per row (the accept step merges them); a chunk is every C-th
+  // tile of its row, so C never exceeds the row's tile count
+  int64_t c1 = (p->V + kK1ChunkElems - 1) / kK1ChunkElems;
+  c1 = c1 < 1 ? 1 : (c1 > kMaxChunks1 ? kMaxChunks1 : c1);
+  p->chunks1 = (int)c1;
   // pass 2: enough chunks per sequence to give about kTargetMassItems waves
   int64_t c3 = (kTargetMassItems + p->B - 1) / (p->B > 0 ? p->B : 1);
   const int64_t max_c3 = (p->V + kDrawStep - 1) / kDrawStep;
@@ -177,7 +174,6 @@ specv_status_t launch_row_stats(const Plan& p, bool vec, const void* target, con
   a.V = p.V;
   a.B = (int32_t)p.B;
   a.chunks = p.chunks1;
-  a.chunk_elems = p.chunk1_elems;
   const int64_t waves = (p.tt + p.td) * p.chunks1;
   if (waves == 0) return SPECV_OK;
   const dim3 grid(blocks_for(waves)), block(kBlock);
