@@ -368,13 +368,15 @@ __device__ Select accept_sequence(const AcceptArgs& a, int64_t b, int lane, bool
     }
     return s;
   };
-  if (a.status[0] & kLayoutError) return finish(-1, -1, false);
+  // independent loads first, so that they are in flight together
+  const uint32_t status = a.status[0];
   const int g = a.gamma[b];
   const float T = a.temperature[b];
+  const int64_t t0 = a.toff[b], d0 = a.doff[b];
+  if (status & kLayoutError) return finish(-1, -1, false);
   const bool greedy = (T == 0.f);
   const bool sampling = (T > 0.f) && (T < pinf());
   if (!greedy && !sampling) return finish(-1, -1, true);
-  const int64_t t0 = a.toff[b], d0 = a.doff[b];
   const float k = sampling ? temp_scale(T) : 0.f;
   RowStat st_t{}, st_d{};
   int x = 0;
