@@ -25,6 +25,12 @@ MUTANT_NONE = 0
 MUTANT_RESIDUAL_IS_P = 1
 MUTANT_RESIDUAL_IS_Q = 2
 MUTANT_N_PLUS_ONE = 3
+MUTANT_LENIENCE_TIMES = 4
+
+# lenience functions f(p, eps) of lossy decoding (DistillSpec section 4, the
+# paragraph on lossy SD; Algorithm A.1 thresholds)
+LENIENCE_NONE, LENIENCE_LIN, LENIENCE_SQ, LENIENCE_EXP = 0, 1, 2, 3
+LENIENCE = {"none": LENIENCE_NONE, "lin": LENIENCE_LIN, "sq": LENIENCE_SQ, "exp": LENIENCE_EXP}
 
 _lib = None
 
@@ -40,7 +46,8 @@ def _load():
     i64, u64 = ctypes.c_int64, ctypes.c_uint64
     lib.oracle_verify.restype = ctypes.c_int
     lib.oracle_verify.argtypes = [i64, i64, i64, ctypes.c_int, i64, i64, P, P, P, P, P,
-                                  u64, u64, P, P, P, P, P, P, P, P, ctypes.c_int]
+                                  u64, u64, ctypes.c_int, ctypes.c_float,
+                                  P, P, P, P, P, P, P, P, ctypes.c_int]
     lib.oracle_row_stats.restype = None
     lib.oracle_row_stats.argtypes = [P, ctypes.c_int, i64, i64, P, P, P, P, P]
     lib.oracle_softmax_row.restype = None
@@ -82,16 +89,19 @@ class VerifyResult:
     next_token: np.ndarray  # [B] int32 emitted token, -1 on a data error
     margin: np.ndarray     # [B] float64 smallest relative decision margin
     near_tie: np.ndarray   # [B] bool, margin < 1e-6
-    ratio: np.ndarray      # [B, max_gamma] float64 p_i(x_i)/q_i(x_i) (NaN if not reached)
+    ratio: np.ndarray      # [B, max_gamma] float64 f(p_i(x_i))/q_i(x_i) (NaN if not reached)
     resmass: np.ndarray    # [B] float64 total weight of the final draw (NaN if greedy)
     layout_ok: bool
 
 
 def verify(target, draft, tokens, gamma, temperature, *, vocab, max_gamma, seed=0,
-           row_offset=0, r=None, u=None, nthreads=None) -> VerifyResult:
+           row_offset=0, r=None, u=None, lenience="none", epsilon=1.0,
+           nthreads=None) -> VerifyResult:
     """Run the oracle over every sequence. ``r`` ([B, max_gamma] float32) and
     ``u`` ([B] float32) inject the uniforms instead of drawing them from
-    Philox4x32-10."""
+    Philox4x32-10. ``lenience`` ("none", "lin", "sq", "exp") and ``epsilon``
+    (a float32 in (0, 1]) select the threshold f(p, eps)/q of lossy
+    decoding."""
     lib = _load()
     gamma = np.ascontiguousarray(gamma, dtype=np.int32)
     B = int(gamma.shape[0])
@@ -115,7 +125,8 @@ def verify(target, draft, tokens, gamma, temperature, *, vocab, max_gamma, seed=
         u = np.ascontiguousarray(u, dtype=np.float32).reshape(B)
     code = lib.oracle_verify(B, vocab, max_gamma, _dtype_code(target), tt, td, _ptr(target),
                              _ptr(draft), _ptr(tokens), _ptr(gamma), _ptr(temperature),
-                             int(seed), int(row_offset), _ptr(r), _ptr(u), _ptr(out_n),
+                             int(seed), int(row_offset), LENIENCE[lenience],
+                             float(np.float32(epsilon)), _ptr(r), _ptr(u), _ptr(out_n),
                              _ptr(out_next), _ptr(margin), _ptr(near), _ptr(ratio),
                              _ptr(resmass), int(nthreads or default_threads()))
     return VerifyResult(out_n, out_next, margin, near.astype(bool),

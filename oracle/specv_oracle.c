@@ -8,11 +8,16 @@
  *
  * What it computes, and where the method is defined:
  *   - DistillSpec (Zhou et al., ICLR 2024), Appendix A.3, Algorithm A.1
- *     "Speculative decoding step", with lenience eps = 1 (lossless): compute
- *     the ratios p_i(x_i)/q_i(x_i), draw one uniform per draft position, take
- *     n = the first position whose uniform exceeds its ratio (gamma if none),
- *     then draw one more token from norm(max(0, p_n - q_n)) when n < gamma,
- *     or from p_gamma when every draft was accepted.
+ *     "Speculative decoding step": compute the thresholds
+ *     f(p_i(x_i), eps)/q_i(x_i), draw one uniform per draft position, take
+ *     n = the first position whose uniform exceeds its threshold (gamma if
+ *     none), then draw one more token from norm(max(0, p_n - q_n)) when
+ *     n < gamma, or from p_gamma when every draft was accepted. Lossless
+ *     decoding is f(p, eps) = p (eps = 1); lossy decoding uses one of the
+ *     lenience functions of DistillSpec section 4 (the paragraph on
+ *     DistillSpec with lossy SD): f_lin = p/eps, f_sq = p/eps^2, f_exp = p^eps, eps in (0, 1].
+ *     The residual of the final draw stays max(0, p - q) as the algorithm
+ *     prints it, whatever the lenience.
  *   - The same step as summarised from Leviathan, Kalman and Matias on
  *     "How speculative decoding lets a small model draft and a large one
  *     check" (1-indexed form of the same rule), and in prose in the study
@@ -67,6 +72,7 @@
 #define MUTANT_RESIDUAL_IS_P 1 /* residual replaced by p_n            */
 #define MUTANT_RESIDUAL_IS_Q 2 /* residual replaced by q_n            */
 #define MUTANT_N_PLUS_ONE 3    /* accepted count off by one (capped)  */
+#define MUTANT_LENIENCE_TIMES 4 /* f_lin applied as p * eps, not p / eps */
 static int g_mutant = MUTANT_NONE;
 
 void oracle_set_mutant(int m) { g_mutant = m; }
@@ -176,6 +182,28 @@ static void row_softmax(const double* z, int64_t V, double T, double* m_out, dou
 /* ------------------------------------------------------------------ */
 /* The verify step.                                                    */
 /* ------------------------------------------------------------------ */
+
+/* Lenience functions (DistillSpec section 4, lossy SD paragraph, and the
+ * thresholds of Algorithm A.1): f is
+ * increasing in p and decreasing in eps, and f(p, 1) = p for all three. */
+#define ORACLE_LENIENCE_NONE 0
+#define ORACLE_LENIENCE_LIN 1
+#define ORACLE_LENIENCE_SQ 2
+#define ORACLE_LENIENCE_EXP 3
+
+static double lenience(double p, int kind, double eps) {
+  switch (kind) {
+    case ORACLE_LENIENCE_LIN:
+      return g_mutant == MUTANT_LENIENCE_TIMES ? p * eps : p / eps;
+    case ORACLE_LENIENCE_SQ:
+      return p / (eps * eps);
+    case ORACLE_LENIENCE_EXP:
+      return pow(p, eps);
+    default:
+      return p;
+  }
+}
+
 typedef struct {
   int64_t batch, vocab, max_gamma;
   int dtype;
@@ -186,13 +214,15 @@ typedef struct {
   const int32_t* gamma;
   const float* temperature;
   uint64_t seed, row_offset;
+  int lenience;       /* ORACLE_LENIENCE_*                              */
+  double eps;         /* lenience parameter, in (0, 1]                  */
   const float* inj_r; /* [batch * max_gamma] or NULL: injected r_i      */
   const float* inj_u; /* [batch] or NULL: injected final-draw uniforms  */
   int32_t* out_n;
   int32_t* out_next;
   double* out_margin;  /* [batch] or NULL */
   uint8_t* out_near;   /* [batch] or NULL */
-  double* out_ratio;   /* [batch * max_gamma] or NULL: p_i(x_i)/q_i(x_i) */
+  double* out_ratio;   /* [batch * max_gamma] or NULL: f(p_i(x_i))/q_i(x_i) */
   double* out_resmass; /* [batch] or NULL: total weight of the final draw */
   const int64_t* toff;
   const int64_t* doff;
@@ -312,8 +342,8 @@ static void verify_sequence(const job_t* J, int64_t b, scratch_t* S) {
   const uint64_t philox_row = J->row_offset + (uint64_t)b;
   double margin = INFINITY;
 
-  /* Accept walk (Algorithm A.1 steps 5-7): ratio_i = p_i(x_i)/q_i(x_i),
-   * reject at the first i with r_i > ratio_i. */
+  /* Accept walk (Algorithm A.1 steps 5-7): ratio_i = f(p_i(x_i), eps) /
+   * q_i(x_i), reject at the first i with r_i > ratio_i. */
   int64_t n = g;
   for (int64_t i = 0; i < g; ++i) {
     const int32_t x = J->tokens[d0 + i];
@@ -324,7 +354,7 @@ static void verify_sequence(const job_t* J, int64_t b, scratch_t* S) {
     load_row(J->draft, J->dtype, V, d0 + i, S->zq);
     row_softmax(S->zq, V, T, &mq, &sq, NULL);
     const double q_x = exp((S->zq[x] - mq) / T) / sq;
-    const double ratio = (q_x == 0.0) ? INFINITY : p_x / q_x;
+    const double ratio = (q_x == 0.0) ? INFINITY : lenience(p_x, J->lenience, J->eps) / q_x;
     if (J->out_ratio) J->out_ratio[b * J->max_gamma + i] = ratio;
     double r;
     if (J->inj_r)
@@ -439,6 +469,7 @@ int oracle_verify(int64_t batch, int64_t vocab, int64_t max_gamma, int dtype,
                   int64_t total_target_rows, int64_t total_draft_rows, const void* target,
                   const void* draft, const int32_t* tokens, const int32_t* gamma,
                   const float* temperature, uint64_t seed, uint64_t row_offset,
+                  int lenience_kind, float eps,
                   const float* inj_r, const float* inj_u, int32_t* out_n, int32_t* out_next,
                   double* out_margin, uint8_t* out_near, double* out_ratio, double* out_resmass,
                   int nthreads) {
@@ -448,6 +479,7 @@ int oracle_verify(int64_t batch, int64_t vocab, int64_t max_gamma, int dtype,
   J.total_target_rows = total_target_rows; J.total_draft_rows = total_draft_rows;
   J.target = target; J.draft = draft; J.tokens = tokens; J.gamma = gamma;
   J.temperature = temperature; J.seed = seed; J.row_offset = row_offset;
+  J.lenience = lenience_kind; J.eps = (double)eps;
   J.inj_r = inj_r; J.inj_u = inj_u;
   J.out_n = out_n; J.out_next = out_next; J.out_margin = out_margin; J.out_near = out_near;
   J.out_ratio = out_ratio; J.out_resmass = out_resmass;

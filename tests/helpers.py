@@ -20,13 +20,14 @@ def pack(seqs, V, dtype="f32", name="hand"):
     return synth.Inputs(name, V, int(max(gam.max(initial=0), 1)), dtype, target, draft, tokens, gam, T)
 
 
-def run_oracle(x, r=None, u=None, seed=None, row_offset=None, max_gamma=None, nthreads=None):
+def run_oracle(x, r=None, u=None, seed=None, row_offset=None, max_gamma=None, nthreads=None,
+               lenience="none", epsilon=1.0):
     import oracle
     return oracle.verify(x.target, x.draft, x.tokens, x.gamma, x.temperature, vocab=x.vocab,
                          max_gamma=x.max_gamma if max_gamma is None else max_gamma,
                          seed=x.seed if seed is None else seed,
                          row_offset=x.row_offset if row_offset is None else row_offset,
-                         r=r, u=u, nthreads=nthreads)
+                         r=r, u=u, lenience=lenience, epsilon=epsilon, nthreads=nthreads)
 
 
 def subset(x, seqs):
