@@ -7,7 +7,11 @@ V = 32128, bf16 logits, T = 1) with 2,000 rounds batched as independent
 sequences into one call. Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                  [--lenience none|lin|sq|exp --epsilon E]
                   [--no-cpu-baseline] [--copy-calibration BYTES]
+
+With --lenience other than none, a step is one specv_verify_lenient call
+(lossy verification, threshold f(p, eps)/q) on the same workload.
 """
 import argparse
 import hashlib
@@ -57,7 +61,7 @@ def make_inputs(name):
     return getattr(synth, base)(**kw), desc
 
 
-def cpu_baseline(x, gpu_n, gpu_next, budget_s=12.0):
+def cpu_baseline(x, gpu_n, gpu_next, budget_s=12.0, lenience="none", epsilon=1.0):
     """The oracle as it stands, on the host's cores, over repeated passes of
     the same step's sequences (bounded by a time budget)."""
     import oracle
@@ -67,7 +71,7 @@ def cpu_baseline(x, gpu_n, gpu_next, budget_s=12.0):
     while True:
         res = oracle.verify(x.target, x.draft, x.tokens, x.gamma, x.temperature, vocab=x.vocab,
                             max_gamma=x.max_gamma, seed=x.seed, row_offset=x.row_offset,
-                            nthreads=threads)
+                            lenience=lenience, epsilon=epsilon, nthreads=threads)
         passes += 1
         el = time.perf_counter() - t0
         if el >= budget_s or el / passes * (passes + 1) > 2.5 * budget_s:
@@ -99,6 +103,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="t5xxl_like", choices=sorted(WORKLOADS))
+    ap.add_argument("--lenience", default="none", choices=["none", "lin", "sq", "exp"])
+    ap.add_argument("--epsilon", type=float, default=1.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="run only a plain device copy of this many bytes (counter calibration)")
@@ -150,7 +156,14 @@ def main():
 
     def step(i, events=None):
         s = sets[i % n_sets]
-        if events is None:
+        if args.lenience != "none":
+            svx.specv_verify_lenient(s["target"], s["draft"], s["draft_tokens"], s["gamma"],
+                                     s["temperature"], args.lenience, args.epsilon,
+                                     max_gamma=x.max_gamma, seed=x.seed,
+                                     philox_row_offset=x.row_offset, out_n=out_n,
+                                     out_next=out_next, workspace=ws, stream=stream,
+                                     events=events)
+        elif events is None:
             svx.specv_verify(s["target"], s["draft"], s["draft_tokens"], s["gamma"],
                              s["temperature"], max_gamma=x.max_gamma, seed=x.seed,
                              philox_row_offset=x.row_offset, out_n=out_n, out_next=out_next,
@@ -218,7 +231,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": desc, "batch": x.batch, "gamma": int(x.gamma.max()),
                    "vocab": x.vocab, "logits": x.dtype,
-                   "temperature": sorted(set(float(t) for t in x.temperature))},
+                   "temperature": sorted(set(float(t) for t in x.temperature)),
+                   "lenience": args.lenience,
+                   "epsilon": args.epsilon if args.lenience != "none" else 1.0},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": load_traffic(args.workload, sha),
@@ -229,13 +244,15 @@ def main():
         "ms_per_step_uninstrumented": ms_step_plain,
         "stage_ms_instrumented": stage_ms,
         "emitted_tokens_per_s": emitted / (ms_step * 1e-3),
+        "mean_tokens_per_sequence": emitted / x.batch,
         "sequences_per_s": x.batch / (ms_step * 1e-3),
         "rotating_input_sets": n_sets,
         "kernel_sha": sha,
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on the host")
-        result["cpu_baseline"] = cpu_baseline(x, n_host, next_host)
+        result["cpu_baseline"] = cpu_baseline(x, n_host, next_host, lenience=args.lenience,
+                                              epsilon=args.epsilon)
     print(json.dumps(result), flush=True)
 
 

@@ -121,6 +121,39 @@ specv_status_t specv_verify_with_uniforms(const specv_shape_t* shape, const void
                                           void* workspace, size_t workspace_bytes,
                                           hipStream_t stream);
 
+/* Lenience functions of lossy verification (DistillSpec section 4, the
+ * paragraph on DistillSpec with lossy SD, and the rejection thresholds of
+ * Algorithm A.1): a drafted token x is accepted with probability
+ * min(1, f(p(x), eps) / q(x)) instead of min(1, p(x) / q(x)). Each f grows
+ * with p, shrinks with eps, and f(p, 1) = p. */
+typedef enum {
+  SPECV_LENIENCE_NONE = 0, /* f = p: lossless                */
+  SPECV_LENIENCE_LIN = 1,  /* f = p / eps                    */
+  SPECV_LENIENCE_SQ = 2,   /* f = p / eps^2                  */
+  SPECV_LENIENCE_EXP = 3   /* f = p^eps                      */
+} specv_lenience_t;
+
+/* The verify step with lenience f and parameter epsilon in (0, 1] (ignored
+ * for SPECV_LENIENCE_NONE; epsilon == 1 is the lossless step). The final
+ * draw after a rejection still samples norm(max(0, p_n - q_n)), as
+ * Algorithm A.1 prints it, so for epsilon < 1 the output no longer follows
+ * the target distribution. Greedy sequences (T_b == 0) are unaffected: their
+ * p is one-hot, f(0, eps) = 0 and f(1, eps) >= 1. The f value, threshold and
+ * comparison are float64. r and u: both NULL draws the uniforms from Philox
+ * as specv_verify does; both given injects them as in
+ * specv_verify_with_uniforms (r may be NULL when max_gamma == 0). An
+ * unknown lenience, an epsilon outside (0, 1] (NaN included) or r without u
+ * is SPECV_ERR_INVALID_ARGUMENT. `events` is NULL or stage events as in
+ * specv_verify_profiled. Everything else as specv_verify. */
+specv_status_t specv_verify_lenient(const specv_shape_t* shape, const void* target_logits,
+                                    const void* draft_logits, const int32_t* draft_tokens,
+                                    const int32_t* gamma_per_row, const float* temperature,
+                                    specv_lenience_t lenience, float epsilon, uint64_t seed,
+                                    uint64_t philox_row_offset, const float* r, const float* u,
+                                    int32_t* out_n_accepted, int32_t* out_next_token,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                    hipEvent_t* events);
+
 /* Stages of one call, in launch order (one kernel each). */
 #define SPECV_STAGE_PLAN 0        /* offsets of the packed rows, per-row T scale */
 #define SPECV_STAGE_ROWSTATS 1    /* pass 1: max, sum of exp (argmax) per row    */

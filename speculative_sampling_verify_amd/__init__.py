@@ -20,6 +20,7 @@ SPECV_MAX_GAMMA = 63
 SPECV_DEV_SEQ_ERROR = 1
 SPECV_DEV_LAYOUT_ERROR = 2
 STAGES = ("plan", "row_stats", "accept_and_mass", "draw")
+LENIENCE = {"none": 0, "lin": 1, "sq": 2, "exp": 3}
 
 if not LIBRARY.exists():
     raise ImportError("libspecverify.so is not built (run __graft_entry__.build() or "
@@ -45,6 +46,9 @@ _lib.specv_verify_profiled.restype = ctypes.c_int
 _lib.specv_verify_profiled.argtypes = [_SHP, _P, _P, _P, _P, _P, _u64, _u64, _P, _P, _P, _sz, _P, _P]
 _lib.specv_verify_with_uniforms.restype = ctypes.c_int
 _lib.specv_verify_with_uniforms.argtypes = [_SHP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _sz, _P]
+_lib.specv_verify_lenient.restype = ctypes.c_int
+_lib.specv_verify_lenient.argtypes = [_SHP, _P, _P, _P, _P, _P, ctypes.c_int, ctypes.c_float, _u64,
+                                      _u64, _P, _P, _P, _P, _P, _sz, _P, _P]
 _lib.specv_row_stats.restype = ctypes.c_int
 _lib.specv_row_stats.argtypes = [_SHP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _sz, _P]
 _lib.specv_softmax_rows.restype = ctypes.c_int
@@ -57,7 +61,7 @@ _lib.specv_status_string.restype = ctypes.c_char_p
 _lib.specv_status_string.argtypes = [ctypes.c_int]
 
 EXPORTED = ("specv_workspace_bytes", "specv_verify", "specv_verify_profiled",
-            "specv_verify_with_uniforms", "specv_row_stats", "specv_softmax_rows",
+            "specv_verify_with_uniforms", "specv_verify_lenient", "specv_row_stats", "specv_softmax_rows",
             "specv_philox4x32_10", "specv_copy_bytes", "specv_status_string")
 
 
@@ -193,6 +197,28 @@ def specv_verify_with_uniforms(target, draft, draft_tokens, gamma, temperature, 
                                          _ptr(workspace), workspace.numel(),
                                          _stream(stream, target.device))
     _check(st, "specv_verify_with_uniforms")
+    return out_n, out_next
+
+
+def specv_verify_lenient(target, draft, draft_tokens, gamma, temperature, lenience, epsilon, *,
+                         max_gamma=None, seed=0, philox_row_offset=0, r=None, u=None, out_n=None,
+                         out_next=None, workspace=None, stream=None, events=None):
+    """Lossy verify step: threshold f(p, epsilon)/q with lenience "none",
+    "lin" (p/eps), "sq" (p/eps^2) or "exp" (p^eps). Uniforms from Philox
+    unless r [B, max_gamma] and u [B] are given; ``events`` is an optional
+    StageEvents."""
+    shape, draft, draft_tokens, gamma, out_n, out_next, workspace = _common(
+        target, draft, draft_tokens, gamma, temperature, max_gamma, out_n, out_next, workspace)
+    _check_tensors(target.device, r=r, u=u)
+    kind = LENIENCE[lenience] if isinstance(lenience, str) else int(lenience)
+    st = _lib.specv_verify_lenient(ctypes.byref(shape), _ptr(target), _ptr(draft),
+                                   _ptr(draft_tokens), _ptr(gamma), _ptr(temperature), kind,
+                                   float(epsilon), int(seed), int(philox_row_offset), _ptr(r),
+                                   _ptr(u), _ptr(out_n), _ptr(out_next), _ptr(workspace),
+                                   workspace.numel(), _stream(stream, target.device),
+                                   None if events is None else
+                                   ctypes.cast(events.array, ctypes.c_void_p))
+    _check(st, "specv_verify_lenient")
     return out_n, out_next
 
 

@@ -33,6 +33,9 @@ struct RowPart {
 
 // What the final draw of one sampling sequence needs (written by the accept step).
 enum : int32_t { kModeNone = 0, kModeResidual = 1, kModeBonus = 2 };
+// Lenience functions f(p, eps) of the acceptance threshold f(p, eps)/q
+// (DistillSpec section 4, lossy SD paragraph; Algorithm A.1 thresholds).
+enum : int32_t { kLenNone = 0, kLenLin = 1, kLenSq = 2, kLenExp = 3 };
 struct Select {
   int32_t mode;
   int32_t n;
@@ -348,7 +351,19 @@ struct AcceptArgs {
   uint64_t seed, row_offset;
   int64_t V;
   int32_t B, max_gamma, chunks;
+  int32_t lenience;  // kLen*; kLenNone is the lossless step
+  float eps;         // lenience parameter in (0, 1)
 };
+
+// f(p, eps): p / eps, p / eps^2 or p^eps, in float64 (f(p, 1) = p; the host
+// passes kLenNone for eps = 1).
+__device__ __forceinline__ double lenient(double p, int32_t kind, float eps) {
+  const double e = (double)eps;
+  if (kind == kLenLin) return p / e;
+  if (kind == kLenSq) return p / (e * e);
+  if (kind == kLenExp) return pow(p, e);
+  return p;
+}
 
 // The accept step of one sequence, by one wave; lane i owns draft position i
 // and target row i. Returns the selection for the final draw (kModeNone for
@@ -416,7 +431,7 @@ __device__ Select accept_sequence(const AcceptArgs& a, int64_t b, int lane, bool
     const float zD = load_logit<DT>(a.draft, (d0 + lane) * a.V + x);
     const double p = exp2((double)zT * (double)k - (double)st_t.rk) / st_t.s;
     const double q = exp2((double)zD * (double)k - (double)st_d.rk) / st_d.s;
-    const double ratio = (q == 0.0) ? (double)pinf() : p / q;
+    const double ratio = (q == 0.0) ? (double)pinf() : lenient(p, a.lenience, a.eps) / q;
     rej = r > ratio;
   }
   const uint64_t mask = ballot(rej);

@@ -108,6 +108,8 @@ struct Call {
   size_t ws_bytes;
   hipStream_t stream;
   hipEvent_t* events;
+  int32_t lenience = kLenNone;
+  float eps = 1.f;
 };
 
 specv_status_t check_common(const specv_shape_t* shape, const void* target, const void* draft,
@@ -221,6 +223,8 @@ AcceptArgs accept_args(const Plan& p, const Call& c) {
   a.B = (int32_t)p.B;
   a.max_gamma = (int32_t)p.max_gamma;
   a.chunks = p.chunks1;
+  a.lenience = c.lenience;
+  a.eps = c.eps;
   return a;
 }
 
@@ -340,6 +344,29 @@ specv_status_t specv_verify_with_uniforms(const specv_shape_t* shape, const void
   Call c{shape, target_logits, draft_logits, draft_tokens, gamma_per_row, temperature,
          0, 0, r ? r : u, u, out_n_accepted, out_next_token,
          workspace, workspace_bytes, stream, nullptr};
+  return run(c);
+}
+
+specv_status_t specv_verify_lenient(const specv_shape_t* shape, const void* target_logits,
+                                    const void* draft_logits, const int32_t* draft_tokens,
+                                    const int32_t* gamma_per_row, const float* temperature,
+                                    specv_lenience_t lenience, float epsilon, uint64_t seed,
+                                    uint64_t philox_row_offset, const float* r, const float* u,
+                                    int32_t* out_n_accepted, int32_t* out_next_token,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                    hipEvent_t* events) {
+  if ((int)lenience < SPECV_LENIENCE_NONE || (int)lenience > SPECV_LENIENCE_EXP)
+    return SPECV_ERR_INVALID_ARGUMENT;
+  if (lenience != SPECV_LENIENCE_NONE && !(epsilon > 0.f && epsilon <= 1.f))
+    return SPECV_ERR_INVALID_ARGUMENT;
+  const bool need_r = shape && shape->max_gamma > 0 && shape->batch > 0;
+  if (u ? (need_r && !r) : (r != nullptr)) return SPECV_ERR_INVALID_ARGUMENT;
+  Call c{shape, target_logits, draft_logits, draft_tokens, gamma_per_row, temperature,
+         seed, philox_row_offset, u ? (r ? r : u) : nullptr, u, out_n_accepted, out_next_token,
+         workspace, workspace_bytes, stream, events};
+  // f(p, 1) = p for every lenience function: eps = 1 is the lossless step
+  c.lenience = (epsilon == 1.f) ? kLenNone : (int32_t)lenience;
+  c.eps = epsilon;
   return run(c);
 }
 

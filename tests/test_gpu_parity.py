@@ -350,3 +350,79 @@ def test_gpu_output_law_chi_square(svx, rounds):
     orc = run_oracle(x)
     mism = ((n != orc.n) | (nxt != orc.next_token)) & ~orc.near_tie
     assert mism.sum() == 0
+
+
+# --------------------------------------------------- lossy verification
+
+def run_gpu_lenient(svx, x, kind, eps, r=None, u=None):
+    d = svx.from_inputs(x)
+    ws = svx.workspace_for(svx._shape_of(d["target"], d["draft"], d["gamma"], x.max_gamma), "cuda")
+    rt = None if r is None else torch.from_numpy(np.ascontiguousarray(r, np.float32)).cuda()
+    ut = None if u is None else torch.from_numpy(np.ascontiguousarray(u, np.float32)).cuda()
+    n, nxt = svx.specv_verify_lenient(d["target"], d["draft"], d["draft_tokens"], d["gamma"],
+                                      d["temperature"], kind, eps, max_gamma=x.max_gamma,
+                                      seed=x.seed, philox_row_offset=x.row_offset, r=rt, u=ut,
+                                      workspace=ws)
+    torch.cuda.synchronize()
+    return n.cpu().numpy(), nxt.cpu().numpy(), svx.read_status(ws)
+
+
+LENIENT_CASES = [("lin", 0.5), ("lin", 0.05), ("sq", 0.7), ("sq", 0.1), ("exp", 0.5),
+                 ("exp", 0.05)]
+
+
+@pytest.mark.parametrize("kind,eps", LENIENT_CASES, ids=["%s-%g" % c for c in LENIENT_CASES])
+def test_lenient_parity_t5xxl_like(svx, kind, eps):
+    # bf16, V = 32128: several pass-1 chunks per row
+    x = synth.t5xxl_like(rounds=96)
+    log("[case] lenient %s eps=%g t5xxl_like B=%d" % (kind, eps, x.batch))
+    got = run_gpu_lenient(svx, x, kind, eps)
+    orc = run_oracle(x, lenience=kind, epsilon=eps)
+    assert got[2] == 0
+    assert_parity("lenient %s %g" % (kind, eps), x, got, orc)
+
+
+def test_lenient_parity_mixed_greedy_fp32(svx):
+    # fp32, odd sequences greedy (lenience must not touch them), V = 256000
+    x = synth.large_vocab(batch=6)
+    log("[case] lenient sq 0.3 large_vocab B=%d" % x.batch)
+    got = run_gpu_lenient(svx, x, "sq", 0.3)
+    orc = run_oracle(x, lenience="sq", epsilon=0.3)
+    assert_parity("lenient sq 0.3 large_vocab", x, got, orc)
+    base = run_gpu(svx, x)
+    greedy = x.temperature == 0
+    np.testing.assert_array_equal(got[0][greedy], base[0][greedy])
+    np.testing.assert_array_equal(got[1][greedy], base[1][greedy])
+
+
+@pytest.mark.parametrize("kind", ["none", "lin", "sq", "exp"])
+def test_lenient_eps_one_equals_lossless(svx, kind):
+    x = synth.tiny_cpu(rounds=512)
+    log("[case] lenient %s eps=1 tiny_cpu" % kind)
+    got = run_gpu_lenient(svx, x, kind, 1.0)
+    base = run_gpu(svx, x)
+    np.testing.assert_array_equal(got[0], base[0])
+    np.testing.assert_array_equal(got[1], base[1])
+
+
+def test_lenient_injected_uniforms_and_monotone(svx):
+    x = synth.tiny_cpu(rounds=512, vocab=64, gamma=6, gen_seed=5)
+    rng = np.random.default_rng(21)
+    r = ((rng.integers(0, 2**24, (x.batch, x.max_gamma)) + 1) * EPS24).astype(np.float32)
+    u = ((rng.integers(0, 2**24, x.batch) + 1) * EPS24).astype(np.float32)
+    log("[case] lenient injected uniforms tiny_cpu V=64")
+    prev = None
+    for eps in [1.0, 0.6, 0.2, 0.02]:
+        got = run_gpu_lenient(svx, x, "lin", eps, r=r, u=u)
+        orc = run_oracle(x, r=r, u=u, lenience="lin", epsilon=eps)
+        assert_parity("lenient lin %g injected" % eps, x, got, orc)
+        if prev is not None:
+            assert (got[0] >= prev).all()
+        prev = got[0]
+
+
+def test_lenient_argument_errors(svx):
+    x = synth.tiny_cpu(rounds=4)
+    for kind, eps in [("lin", 0.0), ("sq", -0.5), ("exp", 1.5), ("lin", float("nan")), (7, 0.5)]:
+        with pytest.raises(svx.SpecvError):
+            run_gpu_lenient(svx, x, kind, eps)
