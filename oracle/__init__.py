@@ -48,6 +48,9 @@ def _load():
     lib.oracle_verify.argtypes = [i64, i64, i64, ctypes.c_int, i64, i64, P, P, P, P, P,
                                   u64, u64, ctypes.c_int, ctypes.c_float,
                                   P, P, P, P, P, P, P, P, ctypes.c_int]
+    lib.oracle_position_diagnostics.restype = ctypes.c_int
+    lib.oracle_position_diagnostics.argtypes = [i64, i64, ctypes.c_int, i64, i64, P, P, P, P, i64,
+                                                P, P, P, P]
     lib.oracle_row_stats.restype = None
     lib.oracle_row_stats.argtypes = [P, ctypes.c_int, i64, i64, P, P, P, P, P]
     lib.oracle_softmax_row.restype = None
@@ -131,6 +134,35 @@ def verify(target, draft, tokens, gamma, temperature, *, vocab, max_gamma, seed=
                              _ptr(resmass), int(nthreads or default_threads()))
     return VerifyResult(out_n, out_next, margin, near.astype(bool),
                         ratio[:, :max_gamma], resmass, code == 0)
+
+
+@dataclass
+class Diagnostics:
+    alpha: np.ndarray        # [draft rows] float64 sum_v min(p_v, q_v)
+    entropy: np.ndarray      # [draft rows] float64 -sum_v q_v ln q_v
+    topk_index: np.ndarray   # [draft rows, k] int32, most probable first
+    topk_prob: np.ndarray    # [draft rows, k] float64 q of those tokens
+
+
+def position_diagnostics(target, draft, gamma, temperature, *, vocab, top_k) -> Diagnostics:
+    """Per draft position: acceptance probability alpha = sum min(p, q),
+    draft entropy and the top-k draft tokens (packed draft-row order)."""
+    lib = _load()
+    gamma = np.ascontiguousarray(gamma, dtype=np.int32)
+    target = np.ascontiguousarray(target)
+    draft = np.ascontiguousarray(draft)
+    temperature = np.ascontiguousarray(temperature, dtype=np.float32)
+    tt, td = target.size // vocab, draft.size // vocab
+    k = int(top_k)
+    alpha, ent = np.empty(td, np.float64), np.empty(td, np.float64)
+    idx, prob = np.empty((td, k), np.int32), np.empty((td, k), np.float64)
+    code = lib.oracle_position_diagnostics(gamma.shape[0], vocab, _dtype_code(target), tt, td,
+                                           _ptr(target), _ptr(draft), _ptr(gamma),
+                                           _ptr(temperature), k, _ptr(alpha), _ptr(ent), _ptr(idx),
+                                           _ptr(prob))
+    if code != 0:
+        raise ValueError("gammas and row totals disagree")
+    return Diagnostics(alpha, ent, idx, prob)
 
 
 def row_stats(logits, vocab, temperature_per_row):

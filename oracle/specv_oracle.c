@@ -525,3 +525,97 @@ void oracle_softmax_row(const void* logits, int dtype, int64_t vocab, int64_t ro
 void oracle_philox_blocks(uint64_t seed, const uint32_t* ctr, uint32_t* out, int64_t count) {
   for (int64_t k = 0; k < count; ++k) oracle_philox4x32_10(seed, ctr + 4 * k, out + 4 * k);
 }
+
+/* ------------------------------------------------------------------ */
+/* Per-position diagnostics of a packed batch.                         */
+/* ------------------------------------------------------------------ */
+
+/* For every draft position i < gamma_b of every sequence b (output index:
+ * the packed draft row doff[b] + i), with p = p_i and q = q_i the
+ * temperature softmaxes of target row i and draft row i:
+ *   alpha   = sum_v min(p_v, q_v): the acceptance probability of a token
+ *             drafted from q (DistillSpec section 3, and its section 4
+ *             reading 1 - alpha as the total variation distance);
+ *   entropy = -sum_v q_v ln q_v (0 ln 0 = 0), the Ent(y^D_i) feature of
+ *             DISCO's stopping classifier (DISCO section 3, Eq. 2);
+ *   top-k   = the k most probable draft tokens and their q, the Top_k(y^D_i)
+ *             feature of the same equation, most probable first; equal
+ *             logits rank the lower index first.
+ * Greedy sequences (T = 0) use the zero-temperature limits that greedy
+ * verification uses: p and q one-hot at their argmax (lowest index), so
+ * alpha is 1 when the two argmaxes agree and 0 otherwise, the entropy is 0
+ * and the top-1 probability is 1. A position whose target or draft row is
+ * unusable (NaN, +inf, no finite logit) or whose T is NaN, negative or +inf
+ * gets alpha = entropy = NaN, indices -1 and probabilities NaN.
+ * Returns 1 (and writes nothing) when the gammas and row totals disagree. */
+int oracle_position_diagnostics(int64_t batch, int64_t vocab, int dtype, int64_t total_target_rows,
+                                int64_t total_draft_rows, const void* target, const void* draft,
+                                const int32_t* gamma, const float* temperature, int64_t top_k,
+                                double* out_alpha, double* out_entropy, int32_t* out_topk_index,
+                                double* out_topk_prob) {
+  int64_t st = 0, sd = 0;
+  for (int64_t b = 0; b < batch; ++b) {
+    if (gamma[b] < 0) return 1;
+    st += gamma[b] + 1;
+    sd += gamma[b];
+  }
+  if (st != total_target_rows || sd != total_draft_rows) return 1;
+  const int64_t V = vocab;
+  double* zp = (double*)malloc((size_t)V * sizeof(double));
+  double* zq = (double*)malloc((size_t)V * sizeof(double));
+  double* p = (double*)malloc((size_t)V * sizeof(double));
+  double* q = (double*)malloc((size_t)V * sizeof(double));
+  uint8_t* taken = (uint8_t*)malloc((size_t)V);
+  int64_t t0 = 0, d0 = 0;
+  for (int64_t b = 0; b < batch; ++b) {
+    const int64_t g = gamma[b];
+    const double T = (double)temperature[b];
+    for (int64_t i = 0; i < g; ++i) {
+      const int64_t j = d0 + i;
+      load_row(target, dtype, V, t0 + i, zp);
+      load_row(draft, dtype, V, d0 + i, zq);
+      const int ok = row_is_valid(zp, V) && row_is_valid(zq, V) && !isnan(T) && T >= 0.0 &&
+                     !isinf(T);
+      if (!ok) {
+        out_alpha[j] = NAN;
+        out_entropy[j] = NAN;
+        for (int64_t k = 0; k < top_k; ++k) {
+          out_topk_index[j * top_k + k] = -1;
+          out_topk_prob[j * top_k + k] = NAN;
+        }
+        continue;
+      }
+      if (T == 0.0) {
+        const int64_t ap = row_argmax(zp, V), aq = row_argmax(zq, V);
+        for (int64_t v = 0; v < V; ++v) {
+          p[v] = (v == ap) ? 1.0 : 0.0;
+          q[v] = (v == aq) ? 1.0 : 0.0;
+        }
+      } else {
+        row_softmax(zp, V, T, NULL, NULL, p);
+        row_softmax(zq, V, T, NULL, NULL, q);
+      }
+      double a = 0.0, h = 0.0;
+      for (int64_t v = 0; v < V; ++v) {
+        a += p[v] < q[v] ? p[v] : q[v];
+        if (q[v] > 0.0) h -= q[v] * log(q[v]);
+      }
+      out_alpha[j] = a;
+      out_entropy[j] = h;
+      /* top-k by repeated selection of the best token not yet taken */
+      memset(taken, 0, (size_t)V);
+      for (int64_t k = 0; k < top_k; ++k) {
+        int64_t best = -1;
+        for (int64_t v = 0; v < V; ++v)
+          if (!taken[v] && (best < 0 || zq[v] > zq[best])) best = v;
+        taken[best] = 1;
+        out_topk_index[j * top_k + k] = (int32_t)best;
+        out_topk_prob[j * top_k + k] = q[best];
+      }
+    }
+    t0 += g + 1;
+    d0 += g;
+  }
+  free(zp); free(zq); free(p); free(q); free(taken);
+  return 0;
+}
