@@ -11,7 +11,9 @@ sequences into one call. Prints one JSON line.
                   [--no-cpu-baseline] [--copy-calibration BYTES]
 
 With --lenience other than none, a step is one specv_verify_lenient call
-(lossy verification, threshold f(p, eps)/q) on the same workload.
+(lossy verification, threshold f(p, eps)/q) on the same workload. With
+--diagnostics K, a step is one specv_position_diagnostics call (alpha,
+draft entropy and top-K per draft position) on the same workload.
 """
 import argparse
 import hashlib
@@ -39,6 +41,7 @@ WORKLOADS = {
     "large_vocab": (dict(), "large vocab: B=128, gamma=8, V=256000, fp32, odd rows greedy"),
 }
 KERNEL_SOURCES = ["speculative_sampling_verify_amd/csrc/kernels.hpp",
+                  "speculative_sampling_verify_amd/csrc/diagnostics.hpp",
                   "speculative_sampling_verify_amd/csrc/device.hpp",
                   "speculative_sampling_verify_amd/csrc/specverify.hip"]
 
@@ -97,6 +100,104 @@ def load_traffic(workload, sha):
     return rec.get("traffic_bytes_per_launch")
 
 
+def diag_cpu_baseline(x, k, budget_s=12.0):
+    """The oracle's diagnostics on the host, over a bounded prefix of the
+    step's sequences."""
+    import oracle
+    toff, doff = x.offsets()
+    nb, t0 = 1, time.perf_counter()
+    done_pos, el = 0, 0.0
+    while True:
+        t = time.perf_counter()
+        sub_t = x.target[:toff[nb]]
+        sub_d = x.draft[:doff[nb]]
+        oracle.position_diagnostics(sub_t, sub_d, x.gamma[:nb], x.temperature[:nb],
+                                    vocab=x.vocab, top_k=k)
+        el += time.perf_counter() - t
+        done_pos += int(doff[nb])
+        if el >= budget_s or nb >= x.batch:
+            break
+        nb = min(x.batch, nb * 2)
+    return {"value": done_pos / el, "unit": "diagnosed draft positions/s", "cores": 1,
+            "kind": "oracle",
+            "sample": "prefixes of the step's sequences (%d positions in all), %.1f s"
+                      % (done_pos, el)}
+
+
+def bench_diagnostics(args, torch, svx, dev):
+    t_gen = time.perf_counter()
+    x, desc = make_inputs(args.workload)
+    log("[bench] generated %s in %.1f s" % (args.workload, time.perf_counter() - t_gen))
+    k = args.diagnostics
+    base = svx.from_inputs(x, dev)
+    set_bytes = sum(t.numel() * t.element_size() for t in (base["target"], base["draft"]))
+    n_sets = max(2, int(np.ceil(4 * MALL_BYTES / max(1, set_bytes))))
+    sets = [base] + [{kk: v.clone() for kk, v in base.items()} for _ in range(n_sets - 1)]
+    shape = svx._shape_of(base["target"], base["draft"], base["gamma"], x.max_gamma)
+    ws = torch.empty(svx.specv_diagnostics_workspace_bytes(shape, k), dtype=torch.uint8,
+                     device=dev)
+    td = x.total_draft_rows
+    out = {"alpha": torch.empty(td, dtype=torch.float64, device=dev),
+           "entropy": torch.empty(td, dtype=torch.float64, device=dev),
+           "topk_index": torch.empty((td, k), dtype=torch.int32, device=dev),
+           "topk_prob": torch.empty((td, k), dtype=torch.float64, device=dev)}
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, events=None):
+        s = sets[i % n_sets]
+        svx.specv_position_diagnostics(s["target"], s["draft"], s["gamma"], s["temperature"], k,
+                                       max_gamma=x.max_gamma, out=out, workspace=ws, stream=stream,
+                                       events=events)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    K = args.steps
+    p2 = svx.STAGES.index("accept_and_mass")  # the pass-2 slot of the diagnostics
+    evs = [svx.StageEvents(stages=(p2,)) for _ in range(K)]
+    t_start, t_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(K):
+        step(i, evs[i])
+    t_stop.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_stop) / K
+    p2_ms = float(np.mean([ev.elapsed_ms(p2) for ev in evs]))
+    all_events = [svx.StageEvents() for _ in range(K)]
+    for i in range(K):
+        step(i, all_events[i])
+    torch.cuda.synchronize()
+    names = ("plan", "pass1_row_stats", "pass2_diag", "merge")
+    stage_ms = {nm: float(np.mean([ev.elapsed_ms(si) for ev in all_events]))
+                for si, nm in enumerate(names)}
+    by = x.diagnostics_bytes()
+    achieved = by["pass2"] / (p2_ms * 1e-3) / 1e9
+    result = {
+        "metric": "diagnosed draft positions/sec (alpha, entropy, top-k) and achieved HBM GB/s "
+                  "vs MI355X peak, 1 GPU",
+        "value": td / (ms_step * 1e-3),
+        "unit": "draft positions/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": desc + "; per-position diagnostics, top-%d" % k, "batch": x.batch,
+                   "vocab": x.vocab, "logits": x.dtype, "top_k": k},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "k5_diag_pass", "algorithmic_bytes_per_launch": by["pass2"],
+                     "avg_launch_ms": p2_ms},
+        "step_gbps": (by["pass1"] + by["pass2"]) / (ms_step * 1e-3) / 1e9,
+        "stage_ms_instrumented": stage_ms,
+        "rotating_input_sets": n_sets,
+        "kernel_sha": kernel_sha(),
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle's diagnostics on the host")
+        result["cpu_baseline"] = diag_cpu_baseline(x, k)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -105,6 +206,8 @@ def main():
     ap.add_argument("--workload", default="t5xxl_like", choices=sorted(WORKLOADS))
     ap.add_argument("--lenience", default="none", choices=["none", "lin", "sq", "exp"])
     ap.add_argument("--epsilon", type=float, default=1.0)
+    ap.add_argument("--diagnostics", type=int, default=-1, metavar="K",
+                    help="time the per-position diagnostics with top-K lists instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="run only a plain device copy of this many bytes (counter calibration)")
@@ -136,6 +239,9 @@ def main():
         ms = s.elapsed_time(e) / 10
         print(json.dumps({"copy_bytes": n, "ms": ms, "gbps": 2 * n / ms / 1e6}))
         return
+
+    if args.diagnostics >= 0:
+        return bench_diagnostics(args, torch, svx, dev)
 
     t_gen = time.perf_counter()
     x, desc = make_inputs(args.workload)

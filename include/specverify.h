@@ -154,6 +154,45 @@ specv_status_t specv_verify_lenient(const specv_shape_t* shape, const void* targ
                                     void* workspace, size_t workspace_bytes, hipStream_t stream,
                                     hipEvent_t* events);
 
+/* Per-position diagnostics. For every draft position i < gamma_b of every
+ * sequence b, written at the packed draft-row index doff_b + i, with
+ * p = p_i and q = q_i the temperature softmaxes of target row i and draft
+ * row i:
+ *   out_alpha[j]   = sum_v min(p_v, q_v), the probability that a token drafted
+ *                    from q is accepted (DistillSpec section 3; 1 - alpha is
+ *                    the total variation distance of its section 4);
+ *   out_entropy[j] = -sum_v q_v ln q_v (nats);
+ *   out_topk_index[j * top_k + l], out_topk_prob[j * top_k + l]: the l-th most
+ *                    probable draft token and its q (larger logit first, equal
+ *                    logits lower index first).
+ * Entropy and top-k are the Ent and Top_k features of DISCO's stopping
+ * classifier (DISCO section 3, Eq. 2). Greedy sequences (T_b == 0) use the
+ * zero-temperature limits of greedy verification: p and q one-hot at their
+ * argmax, so alpha is 1 or 0, the entropy 0 and the top-1 probability 1.
+ * A position whose target or draft row holds NaN or +inf or no finite logit,
+ * or whose T_b is NaN, negative or +inf, gets NaN alpha and entropy, index
+ * -1 and probability NaN; after a layout error (as in specv_verify) every
+ * position reads so, and the status bit is set. 0 <= top_k <= min(V,
+ * SPECV_MAX_TOP_K); with top_k == 0 the top-k pointers may be NULL.
+ * Precision: alpha and entropy are float64 sums of fp32 terms; the top-k
+ * selection compares raw logits (exact); its probabilities are float64.
+ * Device output arrays are caller-owned; `workspace` is at least
+ * specv_diagnostics_workspace_bytes(shape, top_k) bytes, 256-byte aligned.
+ * `events` is NULL or 2 * SPECV_NUM_STAGES events recorded around the
+ * stages as in specv_verify_profiled; the stages here are the plan, pass 1
+ * (row statistics of every target and draft row), pass 2 (SPECV_STAGE_
+ * ACCEPT_MASS slot: the per-position sums and top-k lists) and the merge
+ * (SPECV_STAGE_DRAW slot). */
+#define SPECV_MAX_TOP_K 64
+size_t specv_diagnostics_workspace_bytes(const specv_shape_t* shape, int32_t top_k);
+specv_status_t specv_position_diagnostics(const specv_shape_t* shape, const void* target_logits,
+                                          const void* draft_logits, const int32_t* gamma_per_row,
+                                          const float* temperature, int32_t top_k,
+                                          double* out_alpha, double* out_entropy,
+                                          int32_t* out_topk_index, double* out_topk_prob,
+                                          void* workspace, size_t workspace_bytes,
+                                          hipStream_t stream, hipEvent_t* events);
+
 /* Stages of one call, in launch order (one kernel each). */
 #define SPECV_STAGE_PLAN 0        /* offsets of the packed rows, per-row T scale */
 #define SPECV_STAGE_ROWSTATS 1    /* pass 1: max, sum of exp (argmax) per row    */

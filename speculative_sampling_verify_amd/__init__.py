@@ -49,6 +49,11 @@ _lib.specv_verify_with_uniforms.argtypes = [_SHP, _P, _P, _P, _P, _P, _P, _P, _P
 _lib.specv_verify_lenient.restype = ctypes.c_int
 _lib.specv_verify_lenient.argtypes = [_SHP, _P, _P, _P, _P, _P, ctypes.c_int, ctypes.c_float, _u64,
                                       _u64, _P, _P, _P, _P, _P, _sz, _P, _P]
+_lib.specv_diagnostics_workspace_bytes.restype = _sz
+_lib.specv_diagnostics_workspace_bytes.argtypes = [_SHP, ctypes.c_int32]
+_lib.specv_position_diagnostics.restype = ctypes.c_int
+_lib.specv_position_diagnostics.argtypes = [_SHP, _P, _P, _P, _P, ctypes.c_int32, _P, _P, _P, _P, _P,
+                                            _sz, _P, _P]
 _lib.specv_row_stats.restype = ctypes.c_int
 _lib.specv_row_stats.argtypes = [_SHP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _sz, _P]
 _lib.specv_softmax_rows.restype = ctypes.c_int
@@ -61,7 +66,8 @@ _lib.specv_status_string.restype = ctypes.c_char_p
 _lib.specv_status_string.argtypes = [ctypes.c_int]
 
 EXPORTED = ("specv_workspace_bytes", "specv_verify", "specv_verify_profiled",
-            "specv_verify_with_uniforms", "specv_verify_lenient", "specv_row_stats", "specv_softmax_rows",
+            "specv_verify_with_uniforms", "specv_verify_lenient",
+            "specv_diagnostics_workspace_bytes", "specv_position_diagnostics", "specv_row_stats", "specv_softmax_rows",
             "specv_philox4x32_10", "specv_copy_bytes", "specv_status_string")
 
 
@@ -220,6 +226,42 @@ def specv_verify_lenient(target, draft, draft_tokens, gamma, temperature, lenien
                                    ctypes.cast(events.array, ctypes.c_void_p))
     _check(st, "specv_verify_lenient")
     return out_n, out_next
+
+
+def specv_diagnostics_workspace_bytes(shape: SpecvShape, top_k: int) -> int:
+    return int(_lib.specv_diagnostics_workspace_bytes(ctypes.byref(shape), int(top_k)))
+
+
+def specv_position_diagnostics(target, draft, gamma, temperature, top_k, *, max_gamma=None,
+                               out=None, workspace=None, stream=None, events=None):
+    """Per draft position (packed draft-row order): alpha = sum min(p, q),
+    draft entropy (nats), and the top_k most probable draft tokens with
+    their probabilities. Returns a dict of device tensors."""
+    shape, draft, _, gamma, _, _, _ = _common(target, draft, None, gamma, temperature, max_gamma,
+                                              None, None, torch.empty(0, device=target.device))
+    dev = target.device
+    k = int(top_k)
+    if workspace is None:
+        n = specv_diagnostics_workspace_bytes(shape, k)
+        if n == 0:
+            raise SpecvError("invalid shape or top_k")
+        workspace = torch.empty(n, dtype=torch.uint8, device=dev)
+    td = shape.total_draft_rows
+    if out is None:
+        out = {"alpha": torch.empty(td, dtype=torch.float64, device=dev),
+               "entropy": torch.empty(td, dtype=torch.float64, device=dev),
+               "topk_index": torch.empty((td, k), dtype=torch.int32, device=dev),
+               "topk_prob": torch.empty((td, k), dtype=torch.float64, device=dev)}
+    _check_tensors(dev, workspace=workspace, **out)
+    st = _lib.specv_position_diagnostics(ctypes.byref(shape), _ptr(target), _ptr(draft),
+                                         _ptr(gamma), _ptr(temperature), k, _ptr(out["alpha"]),
+                                         _ptr(out["entropy"]), _ptr(out["topk_index"]),
+                                         _ptr(out["topk_prob"]), _ptr(workspace),
+                                         workspace.numel(), _stream(stream, dev),
+                                         None if events is None else
+                                         ctypes.cast(events.array, ctypes.c_void_p))
+    _check(st, "specv_position_diagnostics")
+    return out
 
 
 def specv_row_stats(target, draft, gamma, temperature, *, max_gamma=None, workspace=None,

@@ -1,0 +1,390 @@
+// diagnostics.hpp -- per-position diagnostics of a packed batch (gfx950).
+//
+// For draft position i of sequence b (packed draft row j, target row j + b):
+//   alpha   = sum_v min(p_v, q_v), the acceptance probability of a token
+//             drafted from q (DistillSpec section 3; 1 - alpha is the total
+//             variation distance of its section 4);
+//   entropy = -sum_v q_v ln q_v, and top-k of q: the Ent and Top_k features
+//             of DISCO's stopping classifier (DISCO section 3, Eq. 2).
+// Pass 1 is k1_row_stats (row max, sum, argmax), run over every draft row.
+// Pass 2 (k5_diag_pass) gives one wave to each (position, chunk) -- the same
+// interleaved tiles as pass 1 -- and accumulates per element, in fp32 terms
+// and fp64 lane sums:
+//   min(t^T_v / S^T, t^D_v / S^D),   t^D_v,   t^D_v * e^D_v,
+// with t = 2^e, e = fl32(z k - rk) exactly as in pass 1. Since
+// q_v = t^D_v / S and ln q_v = e^D_v ln 2 - ln S,
+//   entropy = ln S - ln 2 * (sum_v t^D_v e^D_v) / S,   S = sum_v t^D_v.
+// Top-k: q is monotone in the logit, so the list is selected on raw logits,
+// exactly (larger logit first, equal logits lower index first, as the
+// argmax does). Each wave appends the keys of its chunk that can still reach
+// the best K to a small LDS buffer and cuts the buffer back to the best K by
+// rank counting whenever it fills; the cut also raises the bar that a key
+// must clear. The first bar is the K-th largest lane maximum of the chunk,
+// taken in pass 1. A tile is scanned only when some lane's tile maximum
+// reaches the bar.
+// k6_diag_merge (one wave per position) sums the chunks' partials and merges
+// their lists; probabilities of the selected tokens are 2^(z k - rk) / S in
+// float64, as the accept step computes p(x) and q(x).
+#pragma once
+
+#include <type_traits>
+
+#include "kernels.hpp"
+
+namespace specv {
+
+constexpr int kMaxTopK = 64;
+
+struct DiagPart {
+  double alpha;  // sum min(p, q) over the chunk
+  double s;      // sum t^D
+  double a;      // sum t^D e^D
+};
+
+struct DiagArgs {
+  const void* target;
+  const void* draft;
+  const float* dk;      // per draft row: log2(e)/T, 0 greedy, -1 invalid T
+  const int32_t* dseq;  // per draft row: its sequence
+  const float* bar;     // [total_d * chunks]: K-th largest lane maximum (pass 1)
+  const RowPart* tparts;
+  const RowPart* dparts;
+  const uint32_t* status;
+  DiagPart* parts;      // [total_d * chunks]
+  float* topz;          // [total_d * chunks * K]
+  int32_t* topi;        // [total_d * chunks * K]
+  double* out_alpha;    // [total_d]
+  double* out_entropy;  // [total_d]
+  int32_t* out_index;   // [total_d * K]
+  double* out_prob;     // [total_d * K]
+  int64_t total_d, V;
+  int32_t chunks, K;
+};
+
+// Ranking keys: larger logit first, equal logits lower index first, as one
+// unsigned 64-bit number (order-preserving float bits above the complemented
+// index). -0 is folded onto +0 first, since the two compare equal. NaN never
+// reaches a key (rows holding one are rejected before).
+__device__ __forceinline__ uint64_t rank_key(float z, int32_t idx) {
+  const uint32_t b = __float_as_uint(z + 0.f);
+  const uint32_t o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((uint64_t)o << 32) | (uint32_t)~(uint32_t)idx;
+}
+__device__ __forceinline__ float key_value(uint64_t key) {
+  const uint32_t o = (uint32_t)(key >> 32);
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+__device__ __forceinline__ int32_t key_index(uint64_t key) { return (int32_t)~(uint32_t)key; }
+
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// A wave's candidate buffer in LDS: kDiagGroup slots of a tile are appended
+// between two checks, and the buffer is cut back to the best K whenever it
+// holds more than max(2K, 64) keys, so it never exceeds kDiagCap.
+constexpr int kDiagGroup = 8;
+constexpr int kDiagCap = 2 * kMaxTopK + kDiagGroup * kWave;
+constexpr int kDiagSlots = kDiagCap / kWave;
+
+// rank[s] += number of the keys buf[0..n) above mine[s], for s < ns: eight
+// broadcast reads in flight per step (the buffer is 16-byte aligned and read
+// past n up to the next multiple of 8 only within its capacity, which is a
+// multiple of 8; keys past n are skipped).
+template <int SLOTS>
+__device__ __forceinline__ void count_above(const uint64_t* buf, int n, int ns,
+                                            const uint64_t (&mine)[SLOTS], int (&rank)[SLOTS]) {
+  typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+  const u64x2* v = reinterpret_cast<const u64x2*>(buf);
+  for (int e = 0; e < n; e += 8) {
+    u64x2 o[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) o[u] = v[e / 2 + u];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint64_t key = (u & 1) ? o[u / 2].y : o[u / 2].x;
+      const bool live = e + u < n;
+#pragma unroll
+      for (int s = 0; s < SLOTS; ++s)
+        if (s < ns) rank[s] += (live && key > mine[s]) ? 1 : 0;
+    }
+  }
+}
+
+// Keeps the best min(n, K) of the n distinct keys buf[0..n) in buf[0..), best
+// first: each key's rank is the number of keys above it (broadcast reads of
+// the buffer), then the keys of rank < K move to their rank. Wave-private
+// buffer: the wave's LDS operations complete in program order.
+__device__ __forceinline__ int keep_best(uint64_t* buf, int n, int K, int lane) {
+  uint64_t mine[kDiagSlots];
+  int rank[kDiagSlots];
+  const int ns = (n + kWave - 1) / kWave;
+#pragma unroll
+  for (int s = 0; s < kDiagSlots; ++s) {
+    const int e = lane + s * kWave;
+    mine[s] = (s < ns && e < n) ? buf[e] : 0ull;
+    rank[s] = 0;
+  }
+  count_above<kDiagSlots>(buf, n, ns, mine, rank);
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int s = 0; s < kDiagSlots; ++s) {
+    const int e = lane + s * kWave;
+    if (s < ns && e < n && rank[s] < K) buf[rank[s]] = mine[s];
+  }
+  __builtin_amdgcn_wave_barrier();
+  return n < K ? n : K;
+}
+
+// Slot q of a raw tile as fp32 (the order Tile::widen produces).
+template <int DT, bool VEC, int Q>
+__device__ __forceinline__ float raw_elem(const typename Tile<DT, VEC>::Raw& r) {
+  if constexpr (VEC && DT == kBF16) return (Q & 1) ? bf16_hi(r.d[Q / 2]) : bf16_lo(r.d[Q / 2]);
+  else return __uint_as_float(r.d[Q]);
+}
+
+template <int DT, bool VEC, int G>
+__device__ __forceinline__ void diag_terms(const typename Tile<DT, VEC>::Raw& rd,
+                                           const typename Tile<DT, VEC>::Raw& rt, float k,
+                                           float rkT, float rkD, float iT, float iD, float& sa,
+                                           float& ss, float& sA, float& mx) {
+  float pa[8], ps[8], pA[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    float zD, zT;
+    // unrolled: u and G are compile-time, so the slot index is too
+    switch (u) {
+#define SPECV_SLOT(U)                                  \
+  case U:                                              \
+    zD = raw_elem<DT, VEC, G * 8 + U>(rd);             \
+    zT = raw_elem<DT, VEC, G * 8 + U>(rt);             \
+    break;
+      SPECV_SLOT(0) SPECV_SLOT(1) SPECV_SLOT(2) SPECV_SLOT(3)
+      SPECV_SLOT(4) SPECV_SLOT(5) SPECV_SLOT(6) SPECV_SLOT(7)
+#undef SPECV_SLOT
+    }
+    const float eD = __builtin_fmaf(zD, k, -rkD);
+    const float tD = exp2_hw(eD);
+    const float tT = exp2_hw(__builtin_fmaf(zT, k, -rkT));
+    pa[u] = fminf(tT * iT, tD * iD);
+    ps[u] = tD;
+    pA[u] = (tD == 0.f) ? 0.f : tD * eD;  // masked tokens: 0 * -inf is 0 here
+    mx = fmaxf(mx, zD);
+  }
+  sa = tree_sum(pa);
+  ss = tree_sum(ps);
+  sA = tree_sum(pA);
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kBlock) void k5_diag_pass(DiagArgs a) {
+  using TL = Tile<DT, VEC>;
+  using Raw = typename TL::Raw;
+  constexpr int NE = TL::NE;
+  constexpr int NG = NE / 8;
+  constexpr int64_t esz = (DT == kBF16) ? 2 : 4;
+  __shared__ __attribute__((aligned(16))) uint64_t sbuf[kWavesPerBlock][kDiagCap];
+  const int lane = threadIdx.x & (kWave - 1);
+  uint64_t* buf = sbuf[threadIdx.x >> 6];
+  const int64_t item = wave_uniform((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
+  if (item >= a.total_d * a.chunks) return;
+  const int64_t j = item / a.chunks;
+  const int c = (int)(item - j * a.chunks);
+  if (a.status[0] & kLayoutError) return;
+  const float k = a.dk[j];
+  if (!(k >= 0.f)) return;  // invalid temperature: the merge reports NaN
+  const bool sampling = k > 0.f;
+  const int64_t tr = j + a.dseq[j];
+  const RowStat st_t = merge_row(a.tparts + tr * a.chunks, a.chunks, k, sampling);
+  const RowStat st_d = merge_row(a.dparts + j * a.chunks, a.chunks, k, sampling);
+  if (!st_t.valid || !st_d.valid) return;
+  const void* trow = static_cast<const char*>(a.target) + tr * a.V * esz;
+  const void* drow = static_cast<const char*>(a.draft) + j * a.V * esz;
+  const float iT = sampling ? (float)(1.0 / st_t.s) : 0.f;
+  const float iD = sampling ? (float)(1.0 / st_d.s) : 0.f;
+  const int64_t tiles = (a.V + TL::EPI - 1) / TL::EPI;
+  const int n_iter = (int)((tiles - c + a.chunks - 1) / a.chunks);
+  const int K = a.K;
+  const int limit = (2 * K > kWave) ? 2 * K : kWave;
+  double sa = 0.0, ss = 0.0, sA = 0.0;
+  int count = 0;          // keys in the buffer
+  // The first bar comes from pass 1: the K-th largest lane maximum of this
+  // chunk, a logit with at least K logits of the chunk at or above it, so
+  // keys below its value cannot reach the best K.
+  float thz = (K > 0) ? a.bar[j * a.chunks + c] : ninf();  // logit of th
+  uint64_t th = rank_key(thz, INT32_MAX);  // keys at or below th cannot reach the best K
+  auto tile_start = [&](int it) { return ((int64_t)c + (int64_t)it * a.chunks) * TL::EPI; };
+  auto fetch = [&](int it, Raw& rd, Raw& rt) {
+    const int64_t e0 = tile_start(it);
+    const bool full = e0 + TL::EPI <= a.V;
+    if (full) TL::template load_raw<false>(drow, e0, a.V, 0, lane, rd);
+    else TL::template load_raw<true>(drow, e0, a.V, 0, lane, rd);
+    if (sampling) {
+      if (full) TL::template load_raw<false>(trow, e0, a.V, 0, lane, rt);
+      else TL::template load_raw<true>(trow, e0, a.V, 0, lane, rt);
+    }
+  };
+  // the top-k step of one slot group: one compare per slot against the bar's
+  // logit, the exact key test only where some lane may hold a candidate
+  auto scan_group = [&](const Raw& rd, int64_t e0, auto gq) {
+    constexpr int G = decltype(gq)::value;
+#define SPECV_SCAN(U)                                                       \
+  {                                                                         \
+    const float z = raw_elem<DT, VEC, G * kDiagGroup + U>(rd);              \
+    if (ballot(z >= thz) != 0) {                                            \
+      const int64_t id = TL::index(e0, 0, lane, G * kDiagGroup + U);        \
+      const uint64_t key = rank_key(z, (int32_t)id);                        \
+      const bool cand = id < a.V && key > th;                               \
+      const uint64_t m = ballot(cand);                                      \
+      if (cand) buf[count + lanes_below(m)] = key;                          \
+      count += __popcll(m);                                                 \
+    }                                                                       \
+  }
+    SPECV_SCAN(0) SPECV_SCAN(1) SPECV_SCAN(2) SPECV_SCAN(3)
+    SPECV_SCAN(4) SPECV_SCAN(5) SPECV_SCAN(6) SPECV_SCAN(7)
+#undef SPECV_SCAN
+    if (count > limit) {
+      count = keep_best(buf, count, K, lane);
+      th = buf[K - 1];
+      thz = key_value(th);
+    }
+  };
+  auto process = [&](const Raw& rd, const Raw& rt, int it) {
+    const int64_t e0 = tile_start(it);
+    float mx = ninf();
+    if (sampling) {
+      float ga[NG], gs[NG], gA[NG];
+      diag_terms<DT, VEC, 0>(rd, rt, k, st_t.rk, st_d.rk, iT, iD, ga[0], gs[0], gA[0], mx);
+      diag_terms<DT, VEC, 1>(rd, rt, k, st_t.rk, st_d.rk, iT, iD, ga[1], gs[1], gA[1], mx);
+      if constexpr (NG == 4) {
+        diag_terms<DT, VEC, 2>(rd, rt, k, st_t.rk, st_d.rk, iT, iD, ga[2], gs[2], gA[2], mx);
+        diag_terms<DT, VEC, 3>(rd, rt, k, st_t.rk, st_d.rk, iT, iD, ga[3], gs[3], gA[3], mx);
+      }
+      sa += (double)tree_sum(ga);
+      ss += (double)tree_sum(gs);
+      sA += (double)tree_sum(gA);
+    } else if (K > 0) {
+      float z[NE];
+      TL::widen(rd, z);
+      mx = tile_max(z);
+    }
+    if (K == 0) return;
+    if (ballot(mx >= thz) == 0) return;
+    scan_group(rd, e0, std::integral_constant<int, 0>{});
+    scan_group(rd, e0, std::integral_constant<int, 1>{});
+    if constexpr (NE / kDiagGroup == 4) {
+      scan_group(rd, e0, std::integral_constant<int, 2>{});
+      scan_group(rd, e0, std::integral_constant<int, 3>{});
+    }
+  };
+  // double-buffered: the loads of tile it + 1 are in flight while tile it is
+  // processed
+  Raw da, ta, db, tb;
+  fetch(0, da, ta);
+  for (int it = 0; it < n_iter; it += 2) {
+    if (it + 1 < n_iter) fetch(it + 1, db, tb);
+    process(da, ta, it);
+    if (it + 1 >= n_iter) break;
+    if (it + 2 < n_iter) fetch(it + 2, da, ta);
+    process(db, tb, it + 1);
+  }
+  const int64_t slot = j * a.chunks + c;
+  if (sampling) {
+    sa = wave_sum(sa);
+    ss = wave_sum(ss);
+    sA = wave_sum(sA);
+  }
+  if (lane == 0) a.parts[slot] = DiagPart{sa, ss, sA};
+  if (K > 0) {
+    count = keep_best(buf, count, K, lane);
+    if (lane < K) {
+      const bool have = lane < count;
+      const uint64_t key = have ? buf[lane] : 0ull;
+      a.topz[slot * K + lane] = have ? key_value(key) : ninf();
+      a.topi[slot * K + lane] = have ? key_index(key) : INT32_MAX;
+    }
+  }
+}
+
+// One wave per position: sums the chunk partials and ranks the union of the
+// chunk lists (at most 16 * 64 keys, in LDS); a key's rank is its place in
+// the merged list. Padding entries (index INT32_MAX) take no part: the
+// chunks hold at least K real entries between them, since K <= V.
+constexpr int kMergeCap = 16 * kMaxTopK;
+constexpr int kMergeSlots = kMergeCap / kWave;
+
+__global__ __launch_bounds__(kBlock) void k6_diag_merge(DiagArgs a) {
+  __shared__ __attribute__((aligned(16))) uint64_t sbuf[kWavesPerBlock][kMergeCap];
+  const int lane = threadIdx.x & (kWave - 1);
+  uint64_t* buf = sbuf[threadIdx.x >> 6];
+  const int64_t j = wave_uniform((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
+  if (j >= a.total_d) return;
+  const int K = a.K;
+  auto fail = [&]() {
+    if (lane == 0) {
+      a.out_alpha[j] = __builtin_nan("");
+      a.out_entropy[j] = __builtin_nan("");
+    }
+    if (lane < K) {
+      a.out_index[j * K + lane] = -1;
+      a.out_prob[j * K + lane] = __builtin_nan("");
+    }
+  };
+  if (a.status[0] & kLayoutError) return fail();
+  const float k = a.dk[j];
+  if (!(k >= 0.f)) return fail();
+  const bool sampling = k > 0.f;
+  const int64_t tr = j + a.dseq[j];
+  const RowStat st_t = merge_row(a.tparts + tr * a.chunks, a.chunks, k, sampling);
+  const RowStat st_d = merge_row(a.dparts + j * a.chunks, a.chunks, k, sampling);
+  if (!st_t.valid || !st_d.valid) return fail();
+  double alpha, entropy;
+  if (sampling) {
+    DiagPart p{0.0, 0.0, 0.0};
+    if (lane < a.chunks) p = a.parts[j * a.chunks + lane];
+    alpha = wave_sum(p.alpha);
+    const double S = wave_sum(p.s), A = wave_sum(p.a);
+    entropy = log(S) - 0.69314718055994530942 * A / S;
+  } else {
+    alpha = (st_t.arg == st_d.arg) ? 1.0 : 0.0;
+    entropy = 0.0;
+  }
+  if (lane == 0) {
+    a.out_alpha[j] = alpha;
+    a.out_entropy[j] = entropy;
+  }
+  if (K == 0) return;
+  const int n = a.chunks * K;
+  const int ns = (n + kWave - 1) / kWave;
+  uint64_t mine[kMergeSlots];
+#pragma unroll
+  for (int s = 0; s < kMergeSlots; ++s) {
+    const int e = lane + s * kWave;
+    uint64_t key = 0ull;
+    if (s < ns && e < n) {
+      const int32_t id = a.topi[j * n + e];
+      if (id != INT32_MAX) key = rank_key(a.topz[j * n + e], id);
+      buf[e] = key;
+    }
+    mine[s] = key;
+  }
+  __builtin_amdgcn_wave_barrier();
+  int rank[kMergeSlots];
+#pragma unroll
+  for (int s = 0; s < kMergeSlots; ++s) rank[s] = 0;
+  count_above<kMergeSlots>(buf, n, ns, mine, rank);
+#pragma unroll
+  for (int s = 0; s < kMergeSlots; ++s) {
+    if (s < ns && mine[s] != 0ull && rank[s] < K) {
+      const float z = key_value(mine[s]);
+      double q;
+      if (sampling) q = exp2((double)z * (double)k - (double)st_d.rk) / st_d.s;
+      else q = (rank[s] == 0) ? 1.0 : 0.0;
+      a.out_index[j * K + rank[s]] = key_index(mine[s]);
+      a.out_prob[j * K + rank[s]] = q;
+    }
+  }
+}
+
+}  // namespace specv

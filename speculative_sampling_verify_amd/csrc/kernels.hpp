@@ -57,6 +57,7 @@ struct PlanArgs {
   int64_t* doff;
   float* tk;
   float* dk;
+  int32_t* dseq;  // optional: the sequence of each draft row
   uint32_t* status;
   int64_t total_t, total_d;
   int32_t B, max_gamma;
@@ -131,6 +132,8 @@ __global__ __launch_bounds__(1024) void k0_plan(PlanArgs a) {
     const int64_t tend = min(t + gg + 1, a.total_t), dend = min(d + gg, a.total_d);
     for (int64_t j = t; j < tend; ++j) a.tk[j] = kk;
     for (int64_t j = d; j < dend; ++j) a.dk[j] = kk;
+    if (a.dseq)
+      for (int64_t j = d; j < dend; ++j) a.dseq[j] = b;
     t += gg + 1;
     d += gg;
   }
@@ -150,6 +153,9 @@ struct RowStatsArgs {
   const uint32_t* status;
   int64_t total_t, total_d, V;
   int32_t B, chunks;
+  int32_t all_drafts;  // also read the draft rows of greedy sequences
+  int32_t bar_k;       // > 0: write the bar_k-th largest lane maximum of each
+  float* bar;          //      draft (row, chunk) to bar[row * chunks + chunk]
 };
 
 // Pass-1 loop over one (row, chunk), double-buffered: the loads of tile it+1
@@ -178,7 +184,7 @@ __device__ __forceinline__ void load_tile(const void* row, int64_t V, int64_t t,
 template <int DT, bool VEC, bool SAMPLING, bool WITH_ARG>
 __device__ __forceinline__ RowPart chunk_pass(const void* row, int64_t V, int c, int chunks,
                                               int n_iter, float k, int lane,
-                                              typename Tile<DT, VEC>::Raw& a) {
+                                              typename Tile<DT, VEC>::Raw& a, float& lane_max) {
   using TL = Tile<DT, VEC>;
   using Raw = typename TL::Raw;
   constexpr int NE = TL::NE;
@@ -218,6 +224,7 @@ __device__ __forceinline__ RowPart chunk_pass(const void* row, int64_t V, int c,
     if (it + 2 < n_iter) load_tile<DT, VEC>(row, V, tile_of(it + 2), lane, a);
     process(b, it + 1);
   }
+  lane_max = m;
   // wave merge: maximum first, then one rescale per lane and a float64 sum
   const float M = wave_max(m);
   double S;
@@ -264,7 +271,8 @@ __global__ __launch_bounds__(kBlock) void k1_row_stats(RowStatsArgs a) {
   float k;
   if (is_draft) {
     k = a.dk[j];
-    if (!(k > 0.f)) return;  // greedy (or invalid) sequence: draft row not needed
+    // greedy (or invalid) sequence: the verify step needs no draft row
+    if (!(k > 0.f) && !(a.all_drafts && k == 0.f)) return;
     load_tile<DT, VEC>(row, a.V, c, lane, first);
   } else {
     load_tile<DT, VEC>(row, a.V, c, lane, first);
@@ -273,11 +281,24 @@ __global__ __launch_bounds__(kBlock) void k1_row_stats(RowStatsArgs a) {
   }
   if (a.status[0] & kLayoutError) return;
   RowPart out;
+  float lm;
   if (k > 0.f)
-    out = chunk_pass<DT, VEC, true, WITH_ARG>(row, a.V, c, a.chunks, n_iter, k, lane, first);
+    out = chunk_pass<DT, VEC, true, WITH_ARG>(row, a.V, c, a.chunks, n_iter, k, lane, first, lm);
   else
-    out = chunk_pass<DT, VEC, false, true>(row, a.V, c, a.chunks, n_iter, 0.f, lane, first);
+    out = chunk_pass<DT, VEC, false, true>(row, a.V, c, a.chunks, n_iter, 0.f, lane, first, lm);
   if (lane == 0) (is_draft ? a.dparts : a.tparts)[j * a.chunks + c] = out;
+  if (is_draft && a.bar_k > 0) {
+    // The bar_k-th largest of the lanes' maxima: a logit of the chunk with
+    // at least bar_k logits of the chunk at or above it (-inf when fewer
+    // lanes hold a logit), for the top-k selection of the diagnostics.
+    int rank = 0;
+#pragma unroll
+    for (int l = 0; l < kWave; ++l) {
+      const float o = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(lm), l));
+      rank += (o > lm || (o == lm && l < lane)) ? 1 : 0;
+    }
+    if (rank == a.bar_k - 1) a.bar[j * a.chunks + c] = lm;
+  }
 }
 
 // Per-row merge of the chunk statistics.

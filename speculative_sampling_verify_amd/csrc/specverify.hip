@@ -5,6 +5,7 @@
 
 #include <stdint.h>
 
+#include "diagnostics.hpp"
 #include "kernels.hpp"
 #include "specverify.h"
 
@@ -36,6 +37,9 @@ struct Plan {
   int64_t nsub;
   size_t off_toff, off_doff, off_tk, off_dk, off_tparts, off_dparts, off_sel, off_sub;
   size_t bytes;
+  // per-position diagnostics (after the verify layout)
+  size_t off_dseq, off_bar, off_dgparts, off_topz, off_topi;
+  size_t diag_bytes;
 };
 
 bool shape_ok(const specv_shape_t* s) {
@@ -83,6 +87,18 @@ void make_plan(const specv_shape_t* s, Plan* p) {
   p->nsub = (p->V + kSub - 1) / kSub;
   p->off_sub = off; off = align_up(off + (size_t)p->B * p->nsub * sizeof(double));
   p->bytes = off;
+}
+
+// Workspace of specv_position_diagnostics with top-k lists of K entries.
+void make_diag_plan(Plan* p, int K) {
+  size_t off = p->bytes;
+  const size_t items = (size_t)p->td * p->chunks1;
+  p->off_dseq = off; off = align_up(off + (size_t)p->td * 4);
+  p->off_bar = off; off = align_up(off + items * 4);
+  p->off_dgparts = off; off = align_up(off + items * sizeof(DiagPart));
+  p->off_topz = off; off = align_up(off + items * K * 4);
+  p->off_topi = off; off = align_up(off + items * K * 4);
+  p->diag_bytes = off;
 }
 
 template <typename T>
@@ -144,7 +160,7 @@ inline unsigned blocks_for(int64_t waves) {
 }
 
 specv_status_t launch_plan(const Plan& p, const int32_t* gamma, const float* temperature, void* ws,
-                           hipStream_t st) {
+                           hipStream_t st, int32_t* dseq = nullptr) {
   PlanArgs a;
   a.gamma = gamma;
   a.temperature = temperature;
@@ -152,6 +168,7 @@ specv_status_t launch_plan(const Plan& p, const int32_t* gamma, const float* tem
   a.doff = at<int64_t>(ws, p.off_doff);
   a.tk = at<float>(ws, p.off_tk);
   a.dk = at<float>(ws, p.off_dk);
+  a.dseq = dseq;
   a.status = at<uint32_t>(ws, 0);
   a.total_t = p.tt;
   a.total_d = p.td;
@@ -162,7 +179,8 @@ specv_status_t launch_plan(const Plan& p, const int32_t* gamma, const float* tem
 }
 
 specv_status_t launch_row_stats(const Plan& p, bool vec, const void* target, const void* draft,
-                                void* ws, hipStream_t st, bool with_argmax = false) {
+                                void* ws, hipStream_t st, bool with_argmax = false,
+                                bool all_drafts = false, int bar_k = 0, float* bar = nullptr) {
   RowStatsArgs a;
   a.target = target;
   a.draft = draft;
@@ -176,6 +194,9 @@ specv_status_t launch_row_stats(const Plan& p, bool vec, const void* target, con
   a.V = p.V;
   a.B = (int32_t)p.B;
   a.chunks = p.chunks1;
+  a.all_drafts = all_drafts ? 1 : 0;
+  a.bar_k = bar_k;
+  a.bar = bar;
   const int64_t waves = (p.tt + p.td) * p.chunks1;
   if (waves == 0) return SPECV_OK;
   const dim3 grid(blocks_for(waves)), block(kBlock);
@@ -368,6 +389,84 @@ specv_status_t specv_verify_lenient(const specv_shape_t* shape, const void* targ
   c.lenience = (epsilon == 1.f) ? kLenNone : (int32_t)lenience;
   c.eps = epsilon;
   return run(c);
+}
+
+size_t specv_diagnostics_workspace_bytes(const specv_shape_t* shape, int32_t top_k) {
+  if (!shape_ok(shape) || top_k < 0 || top_k > kMaxTopK || top_k > shape->vocab) return 0;
+  Plan p;
+  make_plan(shape, &p);
+  make_diag_plan(&p, top_k);
+  return p.diag_bytes;
+}
+
+specv_status_t specv_position_diagnostics(const specv_shape_t* shape, const void* target_logits,
+                                          const void* draft_logits, const int32_t* gamma_per_row,
+                                          const float* temperature, int32_t top_k,
+                                          double* out_alpha, double* out_entropy,
+                                          int32_t* out_topk_index, double* out_topk_prob,
+                                          void* workspace, size_t workspace_bytes,
+                                          hipStream_t stream, hipEvent_t* events) {
+  if (top_k < 0 || top_k > kMaxTopK || (shape && top_k > shape->vocab))
+    return SPECV_ERR_INVALID_ARGUMENT;
+  Plan p;
+  specv_status_t st = check_common(shape, target_logits, draft_logits, gamma_per_row, temperature,
+                                   workspace, workspace_bytes, &p);
+  if (st != SPECV_OK || p.B == 0) return st;
+  make_diag_plan(&p, top_k);
+  if (workspace_bytes < p.diag_bytes) return SPECV_ERR_WORKSPACE;
+  if (p.td > 0 && (!out_alpha || !out_entropy)) return SPECV_ERR_INVALID_ARGUMENT;
+  if (p.td > 0 && top_k > 0 && (!out_topk_index || !out_topk_prob))
+    return SPECV_ERR_INVALID_ARGUMENT;
+  const bool vec = vector_path(p, target_logits, draft_logits);
+  int32_t* dseq = at<int32_t>(workspace, p.off_dseq);
+  mark(events, 2 * SPECV_STAGE_PLAN, stream);
+  if ((st = launch_plan(p, gamma_per_row, temperature, workspace, stream, dseq)) != SPECV_OK)
+    return st;
+  mark(events, 2 * SPECV_STAGE_PLAN + 1, stream);
+  mark(events, 2 * SPECV_STAGE_ROWSTATS, stream);
+  float* bar = at<float>(workspace, p.off_bar);
+  if (p.td > 0 && (st = launch_row_stats(p, vec, target_logits, draft_logits, workspace, stream,
+                                         false, true, top_k, bar)) != SPECV_OK)
+    return st;
+  mark(events, 2 * SPECV_STAGE_ROWSTATS + 1, stream);
+  DiagArgs a;
+  a.target = target_logits;
+  a.draft = draft_logits;
+  a.dk = at<float>(workspace, p.off_dk);
+  a.dseq = dseq;
+  a.bar = bar;
+  a.tparts = at<RowPart>(workspace, p.off_tparts);
+  a.dparts = at<RowPart>(workspace, p.off_dparts);
+  a.status = at<uint32_t>(workspace, 0);
+  a.parts = at<DiagPart>(workspace, p.off_dgparts);
+  a.topz = at<float>(workspace, p.off_topz);
+  a.topi = at<int32_t>(workspace, p.off_topi);
+  a.out_alpha = out_alpha;
+  a.out_entropy = out_entropy;
+  a.out_index = out_topk_index;
+  a.out_prob = out_topk_prob;
+  a.total_d = p.td;
+  a.V = p.V;
+  a.chunks = p.chunks1;
+  a.K = top_k;
+  const dim3 grid(blocks_for(p.td * p.chunks1)), block(kBlock);
+  mark(events, 2 * SPECV_STAGE_ACCEPT_MASS, stream);
+  if (p.td == 0) {
+    // nothing to compute
+  } else if (p.dt == kBF16) {
+    if (vec) hipLaunchKernelGGL((k5_diag_pass<kBF16, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((k5_diag_pass<kBF16, false>), grid, block, 0, stream, a);
+  } else {
+    if (vec) hipLaunchKernelGGL((k5_diag_pass<kF32, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((k5_diag_pass<kF32, false>), grid, block, 0, stream, a);
+  }
+  if ((st = launched()) != SPECV_OK) return st;
+  mark(events, 2 * SPECV_STAGE_ACCEPT_MASS + 1, stream);
+  mark(events, 2 * SPECV_STAGE_DRAW, stream);
+  if (p.td > 0) hipLaunchKernelGGL(k6_diag_merge, dim3(blocks_for(p.td)), block, 0, stream, a);
+  if ((st = launched()) != SPECV_OK) return st;
+  mark(events, 2 * SPECV_STAGE_DRAW + 1, stream);
+  return SPECV_OK;
 }
 
 specv_status_t specv_row_stats(const specv_shape_t* shape, const void* target_logits,

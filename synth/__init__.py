@@ -86,6 +86,17 @@ class Inputs:
         rows = int(np.sum(g + 1) + np.sum(g[sampling]))
         return rows * self.vocab * self.bytes_per_logit
 
+    def diagnostics_bytes(self) -> dict:
+        """Bytes the per-position diagnostics must read: pass 1 reads every
+        target and draft row; pass 2 reads each position's draft row and, for
+        sampling sequences, its target row."""
+        g = self.gamma.astype(np.int64)
+        sampling = self.temperature > 0
+        row = self.vocab * self.bytes_per_logit
+        pass1 = int(np.sum(g + 1) + np.sum(g)) * row
+        pass2 = int(np.sum(g) + np.sum(g[sampling])) * row
+        return {"pass1": pass1, "pass2": pass2}
+
 
 def _threads() -> int:
     return max(1, min(os.cpu_count() or 1, 16))

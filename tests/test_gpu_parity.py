@@ -426,3 +426,105 @@ def test_lenient_argument_errors(svx):
     for kind, eps in [("lin", 0.0), ("sq", -0.5), ("exp", 1.5), ("lin", float("nan")), (7, 0.5)]:
         with pytest.raises(svx.SpecvError):
             run_gpu_lenient(svx, x, kind, eps)
+
+
+# ------------------------------------------------ per-position diagnostics
+
+# alpha and entropy are float64 sums of fp32 terms (each within a few ulp):
+# |error(alpha)| <= ~1e-6; the entropy ln S - ln2 * A / S carries the fp32
+# term error times ln S - H <= ln V, so 1e-5 (nats) bounds it at V <= 256000.
+DIAG_ALPHA_TOL = 2e-6
+DIAG_ENTROPY_TOL = 1e-5
+DIAG_PROB_TOL = 1e-5
+
+
+def run_gpu_diag(svx, x, k):
+    d = svx.from_inputs(x)
+    out = svx.specv_position_diagnostics(d["target"], d["draft"], d["gamma"], d["temperature"], k,
+                                         max_gamma=x.max_gamma)
+    torch.cuda.synchronize()
+    return {name: t.cpu().numpy() for name, t in out.items()}
+
+
+def assert_diag_parity(name, x, k):
+    log("[case] diagnostics %s k=%d B=%d V=%d %s" % (name, k, x.batch, x.vocab, x.dtype))
+    got = run_gpu_diag(svx_mod(), x, k)
+    want = oracle.position_diagnostics(x.target, x.draft, x.gamma, x.temperature, vocab=x.vocab,
+                                       top_k=k)
+    nan = np.isnan(want.alpha)
+    np.testing.assert_array_equal(np.isnan(got["alpha"]), nan)
+    np.testing.assert_array_equal(np.isnan(got["entropy"]), np.isnan(want.entropy))
+    ea = np.abs(got["alpha"][~nan] - want.alpha[~nan])
+    ee = np.abs(got["entropy"][~nan] - want.entropy[~nan])
+    log("[parity] diagnostics %s: positions=%d max|d alpha|=%.3g max|d entropy|=%.3g"
+        % (name, len(nan), ea.max(initial=0), ee.max(initial=0)))
+    assert ea.max(initial=0) <= DIAG_ALPHA_TOL and ee.max(initial=0) <= DIAG_ENTROPY_TOL
+    np.testing.assert_array_equal(got["topk_index"], want.topk_index)
+    ok = ~np.isnan(want.topk_prob)
+    np.testing.assert_array_equal(np.isnan(got["topk_prob"]), ~ok)
+    assert np.abs(got["topk_prob"][ok] - want.topk_prob[ok]).max(initial=0) <= DIAG_PROB_TOL
+    return got, want
+
+
+def svx_mod():
+    import speculative_sampling_verify_amd as m
+    return m
+
+
+DIAG_CASES = [
+    ("tiny_cpu", dict(rounds=200), 16),              # fp32, V = 1000, one chunk
+    ("t5xxl_like", dict(rounds=48), 16),             # bf16, V = 32128, bf16 ties
+    ("t5xxl_like_greedy", dict(rounds=32, greedy=True), 8),
+    ("serving_b64", dict(batch=6), 64),              # T = 0.7, K at its maximum
+    ("ragged_b256", dict(batch=10), 1),              # ragged gammas, 10 chunks
+    ("large_vocab", dict(batch=8), 10),              # fp32, V = 256000, odd greedy, p == q rows
+]
+
+
+@pytest.mark.parametrize("name,kw,k", DIAG_CASES, ids=[c[0] for c in DIAG_CASES])
+def test_diagnostics_parity(svx, name, kw, k):
+    assert_diag_parity(name, make(name, **kw), k)
+
+
+def test_diagnostics_edges(svx):
+    rng = np.random.default_rng(8)
+    # odd V (scalar loads), masked tails, ties, a NaN row, T = 0 and k = 0 / k = V
+    V = 13
+    t = np.round(rng.standard_normal((4, V)) * 2).astype(np.float32)  # many equal logits
+    dr = np.round(rng.standard_normal((3, V)) * 2).astype(np.float32)
+    dr[1, 7:] = -np.inf
+    bad = t.copy()
+    bad[0, 2] = np.nan
+    seqs = [{"target": t, "draft": dr, "tokens": [0, 1, 2], "T": 1.0},
+            {"target": t[:2], "draft": dr[1:2], "tokens": [0], "T": 0.0},
+            {"target": bad[:3], "draft": dr[:2], "tokens": [3, 4], "T": 0.5},
+            {"target": t[:1], "draft": dr[:0], "tokens": [], "T": 1.0}]
+    for dtype in ("f32", "bf16"):
+        x = pack(seqs, V, dtype)
+        for k in (0, 1, V):
+            assert_diag_parity("edges %s" % dtype, x, k)
+
+
+def test_diagnostics_heavy_ties(svx):
+    # bf16 logits on an integer grid (thousands of equal values per row) and
+    # an all-equal row: the top-64 boundary falls inside runs of ties, which
+    # rank by index
+    rng = np.random.default_rng(12)
+    V, g = 32128, 3
+    seqs = []
+    for b in range(4):
+        t = np.round(rng.standard_normal((g + 1, V)) * 1.5).astype(np.float32)
+        d = np.round(rng.standard_normal((g, V)) * 1.5).astype(np.float32)
+        if b == 3:
+            d[1] = 0.0
+        seqs.append({"target": t, "draft": d, "tokens": [0] * g, "T": 1.0 if b % 2 == 0 else 0.0})
+    x = pack(seqs, V, "bf16")
+    for k in (64, 7):
+        assert_diag_parity("heavy ties", x, k)
+
+
+def test_diagnostics_argument_errors(svx):
+    x = synth.tiny_cpu(rounds=4, vocab=32)
+    for k in (-1, 33, 65):
+        with pytest.raises(svx.SpecvError):
+            run_gpu_diag(svx, x, k)
