@@ -51,6 +51,9 @@ def _load():
     lib.oracle_position_diagnostics.restype = ctypes.c_int
     lib.oracle_position_diagnostics.argtypes = [i64, i64, ctypes.c_int, i64, i64, P, P, P, P, i64,
                                                 P, P, P, P]
+    lib.oracle_decode_bigram.restype = ctypes.c_int
+    lib.oracle_decode_bigram.argtypes = [i64, i64, i64, i64, ctypes.c_int, P, P, P, P, u64, u64,
+                                         P, P, P, P, ctypes.c_int]
     lib.oracle_row_stats.restype = None
     lib.oracle_row_stats.argtypes = [P, ctypes.c_int, i64, i64, P, P, P, P, P]
     lib.oracle_softmax_row.restype = None
@@ -163,6 +166,39 @@ def position_diagnostics(target, draft, gamma, temperature, *, vocab, top_k) -> 
     if code != 0:
         raise ValueError("gammas and row totals disagree")
     return Diagnostics(alpha, ent, idx, prob)
+
+
+@dataclass
+class DecodeResult:
+    tokens: np.ndarray      # [B, rounds * (gamma + 1)] int32 generated tokens
+    length: np.ndarray      # [B] int32 tokens generated (-1 after a failed round)
+    accepted: np.ndarray    # [B, rounds] int32 n of each round (-1 after a failure)
+    first_near: np.ndarray  # [B] int32 first round with a near-tie (rounds if none)
+
+
+def decode_bigram(target_table, draft_table, temperature, start, *, gamma, rounds, seed=0,
+                  row_offset=0, nthreads=None) -> DecodeResult:
+    """Multi-round speculative decoding with bigram tables [V, V] (row = the
+    previous token), every sequence drafting gamma tokens per round."""
+    lib = _load()
+    ttab = np.ascontiguousarray(target_table)
+    dtab = np.ascontiguousarray(draft_table)
+    if ttab.dtype != dtab.dtype or ttab.shape != dtab.shape or ttab.shape[0] != ttab.shape[1]:
+        raise ValueError("tables must be [V, V] of one dtype")
+    V = ttab.shape[0]
+    temperature = np.ascontiguousarray(temperature, dtype=np.float32)
+    start = np.ascontiguousarray(start, dtype=np.int32)
+    B = start.shape[0]
+    cap = rounds * (gamma + 1)
+    tokens = np.full((B, cap), -1, np.int32)
+    length = np.empty(B, np.int32)
+    accepted = np.empty((B, rounds), np.int32)
+    first_near = np.empty(B, np.int32)
+    lib.oracle_decode_bigram(B, V, gamma, rounds, _dtype_code(ttab), _ptr(ttab), _ptr(dtab),
+                             _ptr(temperature), _ptr(start), int(seed), int(row_offset),
+                             _ptr(tokens), _ptr(length), _ptr(accepted), _ptr(first_near),
+                             int(nthreads or default_threads()))
+    return DecodeResult(tokens, length, accepted, first_near)
 
 
 def row_stats(logits, vocab, temperature_per_row):

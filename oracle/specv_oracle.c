@@ -619,3 +619,109 @@ int oracle_position_diagnostics(int64_t batch, int64_t vocab, int dtype, int64_t
   free(zp); free(zq); free(p); free(q); free(taken);
   return 0;
 }
+
+/* ------------------------------------------------------------------ */
+/* Multi-round decoding with bigram "models".                          */
+/* ------------------------------------------------------------------ */
+
+/* Speculative decoding over several rounds (DistillSpec Algorithm A.1,
+ * repeated: the context grows by the n accepted draft tokens and the one
+ * token of the final draw each round). The models are bigram tables: the
+ * target's logits for the next token are row `prev` of ttab [V, V], the
+ * draft's are row `prev` of dtab, prev being the last token of the context.
+ * Each round and sequence b (Philox row = row_offset + r * batch + b):
+ *   drafting: x_i ~ softmax(dtab[prev] / T_b) for i = 0..gamma-1, prev = the
+ *     context's last token, then x_{i-1}; by inverse CDF in index order with
+ *     u = U(word 0 of Philox(seed; row, i, 1)); T_b = 0 drafts the argmax;
+ *   verification: the step above on target rows ttab[prev_i], i = 0..gamma,
+ *     and draft rows dtab[prev_i], i < gamma, with the same row.
+ * out_tokens [batch, rounds * (gamma + 1)] holds the generated tokens,
+ * out_length [batch] their count (-1 once a round fails: a start token
+ * outside [0, V) or a data error in verification), out_accepted
+ * [batch, rounds] the n of each round (-1 after a failure), and
+ * out_first_near [batch] the first round with a near-tie in drafting or
+ * verification (rounds if none). */
+int oracle_decode_bigram(int64_t batch, int64_t vocab, int64_t gamma, int64_t rounds, int dtype,
+                         const void* ttab, const void* dtab, const float* temperature,
+                         const int32_t* start, uint64_t seed, uint64_t row_offset,
+                         int32_t* out_tokens, int32_t* out_length, int32_t* out_accepted,
+                         int32_t* out_first_near, int nthreads) {
+  const int64_t V = vocab, B = batch, g = gamma;
+  const size_t esz = dtype == ORACLE_BF16 ? 2 : 4;
+  const size_t row_bytes = (size_t)V * esz;
+  const int64_t cap = rounds * (g + 1);
+  char* tpack = (char*)malloc((size_t)(B * (g + 1)) * row_bytes + 1);
+  char* dpack = (char*)malloc((size_t)(B * g) * row_bytes + 1);
+  int32_t* tokens = (int32_t*)malloc((size_t)(B * g + 1) * sizeof(int32_t));
+  int32_t* gam = (int32_t*)malloc((size_t)(B + 1) * sizeof(int32_t));
+  int32_t* cur = (int32_t*)malloc((size_t)(B + 1) * sizeof(int32_t));
+  int32_t* len = (int32_t*)malloc((size_t)(B + 1) * sizeof(int32_t));
+  uint8_t* failed = (uint8_t*)malloc((size_t)B + 1);
+  uint8_t* dnear = (uint8_t*)malloc((size_t)B + 1);
+  int32_t* n_out = (int32_t*)malloc((size_t)(B + 1) * sizeof(int32_t));
+  int32_t* next_out = (int32_t*)malloc((size_t)(B + 1) * sizeof(int32_t));
+  uint8_t* vnear = (uint8_t*)malloc((size_t)B + 1);
+  double* z = (double*)malloc((size_t)V * sizeof(double));
+  double* q = (double*)malloc((size_t)V * sizeof(double));
+  for (int64_t b = 0; b < B; ++b) {
+    gam[b] = (int32_t)g;
+    failed[b] = (uint8_t)(start[b] < 0 || start[b] >= V);
+    cur[b] = failed[b] ? 0 : start[b];
+    len[b] = 0;
+    out_first_near[b] = (int32_t)rounds;
+  }
+  for (int64_t r = 0; r < rounds; ++r) {
+    for (int64_t b = 0; b < B; ++b) {
+      const double T = (double)temperature[b];
+      const uint64_t prow = row_offset + (uint64_t)(r * B + b);
+      int32_t prev = cur[b];
+      dnear[b] = 0;
+      for (int64_t i = 0; i <= g; ++i) {
+        memcpy(tpack + (size_t)(b * (g + 1) + i) * row_bytes,
+               (const char*)ttab + (size_t)prev * row_bytes, row_bytes);
+        if (i == g) break;
+        memcpy(dpack + (size_t)(b * g + i) * row_bytes, (const char*)dtab + (size_t)prev * row_bytes,
+               row_bytes);
+        load_row(dtab, dtype, V, prev, z);
+        int64_t x = 0;
+        if (!row_is_valid(z, V) || isnan(T) || T < 0.0 || isinf(T)) {
+          x = 0; /* verification reports the sequence */
+        } else if (T == 0.0) {
+          x = row_argmax(z, V);
+        } else {
+          row_softmax(z, V, T, NULL, NULL, q);
+          uint32_t ctr[4] = {(uint32_t)prow, (uint32_t)(prow >> 32), (uint32_t)i, 1u};
+          uint32_t w[4];
+          oracle_philox4x32_10(seed, ctr, w);
+          double margin = INFINITY;
+          x = inverse_cdf(q, V, oracle_uniform24(w[0]), &margin, NULL);
+          if (x < 0) x = 0;
+          if (margin < ORACLE_NEAR_TIE) dnear[b] = 1;
+        }
+        tokens[b * g + i] = (int32_t)x;
+        prev = (int32_t)x;
+      }
+    }
+    oracle_verify(B, V, g, dtype, B * (g + 1), B * g, tpack, dpack, tokens, gam, temperature, seed,
+                  row_offset + (uint64_t)(r * B), ORACLE_LENIENCE_NONE, 1.0f, NULL, NULL, n_out,
+                  next_out, NULL, vnear, NULL, NULL, nthreads);
+    for (int64_t b = 0; b < B; ++b) {
+      if (!failed[b] && n_out[b] < 0) failed[b] = 1;
+      if (failed[b]) {
+        out_accepted[b * rounds + r] = -1;
+        continue;
+      }
+      const int32_t n = n_out[b];
+      for (int32_t i = 0; i < n; ++i) out_tokens[b * cap + len[b] + i] = tokens[b * g + i];
+      out_tokens[b * cap + len[b] + n] = next_out[b];
+      len[b] += n + 1;
+      cur[b] = next_out[b];
+      out_accepted[b * rounds + r] = n;
+      if ((dnear[b] || vnear[b]) && out_first_near[b] == rounds) out_first_near[b] = (int32_t)r;
+    }
+  }
+  for (int64_t b = 0; b < B; ++b) out_length[b] = failed[b] ? -1 : len[b];
+  free(tpack); free(dpack); free(tokens); free(gam); free(cur); free(len); free(failed);
+  free(dnear); free(n_out); free(next_out); free(vnear); free(z); free(q);
+  return 0;
+}
