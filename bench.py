@@ -13,7 +13,9 @@ sequences into one call. Prints one JSON line.
 With --lenience other than none, a step is one specv_verify_lenient call
 (lossy verification, threshold f(p, eps)/q) on the same workload. With
 --diagnostics K, a step is one specv_position_diagnostics call (alpha,
-draft entropy and top-K per draft position) on the same workload.
+draft entropy and top-K per draft position) on the same workload. With
+--decode, a step is one specv_decode_bigram call: ROUNDS rounds of drafting
+and verification for a batch of sequences over bigram tables.
 """
 import argparse
 import hashlib
@@ -42,6 +44,7 @@ WORKLOADS = {
 }
 KERNEL_SOURCES = ["speculative_sampling_verify_amd/csrc/kernels.hpp",
                   "speculative_sampling_verify_amd/csrc/diagnostics.hpp",
+                  "speculative_sampling_verify_amd/csrc/decode.hpp",
                   "speculative_sampling_verify_amd/csrc/device.hpp",
                   "speculative_sampling_verify_amd/csrc/specverify.hip"]
 
@@ -198,6 +201,88 @@ def bench_diagnostics(args, torch, svx, dev):
     print(json.dumps(result), flush=True)
 
 
+def bench_decode(args, torch, svx, dev):
+    import synth
+    V, B, g, R = args.decode_vocab, args.decode_batch, args.decode_gamma, args.decode_rounds
+    t_gen = time.perf_counter()
+    tabs = synth.bigram_tables(V)
+    log("[bench] generated bigram tables V=%d in %.1f s" % (V, time.perf_counter() - t_gen))
+    tt = torch.from_numpy(tabs.target.view(np.int16)).to(dev)
+    dt = torch.from_numpy(tabs.draft.view(np.int16)).to(dev)
+    T = torch.ones(B, dtype=torch.float32, device=dev)
+    start = torch.from_numpy(tabs.start(B)).to(dev)
+    shape = svx.SpecvDecodeShape(B, V, g, R, svx.SPECV_BF16)
+    ws = torch.empty(svx.specv_decode_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    out = {"tokens": torch.empty((B, R * (g + 1)), dtype=torch.int32, device=dev),
+           "length": torch.empty(B, dtype=torch.int32, device=dev),
+           "accepted": torch.empty((B, R), dtype=torch.int32, device=dev)}
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, events=None):
+        svx.specv_decode_bigram(tt, dt, T, start, gamma=g, rounds=R, seed=i,
+                                philox_row_offset=0, out=out, workspace=ws, stream=stream,
+                                events=events)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    K = args.steps
+    gi = svx.STAGES.index("row_stats")  # the gather's slot in the decode loop
+    evs = [svx.StageEvents() for _ in range(K)]
+    t_start, t_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for i in range(K):
+        step(i, evs[i])
+    t_stop.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_stop) / K
+    names = ("drafting", "gather", "verify", "append")
+    stage_ms = {nm: float(np.mean([ev.elapsed_ms(si) for ev in evs])) for si, nm in
+                enumerate(names)}
+    length = out["length"].cpu().numpy()
+    tokens = int(length[length > 0].sum())
+    row = V * 2
+    gather_bytes = 2 * B * (2 * g + 1) * row  # read the table rows, write the packed rows
+    achieved = gather_bytes / (stage_ms["gather"] * 1e-3) / 1e9
+    result = {
+        "metric": "generated tokens/sec of speculative decoding with bigram tables "
+                  "(draft + verify per round), 1 GPU",
+        "value": tokens / (ms_step * 1e-3),
+        "unit": "generated tokens/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "bigram decode loop: B=%d sequences, V=%d bf16 tables, gamma=%d, "
+                               "%d rounds, T=1" % (B, V, g, R),
+                   "batch": B, "vocab": V, "gamma": g, "rounds": R},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None, "kernel": "k_dec_gather",
+                     "algorithmic_bytes_per_launch": gather_bytes,
+                     "avg_launch_ms": stage_ms["gather"]},
+        "stage_ms_last_round": stage_ms,
+        "tokens_per_round": tokens / (B * R),
+        "kernel_sha": kernel_sha(),
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        log("[bench] timing the CPU oracle's decode loop on the host")
+        nb, el, res = 8, 0.0, None
+        while True:
+            t0 = time.perf_counter()
+            res = oracle.decode_bigram(tabs.target, tabs.draft, np.ones(nb, np.float32),
+                                       tabs.start(nb), gamma=g, rounds=R, seed=0)
+            el = time.perf_counter() - t0
+            if el >= 5.0 or nb >= B:
+                break
+            nb = min(B, nb * 2)
+        gen = int(res.length[res.length > 0].sum())
+        result["cpu_baseline"] = {"value": gen / el, "unit": "generated tokens/s",
+                                  "cores": oracle.default_threads(), "kind": "oracle",
+                                  "sample": "%d sequences x %d rounds (%d tokens), %.1f s"
+                                            % (nb, R, gen, el)}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -208,6 +293,12 @@ def main():
     ap.add_argument("--epsilon", type=float, default=1.0)
     ap.add_argument("--diagnostics", type=int, default=-1, metavar="K",
                     help="time the per-position diagnostics with top-K lists instead")
+    ap.add_argument("--decode", action="store_true",
+                    help="time the multi-round bigram decode loop instead")
+    ap.add_argument("--decode-vocab", type=int, default=8192)
+    ap.add_argument("--decode-batch", type=int, default=2048)
+    ap.add_argument("--decode-gamma", type=int, default=5)
+    ap.add_argument("--decode-rounds", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="run only a plain device copy of this many bytes (counter calibration)")
@@ -242,6 +333,8 @@ def main():
 
     if args.diagnostics >= 0:
         return bench_diagnostics(args, torch, svx, dev)
+    if args.decode:
+        return bench_decode(args, torch, svx, dev)
 
     t_gen = time.perf_counter()
     x, desc = make_inputs(args.workload)

@@ -193,6 +193,47 @@ specv_status_t specv_position_diagnostics(const specv_shape_t* shape, const void
                                           void* workspace, size_t workspace_bytes,
                                           hipStream_t stream, hipEvent_t* events);
 
+/* Multi-round speculative decoding with bigram "models" (DistillSpec
+ * Algorithm A.1 repeated: each round extends every sequence by its n
+ * accepted draft tokens and the drawn token). The models are bigram logit
+ * tables [V, V] (row s: the logits of the next token after token s), one for
+ * the target and one for the draft, in `dtype`, row-major, device memory.
+ * Round r, sequence b, with row = philox_row_offset + r * batch + b and prev
+ * the sequence's last token (start_token[b] before round 0):
+ *   drafting: x_i ~ softmax(draft_table[prev_i] / T_b), prev_0 = prev,
+ *     prev_{i+1} = x_i, i < gamma: the inverse CDF in index order (smallest
+ *     v with u * C_{V-1} <= C_v) with u = U(word 0 of Philox(seed; counter
+ *     (row lo, row hi, i, 1))); T_b == 0 drafts the argmax (lowest index);
+ *   verification: specv_verify on target rows target_table[prev_i],
+ *     i = 0..gamma, and draft rows draft_table[prev_i], i < gamma, with
+ *     philox_row_offset + r * batch as its row offset.
+ * Outputs (device, caller-owned): out_tokens [batch, rounds * (gamma + 1)]
+ * (generated tokens, -1 past the end), out_length [batch] (tokens generated;
+ * -1 for a sequence whose start token is outside [0, V) or whose round hit a
+ * data error), out_accepted [batch, rounds] (n of each round, -1 from a
+ * failed round on). Rows of the draft table used by greedy sequences are not
+ * checked for NaN. `events`: NULL, or 2 * SPECV_NUM_STAGES events recorded
+ * around the stages of the last round: drafting (SPECV_STAGE_PLAN slot), the
+ * row gather (ROWSTATS slot), the whole verify step (ACCEPT_MASS slot) and
+ * the append (DRAW slot). Argument errors as for specv_verify; the workspace
+ * is specv_decode_workspace_bytes(shape) bytes, 256-byte aligned. */
+typedef struct {
+  int32_t batch;   /* >= 0                               */
+  int32_t vocab;   /* V >= 1; the tables are [V, V]      */
+  int32_t gamma;   /* draft tokens per round, 0..63      */
+  int32_t rounds;  /* >= 0                               */
+  specv_dtype_t dtype;
+} specv_decode_shape_t;
+
+size_t specv_decode_workspace_bytes(const specv_decode_shape_t* shape);
+specv_status_t specv_decode_bigram(const specv_decode_shape_t* shape, const void* target_table,
+                                   const void* draft_table, const float* temperature,
+                                   const int32_t* start_token, uint64_t seed,
+                                   uint64_t philox_row_offset, int32_t* out_tokens,
+                                   int32_t* out_length, int32_t* out_accepted, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream,
+                                   hipEvent_t* events);
+
 /* Stages of one call, in launch order (one kernel each). */
 #define SPECV_STAGE_PLAN 0        /* offsets of the packed rows, per-row T scale */
 #define SPECV_STAGE_ROWSTATS 1    /* pass 1: max, sum of exp (argmax) per row    */

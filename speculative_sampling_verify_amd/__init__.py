@@ -35,8 +35,14 @@ class SpecvShape(ctypes.Structure):
                 ("total_target_rows", ctypes.c_int64), ("total_draft_rows", ctypes.c_int64)]
 
 
+class SpecvDecodeShape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("vocab", ctypes.c_int32), ("gamma", ctypes.c_int32),
+                ("rounds", ctypes.c_int32), ("dtype", ctypes.c_int)]
+
+
 _P = ctypes.c_void_p
 _SHP = ctypes.POINTER(SpecvShape)
+_DSHP = ctypes.POINTER(SpecvDecodeShape)
 _u64, _i64, _sz = ctypes.c_uint64, ctypes.c_int64, ctypes.c_size_t
 _lib.specv_workspace_bytes.restype = _sz
 _lib.specv_workspace_bytes.argtypes = [_SHP]
@@ -54,6 +60,10 @@ _lib.specv_diagnostics_workspace_bytes.argtypes = [_SHP, ctypes.c_int32]
 _lib.specv_position_diagnostics.restype = ctypes.c_int
 _lib.specv_position_diagnostics.argtypes = [_SHP, _P, _P, _P, _P, ctypes.c_int32, _P, _P, _P, _P, _P,
                                             _sz, _P, _P]
+_lib.specv_decode_workspace_bytes.restype = _sz
+_lib.specv_decode_workspace_bytes.argtypes = [_DSHP]
+_lib.specv_decode_bigram.restype = ctypes.c_int
+_lib.specv_decode_bigram.argtypes = [_DSHP, _P, _P, _P, _P, _u64, _u64, _P, _P, _P, _P, _sz, _P, _P]
 _lib.specv_row_stats.restype = ctypes.c_int
 _lib.specv_row_stats.argtypes = [_SHP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _sz, _P]
 _lib.specv_softmax_rows.restype = ctypes.c_int
@@ -67,7 +77,8 @@ _lib.specv_status_string.argtypes = [ctypes.c_int]
 
 EXPORTED = ("specv_workspace_bytes", "specv_verify", "specv_verify_profiled",
             "specv_verify_with_uniforms", "specv_verify_lenient",
-            "specv_diagnostics_workspace_bytes", "specv_position_diagnostics", "specv_row_stats", "specv_softmax_rows",
+            "specv_diagnostics_workspace_bytes", "specv_position_diagnostics",
+            "specv_decode_workspace_bytes", "specv_decode_bigram", "specv_row_stats", "specv_softmax_rows",
             "specv_philox4x32_10", "specv_copy_bytes", "specv_status_string")
 
 
@@ -261,6 +272,48 @@ def specv_position_diagnostics(target, draft, gamma, temperature, top_k, *, max_
                                          None if events is None else
                                          ctypes.cast(events.array, ctypes.c_void_p))
     _check(st, "specv_position_diagnostics")
+    return out
+
+
+def specv_decode_workspace_bytes(shape: SpecvDecodeShape) -> int:
+    return int(_lib.specv_decode_workspace_bytes(ctypes.byref(shape)))
+
+
+def specv_decode_bigram(target_table, draft_table, temperature, start_token, *, gamma, rounds,
+                        seed=0, philox_row_offset=0, out=None, workspace=None, stream=None,
+                        events=None):
+    """Multi-round speculative decoding with bigram tables [V, V] (row = the
+    previous token). Returns a dict of device tensors: tokens [B, rounds *
+    (gamma + 1)], length [B], accepted [B, rounds]."""
+    if target_table.dim() != 2 or target_table.shape != draft_table.shape or \
+            target_table.shape[0] != target_table.shape[1]:
+        raise ValueError("tables must be [V, V] and alike")
+    dev = target_table.device
+    start_token = start_token if start_token.dtype == torch.int32 else start_token.to(torch.int32)
+    B = start_token.shape[0]
+    shape = SpecvDecodeShape(int(B), int(target_table.shape[0]), int(gamma), int(rounds),
+                             _dtype_code(target_table))
+    if _dtype_code(draft_table) != shape.dtype:
+        raise TypeError("tables must share a dtype")
+    if workspace is None:
+        n = specv_decode_workspace_bytes(shape)
+        if n == 0:
+            raise SpecvError("invalid decode shape")
+        workspace = torch.empty(n, dtype=torch.uint8, device=dev)
+    if out is None:
+        out = {"tokens": torch.empty((B, rounds * (gamma + 1)), dtype=torch.int32, device=dev),
+               "length": torch.empty(B, dtype=torch.int32, device=dev),
+               "accepted": torch.empty((B, rounds), dtype=torch.int32, device=dev)}
+    _check_tensors(dev, target_table=target_table, draft_table=draft_table,
+                   temperature=temperature, start_token=start_token, workspace=workspace, **out)
+    st = _lib.specv_decode_bigram(ctypes.byref(shape), _ptr(target_table), _ptr(draft_table),
+                                  _ptr(temperature), _ptr(start_token), int(seed),
+                                  int(philox_row_offset), _ptr(out["tokens"]), _ptr(out["length"]),
+                                  _ptr(out["accepted"]), _ptr(workspace), workspace.numel(),
+                                  _stream(stream, dev),
+                                  None if events is None else
+                                  ctypes.cast(events.array, ctypes.c_void_p))
+    _check(st, "specv_decode_bigram")
     return out
 
 

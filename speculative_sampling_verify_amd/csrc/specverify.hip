@@ -5,6 +5,7 @@
 
 #include <stdint.h>
 
+#include "decode.hpp"
 #include "diagnostics.hpp"
 #include "kernels.hpp"
 #include "specverify.h"
@@ -316,6 +317,55 @@ specv_status_t run(const Call& c) {
   return SPECV_OK;
 }
 
+struct DecodePlan {
+  specv_shape_t vshape;  // the verify step's shape for one round
+  Plan vp;
+  int64_t esz, row_bytes, cap;
+  size_t off_tpack, off_dpack, off_drafts, off_tsrc, off_dsrc, off_gam, off_cur, off_len, off_fail,
+      off_vn, off_vnext;
+  size_t bytes;
+};
+
+bool decode_shape_ok(const specv_decode_shape_t* s) {
+  if (!s) return false;
+  if (s->batch < 0 || s->vocab < 1 || s->gamma < 0 || s->gamma > SPECV_MAX_GAMMA || s->rounds < 0)
+    return false;
+  if (s->dtype != SPECV_F32 && s->dtype != SPECV_BF16) return false;
+  // the [V, V] tables and the token buffer must be addressable
+  if ((int64_t)s->vocab * s->vocab > ((int64_t)1 << 40)) return false;
+  if ((int64_t)s->batch * s->rounds * (s->gamma + 1) > ((int64_t)1 << 40)) return false;
+  return true;
+}
+
+bool make_decode_plan(const specv_decode_shape_t* s, DecodePlan* d) {
+  d->vshape.batch = s->batch;
+  d->vshape.vocab = s->vocab;
+  d->vshape.max_gamma = s->gamma;
+  d->vshape.dtype = s->dtype;
+  d->vshape.total_target_rows = (int64_t)s->batch * (s->gamma + 1);
+  d->vshape.total_draft_rows = (int64_t)s->batch * s->gamma;
+  if (!shape_ok(&d->vshape)) return false;
+  make_plan(&d->vshape, &d->vp);
+  d->esz = (s->dtype == SPECV_BF16) ? 2 : 4;
+  d->row_bytes = (int64_t)s->vocab * d->esz;
+  d->cap = (int64_t)s->rounds * (s->gamma + 1);
+  const int64_t B = s->batch, g = s->gamma;
+  size_t off = d->vp.bytes;
+  d->off_tpack = off; off = align_up(off + (size_t)(B * (g + 1)) * d->row_bytes);
+  d->off_dpack = off; off = align_up(off + (size_t)(B * g) * d->row_bytes);
+  d->off_drafts = off; off = align_up(off + (size_t)(B * g) * 4);
+  d->off_tsrc = off; off = align_up(off + (size_t)(B * (g + 1)) * 4);
+  d->off_dsrc = off; off = align_up(off + (size_t)(B * g) * 4);
+  d->off_gam = off; off = align_up(off + (size_t)B * 4);
+  d->off_cur = off; off = align_up(off + (size_t)B * 4);
+  d->off_len = off; off = align_up(off + (size_t)B * 4);
+  d->off_fail = off; off = align_up(off + (size_t)B * 4);
+  d->off_vn = off; off = align_up(off + (size_t)B * 4);
+  d->off_vnext = off; off = align_up(off + (size_t)B * 4);
+  d->bytes = off;
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -467,6 +517,107 @@ specv_status_t specv_position_diagnostics(const specv_shape_t* shape, const void
   if ((st = launched()) != SPECV_OK) return st;
   mark(events, 2 * SPECV_STAGE_DRAW + 1, stream);
   return SPECV_OK;
+}
+
+size_t specv_decode_workspace_bytes(const specv_decode_shape_t* shape) {
+  if (!decode_shape_ok(shape)) return 0;
+  DecodePlan d;
+  if (!make_decode_plan(shape, &d)) return 0;
+  return d.bytes;
+}
+
+specv_status_t specv_decode_bigram(const specv_decode_shape_t* shape, const void* target_table,
+                                   const void* draft_table, const float* temperature,
+                                   const int32_t* start_token, uint64_t seed,
+                                   uint64_t philox_row_offset, int32_t* out_tokens,
+                                   int32_t* out_length, int32_t* out_accepted, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream,
+                                   hipEvent_t* events) {
+  if (!decode_shape_ok(shape)) return SPECV_ERR_INVALID_ARGUMENT;
+  DecodePlan d;
+  if (!make_decode_plan(shape, &d)) return SPECV_ERR_INVALID_ARGUMENT;
+  const int64_t B = shape->batch, g = shape->gamma, R = shape->rounds;
+  if (B == 0) return SPECV_OK;
+  if (!target_table || !draft_table || !temperature || !start_token || !out_length)
+    return SPECV_ERR_INVALID_ARGUMENT;
+  if (R > 0 && (!out_tokens || !out_accepted)) return SPECV_ERR_INVALID_ARGUMENT;
+  if (!aligned(target_table, (size_t)d.esz) || !aligned(draft_table, (size_t)d.esz))
+    return SPECV_ERR_INVALID_ARGUMENT;
+  if (!workspace || workspace_bytes < d.bytes || !aligned(workspace, kAlign))
+    return SPECV_ERR_WORKSPACE;
+  DecodeArgs a;
+  a.ttab = target_table;
+  a.dtab = draft_table;
+  a.temperature = temperature;
+  a.start = start_token;
+  a.cur = at<int32_t>(workspace, d.off_cur);
+  a.drafts = at<int32_t>(workspace, d.off_drafts);
+  a.trow_src = at<int32_t>(workspace, d.off_tsrc);
+  a.drow_src = at<int32_t>(workspace, d.off_dsrc);
+  a.gam = at<int32_t>(workspace, d.off_gam);
+  a.len = at<int32_t>(workspace, d.off_len);
+  a.fail = at<int32_t>(workspace, d.off_fail);
+  a.vn = at<int32_t>(workspace, d.off_vn);
+  a.vnext = at<int32_t>(workspace, d.off_vnext);
+  a.out_tokens = out_tokens;
+  a.out_length = out_length;
+  a.out_accepted = out_accepted;
+  a.seed = seed;
+  a.V = shape->vocab;
+  a.cap = d.cap;
+  a.B = (int32_t)B;
+  a.gamma = (int32_t)g;
+  a.rounds = (int32_t)R;
+  a.round = 0;
+  a.row_base = philox_row_offset;
+  const dim3 block(kBlock);
+  const unsigned seq_blocks = (unsigned)((B + kBlock - 1) / kBlock);
+  hipLaunchKernelGGL(k_dec_init, dim3(seq_blocks < 1024 ? seq_blocks : 1024), block, 0, stream, a);
+  specv_status_t st = launched();
+  if (st != SPECV_OK) return st;
+  GatherArgs ga;
+  ga.ttab = target_table;
+  ga.dtab = draft_table;
+  ga.trow_src = a.trow_src;
+  ga.drow_src = a.drow_src;
+  ga.tdst = at<char>(workspace, d.off_tpack);
+  ga.ddst = at<char>(workspace, d.off_dpack);
+  ga.row_bytes = d.row_bytes;
+  ga.n_t = B * (g + 1);
+  ga.n_d = B * g;
+  ga.pieces = (int32_t)((d.row_bytes + kGatherPiece - 1) / kGatherPiece);
+  const bool vec = d.row_bytes % 16 == 0 && aligned(target_table, 16) && aligned(draft_table, 16);
+  const int64_t gather_waves = (ga.n_t + ga.n_d) * ga.pieces;
+  for (int64_t r = 0; r < R; ++r) {
+    a.round = (int32_t)r;
+    a.row_base = philox_row_offset + (uint64_t)(r * B);
+    const bool last = r + 1 == R;
+    hipEvent_t* ev = last ? events : nullptr;
+    mark(ev, 2 * SPECV_STAGE_PLAN, stream);
+    if (shape->dtype == SPECV_BF16)
+      hipLaunchKernelGGL((k_dec_draft<kBF16>), dim3(blocks_for(B)), block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((k_dec_draft<kF32>), dim3(blocks_for(B)), block, 0, stream, a);
+    if ((st = launched()) != SPECV_OK) return st;
+    mark(ev, 2 * SPECV_STAGE_PLAN + 1, stream);
+    mark(ev, 2 * SPECV_STAGE_ROWSTATS, stream);
+    if (vec) hipLaunchKernelGGL((k_dec_gather<true>), dim3(blocks_for(gather_waves)), block, 0, stream, ga);
+    else hipLaunchKernelGGL((k_dec_gather<false>), dim3(blocks_for(gather_waves)), block, 0, stream, ga);
+    if ((st = launched()) != SPECV_OK) return st;
+    mark(ev, 2 * SPECV_STAGE_ROWSTATS + 1, stream);
+    mark(ev, 2 * SPECV_STAGE_ACCEPT_MASS, stream);
+    Call c{&d.vshape, ga.tdst, ga.ddst, a.drafts, a.gam, temperature, seed, a.row_base, nullptr,
+           nullptr, at<int32_t>(workspace, d.off_vn), at<int32_t>(workspace, d.off_vnext),
+           workspace, d.vp.bytes, stream, nullptr};
+    if ((st = run(c)) != SPECV_OK) return st;
+    mark(ev, 2 * SPECV_STAGE_ACCEPT_MASS + 1, stream);
+    mark(ev, 2 * SPECV_STAGE_DRAW, stream);
+    hipLaunchKernelGGL(k_dec_append, dim3(seq_blocks), block, 0, stream, a);
+    if ((st = launched()) != SPECV_OK) return st;
+    mark(ev, 2 * SPECV_STAGE_DRAW + 1, stream);
+  }
+  hipLaunchKernelGGL(k_dec_finish, dim3(seq_blocks), block, 0, stream, a);
+  return launched();
 }
 
 specv_status_t specv_row_stats(const specv_shape_t* shape, const void* target_logits,

@@ -280,6 +280,29 @@ def chi_square_set(rounds: int = 1_000_000, vocab: int = 8, gamma: int = 4, gen_
                   meta={"target_rows": t, "draft_rows": d})
 
 
+@dataclass
+class BigramTables:
+    """Bigram "models": row s of each [V, V] table holds the logits of the
+    next token after token s (bf16 bit patterns)."""
+    target: np.ndarray
+    draft: np.ndarray
+    seed: int
+
+    def start(self, n: int) -> np.ndarray:
+        return _rng(self.seed, 99).integers(0, self.target.shape[0], n).astype(np.int32)
+
+
+def bigram_tables(vocab: int = 8192, gen_seed: int = 6) -> BigramTables:
+    """The T5-XXL-like row recipe per table row: target logits N(0, 3^2)
+    with 20 uniformly chosen entries raised by 8, draft = target + N(0, 1)."""
+    rng = _rng(gen_seed, 0)
+    t = rng.standard_normal((vocab, vocab), dtype=np.float32) * 3.0
+    rows = np.repeat(np.arange(vocab), 20)
+    t[rows, rng.integers(0, vocab, vocab * 20)] += 8.0
+    d = t + rng.standard_normal((vocab, vocab), dtype=np.float32)
+    return BigramTables(to_bf16_bits(t), to_bf16_bits(d), gen_seed)
+
+
 def by_name(name: str, **kw) -> Inputs:
     return {"tiny_cpu": tiny_cpu, "t5xxl_like": t5xxl_like, "serving_b64": serving_b64,
             "ragged_b256": ragged_b256, "large_vocab": large_vocab, "chi": chi_square_set}[name](**kw)

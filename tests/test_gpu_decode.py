@@ -1,0 +1,129 @@
+"""GPU parity of the multi-round bigram decode loop (specv_decode_bigram,
+through the C ABI) against the oracle's loop on the same tables, start
+tokens, temperatures and Philox stream.
+
+Bar: generated tokens and per-round accepted counts are identical up to the
+first round in which the oracle saw a near-tie (a decisive uniform within
+1e-6 relative of its threshold, in drafting or in verification); from there
+a sequence may follow another path, and such sequences are counted. The
+GPU's own output law is also tested against the target Markov chain.
+"""
+import numpy as np
+import pytest
+import torch
+from scipy import stats
+
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def svx():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import speculative_sampling_verify_amd as m
+    return m
+
+
+def log(*a):
+    print(*a, flush=True)
+
+
+def to_bf16_bits(a):
+    import synth
+    return synth.to_bf16_bits(np.asarray(a, np.float32))
+
+
+def tables(V, seed, sigma=0.7, scale=1.5):
+    rng = np.random.default_rng(seed)
+    t = (rng.standard_normal((V, V)) * scale).astype(np.float32)
+    d = (t + rng.standard_normal((V, V)) * sigma).astype(np.float32)
+    return t, d
+
+
+def run_gpu(svx, t, d, T, start, gamma, rounds, seed=0, row_offset=0):
+    dev = "cuda"
+    def tens(a):
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+    out = svx.specv_decode_bigram(tens(t), tens(d), tens(np.asarray(T, np.float32)),
+                                  tens(np.asarray(start, np.int32)), gamma=gamma, rounds=rounds,
+                                  seed=seed, philox_row_offset=row_offset)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in out.items()}
+
+
+def assert_decode_parity(name, svx, t, d, T, start, gamma, rounds, seed=0, row_offset=0):
+    log("[case] decode %s B=%d V=%d gamma=%d rounds=%d" % (name, len(start), t.shape[0], gamma,
+                                                          rounds))
+    got = run_gpu(svx, t, d, T, start, gamma, rounds, seed, row_offset)
+    want = oracle.decode_bigram(t, d, T, start, gamma=gamma, rounds=rounds, seed=seed,
+                                row_offset=row_offset)
+    B = len(start)
+    diverged = 0
+    for b in range(B):
+        f = int(want.first_near[b])
+        np.testing.assert_array_equal(got["accepted"][b, :f], want.accepted[b, :f], err_msg=str(b))
+        if want.length[b] < 0:
+            assert got["length"][b] == -1
+            continue
+        upto = int((want.accepted[b, :f] + 1).sum())
+        np.testing.assert_array_equal(got["tokens"][b, :upto], want.tokens[b, :upto],
+                                      err_msg=str(b))
+        if f == rounds:
+            assert got["length"][b] == want.length[b]
+            np.testing.assert_array_equal(got["tokens"][b], want.tokens[b])
+        else:
+            diverged += 1
+    log("[parity] decode %s: sequences=%d with a near-tie=%d mean tokens/round=%.4f"
+        % (name, B, diverged, float(np.mean(got["accepted"][got["accepted"] >= 0] + 1))))
+    # a uniform falls within 1e-6 (relative) of one of the V boundaries of an
+    # inverse CDF with probability about 2e-6 * V per draw; with up to
+    # rounds * (gamma + 1) draws per sequence that bounds the expected share of
+    # sequences with a near-tie; twice that share plus a few is the sanity cap
+    expect = min(1.0, 2e-6 * t.shape[0] * rounds * (gamma + 1))
+    assert diverged <= 2 * expect * B + 4, (diverged, expect)
+    return got, want
+
+
+def test_decode_parity_fp32(svx):
+    t, d = tables(1000, 1)
+    B = 256
+    rng = np.random.default_rng(2)
+    assert_decode_parity("fp32 V=1000", svx, t, d, np.ones(B, np.float32),
+                         rng.integers(0, 1000, B), gamma=4, rounds=6, seed=11)
+
+
+def test_decode_parity_bf16_mixed_greedy(svx):
+    t, d = tables(4096, 3, sigma=1.0, scale=2.0)
+    B = 128
+    T = np.where(np.arange(B) % 2 == 0, 0.8, 0.0).astype(np.float32)
+    rng = np.random.default_rng(4)
+    assert_decode_parity("bf16 V=4096", svx, to_bf16_bits(t), to_bf16_bits(d), T,
+                         rng.integers(0, 4096, B), gamma=5, rounds=5, seed=3, row_offset=1000)
+
+
+def test_decode_parity_odd_vocab_and_bad_starts(svx):
+    # V = 999: rows are not 16-byte multiples (scalar gather and verify paths)
+    t, d = tables(999, 5)
+    B = 64
+    start = np.random.default_rng(6).integers(0, 999, B).astype(np.int32)
+    start[3], start[10] = -1, 999
+    got, _ = assert_decode_parity("bf16 V=999", svx, to_bf16_bits(t), to_bf16_bits(d),
+                                  np.full(B, 1.3, np.float32), start, gamma=3, rounds=4)
+    assert got["length"][3] == -1 and got["length"][10] == -1
+
+
+def test_decode_gpu_sequence_law(svx):
+    # the GPU loop's own output: joint of the first three tokens vs the chain
+    t, d = tables(5, 0)
+    B, c = 400_000, 2
+    got = run_gpu(svx, t, d, np.ones(B, np.float32), np.full(B, c, np.int32), 3, 3, seed=7)
+    P = torch.softmax(torch.from_numpy(t.astype(np.float64)), dim=-1).numpy()
+    y = got["tokens"][:, :3].astype(np.int64)
+    assert (got["length"] >= 3).all()
+    obs = np.bincount((y[:, 0] * 5 + y[:, 1]) * 5 + y[:, 2], minlength=125)
+    exp = np.einsum("a,ab,bc->abc", P[c], P, P).reshape(-1) * B
+    pv = stats.chisquare(obs, exp).pvalue
+    log("[law] decode GPU joint of 3 tokens: p = %.4g" % pv)
+    assert pv > 1e-4
