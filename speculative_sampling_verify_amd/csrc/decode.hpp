@@ -12,10 +12,7 @@
 //   the verify step (plan, pass 1, accept + pass 2, draw);
 //   k_dec_append  appends the n accepted drafts and the drawn token.
 // Within a lane the drafting scan holds 16 consecutive elements, so lane
-// order is index order and the running sums follow the index-order CDF: a
-// tile's per-lane fp32 tree sums are scanned across the wave in float64,
-// and the tile totals are added in tile order; the same code gives the total
-// S and the walk that finds the first cumulative sum >= u * S.
+// order is index order and the walk follows the index-order CDF.
 #pragma once
 
 #include "kernels.hpp"
@@ -61,24 +58,82 @@ __global__ __launch_bounds__(kBlock) void k_dec_init(DecodeArgs a) {
   for (int64_t e = t; e < (int64_t)a.B * a.cap; e += stride) a.out_tokens[e] = -1;
 }
 
-template <int DT>
-__device__ __forceinline__ float dec_elem(const void* row, int64_t V, int64_t e) {
-  return e < V ? load_logit<DT>(row, e) : ninf();
+// The lane's 16 consecutive elements of the drafting tile at e0 (-inf past
+// V): four or two 16-byte loads when rows are 16-byte aligned, else scalar.
+template <int DT, bool VEC>
+__device__ __forceinline__ void dec_load(const void* row, int64_t V, int64_t e0, int lane,
+                                         float (&z)[kDecPL]) {
+  const int64_t base = e0 + (int64_t)lane * kDecPL;
+  if constexpr (VEC) {
+    constexpr int VE = (DT == kBF16) ? 8 : 4;  // elements per 16 bytes
+    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const char*>(row) +
+                                                    base * (DT == kBF16 ? 2 : 4));
+#pragma unroll
+    for (int v = 0; v < kDecPL / VE; ++v) {
+      // V * element size is a multiple of 16 here, so a vector is all in or all out
+      u32x4 q = {0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};
+      if (DT != kBF16) q = u32x4{0xff800000u, 0xff800000u, 0xff800000u, 0xff800000u};
+      if (base + v * VE < V) q = p[v];
+      if constexpr (DT == kBF16) {
+        z[v * 8 + 0] = bf16_lo(q.x); z[v * 8 + 1] = bf16_hi(q.x);
+        z[v * 8 + 2] = bf16_lo(q.y); z[v * 8 + 3] = bf16_hi(q.y);
+        z[v * 8 + 4] = bf16_lo(q.z); z[v * 8 + 5] = bf16_hi(q.z);
+        z[v * 8 + 6] = bf16_lo(q.w); z[v * 8 + 7] = bf16_hi(q.w);
+      } else {
+        z[v * 4 + 0] = __uint_as_float(q.x); z[v * 4 + 1] = __uint_as_float(q.y);
+        z[v * 4 + 2] = __uint_as_float(q.z); z[v * 4 + 3] = __uint_as_float(q.w);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kDecPL; ++j) z[j] = (base + j < V) ? load_logit<DT>(row, base + j) : ninf();
+  }
 }
 
+constexpr int kDecBatch = 4;  // drafting tiles whose loads are issued together
+
 // One draw from softmax(row * k) (k = log2(e)/T), or the argmax for k == 0.
-template <int DT>
+// Pass 1: per-lane online (max, sum of 2^(z k - rk)) over the row, merged
+// across the wave (fp64 sum). Pass 2 walks the tiles in order: a tile's
+// per-lane fp32 tree sums are scanned in fp64 across the wave; the first
+// tile whose running total reaches u * S holds the token, the first lane
+// whose prefix reaches it, and that lane's first element.
+template <int DT, bool VEC>
 __device__ int dec_sample_row(const void* row, int64_t V, float k, double u, int lane) {
-  float m = ninf();
+  const int64_t n_tiles = (V + kDecTE - 1) / kDecTE;
+  float m = ninf(), rk = 0.f;
+  double s = 0.0;
   int64_t arg = INT32_MAX;
-  for (int64_t e0 = 0; e0 < V; e0 += kDecTE) {
+  for (int64_t t0 = 0; t0 < n_tiles; t0 += kDecBatch) {
+    float z[kDecBatch][kDecPL];
 #pragma unroll
-    for (int j = 0; j < kDecPL; ++j) {
-      const int64_t e = e0 + (int64_t)lane * kDecPL + j;
-      const float z = dec_elem<DT>(row, V, e);
-      if (z > m) {
-        m = z;
-        arg = e;
+    for (int b = 0; b < kDecBatch; ++b) {
+      if (t0 + b < n_tiles) dec_load<DT, VEC>(row, V, (t0 + b) * kDecTE, lane, z[b]);
+      else {
+#pragma unroll
+        for (int j = 0; j < kDecPL; ++j) z[b][j] = ninf();
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < kDecBatch; ++b) {
+      const float g = tile_max(z[b]);
+      if (k == 0.f) {
+#pragma unroll
+        for (int j = 0; j < kDecPL; ++j)
+          if (z[b][j] > m) {
+            m = z[b][j];
+            arg = (t0 + b) * kDecTE + (int64_t)lane * kDecPL + j;
+          }
+      } else if (g > ninf()) {
+        const float mn = fmaxf(m, g);
+        const float rkn = ref_point(mn, k);
+        const float sc = (m == ninf()) ? 0.f : exp2_hw(rk - rkn);
+        float e[kDecPL];
+#pragma unroll
+        for (int j = 0; j < kDecPL; ++j) e[j] = exp2_hw(__builtin_fmaf(z[b][j], k, -rkn));
+        s = __builtin_fma(s, (double)sc, (double)tree_sum(e));
+        m = mn;
+        rk = rkn;
       }
     }
   }
@@ -87,57 +142,61 @@ __device__ int dec_sample_row(const void* row, int64_t V, float k, double u, int
     const int best = wave_min((m == M && arg < INT32_MAX) ? (int)arg : INT32_MAX);
     return best == INT32_MAX ? 0 : best;
   }
-  const float rk = ref_point(M, k);
-  auto tile_scan = [&](int64_t e0, float (&w)[kDecPL], float& ls) {
-#pragma unroll
-    for (int j = 0; j < kDecPL; ++j)
-      w[j] = exp2_hw(__builtin_fmaf(dec_elem<DT>(row, V, e0 + (int64_t)lane * kDecPL + j), k, -rk));
-    float t[kDecPL];
-#pragma unroll
-    for (int j = 0; j < kDecPL; ++j) t[j] = w[j];
-    ls = tree_sum(t);
-    return wave_inclusive_scan((double)ls, lane);
-  };
-  double S = 0.0;
-  for (int64_t e0 = 0; e0 < V; e0 += kDecTE) {
-    float w[kDecPL], ls;
-    const double incl = tile_scan(e0, w, ls);
-    S += __shfl(incl, kWave - 1, kWave);
-  }
+  const float rkM = ref_point(M, k);
+  const double S = wave_sum((m == ninf()) ? 0.0 : s * exp2((double)(m * k) - (double)rkM));
   const double target = u * S;
   double C = 0.0;
-  for (int64_t e0 = 0; e0 < V; e0 += kDecTE) {
-    float w[kDecPL], ls;
-    const double incl = tile_scan(e0, w, ls);
-    const double tot = __shfl(incl, kWave - 1, kWave);
-    if (C + tot >= target || e0 + kDecTE >= V) {
-      const uint64_t hit = ballot(C + incl >= target);
-      const uint64_t pos = ballot(ls > 0.f);
-      if (hit == 0 && pos == 0) return 0;  // no mass at all (unusable row)
-      const int L = hit ? first_lane(hit) : 63 - __builtin_clzll(pos);
-      double ex = __shfl_up(incl, 1, kWave);
-      if (lane == 0) ex = 0.0;
-      int tok = -1;
-      if (lane == L) {
-        double c = C + ex;
-        int last = -1;
+  for (int64_t t0 = 0; t0 < n_tiles; t0 += kDecBatch) {
+    float z[kDecBatch][kDecPL];
 #pragma unroll
-        for (int j = 0; j < kDecPL; ++j) {
-          if (w[j] > 0.f) last = j;
-          c += (double)w[j];
-          if (tok < 0 && w[j] > 0.f && c >= target) tok = j;
-        }
-        if (tok < 0) tok = last;
-        tok = (int)(e0 + (int64_t)lane * kDecPL + (tok < 0 ? 0 : tok));
+    for (int b = 0; b < kDecBatch; ++b) {
+      if (t0 + b < n_tiles) dec_load<DT, VEC>(row, V, (t0 + b) * kDecTE, lane, z[b]);
+      else {
+#pragma unroll
+        for (int j = 0; j < kDecPL; ++j) z[b][j] = ninf();
       }
-      return __shfl(tok, L, kWave);
     }
-    C += tot;
+#pragma unroll
+    for (int b = 0; b < kDecBatch; ++b) {
+      if (t0 + b >= n_tiles) break;
+      float w[kDecPL], tw[kDecPL];
+#pragma unroll
+      for (int j = 0; j < kDecPL; ++j) {
+        w[j] = exp2_hw(__builtin_fmaf(z[b][j], k, -rkM));
+        tw[j] = w[j];
+      }
+      const float ls = tree_sum(tw);
+      const double incl = wave_inclusive_scan((double)ls, lane);
+      const double tot = __shfl(incl, kWave - 1, kWave);
+      if (C + tot >= target || t0 + b + 1 >= n_tiles) {
+        const uint64_t hit = ballot(C + incl >= target);
+        const uint64_t pos = ballot(ls > 0.f);
+        if (hit == 0 && pos == 0) return 0;  // no mass at all (unusable row)
+        const int L = hit ? first_lane(hit) : 63 - __builtin_clzll(pos);
+        double ex = __shfl_up(incl, 1, kWave);
+        if (lane == 0) ex = 0.0;
+        int tok = -1;
+        if (lane == L) {
+          double c = C + ex;
+          int last = -1;
+#pragma unroll
+          for (int j = 0; j < kDecPL; ++j) {
+            if (w[j] > 0.f) last = j;
+            c += (double)w[j];
+            if (tok < 0 && w[j] > 0.f && c >= target) tok = j;
+          }
+          if (tok < 0) tok = last < 0 ? 0 : last;
+          tok = (int)((t0 + b) * kDecTE + (int64_t)lane * kDecPL + tok);
+        }
+        return __shfl(tok, L, kWave);
+      }
+      C += tot;
+    }
   }
   return 0;
 }
 
-template <int DT>
+template <int DT, bool VEC>
 __global__ __launch_bounds__(kBlock) void k_dec_draft(DecodeArgs a) {
   constexpr int64_t esz = (DT == kBF16) ? 2 : 4;
   const int lane = threadIdx.x & (kWave - 1);
@@ -162,7 +221,7 @@ __global__ __launch_bounds__(kBlock) void k_dec_draft(DecodeArgs a) {
         u = (double)uniform24(w.w0);
       }
       const void* row = static_cast<const char*>(a.dtab) + (int64_t)prev * a.V * esz;
-      x = dec_sample_row<DT>(row, a.V, k, u, lane);
+      x = dec_sample_row<DT, VEC>(row, a.V, k, u, lane);
       if (x < 0 || (int64_t)x >= a.V) x = 0;
     }
     if (lane == 0) a.drafts[b * a.gamma + i] = x;

@@ -594,10 +594,13 @@ specv_status_t specv_decode_bigram(const specv_decode_shape_t* shape, const void
     const bool last = r + 1 == R;
     hipEvent_t* ev = last ? events : nullptr;
     mark(ev, 2 * SPECV_STAGE_PLAN, stream);
-    if (shape->dtype == SPECV_BF16)
-      hipLaunchKernelGGL((k_dec_draft<kBF16>), dim3(blocks_for(B)), block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((k_dec_draft<kF32>), dim3(blocks_for(B)), block, 0, stream, a);
+    if (shape->dtype == SPECV_BF16) {
+      if (vec) hipLaunchKernelGGL((k_dec_draft<kBF16, true>), dim3(blocks_for(B)), block, 0, stream, a);
+      else hipLaunchKernelGGL((k_dec_draft<kBF16, false>), dim3(blocks_for(B)), block, 0, stream, a);
+    } else {
+      if (vec) hipLaunchKernelGGL((k_dec_draft<kF32, true>), dim3(blocks_for(B)), block, 0, stream, a);
+      else hipLaunchKernelGGL((k_dec_draft<kF32, false>), dim3(blocks_for(B)), block, 0, stream, a);
+    }
     if ((st = launched()) != SPECV_OK) return st;
     mark(ev, 2 * SPECV_STAGE_PLAN + 1, stream);
     mark(ev, 2 * SPECV_STAGE_ROWSTATS, stream);
