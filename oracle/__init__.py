@@ -54,6 +54,10 @@ def _load():
     lib.oracle_decode_bigram.restype = ctypes.c_int
     lib.oracle_decode_bigram.argtypes = [i64, i64, i64, i64, ctypes.c_int, P, P, P, P, u64, u64,
                                          P, P, P, P, ctypes.c_int]
+    lib.oracle_cascade_bigram.restype = ctypes.c_int
+    lib.oracle_cascade_bigram.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int, P, P, P, P, P,
+                                          ctypes.c_int, ctypes.c_float, u64, u64, ctypes.c_int,
+                                          P, P, P, P, ctypes.c_int]
     lib.oracle_row_stats.restype = None
     lib.oracle_row_stats.argtypes = [P, ctypes.c_int, i64, i64, P, P, P, P, P]
     lib.oracle_softmax_row.restype = None
@@ -198,6 +202,35 @@ def decode_bigram(target_table, draft_table, temperature, start, *, gamma, round
                              _ptr(temperature), _ptr(start), int(seed), int(row_offset),
                              _ptr(tokens), _ptr(length), _ptr(accepted), _ptr(first_near),
                              int(nthreads or default_threads()))
+    return DecodeResult(tokens, length, accepted, first_near)
+
+
+def cascade_bigram(target_table, mid_table, small_table, temperature, start, *, k1, k2, rounds,
+                   lenience="none", epsilon=1.0, seed=0, row_offset=0, mutant_q_is_p1=False,
+                   nthreads=None) -> DecodeResult:
+    """CS Drafting's vertical cascade with bigram tables: the smallest table
+    drafts k2 tokens per inner round for the intermediate one (reviewed with
+    the given lenience) until k1 tokens are drafted; the target reviews them
+    without lenience."""
+    lib = _load()
+    tabs = [np.ascontiguousarray(t) for t in (target_table, mid_table, small_table)]
+    if len({(t.dtype, t.shape) for t in tabs}) != 1 or tabs[0].shape[0] != tabs[0].shape[1]:
+        raise ValueError("tables must be [V, V] of one dtype")
+    V = tabs[0].shape[0]
+    temperature = np.ascontiguousarray(temperature, dtype=np.float32)
+    start = np.ascontiguousarray(start, dtype=np.int32)
+    B = start.shape[0]
+    cap = rounds * (k1 + 1)
+    tokens = np.full((B, cap), -1, np.int32)
+    length = np.empty(B, np.int32)
+    accepted = np.empty((B, rounds), np.int32)
+    first_near = np.empty(B, np.int32)
+    lib.oracle_cascade_bigram(B, V, k1, k2, rounds, _dtype_code(tabs[0]), _ptr(tabs[0]),
+                              _ptr(tabs[1]), _ptr(tabs[2]), _ptr(temperature), _ptr(start),
+                              LENIENCE[lenience], float(np.float32(epsilon)), int(seed),
+                              int(row_offset), int(bool(mutant_q_is_p1)), _ptr(tokens),
+                              _ptr(length), _ptr(accepted), _ptr(first_near),
+                              int(nthreads or default_threads()))
     return DecodeResult(tokens, length, accepted, first_near)
 
 

@@ -725,3 +725,244 @@ int oracle_decode_bigram(int64_t batch, int64_t vocab, int64_t gamma, int64_t ro
   free(dnear); free(n_out); free(next_out); free(vnear); free(z); free(q);
   return 0;
 }
+
+/* ------------------------------------------------------------------ */
+/* Vertical cascade with bigram "models".                              */
+/* ------------------------------------------------------------------ */
+
+/* CS Drafting's vertical cascade (Chen et al., "Cascade Speculative
+ * Drafting for Even Faster LLM Inference", sections 3.1 and 3.4) over three
+ * bigram tables: target t, intermediate drafter m1, smallest drafter m2.
+ * Outer round r of sequence b builds a draft of k1 tokens for the target by
+ * inner rounds j = 0, 1, ...: m2 drafts k2 tokens (as in the decode loop),
+ * m1 reviews them with the lenience (kind, eps) -- the step of Algorithm A.1
+ * with threshold f(p1, eps)/q2 -- and its n accepted tokens plus its drawn
+ * token join the draft, until the draft holds k1 tokens (the excess of the
+ * last inner round is dropped). The target then reviews the draft without
+ * lenience. Its draft distribution at each position is the one that token
+ * was drawn from, given everything before it:
+ *   a token from an inner position i < k2 (an accepted draft or the draw
+ *   after a rejection): Q = min(q2, f(p1)) + (1 - beta) * norm(max(0, p1 -
+ *   q2)), beta = sum_v min(q2(v), f(p1(v))) -- the law of that step's output;
+ *   a token from the bonus position k2 (all k2 drafts accepted): Q = p1.
+ * With that Q the target review keeps the target's output law whatever the
+ * inner lenience (the reading of "withholding lenience at the target review
+ * preserves the output distribution"). The outer review runs in fp32 on
+ * target rows converted exactly from the table and draft rows
+ * fl32(T * ln Q) (-inf where Q = 0), so that softmax(row / T) = Q.
+ * Greedy sequences (T = 0) use exact-match reviews throughout.
+ * Philox rows: outer round r uses the block row_offset + r * (k1 + 1) *
+ * batch (+ b), inner round j the block row_offset + (r * (k1 + 1) + 1 + j)
+ * * batch; drafting draws word 0 of counter (row, i, 1), reviews use the
+ * verify step's counters. Every inner round runs over the whole batch;
+ * sequences whose draft is already complete take gamma = 0 and their result
+ * is not used.
+ * Outputs as oracle_decode_bigram, with out_tokens [batch, rounds * (k1 + 1)],
+ * out_accepted the target review's n per round, and out_first_near the first
+ * round with a near-tie anywhere in it. mutant_q_is_p1 = 1 makes the target
+ * review use p1 as the draft distribution at every position (a negative
+ * control: wrong unless eps = 1). */
+static void table_row_f32(const void* tab, int dtype, int64_t V, int64_t row, float* out) {
+  if (dtype == ORACLE_BF16) {
+    const uint16_t* h = (const uint16_t*)tab + row * V;
+    for (int64_t v = 0; v < V; ++v) {
+      uint32_t w = (uint32_t)h[v] << 16;
+      memcpy(&out[v], &w, 4);
+    }
+  } else {
+    memcpy(out, (const float*)tab + row * V, (size_t)V * 4);
+  }
+}
+
+int oracle_cascade_bigram(int64_t batch, int64_t vocab, int64_t k1, int64_t k2, int64_t rounds,
+                          int dtype, const void* ttab, const void* m1tab, const void* m2tab,
+                          const float* temperature, const int32_t* start, int lenience_kind,
+                          float eps, uint64_t seed, uint64_t row_offset, int mutant_q_is_p1,
+                          int32_t* out_tokens, int32_t* out_length, int32_t* out_accepted,
+                          int32_t* out_first_near, int nthreads) {
+  const int64_t V = vocab, B = batch;
+  const size_t esz = dtype == ORACLE_BF16 ? 2 : 4;
+  const size_t row_bytes = (size_t)V * esz;
+  const int64_t cap = rounds * (k1 + 1);
+  const int64_t dcap = k1 + k2 + 1; /* draft buffer per sequence */
+  /* inner review buffers (table dtype) */
+  char* itpack = (char*)malloc((size_t)(B * (k2 + 1)) * row_bytes + 1);
+  char* idpack = (char*)malloc((size_t)(B * k2) * row_bytes + 1);
+  int32_t* itok = (int32_t*)malloc((size_t)(B * k2 + 1) * 4);
+  int32_t* igam = (int32_t*)malloc((size_t)(B + 1) * 4);
+  /* outer review buffers (fp32) */
+  float* otpack = (float*)malloc((size_t)(B * (k1 + 1) * V + 1) * 4);
+  float* odpack = (float*)malloc((size_t)(B * k1 * V + 1) * 4);
+  int32_t* otok = (int32_t*)malloc((size_t)(B * k1 + 1) * 4);
+  int32_t* ogam = (int32_t*)malloc((size_t)(B + 1) * 4);
+  /* per-sequence state */
+  int32_t* dtok = (int32_t*)malloc((size_t)(B * dcap + 1) * 4);   /* draft tokens      */
+  int32_t* dprev = (int32_t*)malloc((size_t)(B * dcap + 1) * 4);  /* their prev token  */
+  int8_t* dbonus = (int8_t*)malloc((size_t)(B * dcap + 1));       /* from a bonus slot */
+  int64_t* dlen = (int64_t*)malloc((size_t)(B + 1) * 8);
+  int32_t* cur = (int32_t*)malloc((size_t)(B + 1) * 4);
+  int32_t* len = (int32_t*)malloc((size_t)(B + 1) * 4);
+  uint8_t* failed = (uint8_t*)malloc((size_t)B + 1);
+  uint8_t* near = (uint8_t*)malloc((size_t)B + 1);
+  uint8_t* vnear = (uint8_t*)malloc((size_t)B + 1);
+  int32_t* n_out = (int32_t*)malloc((size_t)(B + 1) * 4);
+  int32_t* next_out = (int32_t*)malloc((size_t)(B + 1) * 4);
+  int32_t* ipr = (int32_t*)malloc((size_t)(B * (k2 + 1) + 1) * 4); /* inner prev per slot */
+  double* z = (double*)malloc((size_t)V * 8);
+  double* p1 = (double*)malloc((size_t)V * 8);
+  double* q2 = (double*)malloc((size_t)V * 8);
+  for (int64_t b = 0; b < B; ++b) {
+    failed[b] = (uint8_t)(start[b] < 0 || start[b] >= V);
+    cur[b] = failed[b] ? 0 : start[b];
+    len[b] = 0;
+    out_first_near[b] = (int32_t)rounds;
+  }
+  for (int64_t r = 0; r < rounds; ++r) {
+    for (int64_t b = 0; b < B; ++b) {
+      dlen[b] = 0;
+      near[b] = 0;
+    }
+    /* inner rounds: at most k1 (each adds at least one token) */
+    for (int64_t j = 0; j < k1; ++j) {
+      const uint64_t rbase = row_offset + (uint64_t)((r * (k1 + 1) + 1 + j) * B);
+      for (int64_t b = 0; b < B; ++b) {
+        const int active = dlen[b] < k1;
+        igam[b] = active ? (int32_t)k2 : 0;
+        const double T = (double)temperature[b];
+        int32_t prev = dlen[b] > 0 ? dtok[b * dcap + dlen[b] - 1] : cur[b];
+        const int64_t g = igam[b];
+        /* packed offsets of this inner batch: sequence b's rows start at
+         * sum_{b' < b} (g_b' + 1) and sum g_b' (computed below) */
+        for (int64_t i = 0; i <= g; ++i) {
+          ipr[b * (k2 + 1) + i] = prev;
+          if (i == g) break;
+          load_row(m2tab, dtype, V, prev, z);
+          int64_t x = 0;
+          if (!row_is_valid(z, V) || isnan(T) || T < 0.0 || isinf(T)) {
+            x = 0;
+          } else if (T == 0.0) {
+            x = row_argmax(z, V);
+          } else {
+            row_softmax(z, V, T, NULL, NULL, q2);
+            const uint64_t prow = rbase + (uint64_t)b;
+            uint32_t ctr[4] = {(uint32_t)prow, (uint32_t)(prow >> 32), (uint32_t)i, 1u};
+            uint32_t w[4];
+            oracle_philox4x32_10(seed, ctr, w);
+            double margin = INFINITY;
+            x = inverse_cdf(q2, V, oracle_uniform24(w[0]), &margin, NULL);
+            if (x < 0) x = 0;
+            if (margin < ORACLE_NEAR_TIE) near[b] = 1;
+          }
+          itok[b * k2 + i] = (int32_t)x;
+          prev = (int32_t)x;
+        }
+      }
+      /* pack the inner review (ragged: inactive sequences have gamma 0) */
+      int64_t tt = 0, td = 0;
+      for (int64_t b = 0; b < B; ++b) {
+        const int64_t g = igam[b];
+        for (int64_t i = 0; i <= g; ++i)
+          memcpy(itpack + (size_t)(tt + i) * row_bytes,
+                 (const char*)m1tab + (size_t)ipr[b * (k2 + 1) + i] * row_bytes, row_bytes);
+        for (int64_t i = 0; i < g; ++i) {
+          memcpy(idpack + (size_t)(td + i) * row_bytes,
+                 (const char*)m2tab + (size_t)ipr[b * (k2 + 1) + i] * row_bytes, row_bytes);
+          otok[td + i] = itok[b * k2 + i]; /* packed draft tokens (scratch use) */
+        }
+        tt += g + 1;
+        td += g;
+      }
+      oracle_verify(B, V, k2, dtype, tt, td, itpack, idpack, otok, igam, temperature, seed, rbase,
+                    lenience_kind, eps, NULL, NULL, n_out, next_out, NULL, vnear, NULL, NULL,
+                    nthreads);
+      for (int64_t b = 0; b < B; ++b) {
+        if (igam[b] == 0) continue; /* draft already complete: result unused */
+        if (n_out[b] < 0) {
+          failed[b] = 1;
+          /* nothing more to draft: pad with token 0 so that every row the
+           * target review addresses exists; the result is not used */
+          for (int64_t d = dlen[b]; d < k1; ++d) {
+            dtok[b * dcap + d] = 0;
+            dprev[b * dcap + d] = 0;
+            dbonus[b * dcap + d] = 0;
+          }
+          dlen[b] = k1;
+          continue;
+        }
+        if (vnear[b]) near[b] = 1;
+        const int32_t n = n_out[b];
+        for (int32_t i = 0; i <= n; ++i) {
+          const int64_t d = dlen[b] + i;
+          dtok[b * dcap + d] = i < n ? itok[b * k2 + i] : next_out[b];
+          dprev[b * dcap + d] = ipr[b * (k2 + 1) + i];
+          dbonus[b * dcap + d] = (int8_t)(i == k2);
+        }
+        dlen[b] += n + 1;
+      }
+    }
+    /* the target review of the first k1 draft tokens */
+    const uint64_t obase = row_offset + (uint64_t)(r * (k1 + 1) * B);
+    for (int64_t b = 0; b < B; ++b) {
+      ogam[b] = (int32_t)k1;
+      const double T = (double)temperature[b];
+      const int ok = !(isnan(T) || T < 0.0 || isinf(T));
+      for (int64_t i = 0; i <= k1; ++i) {
+        const int32_t prev = i == 0 ? cur[b] : dtok[b * dcap + i - 1];
+        table_row_f32(ttab, dtype, V, prev, otpack + (size_t)(b * (k1 + 1) + i) * V);
+        if (i == k1) break;
+        otok[b * k1 + i] = dtok[b * dcap + i];
+        float* out = odpack + (size_t)(b * k1 + i) * V;
+        if (!ok || T == 0.0 || failed[b]) {
+          for (int64_t v = 0; v < V; ++v) out[v] = 0.f;
+          continue;
+        }
+        const int32_t pv = dprev[b * dcap + i];
+        load_row(m1tab, dtype, V, pv, z);
+        row_softmax(z, V, T, NULL, NULL, p1);
+        if (dbonus[b * dcap + i] || mutant_q_is_p1) {
+          for (int64_t v = 0; v < V; ++v) out[v] = p1[v] > 0.0 ? (float)(T * log(p1[v])) : -INFINITY;
+          continue;
+        }
+        load_row(m2tab, dtype, V, pv, z);
+        row_softmax(z, V, T, NULL, NULL, q2);
+        double beta = 0.0, rmass = 0.0;
+        for (int64_t v = 0; v < V; ++v) {
+          const double f = lenience(p1[v], lenience_kind, (double)eps);
+          beta += q2[v] < f ? q2[v] : f;
+          const double d = p1[v] - q2[v];
+          rmass += d > 0.0 ? d : 0.0;
+        }
+        for (int64_t v = 0; v < V; ++v) {
+          const double f = lenience(p1[v], lenience_kind, (double)eps);
+          double Q = q2[v] < f ? q2[v] : f;
+          const double d = p1[v] - q2[v];
+          if (rmass > 0.0 && d > 0.0) Q += (1.0 - beta) * d / rmass;
+          out[v] = Q > 0.0 ? (float)(T * log(Q)) : -INFINITY;
+        }
+      }
+    }
+    oracle_verify(B, V, k1, ORACLE_F32, B * (k1 + 1), B * k1, otpack, odpack, otok, ogam,
+                  temperature, seed, obase, ORACLE_LENIENCE_NONE, 1.0f, NULL, NULL, n_out,
+                  next_out, NULL, vnear, NULL, NULL, nthreads);
+    for (int64_t b = 0; b < B; ++b) {
+      if (!failed[b] && n_out[b] < 0) failed[b] = 1;
+      if (failed[b]) {
+        out_accepted[b * rounds + r] = -1;
+        continue;
+      }
+      const int32_t n = n_out[b];
+      for (int32_t i = 0; i < n; ++i) out_tokens[b * cap + len[b] + i] = dtok[b * dcap + i];
+      out_tokens[b * cap + len[b] + n] = next_out[b];
+      len[b] += n + 1;
+      cur[b] = next_out[b];
+      out_accepted[b * rounds + r] = n;
+      if ((near[b] || vnear[b]) && out_first_near[b] == rounds) out_first_near[b] = (int32_t)r;
+    }
+  }
+  for (int64_t b = 0; b < B; ++b) out_length[b] = failed[b] ? -1 : len[b];
+  free(itpack); free(idpack); free(itok); free(igam); free(otpack); free(odpack); free(otok);
+  free(ogam); free(dtok); free(dprev); free(dbonus); free(dlen); free(cur); free(len);
+  free(failed); free(near); free(vnear); free(n_out); free(next_out); free(ipr); free(z);
+  free(p1); free(q2);
+  return 0;
+}
