@@ -234,6 +234,48 @@ specv_status_t specv_decode_bigram(const specv_decode_shape_t* shape, const void
                                    size_t workspace_bytes, hipStream_t stream,
                                    hipEvent_t* events);
 
+/* CS Drafting's vertical cascade ("Cascade Speculative Drafting for Even
+ * Faster LLM Inference", sections 3.1 and 3.4) with three bigram tables
+ * [V, V] of one dtype: target, intermediate drafter (mid) and smallest
+ * drafter (small). Outer round r of sequence b: inner rounds j = 0, 1, ...
+ * let the small table draft k2 tokens (drafting as in specv_decode_bigram)
+ * and the mid table review them with the given lenience (specv_verify_lenient
+ * rule), and the n accepted tokens plus the drawn one join a draft, until it
+ * holds k1 tokens (the excess is dropped). The target table then reviews the
+ * first k1 draft tokens without lenience, against the law each was drawn
+ * from: min(q2, f(p1)) + (1 - beta) norm(max(0, p1 - q2)) with beta =
+ * sum_v min(q2(v), f(p1(v))) for a token from an inner position < k2, p1
+ * for a token from the inner bonus position (p1, q2: the mid and small
+ * softmaxes after the token's predecessor). With that law the output follows
+ * the target's distribution whatever the inner lenience; this is the reading
+ * under which the paper's claim holds exactly. The target review runs in
+ * fp32 (target rows converted exactly, draft rows fl32(T ln law)).
+ * Every inner round drafts and reviews all sequences (at most k1 inner
+ * rounds per outer round); results of a sequence whose draft is complete are
+ * unused. Philox rows: the target review of round r uses row offset
+ * philox_row_offset + r (k1 + 1) batch, inner round j uses philox_row_offset
+ * + (r (k1 + 1) + 1 + j) batch (drafting on counter word 3 = 1). Outputs and
+ * failure rules as specv_decode_bigram, with out_tokens [batch, rounds
+ * (k1 + 1)] and out_accepted the target review's n. Lenience and epsilon as
+ * in specv_verify_lenient. */
+typedef struct {
+  int32_t batch;   /* >= 0                                    */
+  int32_t vocab;   /* V >= 1; the tables are [V, V]           */
+  int32_t k1;      /* draft tokens per target review, 0..63   */
+  int32_t k2;      /* small-table drafts per inner round, 0..63 */
+  int32_t rounds;  /* >= 0                                    */
+  specv_dtype_t dtype;
+} specv_cascade_shape_t;
+
+size_t specv_cascade_workspace_bytes(const specv_cascade_shape_t* shape);
+specv_status_t specv_cascade_bigram(const specv_cascade_shape_t* shape, const void* target_table,
+                                    const void* mid_table, const void* small_table,
+                                    const float* temperature, const int32_t* start_token,
+                                    specv_lenience_t lenience, float epsilon, uint64_t seed,
+                                    uint64_t philox_row_offset, int32_t* out_tokens,
+                                    int32_t* out_length, int32_t* out_accepted, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream);
+
 /* Stages of one call, in launch order (one kernel each). */
 #define SPECV_STAGE_PLAN 0        /* offsets of the packed rows, per-row T scale */
 #define SPECV_STAGE_ROWSTATS 1    /* pass 1: max, sum of exp (argmax) per row    */

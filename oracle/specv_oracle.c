@@ -746,17 +746,18 @@ int oracle_decode_bigram(int64_t batch, int64_t vocab, int64_t gamma, int64_t ro
  *   q2)), beta = sum_v min(q2(v), f(p1(v))) -- the law of that step's output;
  *   a token from the bonus position k2 (all k2 drafts accepted): Q = p1.
  * With that Q the target review keeps the target's output law whatever the
- * inner lenience (the reading of "withholding lenience at the target review
- * preserves the output distribution"). The outer review runs in fp32 on
+ * inner lenience: the reading under which the paper's claim, that a target
+ * review without lenience leaves the output law unchanged, holds exactly.
+ * The outer review runs in fp32 on
  * target rows converted exactly from the table and draft rows
  * fl32(T * ln Q) (-inf where Q = 0), so that softmax(row / T) = Q.
  * Greedy sequences (T = 0) use exact-match reviews throughout.
  * Philox rows: outer round r uses the block row_offset + r * (k1 + 1) *
  * batch (+ b), inner round j the block row_offset + (r * (k1 + 1) + 1 + j)
  * * batch; drafting draws word 0 of counter (row, i, 1), reviews use the
- * verify step's counters. Every inner round runs over the whole batch;
- * sequences whose draft is already complete take gamma = 0 and their result
- * is not used.
+ * verify step's counters.
+ * Every inner round drafts and reviews k2 tokens for every sequence; the
+ * result of a sequence whose draft is already complete is not used.
  * Outputs as oracle_decode_bigram, with out_tokens [batch, rounds * (k1 + 1)],
  * out_accepted the target review's n per round, and out_first_near the first
  * round with a near-tie anywhere in it. mutant_q_is_p1 = 1 makes the target
@@ -805,6 +806,7 @@ int oracle_cascade_bigram(int64_t batch, int64_t vocab, int64_t k1, int64_t k2, 
   uint8_t* failed = (uint8_t*)malloc((size_t)B + 1);
   uint8_t* near = (uint8_t*)malloc((size_t)B + 1);
   uint8_t* vnear = (uint8_t*)malloc((size_t)B + 1);
+  uint8_t* dnear = (uint8_t*)malloc((size_t)B + 1);
   int32_t* n_out = (int32_t*)malloc((size_t)(B + 1) * 4);
   int32_t* next_out = (int32_t*)malloc((size_t)(B + 1) * 4);
   int32_t* ipr = (int32_t*)malloc((size_t)(B * (k2 + 1) + 1) * 4); /* inner prev per slot */
@@ -826,11 +828,11 @@ int oracle_cascade_bigram(int64_t batch, int64_t vocab, int64_t k1, int64_t k2, 
     for (int64_t j = 0; j < k1; ++j) {
       const uint64_t rbase = row_offset + (uint64_t)((r * (k1 + 1) + 1 + j) * B);
       for (int64_t b = 0; b < B; ++b) {
-        const int active = dlen[b] < k1;
-        igam[b] = active ? (int32_t)k2 : 0;
+        igam[b] = (int32_t)k2;
         const double T = (double)temperature[b];
         int32_t prev = dlen[b] > 0 ? dtok[b * dcap + dlen[b] - 1] : cur[b];
         const int64_t g = igam[b];
+        dnear[b] = 0;
         /* packed offsets of this inner batch: sequence b's rows start at
          * sum_{b' < b} (g_b' + 1) and sum g_b' (computed below) */
         for (int64_t i = 0; i <= g; ++i) {
@@ -851,7 +853,7 @@ int oracle_cascade_bigram(int64_t batch, int64_t vocab, int64_t k1, int64_t k2, 
             double margin = INFINITY;
             x = inverse_cdf(q2, V, oracle_uniform24(w[0]), &margin, NULL);
             if (x < 0) x = 0;
-            if (margin < ORACLE_NEAR_TIE) near[b] = 1;
+            if (margin < ORACLE_NEAR_TIE) dnear[b] = 1;
           }
           itok[b * k2 + i] = (int32_t)x;
           prev = (int32_t)x;
@@ -876,7 +878,7 @@ int oracle_cascade_bigram(int64_t batch, int64_t vocab, int64_t k1, int64_t k2, 
                     lenience_kind, eps, NULL, NULL, n_out, next_out, NULL, vnear, NULL, NULL,
                     nthreads);
       for (int64_t b = 0; b < B; ++b) {
-        if (igam[b] == 0) continue; /* draft already complete: result unused */
+        if (dlen[b] >= k1) continue; /* draft already complete: result unused */
         if (n_out[b] < 0) {
           failed[b] = 1;
           /* nothing more to draft: pad with token 0 so that every row the
@@ -889,7 +891,7 @@ int oracle_cascade_bigram(int64_t batch, int64_t vocab, int64_t k1, int64_t k2, 
           dlen[b] = k1;
           continue;
         }
-        if (vnear[b]) near[b] = 1;
+        if (vnear[b] || dnear[b]) near[b] = 1;
         const int32_t n = n_out[b];
         for (int32_t i = 0; i <= n; ++i) {
           const int64_t d = dlen[b] + i;
@@ -962,7 +964,7 @@ int oracle_cascade_bigram(int64_t batch, int64_t vocab, int64_t k1, int64_t k2, 
   for (int64_t b = 0; b < B; ++b) out_length[b] = failed[b] ? -1 : len[b];
   free(itpack); free(idpack); free(itok); free(igam); free(otpack); free(odpack); free(otok);
   free(ogam); free(dtok); free(dprev); free(dbonus); free(dlen); free(cur); free(len);
-  free(failed); free(near); free(vnear); free(n_out); free(next_out); free(ipr); free(z);
+  free(failed); free(near); free(vnear); free(dnear); free(n_out); free(next_out); free(ipr); free(z);
   free(p1); free(q2);
   return 0;
 }

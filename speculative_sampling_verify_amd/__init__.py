@@ -40,6 +40,11 @@ class SpecvDecodeShape(ctypes.Structure):
                 ("rounds", ctypes.c_int32), ("dtype", ctypes.c_int)]
 
 
+class SpecvCascadeShape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("vocab", ctypes.c_int32), ("k1", ctypes.c_int32),
+                ("k2", ctypes.c_int32), ("rounds", ctypes.c_int32), ("dtype", ctypes.c_int)]
+
+
 _P = ctypes.c_void_p
 _SHP = ctypes.POINTER(SpecvShape)
 _DSHP = ctypes.POINTER(SpecvDecodeShape)
@@ -64,6 +69,12 @@ _lib.specv_decode_workspace_bytes.restype = _sz
 _lib.specv_decode_workspace_bytes.argtypes = [_DSHP]
 _lib.specv_decode_bigram.restype = ctypes.c_int
 _lib.specv_decode_bigram.argtypes = [_DSHP, _P, _P, _P, _P, _u64, _u64, _P, _P, _P, _P, _sz, _P, _P]
+_CSHP = ctypes.POINTER(SpecvCascadeShape)
+_lib.specv_cascade_workspace_bytes.restype = _sz
+_lib.specv_cascade_workspace_bytes.argtypes = [_CSHP]
+_lib.specv_cascade_bigram.restype = ctypes.c_int
+_lib.specv_cascade_bigram.argtypes = [_CSHP, _P, _P, _P, _P, _P, ctypes.c_int, ctypes.c_float, _u64,
+                                      _u64, _P, _P, _P, _P, _sz, _P]
 _lib.specv_row_stats.restype = ctypes.c_int
 _lib.specv_row_stats.argtypes = [_SHP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _sz, _P]
 _lib.specv_softmax_rows.restype = ctypes.c_int
@@ -78,7 +89,8 @@ _lib.specv_status_string.argtypes = [ctypes.c_int]
 EXPORTED = ("specv_workspace_bytes", "specv_verify", "specv_verify_profiled",
             "specv_verify_with_uniforms", "specv_verify_lenient",
             "specv_diagnostics_workspace_bytes", "specv_position_diagnostics",
-            "specv_decode_workspace_bytes", "specv_decode_bigram", "specv_row_stats", "specv_softmax_rows",
+            "specv_decode_workspace_bytes", "specv_decode_bigram",
+            "specv_cascade_workspace_bytes", "specv_cascade_bigram", "specv_row_stats", "specv_softmax_rows",
             "specv_philox4x32_10", "specv_copy_bytes", "specv_status_string")
 
 
@@ -314,6 +326,49 @@ def specv_decode_bigram(target_table, draft_table, temperature, start_token, *, 
                                   None if events is None else
                                   ctypes.cast(events.array, ctypes.c_void_p))
     _check(st, "specv_decode_bigram")
+    return out
+
+
+def specv_cascade_workspace_bytes(shape: SpecvCascadeShape) -> int:
+    return int(_lib.specv_cascade_workspace_bytes(ctypes.byref(shape)))
+
+
+def specv_cascade_bigram(target_table, mid_table, small_table, temperature, start_token, *, k1,
+                         k2, rounds, lenience="none", epsilon=1.0, seed=0, philox_row_offset=0,
+                         out=None, workspace=None, stream=None):
+    """CS Drafting's vertical cascade over bigram tables [V, V]; returns a
+    dict of device tensors: tokens [B, rounds * (k1 + 1)], length [B],
+    accepted [B, rounds] (the target review's n)."""
+    tabs = (target_table, mid_table, small_table)
+    if any(t.dim() != 2 or t.shape != target_table.shape for t in tabs) or \
+            target_table.shape[0] != target_table.shape[1]:
+        raise ValueError("tables must be [V, V] and alike")
+    dt = _dtype_code(target_table)
+    if any(_dtype_code(t) != dt for t in tabs):
+        raise TypeError("tables must share a dtype")
+    dev = target_table.device
+    start_token = start_token if start_token.dtype == torch.int32 else start_token.to(torch.int32)
+    B = start_token.shape[0]
+    shape = SpecvCascadeShape(int(B), int(target_table.shape[0]), int(k1), int(k2), int(rounds),
+                              dt)
+    if workspace is None:
+        n = specv_cascade_workspace_bytes(shape)
+        if n == 0:
+            raise SpecvError("invalid cascade shape")
+        workspace = torch.empty(n, dtype=torch.uint8, device=dev)
+    if out is None:
+        out = {"tokens": torch.empty((B, rounds * (k1 + 1)), dtype=torch.int32, device=dev),
+               "length": torch.empty(B, dtype=torch.int32, device=dev),
+               "accepted": torch.empty((B, rounds), dtype=torch.int32, device=dev)}
+    _check_tensors(dev, target_table=target_table, mid_table=mid_table, small_table=small_table,
+                   temperature=temperature, start_token=start_token, workspace=workspace, **out)
+    kind = LENIENCE[lenience] if isinstance(lenience, str) else int(lenience)
+    st = _lib.specv_cascade_bigram(ctypes.byref(shape), _ptr(target_table), _ptr(mid_table),
+                                   _ptr(small_table), _ptr(temperature), _ptr(start_token), kind,
+                                   float(epsilon), int(seed), int(philox_row_offset),
+                                   _ptr(out["tokens"]), _ptr(out["length"]), _ptr(out["accepted"]),
+                                   _ptr(workspace), workspace.numel(), _stream(stream, dev))
+    _check(st, "specv_cascade_bigram")
     return out
 
 

@@ -5,6 +5,7 @@
 
 #include <stdint.h>
 
+#include "cascade.hpp"
 #include "decode.hpp"
 #include "diagnostics.hpp"
 #include "kernels.hpp"
@@ -366,6 +367,70 @@ bool make_decode_plan(const specv_decode_shape_t* s, DecodePlan* d) {
   return true;
 }
 
+__global__ __launch_bounds__(kBlock) void k_fill_i32(int32_t* p, int64_t n, int32_t value) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t < n) p[t] = value;
+}
+
+struct CascadePlan {
+  specv_shape_t vin, vout;  // inner (m1 vs m2) and target review shapes
+  Plan pin, pout;
+  int64_t esz, row_bytes, cap, dcap;
+  size_t vbytes;  // verify workspace shared by both reviews (stream-ordered)
+  size_t off_itp, off_idp, off_otp, off_odp, off_itok, off_ipr, off_iprd, off_igam, off_ogam,
+      off_otok, off_cur, off_icur, off_fail, off_len, off_dlen, off_dtok, off_dprev, off_dbonus,
+      off_vn, off_vnext;
+  size_t bytes;
+};
+
+bool cascade_shape_ok(const specv_cascade_shape_t* s) {
+  if (!s) return false;
+  if (s->batch < 0 || s->vocab < 1 || s->rounds < 0) return false;
+  if (s->k1 < 0 || s->k1 > SPECV_MAX_GAMMA || s->k2 < 0 || s->k2 > SPECV_MAX_GAMMA) return false;
+  if (s->dtype != SPECV_F32 && s->dtype != SPECV_BF16) return false;
+  if ((int64_t)s->vocab * s->vocab > ((int64_t)1 << 40)) return false;
+  if ((int64_t)s->batch * s->rounds * (s->k1 + 1) > ((int64_t)1 << 40)) return false;
+  return true;
+}
+
+bool make_cascade_plan(const specv_cascade_shape_t* s, CascadePlan* c) {
+  const int64_t B = s->batch, k1 = s->k1, k2 = s->k2;
+  c->vin = specv_shape_t{s->batch, s->vocab, s->k2, s->dtype, B * (k2 + 1), B * k2};
+  c->vout = specv_shape_t{s->batch, s->vocab, s->k1, SPECV_F32, B * (k1 + 1), B * k1};
+  if (!shape_ok(&c->vin) || !shape_ok(&c->vout)) return false;
+  make_plan(&c->vin, &c->pin);
+  make_plan(&c->vout, &c->pout);
+  c->esz = (s->dtype == SPECV_BF16) ? 2 : 4;
+  c->row_bytes = (int64_t)s->vocab * c->esz;
+  c->cap = (int64_t)s->rounds * (k1 + 1);
+  c->dcap = k1 + k2 + 1;
+  const int64_t V = s->vocab;
+  size_t off = align_up(c->pin.bytes > c->pout.bytes ? c->pin.bytes : c->pout.bytes);
+  c->vbytes = off;
+  c->off_itp = off; off = align_up(off + (size_t)(B * (k2 + 1)) * c->row_bytes);
+  c->off_idp = off; off = align_up(off + (size_t)(B * k2) * c->row_bytes);
+  c->off_otp = off; off = align_up(off + (size_t)(B * (k1 + 1) * V) * 4);
+  c->off_odp = off; off = align_up(off + (size_t)(B * k1 * V) * 4);
+  c->off_itok = off; off = align_up(off + (size_t)(B * k2) * 4);
+  c->off_ipr = off; off = align_up(off + (size_t)(B * (k2 + 1)) * 4);
+  c->off_iprd = off; off = align_up(off + (size_t)(B * k2) * 4);
+  c->off_igam = off; off = align_up(off + (size_t)B * 4);
+  c->off_ogam = off; off = align_up(off + (size_t)B * 4);
+  c->off_otok = off; off = align_up(off + (size_t)(B * k1) * 4);
+  c->off_cur = off; off = align_up(off + (size_t)B * 4);
+  c->off_icur = off; off = align_up(off + (size_t)B * 4);
+  c->off_fail = off; off = align_up(off + (size_t)B * 4);
+  c->off_len = off; off = align_up(off + (size_t)B * 4);
+  c->off_dlen = off; off = align_up(off + (size_t)B * 4);
+  c->off_dtok = off; off = align_up(off + (size_t)(B * c->dcap) * 4);
+  c->off_dprev = off; off = align_up(off + (size_t)(B * c->dcap) * 4);
+  c->off_dbonus = off; off = align_up(off + (size_t)(B * c->dcap) * 4);
+  c->off_vn = off; off = align_up(off + (size_t)B * 4);
+  c->off_vnext = off; off = align_up(off + (size_t)B * 4);
+  c->bytes = off;
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -620,6 +685,157 @@ specv_status_t specv_decode_bigram(const specv_decode_shape_t* shape, const void
     mark(ev, 2 * SPECV_STAGE_DRAW + 1, stream);
   }
   hipLaunchKernelGGL(k_dec_finish, dim3(seq_blocks), block, 0, stream, a);
+  return launched();
+}
+
+size_t specv_cascade_workspace_bytes(const specv_cascade_shape_t* shape) {
+  if (!cascade_shape_ok(shape)) return 0;
+  CascadePlan c;
+  if (!make_cascade_plan(shape, &c)) return 0;
+  return c.bytes;
+}
+
+specv_status_t specv_cascade_bigram(const specv_cascade_shape_t* shape, const void* target_table,
+                                    const void* mid_table, const void* small_table,
+                                    const float* temperature, const int32_t* start_token,
+                                    specv_lenience_t lenience, float epsilon, uint64_t seed,
+                                    uint64_t philox_row_offset, int32_t* out_tokens,
+                                    int32_t* out_length, int32_t* out_accepted, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
+  if (!cascade_shape_ok(shape)) return SPECV_ERR_INVALID_ARGUMENT;
+  if ((int)lenience < SPECV_LENIENCE_NONE || (int)lenience > SPECV_LENIENCE_EXP)
+    return SPECV_ERR_INVALID_ARGUMENT;
+  if (lenience != SPECV_LENIENCE_NONE && !(epsilon > 0.f && epsilon <= 1.f))
+    return SPECV_ERR_INVALID_ARGUMENT;
+  CascadePlan c;
+  if (!make_cascade_plan(shape, &c)) return SPECV_ERR_INVALID_ARGUMENT;
+  const int64_t B = shape->batch, k1 = shape->k1, k2 = shape->k2, R = shape->rounds;
+  if (B == 0) return SPECV_OK;
+  if (!target_table || !mid_table || !small_table || !temperature || !start_token || !out_length)
+    return SPECV_ERR_INVALID_ARGUMENT;
+  if (R > 0 && (!out_tokens || !out_accepted)) return SPECV_ERR_INVALID_ARGUMENT;
+  if (!aligned(target_table, (size_t)c.esz) || !aligned(mid_table, (size_t)c.esz) ||
+      !aligned(small_table, (size_t)c.esz))
+    return SPECV_ERR_INVALID_ARGUMENT;
+  if (!workspace || workspace_bytes < c.bytes || !aligned(workspace, kAlign))
+    return SPECV_ERR_WORKSPACE;
+  const bool bf16 = shape->dtype == SPECV_BF16;
+  const int32_t len_kind = (lenience == SPECV_LENIENCE_NONE || epsilon == 1.f) ? kLenNone
+                                                                                : (int32_t)lenience;
+  // target-review side: the decode loop's state and append
+  DecodeArgs dd{};
+  dd.temperature = temperature;
+  dd.start = start_token;
+  dd.cur = at<int32_t>(workspace, c.off_cur);
+  dd.drafts = at<int32_t>(workspace, c.off_otok);
+  dd.gam = at<int32_t>(workspace, c.off_ogam);
+  dd.len = at<int32_t>(workspace, c.off_len);
+  dd.fail = at<int32_t>(workspace, c.off_fail);
+  dd.vn = at<int32_t>(workspace, c.off_vn);
+  dd.vnext = at<int32_t>(workspace, c.off_vnext);
+  dd.out_tokens = out_tokens;
+  dd.out_length = out_length;
+  dd.out_accepted = out_accepted;
+  dd.seed = seed;
+  dd.V = shape->vocab;
+  dd.cap = c.cap;
+  dd.B = (int32_t)B;
+  dd.gamma = (int32_t)k1;
+  dd.rounds = (int32_t)R;
+  // inner drafting: the decode loop's drafting kernel on the smallest table
+  DecodeArgs di = dd;
+  di.dtab = small_table;
+  di.cur = at<int32_t>(workspace, c.off_icur);
+  di.drafts = at<int32_t>(workspace, c.off_itok);
+  di.trow_src = at<int32_t>(workspace, c.off_ipr);
+  di.drow_src = at<int32_t>(workspace, c.off_iprd);
+  di.gamma = (int32_t)k2;
+  CascadeArgs ca{};
+  ca.ttab = target_table;
+  ca.m1tab = mid_table;
+  ca.m2tab = small_table;
+  ca.temperature = temperature;
+  ca.cur = dd.cur;
+  ca.icur = di.cur;
+  ca.fail = dd.fail;
+  ca.dlen = at<int32_t>(workspace, c.off_dlen);
+  ca.dtok = at<int32_t>(workspace, c.off_dtok);
+  ca.dprev = at<int32_t>(workspace, c.off_dprev);
+  ca.dbonus = at<int32_t>(workspace, c.off_dbonus);
+  ca.itok = di.drafts;
+  ca.ipr = di.trow_src;
+  ca.vn = dd.vn;
+  ca.vnext = dd.vnext;
+  ca.otpack = at<float>(workspace, c.off_otp);
+  ca.odpack = at<float>(workspace, c.off_odp);
+  ca.otok = dd.drafts;
+  ca.lenience = len_kind;
+  ca.eps = epsilon;
+  ca.V = shape->vocab;
+  ca.dcap = c.dcap;
+  ca.B = (int32_t)B;
+  ca.k1 = (int32_t)k1;
+  ca.k2 = (int32_t)k2;
+  GatherArgs ga;
+  ga.ttab = mid_table;
+  ga.dtab = small_table;
+  ga.trow_src = di.trow_src;
+  ga.drow_src = di.drow_src;
+  ga.tdst = at<char>(workspace, c.off_itp);
+  ga.ddst = at<char>(workspace, c.off_idp);
+  ga.row_bytes = c.row_bytes;
+  ga.n_t = B * (k2 + 1);
+  ga.n_d = B * k2;
+  ga.pieces = (int32_t)((c.row_bytes + kGatherPiece - 1) / kGatherPiece);
+  const bool vec = c.row_bytes % 16 == 0 && aligned(mid_table, 16) && aligned(small_table, 16);
+  const dim3 block(kBlock);
+  const unsigned seq_blocks = (unsigned)((B + kBlock - 1) / kBlock);
+  specv_status_t st;
+  hipLaunchKernelGGL(k_dec_init, dim3(seq_blocks < 1024 ? seq_blocks : 1024), block, 0, stream, dd);
+  if ((st = launched()) != SPECV_OK) return st;
+  hipLaunchKernelGGL(k_fill_i32, dim3(seq_blocks), block, 0, stream,
+                     at<int32_t>(workspace, c.off_igam), B, (int32_t)k2);
+  if ((st = launched()) != SPECV_OK) return st;
+  for (int64_t r = 0; r < R; ++r) {
+    hipLaunchKernelGGL(k_cas_round_init, dim3(seq_blocks), block, 0, stream, ca);
+    if ((st = launched()) != SPECV_OK) return st;
+    for (int64_t j = 0; j < k1; ++j) {
+      di.row_base = philox_row_offset + (uint64_t)((r * (k1 + 1) + 1 + j) * B);
+      if (bf16) {
+        if (vec) hipLaunchKernelGGL((k_dec_draft<kBF16, true>), dim3(blocks_for(B)), block, 0, stream, di);
+        else hipLaunchKernelGGL((k_dec_draft<kBF16, false>), dim3(blocks_for(B)), block, 0, stream, di);
+      } else {
+        if (vec) hipLaunchKernelGGL((k_dec_draft<kF32, true>), dim3(blocks_for(B)), block, 0, stream, di);
+        else hipLaunchKernelGGL((k_dec_draft<kF32, false>), dim3(blocks_for(B)), block, 0, stream, di);
+      }
+      if ((st = launched()) != SPECV_OK) return st;
+      const int64_t gw = (ga.n_t + ga.n_d) * ga.pieces;
+      if (vec) hipLaunchKernelGGL((k_dec_gather<true>), dim3(blocks_for(gw)), block, 0, stream, ga);
+      else hipLaunchKernelGGL((k_dec_gather<false>), dim3(blocks_for(gw)), block, 0, stream, ga);
+      if ((st = launched()) != SPECV_OK) return st;
+      Call ci{&c.vin, ga.tdst, ga.ddst, di.drafts, at<int32_t>(workspace, c.off_igam), temperature,
+              seed, di.row_base, nullptr, nullptr, at<int32_t>(workspace, c.off_vn),
+              at<int32_t>(workspace, c.off_vnext), workspace, c.vbytes, stream, nullptr};
+      ci.lenience = len_kind;
+      ci.eps = epsilon;
+      if ((st = run(ci)) != SPECV_OK) return st;
+      hipLaunchKernelGGL(k_cas_inner_append, dim3(seq_blocks), block, 0, stream, ca);
+      if ((st = launched()) != SPECV_OK) return st;
+    }
+    const int64_t ow = B * (k1 + 1);
+    if (bf16) hipLaunchKernelGGL((k_cas_outer_rows<kBF16>), dim3(blocks_for(ow)), block, 0, stream, ca);
+    else hipLaunchKernelGGL((k_cas_outer_rows<kF32>), dim3(blocks_for(ow)), block, 0, stream, ca);
+    if ((st = launched()) != SPECV_OK) return st;
+    Call co{&c.vout, ca.otpack, ca.odpack, ca.otok, dd.gam, temperature, seed,
+            philox_row_offset + (uint64_t)(r * (k1 + 1) * B), nullptr, nullptr,
+            at<int32_t>(workspace, c.off_vn), at<int32_t>(workspace, c.off_vnext), workspace,
+            c.vbytes, stream, nullptr};
+    if ((st = run(co)) != SPECV_OK) return st;
+    dd.round = (int32_t)r;
+    hipLaunchKernelGGL(k_dec_append, dim3(seq_blocks), block, 0, stream, dd);
+    if ((st = launched()) != SPECV_OK) return st;
+  }
+  hipLaunchKernelGGL(k_dec_finish, dim3(seq_blocks), block, 0, stream, dd);
   return launched();
 }
 

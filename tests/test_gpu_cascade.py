@@ -1,0 +1,126 @@
+"""GPU parity of CS Drafting's vertical cascade over bigram tables
+(specv_cascade_bigram, through the C ABI) against the oracle's cascade on
+the same tables, start tokens, temperatures, lenience and Philox stream.
+
+Bar: generated tokens and the target review's accepted counts are identical
+up to the first round in which the oracle saw a near-tie (drafting, the
+intermediate review or the target review); the GPU cascade's own output law
+is tested against the target Markov chain with a lenient intermediate
+review.
+"""
+import numpy as np
+import pytest
+import torch
+from scipy import stats
+
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def svx():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import speculative_sampling_verify_amd as m
+    return m
+
+
+def log(*a):
+    print(*a, flush=True)
+
+
+def bf16(a):
+    import synth
+    return synth.to_bf16_bits(np.asarray(a, np.float32))
+
+
+def tables(V, seed, s_mid=0.6, s_small=1.4, scale=1.5):
+    rng = np.random.default_rng(seed)
+    t = (rng.standard_normal((V, V)) * scale).astype(np.float32)
+    m = (t + rng.standard_normal((V, V)) * s_mid).astype(np.float32)
+    s = (t + rng.standard_normal((V, V)) * s_small).astype(np.float32)
+    return t, m, s
+
+
+def run_gpu(svx, tabs, T, start, **kw):
+    def tens(a):
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).cuda()
+    out = svx.specv_cascade_bigram(*[tens(t) for t in tabs], tens(np.asarray(T, np.float32)),
+                                   tens(np.asarray(start, np.int32)), **kw)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in out.items()}
+
+
+def assert_cascade_parity(name, svx, tabs, T, start, **kw):
+    V = tabs[0].shape[0]
+    log("[case] cascade %s B=%d V=%d %s" % (name, len(start), V, kw))
+    gkw = dict(kw)
+    gkw["philox_row_offset"] = gkw.pop("row_offset", 0)
+    got = run_gpu(svx, tabs, T, start, **gkw)
+    want = oracle.cascade_bigram(*tabs, T, start, **kw)
+    rounds, k1, k2 = kw["rounds"], kw["k1"], kw["k2"]
+    diverged = 0
+    for b in range(len(start)):
+        f = int(want.first_near[b])
+        np.testing.assert_array_equal(got["accepted"][b, :f], want.accepted[b, :f], err_msg=str(b))
+        if want.length[b] < 0:
+            assert got["length"][b] == -1
+            continue
+        upto = int((want.accepted[b, :f] + 1).sum())
+        np.testing.assert_array_equal(got["tokens"][b, :upto], want.tokens[b, :upto], err_msg=str(b))
+        if f == rounds:
+            assert got["length"][b] == want.length[b]
+        else:
+            diverged += 1
+    # draws per sequence and round: k1 inner rounds of k2 drafts and one
+    # inner draw, and the target review's draw; each lands within 1e-6 of
+    # one of V boundaries with probability about 2e-6 V
+    expect = min(1.0, 2e-6 * V * rounds * (k1 * (k2 + 1) + 1))
+    log("[parity] cascade %s: sequences=%d with a near-tie=%d (expected share %.3f)"
+        % (name, len(start), diverged, expect))
+    assert diverged <= 2 * expect * len(start) + 4
+    return got, want
+
+
+def test_cascade_parity_fp32_lenient(svx):
+    tabs = tables(1000, 1)
+    B = 128
+    start = np.random.default_rng(2).integers(0, 1000, B)
+    assert_cascade_parity("fp32 sq 0.5", svx, tabs, np.ones(B, np.float32), start, k1=4, k2=2,
+                          rounds=4, lenience="sq", epsilon=0.5, seed=5)
+
+
+def test_cascade_parity_bf16_mixed_greedy(svx):
+    tabs = [bf16(t) for t in tables(2048, 3, scale=2.0)]
+    B = 96
+    T = np.where(np.arange(B) % 3 == 0, 0.0, 0.8).astype(np.float32)
+    start = np.random.default_rng(4).integers(0, 2048, B)
+    assert_cascade_parity("bf16 exp 0.3", svx, tabs, T, start, k1=3, k2=3, rounds=3,
+                          lenience="exp", epsilon=0.3, seed=7, row_offset=100)
+
+
+def test_cascade_parity_lossless_no_inner_drafts_and_bad_starts(svx):
+    # k2 = 0: every inner round is one draw from the intermediate model
+    tabs = tables(300, 5)
+    B = 64
+    start = np.random.default_rng(6).integers(0, 300, B).astype(np.int32)
+    start[7] = 300
+    got, _ = assert_cascade_parity("fp32 k2=0", svx, tabs, np.full(B, 1.2, np.float32), start,
+                                   k1=3, k2=0, rounds=3)
+    assert got["length"][7] == -1
+
+
+def test_cascade_gpu_target_law(svx):
+    tabs = tables(5, 0)
+    B, c = 400_000, 2
+    got = run_gpu(svx, tabs, np.ones(B, np.float32), np.full(B, c, np.int32), k1=3, k2=2,
+                  rounds=3, lenience="sq", epsilon=0.5, seed=9)
+    assert (got["length"] >= 3).all()
+    P = torch.softmax(torch.from_numpy(tabs[0].astype(np.float64)), dim=-1).numpy()
+    y = got["tokens"][:, :3].astype(np.int64)
+    obs = np.bincount((y[:, 0] * 5 + y[:, 1]) * 5 + y[:, 2], minlength=125)
+    exp = np.einsum("a,ab,bc->abc", P[c], P, P).reshape(-1) * B
+    pv = stats.chisquare(obs, exp).pvalue
+    log("[law] cascade GPU joint of 3 tokens (sq 0.5 inner): p = %.4g" % pv)
+    assert pv > 1e-4
