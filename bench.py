@@ -15,7 +15,10 @@ With --lenience other than none, a step is one specv_verify_lenient call
 --diagnostics K, a step is one specv_position_diagnostics call (alpha,
 draft entropy and top-K per draft position) on the same workload. With
 --decode, a step is one specv_decode_bigram call: ROUNDS rounds of drafting
-and verification for a batch of sequences over bigram tables.
+and verification for a batch of sequences over bigram tables. With
+--cascade, a step is one specv_cascade_bigram call (CS Drafting's vertical
+cascade over three bigram tables, f_sq lenience 0.5 at the intermediate
+review).
 """
 import argparse
 import hashlib
@@ -45,6 +48,7 @@ WORKLOADS = {
 KERNEL_SOURCES = ["speculative_sampling_verify_amd/csrc/kernels.hpp",
                   "speculative_sampling_verify_amd/csrc/diagnostics.hpp",
                   "speculative_sampling_verify_amd/csrc/decode.hpp",
+                  "speculative_sampling_verify_amd/csrc/cascade.hpp",
                   "speculative_sampling_verify_amd/csrc/device.hpp",
                   "speculative_sampling_verify_amd/csrc/specverify.hip"]
 
@@ -283,6 +287,88 @@ def bench_decode(args, torch, svx, dev):
     print(json.dumps(result), flush=True)
 
 
+def bench_cascade(args, torch, svx, dev):
+    import synth
+    V, B, R = args.decode_vocab, args.decode_batch, args.decode_rounds
+    k1, k2, kind, eps = 5, 3, "sq", 0.5
+    t_gen = time.perf_counter()
+    tabs = synth.bigram_tables(V, small=True)
+    log("[bench] generated three bigram tables V=%d in %.1f s" % (V, time.perf_counter() - t_gen))
+    tt, mt, st = [torch.from_numpy(a.view(np.int16)).to(dev)
+                  for a in (tabs.target, tabs.draft, tabs.small)]
+    T = torch.ones(B, dtype=torch.float32, device=dev)
+    start = torch.from_numpy(tabs.start(B)).to(dev)
+    shape = svx.SpecvCascadeShape(B, V, k1, k2, R, svx.SPECV_BF16)
+    ws = torch.empty(svx.specv_cascade_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    out = {"tokens": torch.empty((B, R * (k1 + 1)), dtype=torch.int32, device=dev),
+           "length": torch.empty(B, dtype=torch.int32, device=dev),
+           "accepted": torch.empty((B, R), dtype=torch.int32, device=dev)}
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, events=None):
+        svx.specv_cascade_bigram(tt, mt, st, T, start, k1=k1, k2=k2, rounds=R, lenience=kind,
+                                 epsilon=eps, seed=i, out=out, workspace=ws, stream=stream,
+                                 events=events)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    K = args.steps
+    evs = [svx.StageEvents() for _ in range(K)]
+    t_start, t_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for i in range(K):
+        step(i, evs[i])
+    t_stop.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_stop) / K
+    names = ("inner_drafting", "inner_gather", "inner_review", "target_review")
+    stage_ms = {nm: float(np.mean([ev.elapsed_ms(si) for ev in evs])) for si, nm in
+                enumerate(names)}
+    length = out["length"].cpu().numpy()
+    tokens = int(length[length > 0].sum())
+    gather_bytes = 2 * B * (2 * k2 + 1) * V * 2
+    achieved = gather_bytes / (stage_ms["inner_gather"] * 1e-3) / 1e9
+    result = {
+        "metric": "generated tokens/sec of CS Drafting's vertical cascade with bigram tables, "
+                  "1 GPU",
+        "value": tokens / (ms_step * 1e-3),
+        "unit": "generated tokens/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "vertical cascade: B=%d, V=%d bf16 tables, k1=%d, k2=%d, %d rounds, "
+                               "f_sq eps=%g at the intermediate review, T=1" % (B, V, k1, k2, R, eps),
+                   "batch": B, "vocab": V, "k1": k1, "k2": k2, "rounds": R},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None, "kernel": "k_dec_gather",
+                     "algorithmic_bytes_per_launch": gather_bytes,
+                     "avg_launch_ms": stage_ms["inner_gather"]},
+        "stage_ms_last_round": stage_ms,
+        "tokens_per_target_review": tokens / (B * R),
+        "kernel_sha": kernel_sha(),
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        log("[bench] timing the CPU oracle's cascade on the host")
+        nb = 8
+        while True:
+            t0 = time.perf_counter()
+            res = oracle.cascade_bigram(tabs.target, tabs.draft, tabs.small, np.ones(nb, np.float32),
+                                        tabs.start(nb), k1=k1, k2=k2, rounds=R, lenience=kind,
+                                        epsilon=eps)
+            el = time.perf_counter() - t0
+            if el >= 5.0 or nb >= B:
+                break
+            nb = min(B, nb * 2)
+        gen = int(res.length[res.length > 0].sum())
+        result["cpu_baseline"] = {"value": gen / el, "unit": "generated tokens/s",
+                                  "cores": oracle.default_threads(), "kind": "oracle",
+                                  "sample": "%d sequences x %d rounds (%d tokens), %.1f s"
+                                            % (nb, R, gen, el)}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -299,6 +385,8 @@ def main():
     ap.add_argument("--decode-batch", type=int, default=2048)
     ap.add_argument("--decode-gamma", type=int, default=5)
     ap.add_argument("--decode-rounds", type=int, default=8)
+    ap.add_argument("--cascade", action="store_true",
+                    help="time the vertical cascade over three bigram tables instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="run only a plain device copy of this many bytes (counter calibration)")
@@ -335,6 +423,8 @@ def main():
         return bench_diagnostics(args, torch, svx, dev)
     if args.decode:
         return bench_decode(args, torch, svx, dev)
+    if args.cascade:
+        return bench_cascade(args, torch, svx, dev)
 
     t_gen = time.perf_counter()
     x, desc = make_inputs(args.workload)

@@ -257,7 +257,11 @@ specv_status_t specv_decode_bigram(const specv_decode_shape_t* shape, const void
  * + (r (k1 + 1) + 1 + j) batch (drafting on counter word 3 = 1). Outputs and
  * failure rules as specv_decode_bigram, with out_tokens [batch, rounds
  * (k1 + 1)] and out_accepted the target review's n. Lenience and epsilon as
- * in specv_verify_lenient. */
+ * in specv_verify_lenient. `events`: NULL, or 2 * SPECV_NUM_STAGES events
+ * recorded in the last outer round: around the first inner round's drafting
+ * (SPECV_STAGE_PLAN slot), its row gather (ROWSTATS slot) and its review
+ * (ACCEPT_MASS slot), and around the whole target review with its append
+ * (DRAW slot). */
 typedef struct {
   int32_t batch;   /* >= 0                                    */
   int32_t vocab;   /* V >= 1; the tables are [V, V]           */
@@ -274,7 +278,8 @@ specv_status_t specv_cascade_bigram(const specv_cascade_shape_t* shape, const vo
                                     specv_lenience_t lenience, float epsilon, uint64_t seed,
                                     uint64_t philox_row_offset, int32_t* out_tokens,
                                     int32_t* out_length, int32_t* out_accepted, void* workspace,
-                                    size_t workspace_bytes, hipStream_t stream);
+                                    size_t workspace_bytes, hipStream_t stream,
+                                    hipEvent_t* events);
 
 /* Stages of one call, in launch order (one kernel each). */
 #define SPECV_STAGE_PLAN 0        /* offsets of the packed rows, per-row T scale */

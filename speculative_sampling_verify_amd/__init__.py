@@ -74,7 +74,7 @@ _lib.specv_cascade_workspace_bytes.restype = _sz
 _lib.specv_cascade_workspace_bytes.argtypes = [_CSHP]
 _lib.specv_cascade_bigram.restype = ctypes.c_int
 _lib.specv_cascade_bigram.argtypes = [_CSHP, _P, _P, _P, _P, _P, ctypes.c_int, ctypes.c_float, _u64,
-                                      _u64, _P, _P, _P, _P, _sz, _P]
+                                      _u64, _P, _P, _P, _P, _sz, _P, _P]
 _lib.specv_row_stats.restype = ctypes.c_int
 _lib.specv_row_stats.argtypes = [_SHP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _sz, _P]
 _lib.specv_softmax_rows.restype = ctypes.c_int
@@ -335,7 +335,7 @@ def specv_cascade_workspace_bytes(shape: SpecvCascadeShape) -> int:
 
 def specv_cascade_bigram(target_table, mid_table, small_table, temperature, start_token, *, k1,
                          k2, rounds, lenience="none", epsilon=1.0, seed=0, philox_row_offset=0,
-                         out=None, workspace=None, stream=None):
+                         out=None, workspace=None, stream=None, events=None):
     """CS Drafting's vertical cascade over bigram tables [V, V]; returns a
     dict of device tensors: tokens [B, rounds * (k1 + 1)], length [B],
     accepted [B, rounds] (the target review's n)."""
@@ -367,7 +367,9 @@ def specv_cascade_bigram(target_table, mid_table, small_table, temperature, star
                                    _ptr(small_table), _ptr(temperature), _ptr(start_token), kind,
                                    float(epsilon), int(seed), int(philox_row_offset),
                                    _ptr(out["tokens"]), _ptr(out["length"]), _ptr(out["accepted"]),
-                                   _ptr(workspace), workspace.numel(), _stream(stream, dev))
+                                   _ptr(workspace), workspace.numel(), _stream(stream, dev),
+                                   None if events is None else
+                                   ctypes.cast(events.array, ctypes.c_void_p))
     _check(st, "specv_cascade_bigram")
     return out
 

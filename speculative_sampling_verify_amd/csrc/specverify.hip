@@ -701,7 +701,8 @@ specv_status_t specv_cascade_bigram(const specv_cascade_shape_t* shape, const vo
                                     specv_lenience_t lenience, float epsilon, uint64_t seed,
                                     uint64_t philox_row_offset, int32_t* out_tokens,
                                     int32_t* out_length, int32_t* out_accepted, void* workspace,
-                                    size_t workspace_bytes, hipStream_t stream) {
+                                    size_t workspace_bytes, hipStream_t stream,
+                                    hipEvent_t* events) {
   if (!cascade_shape_ok(shape)) return SPECV_ERR_INVALID_ARGUMENT;
   if ((int)lenience < SPECV_LENIENCE_NONE || (int)lenience > SPECV_LENIENCE_EXP)
     return SPECV_ERR_INVALID_ARGUMENT;
@@ -799,8 +800,11 @@ specv_status_t specv_cascade_bigram(const specv_cascade_shape_t* shape, const vo
   for (int64_t r = 0; r < R; ++r) {
     hipLaunchKernelGGL(k_cas_round_init, dim3(seq_blocks), block, 0, stream, ca);
     if ((st = launched()) != SPECV_OK) return st;
+    const bool last = r + 1 == R;
     for (int64_t j = 0; j < k1; ++j) {
+      hipEvent_t* ev = (last && j == 0) ? events : nullptr;  // the last round's first inner round
       di.row_base = philox_row_offset + (uint64_t)((r * (k1 + 1) + 1 + j) * B);
+      mark(ev, 2 * SPECV_STAGE_PLAN, stream);
       if (bf16) {
         if (vec) hipLaunchKernelGGL((k_dec_draft<kBF16, true>), dim3(blocks_for(B)), block, 0, stream, di);
         else hipLaunchKernelGGL((k_dec_draft<kBF16, false>), dim3(blocks_for(B)), block, 0, stream, di);
@@ -809,19 +813,26 @@ specv_status_t specv_cascade_bigram(const specv_cascade_shape_t* shape, const vo
         else hipLaunchKernelGGL((k_dec_draft<kF32, false>), dim3(blocks_for(B)), block, 0, stream, di);
       }
       if ((st = launched()) != SPECV_OK) return st;
+      mark(ev, 2 * SPECV_STAGE_PLAN + 1, stream);
+      mark(ev, 2 * SPECV_STAGE_ROWSTATS, stream);
       const int64_t gw = (ga.n_t + ga.n_d) * ga.pieces;
       if (vec) hipLaunchKernelGGL((k_dec_gather<true>), dim3(blocks_for(gw)), block, 0, stream, ga);
       else hipLaunchKernelGGL((k_dec_gather<false>), dim3(blocks_for(gw)), block, 0, stream, ga);
       if ((st = launched()) != SPECV_OK) return st;
+      mark(ev, 2 * SPECV_STAGE_ROWSTATS + 1, stream);
+      mark(ev, 2 * SPECV_STAGE_ACCEPT_MASS, stream);
       Call ci{&c.vin, ga.tdst, ga.ddst, di.drafts, at<int32_t>(workspace, c.off_igam), temperature,
               seed, di.row_base, nullptr, nullptr, at<int32_t>(workspace, c.off_vn),
               at<int32_t>(workspace, c.off_vnext), workspace, c.vbytes, stream, nullptr};
       ci.lenience = len_kind;
       ci.eps = epsilon;
       if ((st = run(ci)) != SPECV_OK) return st;
+      mark(ev, 2 * SPECV_STAGE_ACCEPT_MASS + 1, stream);
       hipLaunchKernelGGL(k_cas_inner_append, dim3(seq_blocks), block, 0, stream, ca);
       if ((st = launched()) != SPECV_OK) return st;
     }
+    hipEvent_t* evo = last ? events : nullptr;
+    mark(evo, 2 * SPECV_STAGE_DRAW, stream);
     const int64_t ow = B * (k1 + 1);
     if (bf16) hipLaunchKernelGGL((k_cas_outer_rows<kBF16>), dim3(blocks_for(ow)), block, 0, stream, ca);
     else hipLaunchKernelGGL((k_cas_outer_rows<kF32>), dim3(blocks_for(ow)), block, 0, stream, ca);
@@ -834,6 +845,7 @@ specv_status_t specv_cascade_bigram(const specv_cascade_shape_t* shape, const vo
     dd.round = (int32_t)r;
     hipLaunchKernelGGL(k_dec_append, dim3(seq_blocks), block, 0, stream, dd);
     if ((st = launched()) != SPECV_OK) return st;
+    mark(evo, 2 * SPECV_STAGE_DRAW + 1, stream);
   }
   hipLaunchKernelGGL(k_dec_finish, dim3(seq_blocks), block, 0, stream, dd);
   return launched();

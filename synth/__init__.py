@@ -283,24 +283,30 @@ def chi_square_set(rounds: int = 1_000_000, vocab: int = 8, gamma: int = 4, gen_
 @dataclass
 class BigramTables:
     """Bigram "models": row s of each [V, V] table holds the logits of the
-    next token after token s (bf16 bit patterns)."""
+    next token after token s (bf16 bit patterns). `small` is a second, weaker
+    drafter for cascades (None unless asked for)."""
     target: np.ndarray
     draft: np.ndarray
     seed: int
+    small: np.ndarray = None
 
     def start(self, n: int) -> np.ndarray:
         return _rng(self.seed, 99).integers(0, self.target.shape[0], n).astype(np.int32)
 
 
-def bigram_tables(vocab: int = 8192, gen_seed: int = 6) -> BigramTables:
+def bigram_tables(vocab: int = 8192, gen_seed: int = 6, small: bool = False) -> BigramTables:
     """The T5-XXL-like row recipe per table row: target logits N(0, 3^2)
-    with 20 uniformly chosen entries raised by 8, draft = target + N(0, 1)."""
+    with 20 uniformly chosen entries raised by 8, draft = target + N(0, 1);
+    the small drafter (cascades) = target + N(0, 2^2)."""
     rng = _rng(gen_seed, 0)
     t = rng.standard_normal((vocab, vocab), dtype=np.float32) * 3.0
     rows = np.repeat(np.arange(vocab), 20)
     t[rows, rng.integers(0, vocab, vocab * 20)] += 8.0
     d = t + rng.standard_normal((vocab, vocab), dtype=np.float32)
-    return BigramTables(to_bf16_bits(t), to_bf16_bits(d), gen_seed)
+    s = None
+    if small:
+        s = to_bf16_bits(t + rng.standard_normal((vocab, vocab), dtype=np.float32) * 2.0)
+    return BigramTables(to_bf16_bits(t), to_bf16_bits(d), gen_seed, s)
 
 
 def by_name(name: str, **kw) -> Inputs:
