@@ -427,17 +427,23 @@ def specv_copy_bytes(dst, src, stream=None):
     _check(st, "specv_copy_bytes")
 
 
+# hipEventDisableSystemFence: the event only timestamps; recording it does not
+# write back and invalidate the caches as a system-scope fence would (on a
+# multi-XCD part that fence costs about as much as a small kernel).
+HIP_EVENT_TIMING_ONLY = 0x20000000
+
+
 class StageEvents:
     """2 * len(STAGES) HIP event slots for specv_verify_profiled (created
-    through the HIP runtime). Only the stages listed get events; the other
-    slots stay NULL and are not recorded."""
+    through the HIP runtime as timing-only events). Only the stages listed get
+    events; the other slots stay NULL and are not recorded."""
 
     _hip = None
 
     def __init__(self, stages=None):
         if StageEvents._hip is None:
             h = ctypes.CDLL("libamdhip64.so")
-            h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+            h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
             h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                               ctypes.c_void_p]
             h.hipEventSynchronize.argtypes = [ctypes.c_void_p]
@@ -448,8 +454,8 @@ class StageEvents:
         wanted = range(len(STAGES)) if stages is None else stages
         for i in [2 * st + h for st in wanted for h in (0, 1)]:
             ev = ctypes.c_void_p()
-            if StageEvents._hip.hipEventCreate(ctypes.byref(ev)) != 0:
-                raise SpecvError("hipEventCreate failed")
+            if StageEvents._hip.hipEventCreateWithFlags(ctypes.byref(ev), HIP_EVENT_TIMING_ONLY) != 0:
+                raise SpecvError("hipEventCreateWithFlags failed")
             self.array[i] = ev
 
     def elapsed_ms(self, stage: int) -> float:

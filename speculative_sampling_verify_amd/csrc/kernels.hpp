@@ -143,6 +143,24 @@ __global__ __launch_bounds__(1024) void k0_plan(PlanArgs a) {
   }
 }
 
+// Per-sequence temperature scale as k0_plan writes it per row: log2(e)/T for
+// a sampling sequence, 0 for a greedy one, -1 for an invalid temperature.
+__device__ __forceinline__ float seq_scale(float T) {
+  return (T > 0.f && T < pinf()) ? temp_scale(T) : (T == 0.f ? 0.f : -1.f);
+}
+
+// Plan for a uniform batch (every gamma_b == max_gamma, the only way the row
+// totals can equal B * (max_gamma + 1) with valid gammas): offsets and row
+// scales are arithmetic (sequence of target row j: j / (gamma + 1), of draft
+// row j: j / gamma), so only the gammas are checked and the status word is
+// set. One workgroup; a gamma other than max_gamma is a layout error.
+__global__ __launch_bounds__(1024) void k0_plan_uniform(PlanArgs a) {
+  bool bad = false;
+  for (int64_t b = threadIdx.x; b < a.B; b += blockDim.x) bad |= a.gamma[b] != a.max_gamma;
+  bad = __syncthreads_or(bad);
+  if (threadIdx.x == 0) a.status[0] = bad ? kLayoutError : 0u;
+}
+
 struct RowStatsArgs {
   const void* target;
   const void* draft;
@@ -156,6 +174,8 @@ struct RowStatsArgs {
   int32_t all_drafts;  // also read the draft rows of greedy sequences
   int32_t bar_k;       // > 0: write the bar_k-th largest lane maximum of each
   float* bar;          //      draft (row, chunk) to bar[row * chunks + chunk]
+  int32_t uniform_g;   // >= 0: uniform batch with this gamma (row scales from
+  const float* temperature;  // temperature[row / (gamma (+1))], tk/dk unused)
 };
 
 // Pass-1 loop over one (row, chunk), double-buffered: the loads of tile it+1
@@ -270,13 +290,13 @@ __global__ __launch_bounds__(kBlock) void k1_row_stats(RowStatsArgs a) {
   typename TL::Raw first;
   float k;
   if (is_draft) {
-    k = a.dk[j];
+    k = (a.uniform_g >= 0) ? seq_scale(a.temperature[j / a.uniform_g]) : a.dk[j];
     // greedy (or invalid) sequence: the verify step needs no draft row
     if (!(k > 0.f) && !(a.all_drafts && k == 0.f)) return;
     load_tile<DT, VEC>(row, a.V, c, lane, first);
   } else {
     load_tile<DT, VEC>(row, a.V, c, lane, first);
-    k = a.tk[j];
+    k = (a.uniform_g >= 0) ? seq_scale(a.temperature[j / (a.uniform_g + 1)]) : a.tk[j];
     if (!(k >= 0.f)) return;  // invalid temperature: the accept step fails the sequence
   }
   if (a.status[0] & kLayoutError) return;
@@ -374,6 +394,7 @@ struct AcceptArgs {
   int32_t B, max_gamma, chunks;
   int32_t lenience;  // kLen*; kLenNone is the lossless step
   float eps;         // lenience parameter in (0, 1)
+  int32_t uniform_g;  // >= 0: uniform batch with this gamma (offsets arithmetic)
 };
 
 // f(p, eps): p / eps, p / eps^2 or p^eps, in float64 (f(p, 1) = p; the host
@@ -408,7 +429,8 @@ __device__ Select accept_sequence(const AcceptArgs& a, int64_t b, int lane, bool
   const uint32_t status = a.status[0];
   const int g = a.gamma[b];
   const float T = a.temperature[b];
-  const int64_t t0 = a.toff[b], d0 = a.doff[b];
+  const int64_t t0 = (a.uniform_g >= 0) ? b * (a.uniform_g + 1) : a.toff[b];
+  const int64_t d0 = (a.uniform_g >= 0) ? b * a.uniform_g : a.doff[b];
   if (status & kLayoutError) return finish(-1, -1, false);
   const bool greedy = (T == 0.f);
   const bool sampling = (T > 0.f) && (T < pinf());

@@ -161,8 +161,12 @@ inline unsigned blocks_for(int64_t waves) {
   return (unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock);
 }
 
+// A batch is uniform when its row totals equal B * (max_gamma + 1): with
+// every gamma_b <= max_gamma (checked on the device) all equal max_gamma.
+bool uniform_batch(const Plan& p) { return p.B > 0 && p.tt == p.B * (p.max_gamma + 1); }
+
 specv_status_t launch_plan(const Plan& p, const int32_t* gamma, const float* temperature, void* ws,
-                           hipStream_t st, int32_t* dseq = nullptr) {
+                           hipStream_t st, int32_t* dseq = nullptr, bool uniform = false) {
   PlanArgs a;
   a.gamma = gamma;
   a.temperature = temperature;
@@ -176,13 +180,15 @@ specv_status_t launch_plan(const Plan& p, const int32_t* gamma, const float* tem
   a.total_d = p.td;
   a.B = (int32_t)p.B;
   a.max_gamma = (int32_t)p.max_gamma;
-  hipLaunchKernelGGL(k0_plan, dim3(1), dim3(1024), 0, st, a);
+  if (uniform) hipLaunchKernelGGL(k0_plan_uniform, dim3(1), dim3(1024), 0, st, a);
+  else hipLaunchKernelGGL(k0_plan, dim3(1), dim3(1024), 0, st, a);
   return launched();
 }
 
 specv_status_t launch_row_stats(const Plan& p, bool vec, const void* target, const void* draft,
                                 void* ws, hipStream_t st, bool with_argmax = false,
-                                bool all_drafts = false, int bar_k = 0, float* bar = nullptr) {
+                                bool all_drafts = false, int bar_k = 0, float* bar = nullptr,
+                                const float* temperature = nullptr, bool uniform = false) {
   RowStatsArgs a;
   a.target = target;
   a.draft = draft;
@@ -199,6 +205,8 @@ specv_status_t launch_row_stats(const Plan& p, bool vec, const void* target, con
   a.all_drafts = all_drafts ? 1 : 0;
   a.bar_k = bar_k;
   a.bar = bar;
+  a.uniform_g = uniform ? (int32_t)p.max_gamma : -1;
+  a.temperature = temperature;
   const int64_t waves = (p.tt + p.td) * p.chunks1;
   if (waves == 0) return SPECV_OK;
   const dim3 grid(blocks_for(waves)), block(kBlock);
@@ -248,6 +256,7 @@ AcceptArgs accept_args(const Plan& p, const Call& c) {
   a.chunks = p.chunks1;
   a.lenience = c.lenience;
   a.eps = c.eps;
+  a.uniform_g = uniform_batch(p) ? (int32_t)p.max_gamma : -1;
   return a;
 }
 
@@ -302,11 +311,14 @@ specv_status_t run(const Call& c) {
   if (p.td > 0 && !c.tokens) return SPECV_ERR_INVALID_ARGUMENT;
   if ((c.inj_r == nullptr) != (c.inj_u == nullptr)) return SPECV_ERR_INVALID_ARGUMENT;
   const bool vec = vector_path(p, c.target, c.draft);
+  const bool uniform = uniform_batch(p);
   mark(c.events, 2 * SPECV_STAGE_PLAN, c.stream);
-  if ((st = launch_plan(p, c.gamma, c.temperature, c.ws, c.stream)) != SPECV_OK) return st;
+  if ((st = launch_plan(p, c.gamma, c.temperature, c.ws, c.stream, nullptr, uniform)) != SPECV_OK)
+    return st;
   mark(c.events, 2 * SPECV_STAGE_PLAN + 1, c.stream);
   mark(c.events, 2 * SPECV_STAGE_ROWSTATS, c.stream);
-  if ((st = launch_row_stats(p, vec, c.target, c.draft, c.ws, c.stream)) != SPECV_OK)
+  if ((st = launch_row_stats(p, vec, c.target, c.draft, c.ws, c.stream, false, false, 0, nullptr,
+                             c.temperature, uniform)) != SPECV_OK)
     return st;
   mark(c.events, 2 * SPECV_STAGE_ROWSTATS + 1, c.stream);
   mark(c.events, 2 * SPECV_STAGE_ACCEPT_MASS, c.stream);
