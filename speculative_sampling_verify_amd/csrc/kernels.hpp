@@ -330,7 +330,15 @@ struct RowStat {
   bool valid;  // no NaN/+inf and at least one finite logit
 };
 
-__device__ __forceinline__ RowStat merge_row(const RowPart* p, int chunks, float k, bool sampling) {
+// The first four chunk partials of a row (padding past `chunks`), loaded on
+// their own so that a caller can issue them early.
+__device__ __forceinline__ void load_parts4(const RowPart* p, int chunks, RowPart (&q)[4]) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) q[u] = (u < chunks) ? p[u] : RowPart{0.0, ninf(), INT32_MAX};
+}
+
+__device__ __forceinline__ RowStat merge_row_from(const RowPart (&q0)[4], const RowPart* p,
+                                                  int chunks, float k, bool sampling) {
   // Chunks in order, four loads in flight at a time: a running maximum (the
   // lowest index attaining it gives the argmax), the running sum moved onto
   // the new maximum's reference when it grows, and each group's terms moved
@@ -344,7 +352,7 @@ __device__ __forceinline__ RowStat merge_row(const RowPart* p, int chunks, float
     RowPart q[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      q[u] = (c0 + u < chunks) ? p[c0 + u] : RowPart{0.0, ninf(), INT32_MAX};
+      q[u] = (c0 == 0) ? q0[u] : (c0 + u < chunks) ? p[c0 + u] : RowPart{0.0, ninf(), INT32_MAX};
     float mg = M;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -371,6 +379,12 @@ __device__ __forceinline__ RowStat merge_row(const RowPart* p, int chunks, float
   st.arg = arg;
   st.valid = (M > ninf()) && (M < pinf()) && !__builtin_isnan(S);
   return st;
+}
+
+__device__ __forceinline__ RowStat merge_row(const RowPart* p, int chunks, float k, bool sampling) {
+  RowPart q0[4];
+  load_parts4(p, chunks, q0);
+  return merge_row_from(q0, p, chunks, k, sampling);
 }
 
 struct AcceptArgs {
@@ -425,29 +439,43 @@ __device__ Select accept_sequence(const AcceptArgs& a, int64_t b, int lane, bool
     }
     return s;
   };
-  // independent loads first, so that they are in flight together
+  // Independent loads first, so that they are in flight together. In a
+  // uniform batch gamma and the offsets are known without any load, so the
+  // chunk partials and the draft tokens are requested with the metadata (all
+  // addresses stay inside the packed arrays whatever the data holds).
+  const bool uni = a.uniform_g >= 0;
   const uint32_t status = a.status[0];
-  const int g = a.gamma[b];
+  const int g = uni ? a.uniform_g : a.gamma[b];
   const float T = a.temperature[b];
-  const int64_t t0 = (a.uniform_g >= 0) ? b * (a.uniform_g + 1) : a.toff[b];
-  const int64_t d0 = (a.uniform_g >= 0) ? b * a.uniform_g : a.doff[b];
+  const int64_t t0 = uni ? b * (a.uniform_g + 1) : a.toff[b];
+  const int64_t d0 = uni ? b * a.uniform_g : a.doff[b];
+  RowPart tq[4], dq[4];
+  int x = 0;
+  if (uni) {
+    if (lane <= g) load_parts4(a.tparts + (t0 + lane) * a.chunks, a.chunks, tq);
+    if (lane < g) {
+      x = a.tokens[d0 + lane];
+      load_parts4(a.dparts + (d0 + lane) * a.chunks, a.chunks, dq);
+    }
+  }
   if (status & kLayoutError) return finish(-1, -1, false);
   const bool greedy = (T == 0.f);
   const bool sampling = (T > 0.f) && (T < pinf());
   if (!greedy && !sampling) return finish(-1, -1, true);
   const float k = sampling ? temp_scale(T) : 0.f;
   RowStat st_t{}, st_d{};
-  int x = 0;
   bool bad = false;
   if (lane <= g) {
-    st_t = merge_row(a.tparts + (t0 + lane) * a.chunks, a.chunks, k, sampling);
+    if (!uni) load_parts4(a.tparts + (t0 + lane) * a.chunks, a.chunks, tq);
+    st_t = merge_row_from(tq, a.tparts + (t0 + lane) * a.chunks, a.chunks, k, sampling);
     bad |= !st_t.valid;
   }
   if (lane < g) {
-    x = a.tokens[d0 + lane];
+    if (!uni) x = a.tokens[d0 + lane];
     bad |= (x < 0) || ((int64_t)x >= a.V);
     if (sampling) {
-      st_d = merge_row(a.dparts + (d0 + lane) * a.chunks, a.chunks, k, true);
+      if (!uni) load_parts4(a.dparts + (d0 + lane) * a.chunks, a.chunks, dq);
+      st_d = merge_row_from(dq, a.dparts + (d0 + lane) * a.chunks, a.chunks, k, true);
       bad |= !st_d.valid;
     }
   }
