@@ -83,9 +83,64 @@ __global__ __launch_bounds__(kBlock) void k_cas_inner_append(CascadeArgs a) {
   a.icur[b] = tok[d + n];
 }
 
+// Eight consecutive elements at v0 (-inf past V): one 16-byte load for bf16,
+// two for fp32, when rows are 16-byte multiples and aligned; else scalar.
+template <int DT, bool VEC>
+__device__ __forceinline__ void cas_load8(const void* row, int64_t V, int64_t v0, float (&z)[8]) {
+  if constexpr (VEC) {
+    // V is a multiple of the vector width here: a vector is all in or all out
+    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const char*>(row) +
+                                                    v0 * (DT == kBF16 ? 2 : 4));
+    if constexpr (DT == kBF16) {
+      u32x4 q = {0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};
+      if (v0 < V) q = p[0];
+      z[0] = bf16_lo(q.x); z[1] = bf16_hi(q.x); z[2] = bf16_lo(q.y); z[3] = bf16_hi(q.y);
+      z[4] = bf16_lo(q.z); z[5] = bf16_hi(q.z); z[6] = bf16_lo(q.w); z[7] = bf16_hi(q.w);
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        u32x4 q = {0xff800000u, 0xff800000u, 0xff800000u, 0xff800000u};
+        if (v0 + 4 * h < V) q = p[h];
+        z[4 * h + 0] = __uint_as_float(q.x); z[4 * h + 1] = __uint_as_float(q.y);
+        z[4 * h + 2] = __uint_as_float(q.z); z[4 * h + 3] = __uint_as_float(q.w);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) z[j] = (v0 + j < V) ? load_logit<DT>(row, v0 + j) : ninf();
+  }
+}
+
+template <bool VEC>
+__device__ __forceinline__ void cas_store8(float* row, int64_t V, int64_t v0, const float (&z)[8]) {
+  if constexpr (VEC) {
+    if (v0 >= V) return;
+    f32x4* p = reinterpret_cast<f32x4*>(row + v0);
+    p[0] = f32x4{z[0], z[1], z[2], z[3]};
+    if (v0 + 4 < V) p[1] = f32x4{z[4], z[5], z[6], z[7]};
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (v0 + j < V) row[v0 + j] = z[j];
+  }
+}
+
+// T ln Q in float64 from the exact binary exponent of Q and v_log_f32 of its
+// mantissa in [1, 2): the error is absolute (about 1e-7 T), below the fp32
+// rounding of the result.
+__device__ __forceinline__ float t_ln(double Q, double T_ln2) {
+  if (!(Q > 0.0)) return ninf();
+  int e;
+  const double mant = frexp(Q, &e);  // Q = mant * 2^e, mant in [0.5, 1)
+  const float l = __builtin_amdgcn_logf((float)(2.0 * mant));  // log2 of [1, 2)
+  return (float)(T_ln2 * ((double)(e - 1) + (double)l));
+}
+
 // One wave per (sequence, position i <= k1): the target row of position i
-// and, for i < k1, the draft row fl32(T ln Q).
-template <int DT>
+// and, for i < k1, the draft row fl32(T ln Q). Eight consecutive elements per
+// lane per step; Q's row statistics in one online (max, sum) pass, then a
+// pass for beta and the residual mass and a pass that writes the row.
+template <int DT, bool VEC>
 __global__ __launch_bounds__(kBlock) void k_cas_outer_rows(CascadeArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t item = wave_uniform((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
@@ -93,12 +148,17 @@ __global__ __launch_bounds__(kBlock) void k_cas_outer_rows(CascadeArgs a) {
   const int64_t b = item / (a.k1 + 1);
   const int i = (int)(item - b * (a.k1 + 1));
   const int64_t V = a.V;
+  constexpr int64_t kStep = kWave * 8;
   const int32_t prev = (i == 0) ? a.cur[b] : a.dtok[b * a.dcap + i - 1];
   constexpr int64_t esz = (DT == kBF16) ? 2 : 4;
   {
     const void* src = static_cast<const char*>(a.ttab) + (int64_t)prev * V * esz;
     float* dst = a.otpack + (b * (a.k1 + 1) + i) * V;
-    for (int64_t v = lane; v < V; v += kWave) dst[v] = load_logit<DT>(src, v);
+    for (int64_t v0 = (int64_t)lane * 8; v0 < V; v0 += kStep) {
+      float z[8];
+      cas_load8<DT, VEC>(src, V, v0, z);
+      cas_store8<VEC>(dst, V, v0, z);
+    }
   }
   if (i == a.k1) return;
   if (lane == 0) a.otok[b * a.k1 + i] = a.dtok[b * a.dcap + i];
@@ -106,49 +166,85 @@ __global__ __launch_bounds__(kBlock) void k_cas_outer_rows(CascadeArgs a) {
   const float T = a.temperature[b];
   const bool sampling = T > 0.f && T < pinf();
   if (!sampling || a.fail[b]) {
-    for (int64_t v = lane; v < V; v += kWave) out[v] = 0.f;  // not read (greedy or failed)
-    return;
+    const float zero[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int64_t v0 = (int64_t)lane * 8; v0 < V; v0 += kStep) cas_store8<VEC>(out, V, v0, zero);
+    return;  // not read (greedy or failed)
   }
   const int32_t pv = a.dprev[b * a.dcap + i];
   const void* r1 = static_cast<const char*>(a.m1tab) + (int64_t)pv * V * esz;
-  if (a.dbonus[b * a.dcap + i]) {
-    for (int64_t v = lane; v < V; v += kWave) out[v] = load_logit<DT>(r1, v);  // Q = p1
+  if (a.dbonus[b * a.dcap + i]) {  // Q = p1: the m1 row itself
+    for (int64_t v0 = (int64_t)lane * 8; v0 < V; v0 += kStep) {
+      float z[8];
+      cas_load8<DT, VEC>(r1, V, v0, z);
+      cas_store8<VEC>(out, V, v0, z);
+    }
     return;
   }
   const void* r2 = static_cast<const char*>(a.m2tab) + (int64_t)pv * V * esz;
   const float k = temp_scale(T);
-  float m1 = ninf(), m2 = ninf();
-  for (int64_t v = lane; v < V; v += kWave) {
-    m1 = fmaxf(m1, load_logit<DT>(r1, v));
-    m2 = fmaxf(m2, load_logit<DT>(r2, v));
-  }
-  const float rk1 = ref_point(wave_max(m1), k), rk2 = ref_point(wave_max(m2), k);
+  // pass 1: per-lane online max and sum of 2^(z k - rk) for both rows
+  float m1 = ninf(), m2 = ninf(), rk1 = 0.f, rk2 = 0.f;
   double s1 = 0.0, s2 = 0.0;
-  for (int64_t v = lane; v < V; v += kWave) {
-    s1 += (double)exp2_hw(__builtin_fmaf(load_logit<DT>(r1, v), k, -rk1));
-    s2 += (double)exp2_hw(__builtin_fmaf(load_logit<DT>(r2, v), k, -rk2));
-  }
-  const double S1 = wave_sum(s1), S2 = wave_sum(s2);
-  auto probs = [&](int64_t v, double& p1, double& q2) {
-    p1 = (double)exp2_hw(__builtin_fmaf(load_logit<DT>(r1, v), k, -rk1)) / S1;
-    q2 = (double)exp2_hw(__builtin_fmaf(load_logit<DT>(r2, v), k, -rk2)) / S2;
+  auto online = [&](const float (&z)[8], float& m, float& rk, double& s) {
+    const float g = tile_max(z);
+    if (!(g > ninf())) return;
+    const float mn = fmaxf(m, g);
+    const float rkn = ref_point(mn, k);
+    const float sc = (m == ninf()) ? 0.f : exp2_hw(rk - rkn);
+    float e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = exp2_hw(__builtin_fmaf(z[j], k, -rkn));
+    s = __builtin_fma(s, (double)sc, (double)tree_sum(e));
+    m = mn;
+    rk = rkn;
   };
+  for (int64_t v0 = (int64_t)lane * 8; v0 < V; v0 += kStep) {
+    float z1[8], z2[8];
+    cas_load8<DT, VEC>(r1, V, v0, z1);
+    cas_load8<DT, VEC>(r2, V, v0, z2);
+    online(z1, m1, rk1, s1);
+    online(z2, m2, rk2, s2);
+  }
+  const float M1 = wave_max(m1), M2 = wave_max(m2);
+  const float R1 = ref_point(M1, k), R2 = ref_point(M2, k);
+  const double S1 = wave_sum((m1 == ninf()) ? 0.0 : s1 * exp2((double)(m1 * k) - (double)R1));
+  const double S2 = wave_sum((m2 == ninf()) ? 0.0 : s2 * exp2((double)(m2 * k) - (double)R2));
+  const double i1 = 1.0 / S1, i2 = 1.0 / S2;
+  auto probs = [&](float z1, float z2, double& p1, double& q2) {
+    p1 = (double)exp2_hw(__builtin_fmaf(z1, k, -R1)) * i1;
+    q2 = (double)exp2_hw(__builtin_fmaf(z2, k, -R2)) * i2;
+  };
+  // pass 2: beta = sum min(q2, f(p1)) and the residual mass sum max(0, p1 - q2)
   double beta = 0.0, rmass = 0.0;
-  for (int64_t v = lane; v < V; v += kWave) {
-    double p1, q2;
-    probs(v, p1, q2);
-    beta += fmin(q2, lenient(p1, a.lenience, a.eps));
-    rmass += fmax(p1 - q2, 0.0);
+  for (int64_t v0 = (int64_t)lane * 8; v0 < V; v0 += kStep) {
+    float z1[8], z2[8];
+    cas_load8<DT, VEC>(r1, V, v0, z1);
+    cas_load8<DT, VEC>(r2, V, v0, z2);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      double p1, q2;
+      probs(z1[j], z2[j], p1, q2);
+      beta += fmin(q2, lenient(p1, a.lenience, a.eps));
+      rmass += fmax(p1 - q2, 0.0);
+    }
   }
   beta = wave_sum(beta);
   rmass = wave_sum(rmass);
-  for (int64_t v = lane; v < V; v += kWave) {
-    double p1, q2;
-    probs(v, p1, q2);
-    double Q = fmin(q2, lenient(p1, a.lenience, a.eps));
-    const double d = p1 - q2;
-    if (rmass > 0.0 && d > 0.0) Q += (1.0 - beta) * d / rmass;
-    out[v] = (Q > 0.0) ? (float)((double)T * log(Q)) : ninf();
+  const double c = (rmass > 0.0) ? (1.0 - beta) / rmass : 0.0;
+  const double T_ln2 = (double)T * 0.69314718055994530942;
+  // pass 3: Q and the row fl32(T ln Q)
+  for (int64_t v0 = (int64_t)lane * 8; v0 < V; v0 += kStep) {
+    float z1[8], z2[8], o[8];
+    cas_load8<DT, VEC>(r1, V, v0, z1);
+    cas_load8<DT, VEC>(r2, V, v0, z2);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      double p1, q2;
+      probs(z1[j], z2[j], p1, q2);
+      const double Q = fmin(q2, lenient(p1, a.lenience, a.eps)) + c * fmax(p1 - q2, 0.0);
+      o[j] = t_ln(Q, T_ln2);
+    }
+    cas_store8<VEC>(out, V, v0, o);
   }
 }
 

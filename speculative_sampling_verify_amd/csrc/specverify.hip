@@ -846,8 +846,16 @@ specv_status_t specv_cascade_bigram(const specv_cascade_shape_t* shape, const vo
     hipEvent_t* evo = last ? events : nullptr;
     mark(evo, 2 * SPECV_STAGE_DRAW, stream);
     const int64_t ow = B * (k1 + 1);
-    if (bf16) hipLaunchKernelGGL((k_cas_outer_rows<kBF16>), dim3(blocks_for(ow)), block, 0, stream, ca);
-    else hipLaunchKernelGGL((k_cas_outer_rows<kF32>), dim3(blocks_for(ow)), block, 0, stream, ca);
+    // fp32 review rows are 16-byte aligned when V is a multiple of 4 (table
+    // rows: a 16-byte multiple, the same condition as the gather's)
+    const bool ovec = vec && shape->vocab % 4 == 0 && aligned(target_table, 16);
+    if (bf16) {
+      if (ovec) hipLaunchKernelGGL((k_cas_outer_rows<kBF16, true>), dim3(blocks_for(ow)), block, 0, stream, ca);
+      else hipLaunchKernelGGL((k_cas_outer_rows<kBF16, false>), dim3(blocks_for(ow)), block, 0, stream, ca);
+    } else {
+      if (ovec) hipLaunchKernelGGL((k_cas_outer_rows<kF32, true>), dim3(blocks_for(ow)), block, 0, stream, ca);
+      else hipLaunchKernelGGL((k_cas_outer_rows<kF32, false>), dim3(blocks_for(ow)), block, 0, stream, ca);
+    }
     if ((st = launched()) != SPECV_OK) return st;
     Call co{&c.vout, ca.otpack, ca.odpack, ca.otok, dd.gam, temperature, seed,
             philox_row_offset + (uint64_t)(r * (k1 + 1) * B), nullptr, nullptr,

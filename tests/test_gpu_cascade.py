@@ -124,3 +124,13 @@ def test_cascade_gpu_target_law(svx):
     pv = stats.chisquare(obs, exp).pvalue
     log("[law] cascade GPU joint of 3 tokens (sq 0.5 inner): p = %.4g" % pv)
     assert pv > 1e-4
+
+
+def test_cascade_parity_scalar_rows(svx):
+    # V = 999 (bf16): rows are not 16-byte multiples, so every kernel of the
+    # cascade takes its scalar path
+    tabs = [bf16(t) for t in tables(999, 8)]
+    B = 48
+    start = np.random.default_rng(9).integers(0, 999, B)
+    assert_cascade_parity("bf16 V=999 lin 0.4", svx, tabs, np.full(B, 0.9, np.float32), start,
+                          k1=3, k2=2, rounds=3, lenience="lin", epsilon=0.4, seed=12)
