@@ -314,10 +314,13 @@ __global__ __launch_bounds__(kBlock) void k5_diag_pass(DiagArgs a) {
 constexpr int kMergeCap = 16 * kMaxTopK;
 constexpr int kMergeSlots = kMergeCap / kWave;
 
+// LDS: kWavesPerBlock buffers of chunks * K keys (rounded up to a multiple of
+// 8 keys), sized at launch.
 __global__ __launch_bounds__(kBlock) void k6_diag_merge(DiagArgs a) {
-  __shared__ __attribute__((aligned(16))) uint64_t sbuf[kWavesPerBlock][kMergeCap];
+  extern __shared__ __attribute__((aligned(16))) uint64_t merge_lds[];
   const int lane = threadIdx.x & (kWave - 1);
-  uint64_t* buf = sbuf[threadIdx.x >> 6];
+  const int stride = (a.chunks * a.K + 7) / 8 * 8;
+  uint64_t* buf = merge_lds + (threadIdx.x >> 6) * stride;
   const int64_t j = wave_uniform((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
   if (j >= a.total_d) return;
   const int K = a.K;

@@ -590,7 +590,9 @@ specv_status_t specv_position_diagnostics(const specv_shape_t* shape, const void
   if ((st = launched()) != SPECV_OK) return st;
   mark(events, 2 * SPECV_STAGE_ACCEPT_MASS + 1, stream);
   mark(events, 2 * SPECV_STAGE_DRAW, stream);
-  if (p.td > 0) hipLaunchKernelGGL(k6_diag_merge, dim3(blocks_for(p.td)), block, 0, stream, a);
+  const size_t merge_lds = (size_t)kWavesPerBlock * ((p.chunks1 * top_k + 7) / 8 * 8) * 8;
+  if (p.td > 0)
+    hipLaunchKernelGGL(k6_diag_merge, dim3(blocks_for(p.td)), block, merge_lds, stream, a);
   if ((st = launched()) != SPECV_OK) return st;
   mark(events, 2 * SPECV_STAGE_DRAW + 1, stream);
   return SPECV_OK;
