@@ -528,3 +528,23 @@ def test_diagnostics_argument_errors(svx):
     for k in (-1, 33, 65):
         with pytest.raises(svx.SpecvError):
             run_gpu_diag(svx, x, k)
+
+
+def test_max_gamma_63(svx):
+    # gamma = 63: the accept step's wave has one lane per target row (64)
+    x = synth.tiny_cpu(rounds=96, vocab=512, gamma=63, gen_seed=41)
+    parity_case(svx, "gamma=63 uniform", x, repeat=False)
+    # ragged 0 / 63 mix, and sequences whose draft rows equal their target
+    # rows (every draft accepted: n = 63, the token drawn from row 63)
+    rng = np.random.default_rng(42)
+    V, seqs = 256, []
+    for b in range(24):
+        g = 63 if b % 3 else 0
+        t = rng.standard_normal((g + 1, V)).astype(np.float32) * 2
+        same = b % 3 == 1
+        d = t[:g].copy() if same else (t[:g] + rng.standard_normal((g, V)).astype(np.float32))
+        toks = [int(np.argmax(d[i] + rng.gumbel(size=V))) for i in range(g)]
+        seqs.append({"target": t, "draft": d, "tokens": toks, "T": 1.0})
+    x = pack(seqs, V, "bf16")
+    got, orc = parity_case(svx, "gamma 0/63 ragged", x, repeat=False)
+    assert (orc.n[1::3] == 63).all() and (got[0][1::3] == 63).all()
