@@ -71,6 +71,35 @@ def make_inputs(name):
     return getattr(synth, base)(**kw), desc
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def copy_gbps(torch, svx, dev, nbytes=1 << 30):
+    """Device-to-device copy bandwidth of the library's plain copy kernel
+    (bytes read + bytes written per second), as context for the HBM figures."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        svx.specv_copy_bytes(dst, src)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(10):
+        svx.specv_copy_bytes(dst, src)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / 10
+    del src, dst
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
 def cpu_baseline(x, gpu_n, gpu_next, budget_s=12.0, lenience="none", epsilon=1.0):
     """The oracle as it stands, on the host's cores, over repeated passes of
     the same step's sequences (bounded by a time budget)."""
@@ -88,8 +117,16 @@ def cpu_baseline(x, gpu_n, gpu_next, budget_s=12.0, lenience="none", epsilon=1.0
             break
     rows = passes * x.total_target_rows
     mism = (gpu_n != res.n) | (gpu_next != res.next_token)
+    # one thread, over the first eighth of the sequences
+    import synth
+    sub = synth.subset(x, np.arange(max(1, x.batch // 8)))
+    t1 = time.perf_counter()
+    oracle.verify(sub.target, sub.draft, sub.tokens, sub.gamma, sub.temperature, vocab=sub.vocab,
+                  max_gamma=sub.max_gamma, seed=sub.seed, row_offset=sub.row_offset,
+                  lenience=lenience, epsilon=epsilon, nthreads=1)
+    single = sub.total_target_rows / (time.perf_counter() - t1)
     return {"value": rows / el, "unit": "verified target rows/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "single_thread_value": single, "cpu_model": cpu_model(),
             "sample": "%d pass(es) over the step's %d sequences (%d target rows each pass), %.1f s"
                       % (passes, x.batch, x.total_target_rows, el),
             "parity_vs_gpu": {"sequences": int(x.batch), "mismatches": int(mism.sum()),
@@ -541,6 +578,9 @@ def main():
         "rotating_input_sets": n_sets,
         "kernel_sha": sha,
     }
+    cg = copy_gbps(torch, svx, dev)
+    result["copy_gbps"] = cg
+    result["roofline"]["frac_of_copy"] = achieved / cg
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on the host")
         result["cpu_baseline"] = cpu_baseline(x, n_host, next_host, lenience=args.lenience,

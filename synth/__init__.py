@@ -280,6 +280,20 @@ def chi_square_set(rounds: int = 1_000_000, vocab: int = 8, gamma: int = 4, gen_
                   meta={"target_rows": t, "draft_rows": d})
 
 
+def subset(x: Inputs, seqs) -> Inputs:
+    """The packed inputs of sequences `seqs` (in order) of x: slicing only.
+    Note that a sequence keeps its Philox row only where its index is
+    unchanged (the row is row_offset + its position in the batch)."""
+    toff, doff = x.offsets()
+    t = np.concatenate([x.target[toff[b]:toff[b + 1]] for b in seqs])
+    d = [x.draft[doff[b]:doff[b + 1]] for b in seqs]
+    d = np.concatenate(d) if sum(len(a) for a in d) else x.draft[:0]
+    k = [x.tokens[doff[b]:doff[b + 1]] for b in seqs]
+    k = np.concatenate(k) if sum(len(a) for a in k) else x.tokens[:0]
+    return Inputs(x.name, x.vocab, x.max_gamma, x.dtype, t, d, k, x.gamma[seqs].copy(),
+                  x.temperature[seqs].copy(), x.seed, x.row_offset, dict(x.meta))
+
+
 @dataclass
 class BigramTables:
     """Bigram "models": row s of each [V, V] table holds the logits of the

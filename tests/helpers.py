@@ -32,11 +32,4 @@ def run_oracle(x, r=None, u=None, seed=None, row_offset=None, max_gamma=None, nt
 
 def subset(x, seqs):
     """The packed inputs of sequences `seqs` (in order) of x."""
-    toff, doff = x.offsets()
-    t = np.concatenate([x.target[toff[b]:toff[b + 1]] for b in seqs])
-    d = [x.draft[doff[b]:doff[b + 1]] for b in seqs]
-    d = np.concatenate(d) if sum(len(a) for a in d) else x.draft[:0]
-    k = [x.tokens[doff[b]:doff[b + 1]] for b in seqs]
-    k = np.concatenate(k) if sum(len(a) for a in k) else x.tokens[:0]
-    return synth.Inputs(x.name, x.vocab, x.max_gamma, x.dtype, t, d, k, x.gamma[seqs].copy(),
-                        x.temperature[seqs].copy(), x.seed, x.row_offset, dict(x.meta))
+    return synth.subset(x, seqs)
