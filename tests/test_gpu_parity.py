@@ -548,3 +548,39 @@ def test_max_gamma_63(svx):
     x = pack(seqs, V, "bf16")
     got, orc = parity_case(svx, "gamma 0/63 ragged", x, repeat=False)
     assert (orc.n[1::3] == 63).all() and (got[0][1::3] == 63).all()
+
+
+def random_case(seed):
+    """A seeded random shape: V (16-byte aligned or not), dtype, batch,
+    ragged gammas up to 20, greedy and sampling temperatures, masked tokens
+    (-inf) in some rows, draft tokens drawn from the draft rows."""
+    rng = np.random.default_rng(1000 + seed)
+    V = int(rng.choice([1, 2, 7, 63, 64, 513, 1000, 2049, 4096, 8191, 16384, 33333, 65536]))
+    dtype = "bf16" if rng.random() < 0.5 else "f32"
+    B = int(rng.integers(1, 40))
+    mg = int(rng.integers(0, 21))
+    seqs = []
+    for b in range(B):
+        g = int(rng.integers(0, mg + 1))
+        scale = float(rng.choice([0.5, 2.0, 4.0]))
+        t = (rng.standard_normal((g + 1, V)) * scale).astype(np.float32)
+        d = (t[:g] + rng.standard_normal((g, V)) * float(rng.choice([0.1, 1.0, 3.0]))).astype(np.float32)
+        if V > 4 and rng.random() < 0.3:
+            cols = rng.choice(V, size=V // 4, replace=False)
+            t[:, cols] = -np.inf
+            d[:, cols[: len(cols) // 2]] = -np.inf
+        T = 0.0 if rng.random() < 0.25 else float(rng.uniform(0.3, 2.0))
+        toks = []
+        for i in range(g):
+            z = d[i].astype(np.float64) / (T if T > 0 else 1.0)
+            z = np.where(np.isfinite(z), z, -np.inf)
+            toks.append(int(np.argmax(z + rng.gumbel(size=V))))
+        seqs.append({"target": t, "draft": d, "tokens": toks, "T": T})
+    return pack(seqs, V, dtype)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_shapes_parity(svx, seed):
+    x = random_case(seed)
+    parity_case(svx, "random %d (V=%d %s B=%d max_gamma=%d)" % (seed, x.vocab, x.dtype, x.batch,
+                                                               x.max_gamma), x, repeat=False)
