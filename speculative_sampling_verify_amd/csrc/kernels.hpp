@@ -2,7 +2,10 @@
 //
 // The step (DistillSpec, Appendix A.3, Algorithm A.1, lenience 1) runs as:
 //   k0_plan        offsets of the packed ragged rows, row -> sequence maps,
-//                  layout validation; initialises the status word.
+//                  layout validation; initialises the status word. Not
+//                  launched for a uniform batch (every gamma equal), whose
+//                  offsets are arithmetic: k1's first workgroup checks the
+//                  gammas and initialises the status word instead.
 //   k1_row_stats   pass 1, the HBM-bound hot loop: every needed logit row is
 //                  streamed once with 16-byte non-temporal loads; each wave
 //                  owns one (row, chunk) and keeps (max, sum of 2^(z k - rk),
@@ -16,6 +19,9 @@
 //   k4_draw        one wave per sampling sequence picks the sub-block that
 //                  holds u * total and a wave prefix scan inside it finds the
 //                  token (inverse CDF in index order).
+//   k3_accept_mass_draw  both of the last two in one launch when a sequence's
+//                  pass-2 waves fit one workgroup (a barrier, not a kernel
+//                  boundary, orders the masses before the draw).
 #pragma once
 
 #include "device.hpp"
@@ -149,18 +155,6 @@ __device__ __forceinline__ float seq_scale(float T) {
   return (T > 0.f && T < pinf()) ? temp_scale(T) : (T == 0.f ? 0.f : -1.f);
 }
 
-// Plan for a uniform batch (every gamma_b == max_gamma, the only way the row
-// totals can equal B * (max_gamma + 1) with valid gammas): offsets and row
-// scales are arithmetic (sequence of target row j: j / (gamma + 1), of draft
-// row j: j / gamma), so only the gammas are checked and the status word is
-// set. One workgroup; a gamma other than max_gamma is a layout error.
-__global__ __launch_bounds__(1024) void k0_plan_uniform(PlanArgs a) {
-  bool bad = false;
-  for (int64_t b = threadIdx.x; b < a.B; b += blockDim.x) bad |= a.gamma[b] != a.max_gamma;
-  bad = __syncthreads_or(bad);
-  if (threadIdx.x == 0) a.status[0] = bad ? kLayoutError : 0u;
-}
-
 struct RowStatsArgs {
   const void* target;
   const void* draft;
@@ -176,6 +170,8 @@ struct RowStatsArgs {
   float* bar;          //      draft (row, chunk) to bar[row * chunks + chunk]
   int32_t uniform_g;   // >= 0: uniform batch with this gamma (row scales from
   const float* temperature;  // temperature[row / (gamma (+1))], tk/dk unused)
+  const int32_t* gamma;  // non-null (uniform batch): workgroup 0 also does the
+  uint32_t* status_out;  // plan's check (every gamma == uniform_g) and sets the status word
 };
 
 // Pass-1 loop over one (row, chunk), double-buffered: the loads of tile it+1
@@ -237,7 +233,23 @@ __device__ __forceinline__ RowPart chunk_pass(const void* row, int64_t V, int c,
   };
   auto tile_of = [&](int it) { return (int64_t)c + (int64_t)it * chunks; };
   Raw b;
-  for (int it = 0; it < n_iter; it += 2) {
+  int it = 0;
+  if constexpr (DT == kBF16) {
+    // Only a chunk's last tile can be partial (it is the row's last tile).
+    // This loop loads full tiles only, with no branch around the loads: each
+    // step issues one tile and then works on the one before it, so the
+    // compiler's wait before that work leaves the new tile in flight (a load
+    // under a branch makes it wait for every load). The last one to three
+    // tiles take the loop below. For fp32 tiles the extra live tile costs
+    // occupancy (7 -> 5 waves per SIMD) and the plain loop is faster.
+    for (; it + 3 < n_iter; it += 2) {
+      TL::template load_raw<false>(row, tile_of(it + 1) * TL::EPI, V, 0, lane, b);
+      process(a, it);
+      TL::template load_raw<false>(row, tile_of(it + 2) * TL::EPI, V, 0, lane, a);
+      process(b, it + 1);
+    }
+  }
+  for (; it < n_iter; it += 2) {
     if (it + 1 < n_iter) load_tile<DT, VEC>(row, V, tile_of(it + 1), lane, b);
     process(a, it);
     if (it + 1 >= n_iter) break;
@@ -272,6 +284,16 @@ __device__ __forceinline__ RowPart chunk_pass(const void* row, int64_t V, int c,
 template <int DT, bool VEC, bool WITH_ARG>
 __global__ __launch_bounds__(kBlock) void k1_row_stats(RowStatsArgs a) {
   using TL = Tile<DT, VEC>;
+  if (a.gamma && blockIdx.x == 0) {
+    // The uniform batch's plan, in this launch: offsets and row scales are
+    // arithmetic, so only the gammas are checked and the status word is set
+    // (read after this launch ends). The whole workgroup takes this branch
+    // before any of its waves can return.
+    bool bad = false;
+    for (int64_t b = threadIdx.x; b < a.B; b += blockDim.x) bad |= a.gamma[b] != a.uniform_g;
+    bad = __syncthreads_or(bad);
+    if (threadIdx.x == 0) a.status_out[0] = bad ? kLayoutError : 0u;
+  }
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t item = wave_uniform((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
   const int64_t rows = a.total_t + a.total_d;
@@ -299,7 +321,9 @@ __global__ __launch_bounds__(kBlock) void k1_row_stats(RowStatsArgs a) {
     k = (a.uniform_g >= 0) ? seq_scale(a.temperature[j / (a.uniform_g + 1)]) : a.tk[j];
     if (!(k >= 0.f)) return;  // invalid temperature: the accept step fails the sequence
   }
-  if (a.status[0] & kLayoutError) return;
+  // a uniform batch reads only arithmetic offsets: its rows are computed
+  // whatever the gammas hold, and the accept step reports a layout error
+  if (!a.gamma && (a.status[0] & kLayoutError)) return;
   RowPart out;
   float lm;
   if (k > 0.f)
@@ -525,6 +549,33 @@ __device__ Select accept_sequence(const AcceptArgs& a, int64_t b, int lane, bool
   return s;
 }
 
+// The selection is the same in every lane after the accept step's shuffles;
+// v_readfirstlane moves it to scalar registers for the passes that follow.
+__device__ __forceinline__ double uniform_f64(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+__device__ __forceinline__ float uniform_f32(float v) {
+  return __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(v)));
+}
+__device__ __forceinline__ Select uniform_select(const Select& s) {
+  Select u;
+  u.mode = __builtin_amdgcn_readfirstlane(s.mode);
+  u.n = __builtin_amdgcn_readfirstlane(s.n);
+  u.trow = wave_uniform(s.trow);
+  u.drow = wave_uniform(s.drow);
+  u.k = uniform_f32(s.k);
+  u.rkT = uniform_f32(s.rkT);
+  u.rkD = uniform_f32(s.rkD);
+  u.pad = 0;
+  u.sT = uniform_f64(s.sT);
+  u.sD = uniform_f64(s.sD);
+  u.u = uniform_f64(s.u);
+  return u;
+}
+
 // Weight of one token in the final draw: max(0, p - q) or p, in fp32.
 struct Weights {
   float k, rkT, rkD, iT, iD;
@@ -634,33 +685,39 @@ __device__ int wave_draw(const void* trow, const void* drow, const Weights& W, i
     float w[16], zt[16], zd[16];
     load16<DT, VEC>(trow, lo, V, zt);
     if (W.residual) load16<DT, VEC>(drow, lo, V, zd);
+    // positions within the lane's run are kept as 0..15 (not as 64-bit
+    // element indices): it halves the registers the walk needs
     double ls = 0.0;
+    int lastj = -1;  // last slot of positive weight in this lane's run
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       w[j] = W(zt[j], W.residual ? zd[j] : 0.f);
-      if (w[j] > 0.f) lastpos = lo + j;
+      lastj = (w[j] > 0.f) ? j : lastj;
       ls += (double)w[j];
     }
+    if (lastj >= 0) lastpos = lo + lastj;
     const double incl = wave_inclusive_scan(ls, lane) + carry;
     const double prev = __shfl_up(incl, 1, kWave);
     const double excl = (lane == 0) ? carry : prev;
     if (t >= 0.0) {
       const uint64_t m = ballot(incl >= t);
       if (m) {
+        // Lane L's run reaches t: every lane walks L's sixteen weights, read
+        // with v_readlane (wave-uniform values, so the walk's float64
+        // conversions are not the ones of the lane sum above and those die
+        // there instead of staying live across the scan).
         const int L = first_lane(m);
-        int tok = -1;
-        if (lane == L) {
-          double cum = excl;
-          int64_t lp = -1;
+        double cum = __shfl(excl, L, kWave);
+        int tj = -1;  // first slot of positive weight whose prefix reaches t
 #pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            cum += (double)w[j];
-            if (w[j] > 0.f) lp = lo + j;
-            if (tok < 0 && w[j] > 0.f && t <= cum) tok = (int)(lo + j);
-          }
-          if (tok < 0) tok = (int)lp;  // rounding: stay inside the run that reached t
+        for (int j = 0; j < 16; ++j) {
+          const float wl = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(w[j]), L));
+          cum += (double)wl;
+          tj = (tj < 0 && wl > 0.f && t <= cum) ? j : tj;
         }
-        return __shfl(tok, L, kWave);
+        // rounding: stay inside the run that reached t (its last positive slot)
+        if (tj < 0) tj = __builtin_amdgcn_readlane(lastj, L);
+        return (tj >= 0) ? (int)(sb * kSub + (int64_t)L * 16 + tj) : -1;
       }
     }
     carry = __shfl(incl, kWave - 1, kWave);
@@ -675,14 +732,14 @@ __device__ int wave_draw(const void* trow, const void* drow, const Weights& W, i
   return -1;
 }
 
-// The final draw of sequence b by one wave: picks the sub-block that holds
-// u * total from the pass-2 masses, then walks that sub-block.
+// The final draw of one sequence by one wave: picks the sub-block that holds
+// u * total from the pass-2 masses `sub` (global or LDS), then walks that
+// sub-block.
 template <int DT, bool VEC>
-__device__ int draw_token(const DrawArgs& a, int64_t b, const Select& s, int lane) {
+__device__ int draw_token(const DrawArgs& a, const double* sub, const Select& s, int lane) {
   constexpr int64_t esz = (DT == kBF16) ? 2 : 4;
   const void* trow = static_cast<const char*>(a.target) + s.trow * a.V * esz;
   const void* drow = (s.mode == kModeResidual) ? static_cast<const char*>(a.draft) + s.drow * a.V * esz : nullptr;
-  const double* sub = a.sub + b * a.nsub;
   double total = 0.0;
   wave_scan_subs(sub, a.nsub, -1.0, lane, nullptr, &total);
   int token = -1;
@@ -721,19 +778,16 @@ __device__ int draw_token(const DrawArgs& a, int64_t b, const Select& s, int lan
 // that the draw only has to scan one sub-block. A tile (EPI = 1024 or 2048
 // elements) holds one or two sub-blocks: in the bf16 vector tile, slots
 // 0..15 of every lane lie in the first 1024 elements.
+// Pass 2 over chunk c of the selected row pair of one sequence: the weight
+// mass of every 1024-element sub-block of the chunk, stored to out[sub-block]
+// (global memory or LDS).
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kBlock) void k3_accept_mass(AcceptArgs acc, DrawArgs a) {
+__device__ __forceinline__ void chunk_masses(const DrawArgs& a, const Select& s, int c, int lane,
+                                             double* out) {
   using TL = Tile<DT, VEC>;
   constexpr int NE = TL::NE;
   constexpr int SUBS = TL::EPI / kSub;  // sub-blocks per tile (1 or 2)
   constexpr int PER = NE / SUBS;        // slots per lane per sub-block
-  const int lane = threadIdx.x & (kWave - 1);
-  const int64_t item = wave_uniform((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
-  if (item >= (int64_t)a.B * a.chunks3) return;
-  const int64_t b = item / a.chunks3;
-  const int c = (int)(item - b * a.chunks3);
-  const Select s = accept_sequence<DT>(acc, b, lane, c == 0);
-  if (s.mode == kModeNone) return;
   const Weights W = make_weights(s, false);
   constexpr int64_t esz = (DT == kBF16) ? 2 : 4;
   const void* trow = static_cast<const char*>(a.target) + s.trow * a.V * esz;
@@ -741,7 +795,6 @@ __global__ __launch_bounds__(kBlock) void k3_accept_mass(AcceptArgs acc, DrawArg
   const int64_t e0 = (int64_t)c * a.chunk3_elems, e1 = min(a.V, e0 + a.chunk3_elems);
   const int64_t n = e1 - e0;
   const int n_full = (int)(n / TL::EPI), n_iter = (int)((n + TL::EPI - 1) / TL::EPI);
-  double* out = a.sub + b * a.nsub;
   typename TL::Raw rt, rd;
   float w[NE];
   for (int it = 0; it < n_iter; ++it) {
@@ -770,6 +823,18 @@ __global__ __launch_bounds__(kBlock) void k3_accept_mass(AcceptArgs acc, DrawArg
   }
 }
 
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kBlock) void k3_accept_mass(AcceptArgs acc, DrawArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t item = wave_uniform((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
+  if (item >= (int64_t)a.B * a.chunks3) return;
+  const int64_t b = item / a.chunks3;
+  const int c = (int)(item - b * a.chunks3);
+  const Select s = uniform_select(accept_sequence<DT>(acc, b, lane, c == 0));
+  if (s.mode == kModeNone) return;
+  chunk_masses<DT, VEC>(a, s, c, lane, a.sub + b * a.nsub);
+}
+
 // The final draw: one wave per sampling sequence, in its own launch (the
 // kernel boundary orders every pass-2 store before the draw's reads).
 template <int DT, bool VEC>
@@ -779,8 +844,32 @@ __global__ __launch_bounds__(kBlock) void k4_draw(DrawArgs a) {
   if (b >= a.B) return;
   const Select s = a.sel[b];
   if (s.mode == kModeNone) return;
-  const int token = draw_token<DT, VEC>(a, b, s, lane);
+  const int token = draw_token<DT, VEC>(a, a.sub + b * a.nsub, s, lane);
   if (lane == 0) a.out_next[b] = token;
+}
+
+// Accept step, pass 2 and the final draw in one launch, one workgroup per
+// sequence with one wave per pass-2 chunk (blockDim = 64 * chunks3, at most
+// 1024). Every wave runs the same accept step (wave 0 stores it), takes the
+// masses of its chunk into LDS, and after the workgroup barrier wave 0 draws
+// from them: the barrier replaces the kernel boundary of the two-launch form,
+// and the arithmetic is the same, so both forms give the same bits. Every
+// wave reaches the barrier: the accept step's outcome is the same in all of
+// them, and nothing returns before it.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(1024) void k3_accept_mass_draw(AcceptArgs acc, DrawArgs a) {
+  extern __shared__ double sub_lds[];  // [nsub] masses of the sequence's sub-blocks
+  const int lane = threadIdx.x & (kWave - 1);
+  const int c = (int)(threadIdx.x >> 6);
+  const int64_t b = blockIdx.x;
+  const Select s = uniform_select(accept_sequence<DT>(acc, b, lane, c == 0));
+  const bool active = s.mode != kModeNone;
+  if (active) chunk_masses<DT, VEC>(a, s, c, lane, sub_lds);
+  __syncthreads();
+  if (active && c == 0) {
+    const int token = draw_token<DT, VEC>(a, sub_lds, s, lane);
+    if (lane == 0) a.out_next[b] = token;
+  }
 }
 
 // ----------------------------- test exports --------------------------------

@@ -27,6 +27,12 @@ constexpr int64_t kK1ChunkElems = SPECV_K1_CHUNK_ELEMS;  // pass-1 work item: el
 constexpr int64_t kMaxChunks1 = 16;                  // pass-1 chunks per row (at most)
 constexpr int kDrawStep = kBlock * 8; // elements per workgroup scan step of the draw
 constexpr int64_t kTargetMassItems = SPECV_MASS_WAVES;  // pass-2 waves to aim for
+// Accept step, pass 2 and draw in one launch when a sequence's pass-2 waves fit
+// one workgroup and its sub-block masses fit this much LDS.
+#ifndef SPECV_FUSED_DRAW
+#define SPECV_FUSED_DRAW 1
+#endif
+constexpr size_t kFusedDrawLds = 64 * 1024;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -37,6 +43,7 @@ struct Plan {
   int chunks1;
   int chunks3, chunk3_elems;
   int64_t nsub;
+  bool fused_draw;  // k3_accept_mass_draw instead of k3_accept_mass + k4_draw
   size_t off_toff, off_doff, off_tk, off_dk, off_tparts, off_dparts, off_sel, off_sub;
   size_t bytes;
   // per-position diagnostics (after the verify layout)
@@ -87,6 +94,8 @@ void make_plan(const specv_shape_t* s, Plan* p) {
   p->off_dparts = off; off = align_up(off + (size_t)p->td * p->chunks1 * sizeof(RowPart));
   p->off_sel = off; off = align_up(off + (size_t)p->B * sizeof(Select));
   p->nsub = (p->V + kSub - 1) / kSub;
+  p->fused_draw = SPECV_FUSED_DRAW && p->chunks3 * kWave <= 1024 &&
+                  (size_t)p->nsub * sizeof(double) <= kFusedDrawLds;
   p->off_sub = off; off = align_up(off + (size_t)p->B * p->nsub * sizeof(double));
   p->bytes = off;
 }
@@ -166,7 +175,7 @@ inline unsigned blocks_for(int64_t waves) {
 bool uniform_batch(const Plan& p) { return p.B > 0 && p.tt == p.B * (p.max_gamma + 1); }
 
 specv_status_t launch_plan(const Plan& p, const int32_t* gamma, const float* temperature, void* ws,
-                           hipStream_t st, int32_t* dseq = nullptr, bool uniform = false) {
+                           hipStream_t st, int32_t* dseq = nullptr) {
   PlanArgs a;
   a.gamma = gamma;
   a.temperature = temperature;
@@ -180,15 +189,15 @@ specv_status_t launch_plan(const Plan& p, const int32_t* gamma, const float* tem
   a.total_d = p.td;
   a.B = (int32_t)p.B;
   a.max_gamma = (int32_t)p.max_gamma;
-  if (uniform) hipLaunchKernelGGL(k0_plan_uniform, dim3(1), dim3(1024), 0, st, a);
-  else hipLaunchKernelGGL(k0_plan, dim3(1), dim3(1024), 0, st, a);
+  hipLaunchKernelGGL(k0_plan, dim3(1), dim3(1024), 0, st, a);
   return launched();
 }
 
 specv_status_t launch_row_stats(const Plan& p, bool vec, const void* target, const void* draft,
                                 void* ws, hipStream_t st, bool with_argmax = false,
                                 bool all_drafts = false, int bar_k = 0, float* bar = nullptr,
-                                const float* temperature = nullptr, bool uniform = false) {
+                                const float* temperature = nullptr, bool uniform = false,
+                                const int32_t* plan_gamma = nullptr) {
   RowStatsArgs a;
   a.target = target;
   a.draft = draft;
@@ -207,6 +216,8 @@ specv_status_t launch_row_stats(const Plan& p, bool vec, const void* target, con
   a.bar = bar;
   a.uniform_g = uniform ? (int32_t)p.max_gamma : -1;
   a.temperature = temperature;
+  a.gamma = uniform ? plan_gamma : nullptr;
+  a.status_out = at<uint32_t>(ws, 0);
   const int64_t waves = (p.tt + p.td) * p.chunks1;
   if (waves == 0) return SPECV_OK;
   const dim3 grid(blocks_for(waves)), block(kBlock);
@@ -278,6 +289,19 @@ DrawArgs draw_args(const Plan& p, const Call& c) {
 specv_status_t launch_accept_mass(const Plan& p, bool vec, const Call& c) {
   const AcceptArgs acc = accept_args(p, c);
   const DrawArgs a = draw_args(p, c);
+  if (p.fused_draw) {
+    // one workgroup per sequence, one wave per pass-2 chunk; masses in LDS
+    const dim3 grid((unsigned)p.B), block((unsigned)(p.chunks3 * kWave));
+    const size_t lds = (size_t)p.nsub * sizeof(double);
+    if (p.dt == kBF16) {
+      if (vec) hipLaunchKernelGGL((k3_accept_mass_draw<kBF16, true>), grid, block, lds, c.stream, acc, a);
+      else hipLaunchKernelGGL((k3_accept_mass_draw<kBF16, false>), grid, block, lds, c.stream, acc, a);
+    } else {
+      if (vec) hipLaunchKernelGGL((k3_accept_mass_draw<kF32, true>), grid, block, lds, c.stream, acc, a);
+      else hipLaunchKernelGGL((k3_accept_mass_draw<kF32, false>), grid, block, lds, c.stream, acc, a);
+    }
+    return launched();
+  }
   const dim3 grid(blocks_for(p.B * p.chunks3)), block(kBlock);
   if (p.dt == kBF16) {
     if (vec) hipLaunchKernelGGL((k3_accept_mass<kBF16, true>), grid, block, 0, c.stream, acc, a);
@@ -290,6 +314,7 @@ specv_status_t launch_accept_mass(const Plan& p, bool vec, const Call& c) {
 }
 
 specv_status_t launch_draw(const Plan& p, bool vec, const Call& c) {
+  if (p.fused_draw) return SPECV_OK;  // drawn by k3_accept_mass_draw
   const DrawArgs a = draw_args(p, c);
   const dim3 grid(blocks_for(p.B)), block(kBlock);
   if (p.dt == kBF16) {
@@ -312,13 +337,15 @@ specv_status_t run(const Call& c) {
   if ((c.inj_r == nullptr) != (c.inj_u == nullptr)) return SPECV_ERR_INVALID_ARGUMENT;
   const bool vec = vector_path(p, c.target, c.draft);
   const bool uniform = uniform_batch(p);
+  // A uniform batch has no plan launch: pass 1's first workgroup checks the
+  // gammas and sets the status word.
   mark(c.events, 2 * SPECV_STAGE_PLAN, c.stream);
-  if ((st = launch_plan(p, c.gamma, c.temperature, c.ws, c.stream, nullptr, uniform)) != SPECV_OK)
+  if (!uniform && (st = launch_plan(p, c.gamma, c.temperature, c.ws, c.stream)) != SPECV_OK)
     return st;
   mark(c.events, 2 * SPECV_STAGE_PLAN + 1, c.stream);
   mark(c.events, 2 * SPECV_STAGE_ROWSTATS, c.stream);
   if ((st = launch_row_stats(p, vec, c.target, c.draft, c.ws, c.stream, false, false, 0, nullptr,
-                             c.temperature, uniform)) != SPECV_OK)
+                             c.temperature, uniform, c.gamma)) != SPECV_OK)
     return st;
   mark(c.events, 2 * SPECV_STAGE_ROWSTATS + 1, c.stream);
   mark(c.events, 2 * SPECV_STAGE_ACCEPT_MASS, c.stream);
