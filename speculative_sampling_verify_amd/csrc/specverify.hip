@@ -17,13 +17,18 @@ namespace {
 
 constexpr size_t kAlign = 256;
 // Tuning constants (measured on MI355X; see the design notes).
-#ifndef SPECV_K1_CHUNK_ELEMS
-#define SPECV_K1_CHUNK_ELEMS 16384
+#ifndef SPECV_K1_CHUNK_BF16
+#define SPECV_K1_CHUNK_BF16 32768
+#endif
+#ifndef SPECV_K1_CHUNK_F32
+#define SPECV_K1_CHUNK_F32 24576
 #endif
 #ifndef SPECV_MASS_WAVES
 #define SPECV_MASS_WAVES 8192
 #endif
-constexpr int64_t kK1ChunkElems = SPECV_K1_CHUNK_ELEMS;  // pass-1 work item: elements of one row
+// pass-1 work item: about this many elements of one row (swept per dtype)
+constexpr int64_t kK1ChunkBF16 = SPECV_K1_CHUNK_BF16;
+constexpr int64_t kK1ChunkF32 = SPECV_K1_CHUNK_F32;
 constexpr int64_t kMaxChunks1 = 16;                  // pass-1 chunks per row (at most)
 constexpr int kDrawStep = kBlock * 8; // elements per workgroup scan step of the draw
 constexpr int64_t kTargetMassItems = SPECV_MASS_WAVES;  // pass-2 waves to aim for
@@ -71,10 +76,14 @@ void make_plan(const specv_shape_t* s, Plan* p) {
   p->tt = s->total_target_rows;
   p->td = s->total_draft_rows;
   p->esz = (p->dt == kBF16) ? 2 : 4;
-  // pass 1: about kK1ChunkElems elements per (row, chunk) work item, at most
-  // 16 chunks per row (the accept step merges them); a chunk is every C-th
-  // tile of its row, so C never exceeds the row's tile count
-  int64_t c1 = (p->V + kK1ChunkElems - 1) / kK1ChunkElems;
+  // pass 1: about kK1Chunk* elements per (row, chunk) work item, but two
+  // chunks at least once a row is longer than 2048 elements (two waves on
+  // a row read it faster than one), and at most 16 (the accept step merges
+  // them). A chunk is every C-th tile of its row and a tile holds at most
+  // 2048 elements, so C never exceeds the row's tile count.
+  const int64_t per = (p->dt == kBF16) ? kK1ChunkBF16 : kK1ChunkF32;
+  int64_t c1 = (p->V + per - 1) / per;
+  if (c1 < 2 && p->V > 2048) c1 = 2;
   c1 = c1 < 1 ? 1 : (c1 > kMaxChunks1 ? kMaxChunks1 : c1);
   p->chunks1 = (int)c1;
   // pass 2: enough chunks per sequence to give about kTargetMassItems waves
