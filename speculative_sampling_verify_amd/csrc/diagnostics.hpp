@@ -59,7 +59,18 @@ struct DiagArgs {
   double* out_prob;     // [total_d * K]
   int64_t total_d, V;
   int32_t chunks, K;
+  int32_t uniform_g;          // >= 0: uniform batch with this gamma; draft row j
+  const float* temperature;   // belongs to sequence j / gamma (dk, dseq unused)
 };
+
+// Sequence and temperature scale of draft row j: arithmetic in a uniform
+// batch, else from the plan's per-row arrays.
+__device__ __forceinline__ int64_t diag_seq(const DiagArgs& a, int64_t j) {
+  return (a.uniform_g > 0) ? j / a.uniform_g : (int64_t)a.dseq[j];
+}
+__device__ __forceinline__ float diag_scale(const DiagArgs& a, int64_t j, int64_t b) {
+  return (a.uniform_g > 0) ? seq_scale(a.temperature[b]) : a.dk[j];
+}
 
 // Ranking keys: larger logit first, equal logits lower index first, as one
 // unsigned 64-bit number (order-preserving float bits above the complemented
@@ -192,10 +203,11 @@ __global__ __launch_bounds__(kBlock) void k5_diag_pass(DiagArgs a) {
   const int64_t j = item / a.chunks;
   const int c = (int)(item - j * a.chunks);
   if (a.status[0] & kLayoutError) return;
-  const float k = a.dk[j];
+  const int64_t b = diag_seq(a, j);
+  const float k = diag_scale(a, j, b);
   if (!(k >= 0.f)) return;  // invalid temperature: the merge reports NaN
   const bool sampling = k > 0.f;
-  const int64_t tr = j + a.dseq[j];
+  const int64_t tr = j + b;
   const RowStat st_t = merge_row(a.tparts + tr * a.chunks, a.chunks, k, sampling);
   const RowStat st_d = merge_row(a.dparts + j * a.chunks, a.chunks, k, sampling);
   if (!st_t.valid || !st_d.valid) return;
@@ -278,16 +290,11 @@ __global__ __launch_bounds__(kBlock) void k5_diag_pass(DiagArgs a) {
       scan_group(rd, e0, std::integral_constant<int, 3>{});
     }
   };
-  // double-buffered: the loads of tile it + 1 are in flight while tile it is
-  // processed
-  Raw da, ta, db, tb;
-  fetch(0, da, ta);
-  for (int it = 0; it < n_iter; it += 2) {
-    if (it + 1 < n_iter) fetch(it + 1, db, tb);
+  // single-buffered: one tile (both rows) in flight at a time per wave
+  Raw da, ta;
+  for (int it = 0; it < n_iter; ++it) {
+    fetch(it, da, ta);
     process(da, ta, it);
-    if (it + 1 >= n_iter) break;
-    if (it + 2 < n_iter) fetch(it + 2, da, ta);
-    process(db, tb, it + 1);
   }
   const int64_t slot = j * a.chunks + c;
   if (sampling) {
@@ -310,12 +317,16 @@ __global__ __launch_bounds__(kBlock) void k5_diag_pass(DiagArgs a) {
 // One wave per position: sums the chunk partials and ranks the union of the
 // chunk lists (at most 16 * 64 keys, in LDS); a key's rank is its place in
 // the merged list. Padding entries (index INT32_MAX) take no part: the
-// chunks hold at least K real entries between them, since K <= V.
-constexpr int kMergeCap = 16 * kMaxTopK;
-constexpr int kMergeSlots = kMergeCap / kWave;
-
+// chunks hold at least K real entries between them, since K <= V. NS: 64-key
+// slots per lane, the smallest power of two with 64 NS >= chunks * K (chosen
+// at launch), so small lists keep few registers. Every load that depends
+// only on the position is issued before the checks that may end the wave.
+//
 // LDS: kWavesPerBlock buffers of chunks * K keys (rounded up to a multiple of
 // 8 keys), sized at launch.
+constexpr int kMergeCap = 16 * kMaxTopK;
+
+template <int NS>
 __global__ __launch_bounds__(kBlock) void k6_diag_merge(DiagArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint64_t merge_lds[];
   const int lane = threadIdx.x & (kWave - 1);
@@ -324,6 +335,26 @@ __global__ __launch_bounds__(kBlock) void k6_diag_merge(DiagArgs a) {
   const int64_t j = wave_uniform((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
   if (j >= a.total_d) return;
   const int K = a.K;
+  const int n = a.chunks * K;
+  const int ns = (n + kWave - 1) / kWave;
+  // independent loads
+  const uint32_t status = a.status[0];
+  const int64_t b = diag_seq(a, j);
+  const float k = diag_scale(a, j, b);
+  DiagPart part{0.0, 0.0, 0.0};
+  if (lane < a.chunks) part = a.parts[j * a.chunks + lane];
+  int32_t ids[NS];
+  float zs[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int e = lane + s * kWave;
+    ids[s] = INT32_MAX;
+    zs[s] = 0.f;
+    if (s < ns && e < n) {
+      ids[s] = a.topi[j * n + e];
+      zs[s] = a.topz[j * n + e];
+    }
+  }
   auto fail = [&]() {
     if (lane == 0) {
       a.out_alpha[j] = __builtin_nan("");
@@ -334,20 +365,17 @@ __global__ __launch_bounds__(kBlock) void k6_diag_merge(DiagArgs a) {
       a.out_prob[j * K + lane] = __builtin_nan("");
     }
   };
-  if (a.status[0] & kLayoutError) return fail();
-  const float k = a.dk[j];
+  if (status & kLayoutError) return fail();
   if (!(k >= 0.f)) return fail();
   const bool sampling = k > 0.f;
-  const int64_t tr = j + a.dseq[j];
+  const int64_t tr = j + b;
   const RowStat st_t = merge_row(a.tparts + tr * a.chunks, a.chunks, k, sampling);
   const RowStat st_d = merge_row(a.dparts + j * a.chunks, a.chunks, k, sampling);
   if (!st_t.valid || !st_d.valid) return fail();
   double alpha, entropy;
   if (sampling) {
-    DiagPart p{0.0, 0.0, 0.0};
-    if (lane < a.chunks) p = a.parts[j * a.chunks + lane];
-    alpha = wave_sum(p.alpha);
-    const double S = wave_sum(p.s), A = wave_sum(p.a);
+    alpha = wave_sum(part.alpha);
+    const double S = wave_sum(part.s), A = wave_sum(part.a);
     entropy = log(S) - 0.69314718055994530942 * A / S;
   } else {
     alpha = (st_t.arg == st_d.arg) ? 1.0 : 0.0;
@@ -358,27 +386,21 @@ __global__ __launch_bounds__(kBlock) void k6_diag_merge(DiagArgs a) {
     a.out_entropy[j] = entropy;
   }
   if (K == 0) return;
-  const int n = a.chunks * K;
-  const int ns = (n + kWave - 1) / kWave;
-  uint64_t mine[kMergeSlots];
+  uint64_t mine[NS];
 #pragma unroll
-  for (int s = 0; s < kMergeSlots; ++s) {
+  for (int s = 0; s < NS; ++s) {
     const int e = lane + s * kWave;
-    uint64_t key = 0ull;
-    if (s < ns && e < n) {
-      const int32_t id = a.topi[j * n + e];
-      if (id != INT32_MAX) key = rank_key(a.topz[j * n + e], id);
-      buf[e] = key;
-    }
+    const uint64_t key = (ids[s] != INT32_MAX) ? rank_key(zs[s], ids[s]) : 0ull;
+    if (s < ns && e < n) buf[e] = key;
     mine[s] = key;
   }
   __builtin_amdgcn_wave_barrier();
-  int rank[kMergeSlots];
+  int rank[NS];
 #pragma unroll
-  for (int s = 0; s < kMergeSlots; ++s) rank[s] = 0;
-  count_above<kMergeSlots>(buf, n, ns, mine, rank);
+  for (int s = 0; s < NS; ++s) rank[s] = 0;
+  count_above<NS>(buf, n, ns, mine, rank);
 #pragma unroll
-  for (int s = 0; s < kMergeSlots; ++s) {
+  for (int s = 0; s < NS; ++s) {
     if (s < ns && mine[s] != 0ull && rank[s] < K) {
       const float z = key_value(mine[s]);
       double q;

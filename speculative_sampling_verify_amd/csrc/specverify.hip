@@ -582,14 +582,19 @@ specv_status_t specv_position_diagnostics(const specv_shape_t* shape, const void
     return SPECV_ERR_INVALID_ARGUMENT;
   const bool vec = vector_path(p, target_logits, draft_logits);
   int32_t* dseq = at<int32_t>(workspace, p.off_dseq);
+  // A uniform batch with draft rows has no plan launch: pass 1 checks the
+  // gammas and sets the status word, and the row -> sequence map is j / gamma.
+  const bool uniform = uniform_batch(p) && p.td > 0;
   mark(events, 2 * SPECV_STAGE_PLAN, stream);
-  if ((st = launch_plan(p, gamma_per_row, temperature, workspace, stream, dseq)) != SPECV_OK)
+  if (!uniform &&
+      (st = launch_plan(p, gamma_per_row, temperature, workspace, stream, dseq)) != SPECV_OK)
     return st;
   mark(events, 2 * SPECV_STAGE_PLAN + 1, stream);
   mark(events, 2 * SPECV_STAGE_ROWSTATS, stream);
   float* bar = at<float>(workspace, p.off_bar);
   if (p.td > 0 && (st = launch_row_stats(p, vec, target_logits, draft_logits, workspace, stream,
-                                         false, true, top_k, bar)) != SPECV_OK)
+                                         false, true, top_k, bar, temperature, uniform,
+                                         gamma_per_row)) != SPECV_OK)
     return st;
   mark(events, 2 * SPECV_STAGE_ROWSTATS + 1, stream);
   DiagArgs a;
@@ -612,6 +617,8 @@ specv_status_t specv_position_diagnostics(const specv_shape_t* shape, const void
   a.V = p.V;
   a.chunks = p.chunks1;
   a.K = top_k;
+  a.uniform_g = uniform ? (int32_t)p.max_gamma : -1;
+  a.temperature = temperature;
   const dim3 grid(blocks_for(p.td * p.chunks1)), block(kBlock);
   mark(events, 2 * SPECV_STAGE_ACCEPT_MASS, stream);
   if (p.td == 0) {
@@ -627,8 +634,16 @@ specv_status_t specv_position_diagnostics(const specv_shape_t* shape, const void
   mark(events, 2 * SPECV_STAGE_ACCEPT_MASS + 1, stream);
   mark(events, 2 * SPECV_STAGE_DRAW, stream);
   const size_t merge_lds = (size_t)kWavesPerBlock * ((p.chunks1 * top_k + 7) / 8 * 8) * 8;
-  if (p.td > 0)
-    hipLaunchKernelGGL(k6_diag_merge, dim3(blocks_for(p.td)), block, merge_lds, stream, a);
+  if (p.td > 0) {
+    // 64-key slots per lane for the union of the chunk lists
+    const int n = p.chunks1 * top_k, ns = (n + kWave - 1) / kWave;
+    const dim3 mg(blocks_for(p.td));
+    if (ns <= 1) hipLaunchKernelGGL(k6_diag_merge<1>, mg, block, merge_lds, stream, a);
+    else if (ns <= 2) hipLaunchKernelGGL(k6_diag_merge<2>, mg, block, merge_lds, stream, a);
+    else if (ns <= 4) hipLaunchKernelGGL(k6_diag_merge<4>, mg, block, merge_lds, stream, a);
+    else if (ns <= 8) hipLaunchKernelGGL(k6_diag_merge<8>, mg, block, merge_lds, stream, a);
+    else hipLaunchKernelGGL(k6_diag_merge<16>, mg, block, merge_lds, stream, a);
+  }
   if ((st = launched()) != SPECV_OK) return st;
   mark(events, 2 * SPECV_STAGE_DRAW + 1, stream);
   return SPECV_OK;
