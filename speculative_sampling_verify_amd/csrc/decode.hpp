@@ -90,7 +90,12 @@ __device__ __forceinline__ void dec_load(const void* row, int64_t V, int64_t e0,
   }
 }
 
-constexpr int kDecBatch = 4;  // drafting tiles whose loads are issued together
+// Drafting tiles whose loads are issued together. One wave drafts one
+// sequence and the launch has only B waves (a few per SIMD), so registers are
+// not what limits it: a row of up to kDecBatch tiles (8192 elements) is read
+// once, with all its loads in flight together, and stays in registers for the
+// CDF walk.
+constexpr int kDecBatch = 8;
 
 // One draw from softmax(row * k) (k = log2(e)/T), or the argmax for k == 0.
 // Pass 1: per-lane online (max, sum of 2^(z k - rk)) over the row, merged
@@ -101,11 +106,9 @@ constexpr int kDecBatch = 4;  // drafting tiles whose loads are issued together
 template <int DT, bool VEC>
 __device__ int dec_sample_row(const void* row, int64_t V, float k, double u, int lane) {
   const int64_t n_tiles = (V + kDecTE - 1) / kDecTE;
-  float m = ninf(), rk = 0.f;
-  double s = 0.0;
-  int64_t arg = INT32_MAX;
-  for (int64_t t0 = 0; t0 < n_tiles; t0 += kDecBatch) {
-    float z[kDecBatch][kDecPL];
+  const bool resident = n_tiles <= kDecBatch;  // one batch: pass 2 reuses the registers
+  float z[kDecBatch][kDecPL];
+  auto load_batch = [&](int64_t t0) {
 #pragma unroll
     for (int b = 0; b < kDecBatch; ++b) {
       if (t0 + b < n_tiles) dec_load<DT, VEC>(row, V, (t0 + b) * kDecTE, lane, z[b]);
@@ -114,6 +117,12 @@ __device__ int dec_sample_row(const void* row, int64_t V, float k, double u, int
         for (int j = 0; j < kDecPL; ++j) z[b][j] = ninf();
       }
     }
+  };
+  float m = ninf(), rk = 0.f;
+  double s = 0.0;
+  int64_t arg = INT32_MAX;
+  for (int64_t t0 = 0; t0 < n_tiles; t0 += kDecBatch) {
+    load_batch(t0);
 #pragma unroll
     for (int b = 0; b < kDecBatch; ++b) {
       const float g = tile_max(z[b]);
@@ -147,15 +156,7 @@ __device__ int dec_sample_row(const void* row, int64_t V, float k, double u, int
   const double target = u * S;
   double C = 0.0;
   for (int64_t t0 = 0; t0 < n_tiles; t0 += kDecBatch) {
-    float z[kDecBatch][kDecPL];
-#pragma unroll
-    for (int b = 0; b < kDecBatch; ++b) {
-      if (t0 + b < n_tiles) dec_load<DT, VEC>(row, V, (t0 + b) * kDecTE, lane, z[b]);
-      else {
-#pragma unroll
-        for (int j = 0; j < kDecPL; ++j) z[b][j] = ninf();
-      }
-    }
+    if (!resident) load_batch(t0);
 #pragma unroll
     for (int b = 0; b < kDecBatch; ++b) {
       if (t0 + b >= n_tiles) break;
@@ -225,6 +226,206 @@ __global__ __launch_bounds__(kBlock) void k_dec_draft(DecodeArgs a) {
       if (x < 0 || (int64_t)x >= a.V) x = 0;
     }
     if (lane == 0) a.drafts[b * a.gamma + i] = x;
+    prev = x;
+  }
+}
+
+// Drafting by a workgroup of kDecWaves waves per sequence, for rows of at
+// most kDecWaves * kDecTPW tiles (8192 elements): wave w holds the tiles
+// [w tpw, (w + 1) tpw) of the row in registers (tpw = ceil(tiles / waves)),
+// so a drafted token costs one row load and three LDS exchanges:
+//   1. each wave's maximum (and its lowest index attaining it); greedy
+//      sequences take the row's argmax from these and stop here;
+//   2. weights 2^(fl32(z k - rk(M))) against the row maximum M, per-lane fp32
+//      tree sums per tile, a wave inclusive scan per tile (fp64) whose last
+//      lane is the tile's mass, and the wave's segment mass (its tiles'
+//      masses added in order); S = the segment masses added in wave order;
+//   3. the first wave whose running total reaches u * S walks its tiles and
+//      lanes in index order (the same additions, so the total is reached)
+//      and publishes the token.
+// The LDS slots alternate between two sets by token parity: a set is
+// rewritten two tokens later, after every wave has passed the barriers of
+// the token in between, so no wave can still be reading it.
+#ifndef SPECV_DEC_WAVES
+#define SPECV_DEC_WAVES 4
+#endif
+constexpr int kDecWaves = SPECV_DEC_WAVES;
+constexpr int kDecTPW = 8 / kDecWaves;
+constexpr int64_t kDecResident = (int64_t)kDecWaves * kDecTPW * kDecTE;
+
+struct DecLds {
+  float m[2][kDecWaves];
+  int32_t arg[2][kDecWaves];
+  double seg[2][kDecWaves];
+  int32_t x[2];
+};
+
+template <int DT, bool VEC>
+__device__ int wg_sample_row(const void* row, int64_t V, float k, double u, int lane, int w,
+                             int par, DecLds& sh) {
+  const int64_t n_tiles = (V + kDecTE - 1) / kDecTE;
+  const int64_t tpw = (n_tiles + kDecWaves - 1) / kDecWaves;
+  const int64_t t_lo = (int64_t)w * tpw;
+  float z[kDecTPW][kDecPL];
+#pragma unroll
+  for (int t = 0; t < kDecTPW; ++t) {
+    if (t < tpw && t_lo + t < n_tiles) dec_load<DT, VEC>(row, V, (t_lo + t) * kDecTE, lane, z[t]);
+    else {
+#pragma unroll
+      for (int j = 0; j < kDecPL; ++j) z[t][j] = ninf();
+    }
+  }
+  // 1. maxima; within a lane the index grows with t, then j
+  float m = ninf();
+  int arg = INT32_MAX;
+#pragma unroll
+  for (int t = 0; t < kDecTPW; ++t)
+#pragma unroll
+    for (int j = 0; j < kDecPL; ++j)
+      if (z[t][j] > m) {
+        m = z[t][j];
+        arg = (int)((t_lo + t) * kDecTE + (int64_t)lane * kDecPL + j);
+      }
+  const float Mw = wave_max(m);
+  const int aw = wave_min((m == Mw && m > ninf()) ? arg : INT32_MAX);
+  if (lane == 0) {
+    sh.m[par][w] = Mw;
+    sh.arg[par][w] = aw;
+  }
+  __syncthreads();
+  float M = ninf();
+#pragma unroll
+  for (int q = 0; q < kDecWaves; ++q) M = fmaxf(M, sh.m[par][q]);
+  if (k == 0.f) {
+    int best = INT32_MAX;
+#pragma unroll
+    for (int q = 0; q < kDecWaves; ++q)
+      if (sh.m[par][q] == M) best = min(best, sh.arg[par][q]);
+    return best == INT32_MAX ? 0 : best;
+  }
+  // 2. weights, tile scans and segment masses
+  const float rkM = ref_point(M, k);
+  float ls[kDecTPW];
+  double incl[kDecTPW];
+  double seg = 0.0;
+#pragma unroll
+  for (int t = 0; t < kDecTPW; ++t) {
+    float tw[kDecPL];
+#pragma unroll
+    for (int j = 0; j < kDecPL; ++j) {
+      z[t][j] = exp2_hw(__builtin_fmaf(z[t][j], k, -rkM));  // the weight, in place
+      tw[j] = z[t][j];
+    }
+    ls[t] = tree_sum(tw);
+    incl[t] = wave_inclusive_scan((double)ls[t], lane);
+    seg += __shfl(incl[t], kWave - 1, kWave);
+  }
+  if (lane == 0) sh.seg[par][w] = seg;
+  __syncthreads();
+  double S = 0.0, Cw = 0.0;
+  int hw = -1;
+#pragma unroll
+  for (int q = 0; q < kDecWaves; ++q) {
+    if (q == w) Cw = S;
+    S += sh.seg[par][q];
+  }
+  const double target = u * S;
+  {
+    double C = 0.0;
+#pragma unroll
+    for (int q = 0; q < kDecWaves; ++q) {
+      if (hw < 0 && sh.seg[par][q] > 0.0 && C + sh.seg[par][q] >= target) hw = q;
+      C += sh.seg[par][q];
+    }
+  }
+  // 3. the walk in the wave that holds the target: its first tile whose
+  // running total reaches it, else (rounding: the segment mass was added as
+  // one number) its last tile of positive mass, then the lane and the slot
+  // likewise
+  if (w == hw) {
+    int tsel = -1, tlast = -1;
+    double Csel = 0.0, Clast = 0.0, C = Cw;
+#pragma unroll
+    for (int t = 0; t < kDecTPW; ++t) {
+      const double tot = __shfl(incl[t], kWave - 1, kWave);
+      if (tot > 0.0) {
+        if (tsel < 0 && C + tot >= target) {
+          tsel = t;
+          Csel = C;
+        }
+        tlast = t;
+        Clast = C;
+      }
+      C += tot;
+    }
+    if (tsel < 0) {
+      tsel = tlast;
+      Csel = Clast;
+    }
+    int tok = 0;
+#pragma unroll
+    for (int t = 0; t < kDecTPW; ++t) {
+      if (t != tsel) continue;
+      const uint64_t hit = ballot(Csel + incl[t] >= target);
+      const uint64_t pos = ballot(ls[t] > 0.f);
+      const int L = hit ? first_lane(hit) : 63 - __builtin_clzll(pos);
+      double ex = __shfl_up(incl[t], 1, kWave);
+      if (lane == 0) ex = 0.0;
+      int tl = -1;
+      if (lane == L) {
+        double c = Csel + ex;
+        int lastj = -1;
+#pragma unroll
+        for (int j = 0; j < kDecPL; ++j) {
+          if (z[t][j] > 0.f) lastj = j;
+          c += (double)z[t][j];
+          if (tl < 0 && z[t][j] > 0.f && c >= target) tl = j;
+        }
+        if (tl < 0) tl = lastj < 0 ? 0 : lastj;
+        tl = (int)((t_lo + t) * kDecTE + (int64_t)lane * kDecPL + tl);
+      }
+      tok = __shfl(tl, L, kWave);
+    }
+    if (lane == 0) sh.x[par] = tok;
+  }
+  __syncthreads();
+  return (hw < 0) ? 0 : sh.x[par];  // no mass at all (unusable row): token 0
+}
+
+// One workgroup of kDecWaves waves per sequence (grid = B workgroups). Every
+// wave runs the same loop and reaches every barrier: gamma, the temperature
+// and the drafted tokens are the same in all of them.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kDecWaves * kWave) void k_dec_draft_wg(DecodeArgs a) {
+  constexpr int64_t esz = (DT == kBF16) ? 2 : 4;
+  __shared__ DecLds sh;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = (int)(threadIdx.x >> 6);
+  const int64_t b = blockIdx.x;
+  const float T = a.temperature[b];
+  const bool sampling = T > 0.f && T < pinf();
+  const bool greedy = T == 0.f;
+  const float k = sampling ? temp_scale(T) : 0.f;
+  const uint64_t prow = a.row_base + (uint64_t)b;
+  const bool lead = (threadIdx.x == 0);
+  int32_t prev = a.cur[b];
+  for (int i = 0; i <= a.gamma; ++i) {
+    if (lead) a.trow_src[b * (a.gamma + 1) + i] = prev;
+    if (i == a.gamma) break;
+    if (lead) a.drow_src[b * a.gamma + i] = prev;
+    int x = 0;  // an invalid temperature drafts token 0; the verify step fails the sequence
+    if (sampling || greedy) {
+      double u = 0.0;
+      if (sampling) {
+        const PhiloxBlock pw = philox4x32_10(a.seed, (uint32_t)prow, (uint32_t)(prow >> 32),
+                                             (uint32_t)i, 1u);
+        u = (double)uniform24(pw.w0);
+      }
+      const void* row = static_cast<const char*>(a.dtab) + (int64_t)prev * a.V * esz;
+      x = wg_sample_row<DT, VEC>(row, a.V, k, u, lane, w, i & 1, sh);
+      if (x < 0 || (int64_t)x >= a.V) x = 0;
+    }
+    if (lead) a.drafts[b * a.gamma + i] = x;
     prev = x;
   }
 }

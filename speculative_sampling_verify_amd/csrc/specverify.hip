@@ -649,6 +649,29 @@ specv_status_t specv_position_diagnostics(const specv_shape_t* shape, const void
   return SPECV_OK;
 }
 
+// Drafting of one round: a workgroup per sequence when its rows fit the
+// workgroup's registers (V <= 8192), else one wave per sequence streaming the row.
+specv_status_t launch_draft(bool bf16, bool vec, const DecodeArgs& a, int64_t B, hipStream_t stream) {
+  const dim3 block(kBlock);
+  if (a.V <= kDecResident) {
+    const dim3 g((unsigned)B), wg(kDecWaves * kWave);
+    if (bf16) {
+      if (vec) hipLaunchKernelGGL((k_dec_draft_wg<kBF16, true>), g, wg, 0, stream, a);
+      else hipLaunchKernelGGL((k_dec_draft_wg<kBF16, false>), g, wg, 0, stream, a);
+    } else {
+      if (vec) hipLaunchKernelGGL((k_dec_draft_wg<kF32, true>), g, wg, 0, stream, a);
+      else hipLaunchKernelGGL((k_dec_draft_wg<kF32, false>), g, wg, 0, stream, a);
+    }
+  } else if (bf16) {
+    if (vec) hipLaunchKernelGGL((k_dec_draft<kBF16, true>), dim3(blocks_for(B)), block, 0, stream, a);
+    else hipLaunchKernelGGL((k_dec_draft<kBF16, false>), dim3(blocks_for(B)), block, 0, stream, a);
+  } else {
+    if (vec) hipLaunchKernelGGL((k_dec_draft<kF32, true>), dim3(blocks_for(B)), block, 0, stream, a);
+    else hipLaunchKernelGGL((k_dec_draft<kF32, false>), dim3(blocks_for(B)), block, 0, stream, a);
+  }
+  return launched();
+}
+
 size_t specv_decode_workspace_bytes(const specv_decode_shape_t* shape) {
   if (!decode_shape_ok(shape)) return 0;
   DecodePlan d;
@@ -724,14 +747,7 @@ specv_status_t specv_decode_bigram(const specv_decode_shape_t* shape, const void
     const bool last = r + 1 == R;
     hipEvent_t* ev = last ? events : nullptr;
     mark(ev, 2 * SPECV_STAGE_PLAN, stream);
-    if (shape->dtype == SPECV_BF16) {
-      if (vec) hipLaunchKernelGGL((k_dec_draft<kBF16, true>), dim3(blocks_for(B)), block, 0, stream, a);
-      else hipLaunchKernelGGL((k_dec_draft<kBF16, false>), dim3(blocks_for(B)), block, 0, stream, a);
-    } else {
-      if (vec) hipLaunchKernelGGL((k_dec_draft<kF32, true>), dim3(blocks_for(B)), block, 0, stream, a);
-      else hipLaunchKernelGGL((k_dec_draft<kF32, false>), dim3(blocks_for(B)), block, 0, stream, a);
-    }
-    if ((st = launched()) != SPECV_OK) return st;
+    if ((st = launch_draft(shape->dtype == SPECV_BF16, vec, a, B, stream)) != SPECV_OK) return st;
     mark(ev, 2 * SPECV_STAGE_PLAN + 1, stream);
     mark(ev, 2 * SPECV_STAGE_ROWSTATS, stream);
     if (vec) hipLaunchKernelGGL((k_dec_gather<true>), dim3(blocks_for(gather_waves)), block, 0, stream, ga);
@@ -870,14 +886,7 @@ specv_status_t specv_cascade_bigram(const specv_cascade_shape_t* shape, const vo
       hipEvent_t* ev = (last && j == 0) ? events : nullptr;  // the last round's first inner round
       di.row_base = philox_row_offset + (uint64_t)((r * (k1 + 1) + 1 + j) * B);
       mark(ev, 2 * SPECV_STAGE_PLAN, stream);
-      if (bf16) {
-        if (vec) hipLaunchKernelGGL((k_dec_draft<kBF16, true>), dim3(blocks_for(B)), block, 0, stream, di);
-        else hipLaunchKernelGGL((k_dec_draft<kBF16, false>), dim3(blocks_for(B)), block, 0, stream, di);
-      } else {
-        if (vec) hipLaunchKernelGGL((k_dec_draft<kF32, true>), dim3(blocks_for(B)), block, 0, stream, di);
-        else hipLaunchKernelGGL((k_dec_draft<kF32, false>), dim3(blocks_for(B)), block, 0, stream, di);
-      }
-      if ((st = launched()) != SPECV_OK) return st;
+      if ((st = launch_draft(bf16, vec, di, B, stream)) != SPECV_OK) return st;
       mark(ev, 2 * SPECV_STAGE_PLAN + 1, stream);
       mark(ev, 2 * SPECV_STAGE_ROWSTATS, stream);
       const int64_t gw = (ga.n_t + ga.n_d) * ga.pieces;

@@ -114,6 +114,17 @@ def test_decode_parity_odd_vocab_and_bad_starts(svx):
     assert got["length"][3] == -1 and got["length"][10] == -1
 
 
+def test_decode_parity_streamed_rows(svx):
+    # V = 9000: rows longer than the 8192 elements a drafting workgroup holds in
+    # registers, so each sequence is drafted by one wave that streams its row
+    t, d = tables(9000, 8)
+    B = 48
+    rng = np.random.default_rng(9)
+    T = np.where(np.arange(B) % 3 == 0, 0.0, 0.9).astype(np.float32)
+    assert_decode_parity("bf16 V=9000", svx, to_bf16_bits(t), to_bf16_bits(d), T,
+                         rng.integers(0, 9000, B), gamma=4, rounds=3, seed=21)
+
+
 def test_decode_gpu_sequence_law(svx):
     # the GPU loop's own output: joint of the first three tokens vs the chain
     t, d = tables(5, 0)
