@@ -125,15 +125,22 @@ __device__ __forceinline__ void cas_store8(float* row, int64_t V, int64_t v0, co
   }
 }
 
-// T ln Q in float64 from the exact binary exponent of Q and v_log_f32 of its
-// mantissa in [1, 2): the error is absolute (about 1e-7 T), below the fp32
-// rounding of the result.
-__device__ __forceinline__ float t_ln(double Q, double T_ln2) {
-  if (!(Q > 0.0)) return ninf();
-  int e;
-  const double mant = frexp(Q, &e);  // Q = mant * 2^e, mant in [0.5, 1)
-  const float l = __builtin_amdgcn_logf((float)(2.0 * mant));  // log2 of [1, 2)
-  return (float)(T_ln2 * ((double)(e - 1) + (double)l));
+// T ln Q in fp32: v_log_f32 (log2, within about 1 ulp) times T ln 2. A
+// subnormal Q is scaled by 2^64 first (the hardware logarithm flushes
+// subnormal inputs); Q <= 0 gives -inf.
+__device__ __forceinline__ float t_ln32(float Q, float T_ln2) {
+  if (!(Q > 0.f)) return ninf();
+  const float l = (Q < 1.17549435e-38f) ? __builtin_amdgcn_logf(Q * 0x1p64f) - 64.f
+                                        : __builtin_amdgcn_logf(Q);
+  return T_ln2 * l;
+}
+
+// f(p, eps) in fp32 for the row builder: p / eps and p / eps^2 as products
+// with the reciprocal, p^eps = 2^(eps log2 p) on the transcendental unit.
+__device__ __forceinline__ float lenient32(float p, int32_t kind, float eps, float inv) {
+  if (kind == kLenLin || kind == kLenSq) return p * inv;
+  if (kind == kLenExp) return (p > 0.f) ? exp2_hw(eps * __builtin_amdgcn_logf(p)) : 0.f;
+  return p;
 }
 
 // One wave per (sequence, position i <= k1): the target row of position i
@@ -209,29 +216,36 @@ __global__ __launch_bounds__(kBlock) void k_cas_outer_rows(CascadeArgs a) {
   const float R1 = ref_point(M1, k), R2 = ref_point(M2, k);
   const double S1 = wave_sum((m1 == ninf()) ? 0.0 : s1 * exp2((double)(m1 * k) - (double)R1));
   const double S2 = wave_sum((m2 == ninf()) ? 0.0 : s2 * exp2((double)(m2 * k) - (double)R2));
-  const double i1 = 1.0 / S1, i2 = 1.0 / S2;
-  auto probs = [&](float z1, float z2, double& p1, double& q2) {
-    p1 = (double)exp2_hw(__builtin_fmaf(z1, k, -R1)) * i1;
-    q2 = (double)exp2_hw(__builtin_fmaf(z2, k, -R2)) * i2;
+  // Passes 2 and 3 work per element in fp32 (p1 and q2 come from fp32
+  // terms already) and add in fp64 per lane: the rows are fp32, and the
+  // error stays near 1e-7 relative.
+  const float i1 = (float)(1.0 / S1), i2 = (float)(1.0 / S2);
+  const float inv = (a.lenience == kLenLin) ? (float)(1.0 / (double)a.eps)
+                    : (a.lenience == kLenSq) ? (float)(1.0 / ((double)a.eps * (double)a.eps)) : 1.f;
+  auto probs = [&](float z1, float z2, float& p1, float& q2) {
+    p1 = exp2_hw(__builtin_fmaf(z1, k, -R1)) * i1;
+    q2 = exp2_hw(__builtin_fmaf(z2, k, -R2)) * i2;
   };
   // pass 2: beta = sum min(q2, f(p1)) and the residual mass sum max(0, p1 - q2)
   double beta = 0.0, rmass = 0.0;
   for (int64_t v0 = (int64_t)lane * 8; v0 < V; v0 += kStep) {
-    float z1[8], z2[8];
+    float z1[8], z2[8], bb[8], rr[8];
     cas_load8<DT, VEC>(r1, V, v0, z1);
     cas_load8<DT, VEC>(r2, V, v0, z2);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      double p1, q2;
+      float p1, q2;
       probs(z1[j], z2[j], p1, q2);
-      beta += fmin(q2, lenient(p1, a.lenience, a.eps));
-      rmass += fmax(p1 - q2, 0.0);
+      bb[j] = fminf(q2, lenient32(p1, a.lenience, a.eps, inv));
+      rr[j] = fmaxf(p1 - q2, 0.f);
     }
+    beta += (double)tree_sum(bb);
+    rmass += (double)tree_sum(rr);
   }
   beta = wave_sum(beta);
   rmass = wave_sum(rmass);
-  const double c = (rmass > 0.0) ? (1.0 - beta) / rmass : 0.0;
-  const double T_ln2 = (double)T * 0.69314718055994530942;
+  const float c = (rmass > 0.0) ? (float)((1.0 - beta) / rmass) : 0.f;
+  const float T_ln2 = (float)((double)T * 0.69314718055994530942);
   // pass 3: Q and the row fl32(T ln Q)
   for (int64_t v0 = (int64_t)lane * 8; v0 < V; v0 += kStep) {
     float z1[8], z2[8], o[8];
@@ -239,10 +253,10 @@ __global__ __launch_bounds__(kBlock) void k_cas_outer_rows(CascadeArgs a) {
     cas_load8<DT, VEC>(r2, V, v0, z2);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      double p1, q2;
+      float p1, q2;
       probs(z1[j], z2[j], p1, q2);
-      const double Q = fmin(q2, lenient(p1, a.lenience, a.eps)) + c * fmax(p1 - q2, 0.0);
-      o[j] = t_ln(Q, T_ln2);
+      const float Q = fminf(q2, lenient32(p1, a.lenience, a.eps, inv)) + c * fmaxf(p1 - q2, 0.f);
+      o[j] = t_ln32(Q, T_ln2);
     }
     cas_store8<VEC>(out, V, v0, o);
   }
