@@ -23,6 +23,9 @@ constexpr size_t kAlign = 256;
 #ifndef SPECV_K1_CHUNK_F32
 #define SPECV_K1_CHUNK_F32 24576
 #endif
+#ifndef SPECV_K1_TWO_CHUNKS_ABOVE
+#define SPECV_K1_TWO_CHUNKS_ABOVE 2048
+#endif
 #ifndef SPECV_MASS_WAVES
 #define SPECV_MASS_WAVES 8192
 #endif
@@ -83,7 +86,7 @@ void make_plan(const specv_shape_t* s, Plan* p) {
   // 2048 elements, so C never exceeds the row's tile count.
   const int64_t per = (p->dt == kBF16) ? kK1ChunkBF16 : kK1ChunkF32;
   int64_t c1 = (p->V + per - 1) / per;
-  if (c1 < 2 && p->V > 2048) c1 = 2;
+  if (c1 < 2 && p->V > SPECV_K1_TWO_CHUNKS_ABOVE) c1 = 2;
   c1 = c1 < 1 ? 1 : (c1 > kMaxChunks1 ? kMaxChunks1 : c1);
   p->chunks1 = (int)c1;
   // pass 2: enough chunks per sequence to give about kTargetMassItems waves
