@@ -262,4 +262,173 @@ __global__ __launch_bounds__(kBlock) void k_cas_outer_rows(CascadeArgs a) {
   }
 }
 
+// The same rows by a workgroup of kCasWaves waves per (sequence, position),
+// for V <= kCasResident: wave w holds the 512-element steps w, w + W, ... of
+// both drafter rows in registers, so each row is read once and each weight
+// formed once; the passes exchange per-wave results through LDS:
+//   1. the rows' maxima M1, M2;
+//   2. the weights 2^(fl32(z k - rk(M))) in place, and S1, S2 (per-lane fp32
+//      tree sums of eight, fp64 lane and wave sums, the waves added in order);
+//   3. beta and the residual mass from p1 = t1 fl32(1/S1), q2 = t2 fl32(1/S2);
+// then each wave writes its steps of fl32(T ln Q). Every early return depends
+// only on (sequence, position) and comes before the first barrier.
+constexpr int kCasWaves = 4;
+constexpr int kCasSteps = 4;
+constexpr int64_t kCasResident = (int64_t)kCasWaves * kCasSteps * kWave * 8;
+
+struct CasLds {
+  float m1[kCasWaves], m2[kCasWaves];
+  double s1[kCasWaves], s2[kCasWaves], beta[kCasWaves], rmass[kCasWaves];
+};
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kCasWaves * kWave) void k_cas_outer_rows_wg(CascadeArgs a) {
+  __shared__ CasLds sh;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = (int)(threadIdx.x >> 6);
+  const int64_t item = blockIdx.x;
+  const int64_t b = item / (a.k1 + 1);
+  const int i = (int)(item - b * (a.k1 + 1));
+  const int64_t V = a.V;
+  constexpr int64_t kStep = kWave * 8;
+  const int64_t n_steps = (V + kStep - 1) / kStep;
+  constexpr int64_t esz = (DT == kBF16) ? 2 : 4;
+  const int32_t prev = (i == 0) ? a.cur[b] : a.dtok[b * a.dcap + i - 1];
+  auto copy_row = [&](const void* src, float* dst) {
+    for (int64_t st = w; st < n_steps; st += kCasWaves) {
+      float z[8];
+      cas_load8<DT, VEC>(src, V, st * kStep + (int64_t)lane * 8, z);
+      cas_store8<VEC>(dst, V, st * kStep + (int64_t)lane * 8, z);
+    }
+  };
+  copy_row(static_cast<const char*>(a.ttab) + (int64_t)prev * V * esz,
+           a.otpack + (b * (a.k1 + 1) + i) * V);
+  if (i == a.k1) return;
+  if (threadIdx.x == 0) a.otok[b * a.k1 + i] = a.dtok[b * a.dcap + i];
+  float* out = a.odpack + (b * a.k1 + i) * V;
+  const float T = a.temperature[b];
+  const bool sampling = T > 0.f && T < pinf();
+  if (!sampling || a.fail[b]) {
+    const float zero[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int64_t st = w; st < n_steps; st += kCasWaves)
+      cas_store8<VEC>(out, V, st * kStep + (int64_t)lane * 8, zero);
+    return;  // not read (greedy or failed)
+  }
+  const int32_t pv = a.dprev[b * a.dcap + i];
+  const void* r1 = static_cast<const char*>(a.m1tab) + (int64_t)pv * V * esz;
+  if (a.dbonus[b * a.dcap + i]) {  // Q = p1: the m1 row itself
+    copy_row(r1, out);
+    return;
+  }
+  const void* r2 = static_cast<const char*>(a.m2tab) + (int64_t)pv * V * esz;
+  const float k = temp_scale(T);
+  float z1[kCasSteps][8], z2[kCasSteps][8];
+#pragma unroll
+  for (int q = 0; q < kCasSteps; ++q) {
+    const int64_t st = w + (int64_t)q * kCasWaves;
+    if (st < n_steps) {
+      cas_load8<DT, VEC>(r1, V, st * kStep + (int64_t)lane * 8, z1[q]);
+      cas_load8<DT, VEC>(r2, V, st * kStep + (int64_t)lane * 8, z2[q]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) z1[q][j] = z2[q][j] = ninf();
+    }
+  }
+  // 1. maxima
+  float m1 = ninf(), m2 = ninf();
+#pragma unroll
+  for (int q = 0; q < kCasSteps; ++q) {
+    m1 = fmaxf(m1, tile_max(z1[q]));
+    m2 = fmaxf(m2, tile_max(z2[q]));
+  }
+  m1 = wave_max(m1);
+  m2 = wave_max(m2);
+  if (lane == 0) {
+    sh.m1[w] = m1;
+    sh.m2[w] = m2;
+  }
+  __syncthreads();
+  float M1 = ninf(), M2 = ninf();
+#pragma unroll
+  for (int q = 0; q < kCasWaves; ++q) {
+    M1 = fmaxf(M1, sh.m1[q]);
+    M2 = fmaxf(M2, sh.m2[q]);
+  }
+  const float R1 = ref_point(M1, k), R2 = ref_point(M2, k);
+  // 2. weights in place and the row sums
+  double s1 = 0.0, s2 = 0.0;
+#pragma unroll
+  for (int q = 0; q < kCasSteps; ++q) {
+    float e1[8], e2[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      z1[q][j] = exp2_hw(__builtin_fmaf(z1[q][j], k, -R1));
+      z2[q][j] = exp2_hw(__builtin_fmaf(z2[q][j], k, -R2));
+      e1[j] = z1[q][j];
+      e2[j] = z2[q][j];
+    }
+    s1 += (double)tree_sum(e1);
+    s2 += (double)tree_sum(e2);
+  }
+  s1 = wave_sum(s1);
+  s2 = wave_sum(s2);
+  if (lane == 0) {
+    sh.s1[w] = s1;
+    sh.s2[w] = s2;
+  }
+  __syncthreads();
+  double S1 = 0.0, S2 = 0.0;
+#pragma unroll
+  for (int q = 0; q < kCasWaves; ++q) {
+    S1 += sh.s1[q];
+    S2 += sh.s2[q];
+  }
+  const float i1 = (float)(1.0 / S1), i2 = (float)(1.0 / S2);
+  const float inv = (a.lenience == kLenLin) ? (float)(1.0 / (double)a.eps)
+                    : (a.lenience == kLenSq) ? (float)(1.0 / ((double)a.eps * (double)a.eps)) : 1.f;
+  // 3. beta and the residual mass
+  double beta = 0.0, rmass = 0.0;
+#pragma unroll
+  for (int q = 0; q < kCasSteps; ++q) {
+    float bb[8], rr[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float p1 = z1[q][j] * i1, q2 = z2[q][j] * i2;
+      bb[j] = fminf(q2, lenient32(p1, a.lenience, a.eps, inv));
+      rr[j] = fmaxf(p1 - q2, 0.f);
+    }
+    beta += (double)tree_sum(bb);
+    rmass += (double)tree_sum(rr);
+  }
+  beta = wave_sum(beta);
+  rmass = wave_sum(rmass);
+  if (lane == 0) {
+    sh.beta[w] = beta;
+    sh.rmass[w] = rmass;
+  }
+  __syncthreads();
+  double B = 0.0, Rm = 0.0;
+#pragma unroll
+  for (int q = 0; q < kCasWaves; ++q) {
+    B += sh.beta[q];
+    Rm += sh.rmass[q];
+  }
+  const float c = (Rm > 0.0) ? (float)((1.0 - B) / Rm) : 0.f;
+  const float T_ln2 = (float)((double)T * 0.69314718055994530942);
+  // the row fl32(T ln Q)
+#pragma unroll
+  for (int q = 0; q < kCasSteps; ++q) {
+    const int64_t st = w + (int64_t)q * kCasWaves;
+    if (st >= n_steps) break;
+    float o[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float p1 = z1[q][j] * i1, q2 = z2[q][j] * i2;
+      const float Q = fminf(q2, lenient32(p1, a.lenience, a.eps, inv)) + c * fmaxf(p1 - q2, 0.f);
+      o[j] = t_ln32(Q, T_ln2);
+    }
+    cas_store8<VEC>(out, V, st * kStep + (int64_t)lane * 8, o);
+  }
+}
+
 }  // namespace specv

@@ -914,7 +914,17 @@ specv_status_t specv_cascade_bigram(const specv_cascade_shape_t* shape, const vo
     // fp32 review rows are 16-byte aligned when V is a multiple of 4 (table
     // rows: a 16-byte multiple, the same condition as the gather's)
     const bool ovec = vec && shape->vocab % 4 == 0 && aligned(target_table, 16);
-    if (bf16) {
+    if (shape->vocab <= kCasResident) {
+      // a workgroup per (sequence, position): both drafter rows stay in registers
+      const dim3 g((unsigned)ow), wg(kCasWaves * kWave);
+      if (bf16) {
+        if (ovec) hipLaunchKernelGGL((k_cas_outer_rows_wg<kBF16, true>), g, wg, 0, stream, ca);
+        else hipLaunchKernelGGL((k_cas_outer_rows_wg<kBF16, false>), g, wg, 0, stream, ca);
+      } else {
+        if (ovec) hipLaunchKernelGGL((k_cas_outer_rows_wg<kF32, true>), g, wg, 0, stream, ca);
+        else hipLaunchKernelGGL((k_cas_outer_rows_wg<kF32, false>), g, wg, 0, stream, ca);
+      }
+    } else if (bf16) {
       if (ovec) hipLaunchKernelGGL((k_cas_outer_rows<kBF16, true>), dim3(blocks_for(ow)), block, 0, stream, ca);
       else hipLaunchKernelGGL((k_cas_outer_rows<kBF16, false>), dim3(blocks_for(ow)), block, 0, stream, ca);
     } else {

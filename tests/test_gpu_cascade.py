@@ -134,3 +134,15 @@ def test_cascade_parity_scalar_rows(svx):
     start = np.random.default_rng(9).integers(0, 999, B)
     assert_cascade_parity("bf16 V=999 lin 0.4", svx, tabs, np.full(B, 0.9, np.float32), start,
                           k1=3, k2=2, rounds=3, lenience="lin", epsilon=0.4, seed=12)
+
+
+def test_cascade_parity_streamed_rows(svx):
+    # V = 9000: rows longer than the 8192 elements a workgroup holds in
+    # registers, so drafting and the target review's row builder take their
+    # one-wave streaming kernels
+    tabs = [bf16(t) for t in tables(9000, 10)]
+    B = 32
+    T = np.where(np.arange(B) % 4 == 0, 0.0, 1.0).astype(np.float32)
+    start = np.random.default_rng(11).integers(0, 9000, B)
+    assert_cascade_parity("bf16 V=9000 sq 0.5", svx, tabs, T, start, k1=3, k2=2, rounds=2,
+                          lenience="sq", epsilon=0.5, seed=13)
