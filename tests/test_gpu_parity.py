@@ -290,6 +290,23 @@ def test_gamma_zero_mixed_temperatures_and_ties(svx):
         parity_case(svx, "gamma 0..4, T in {0, .5, 1, 2}, ties, masks (%s)" % dt, x)
 
 
+def test_uniform_gamma_zero_batch(svx):
+    # every gamma 0: a uniform batch with no draft rows, so pass 1 covers the
+    # target rows only and its first workgroup still sets the status word;
+    # each sequence emits one token drawn from p_0 (argmax when greedy)
+    rng = np.random.default_rng(23)
+    V = 5000
+    seqs = [{"target": (rng.standard_normal((1, V)) * 2).astype(np.float32),
+             "draft": np.zeros((0, V), np.float32), "tokens": [],
+             "T": [1.0, 0.0, 0.7][b % 3]} for b in range(300)]
+    for dt in ("bf16", "f32"):
+        x = pack(seqs, V, dt)
+        x.max_gamma = 0
+        x.seed, x.row_offset = 9, 77
+        got, _ = parity_case(svx, "uniform gamma 0, B=300 (%s)" % dt, x, repeat=False)
+        assert (got[0] == 0).all() and got[2] == 0
+
+
 def test_data_errors(svx):
     V = 64
     rng = np.random.default_rng(2)
