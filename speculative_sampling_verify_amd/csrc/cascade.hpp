@@ -11,8 +11,9 @@
 //   from an inner position i < k2: Q = min(q2, f(p1)) + (1 - beta) *
 //     norm(max(0, p1 - q2)), beta = sum_v min(q2(v), f(p1(v)));
 //   from the inner bonus position: Q = p1 (the m1 row itself serves).
-// k_cas_outer_rows writes the target review's fp32 rows: the target table
-// rows, and draft rows fl32(T ln Q) so that softmax(row / T) = Q.
+// k_cas_outer_rows_wg (V <= 8192; else k_cas_outer_rows) writes the target
+// review's fp32 rows: the target table rows, and draft rows fl32(T ln Q) so
+// that softmax(row / T) = Q.
 #pragma once
 
 #include "decode.hpp"

@@ -3,7 +3,8 @@
 // The step of DistillSpec Algorithm A.1 repeated over rounds, with models
 // that are bigram tables: the logits of the next token after token s are row
 // s of a [V, V] table (one for the target, one for the draft). One round:
-//   k_dec_draft   one wave per sequence drafts gamma tokens autoregressively
+//   k_dec_draft_wg  (V <= 8192; else k_dec_draft, one wave per sequence)
+//                 a workgroup per sequence drafts gamma tokens autoregressively
 //                 from softmax(draft row / T) by inverse CDF in index order
 //                 (u = word 0 of Philox(seed; row, i, 1)), or by argmax when
 //                 T = 0, and records which table row feeds each packed row;
