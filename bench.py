@@ -100,6 +100,27 @@ def copy_gbps(torch, svx, dev, nbytes=1 << 30):
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
+def read_gbps(torch, svx, dev, nbytes=1536 << 20):
+    """Read bandwidth of the library's read probe: pass 1's access pattern
+    (64 KiB segments, two sibling waves on alternate 4 KiB tiles) with no
+    arithmetic, over a buffer of the size pass 1 reads; context for how close
+    pass 1 comes to what this pattern reaches on the part."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    sink = torch.empty(nbytes // 32768, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        svx.specv_read_bytes(src, sink)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(10):
+        svx.specv_read_bytes(src, sink)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / 10
+    del src, sink
+    return nbytes / (ms * 1e-3) / 1e9
+
+
 def cpu_baseline(x, gpu_n, gpu_next, budget_s=12.0, lenience="none", epsilon=1.0):
     """The oracle as it stands, on the host's cores, over repeated passes of
     the same step's sequences (bounded by a time budget)."""
@@ -581,6 +602,9 @@ def main():
     cg = copy_gbps(torch, svx, dev)
     result["copy_gbps"] = cg
     result["roofline"]["frac_of_copy"] = achieved / cg
+    rg = read_gbps(torch, svx, dev)
+    result["read_probe_gbps"] = rg
+    result["roofline"]["frac_of_read_probe"] = achieved / rg
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on the host")
         result["cpu_baseline"] = cpu_baseline(x, n_host, next_host, lenience=args.lenience,

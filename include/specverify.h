@@ -337,6 +337,16 @@ specv_status_t specv_philox4x32_10(uint64_t seed, const uint32_t* ctr, uint32_t*
  * calibration kernel for memory counters and copy bandwidth. */
 specv_status_t specv_copy_bytes(void* dst, const void* src, size_t bytes, hipStream_t stream);
 
+/* Read-only stream of `bytes` bytes at src (device, 16-byte aligned; bytes a
+ * multiple of 65,536) with the access pattern of pass 1: each 64 KiB segment
+ * is read by two sibling waves taking alternate 4 KiB tiles with 16-byte
+ * non-temporal loads. sink (device, bytes / 32,768 words) receives one XOR
+ * checksum of the dwords each wave read: wave 2s + h of segment s reads its
+ * tiles h, h + 2, ..., h + 14. A calibration kernel: the read bandwidth this
+ * part reaches with that pattern. Invalid sizes or pointers return
+ * SPECV_ERR_INVALID_ARGUMENT before anything is enqueued. */
+specv_status_t specv_read_bytes(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 const char* specv_status_string(specv_status_t status);
 
 #ifdef __cplusplus

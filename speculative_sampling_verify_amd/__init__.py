@@ -83,6 +83,8 @@ _lib.specv_philox4x32_10.restype = ctypes.c_int
 _lib.specv_philox4x32_10.argtypes = [_u64, _P, _P, _i64, _P]
 _lib.specv_copy_bytes.restype = ctypes.c_int
 _lib.specv_copy_bytes.argtypes = [_P, _P, _sz, _P]
+_lib.specv_read_bytes.restype = ctypes.c_int
+_lib.specv_read_bytes.argtypes = [_P, _sz, _P, _P]
 _lib.specv_status_string.restype = ctypes.c_char_p
 _lib.specv_status_string.argtypes = [ctypes.c_int]
 
@@ -91,7 +93,7 @@ EXPORTED = ("specv_workspace_bytes", "specv_verify", "specv_verify_profiled",
             "specv_diagnostics_workspace_bytes", "specv_position_diagnostics",
             "specv_decode_workspace_bytes", "specv_decode_bigram",
             "specv_cascade_workspace_bytes", "specv_cascade_bigram", "specv_row_stats", "specv_softmax_rows",
-            "specv_philox4x32_10", "specv_copy_bytes", "specv_status_string")
+            "specv_philox4x32_10", "specv_copy_bytes", "specv_read_bytes", "specv_status_string")
 
 
 class SpecvError(RuntimeError):
@@ -425,6 +427,18 @@ def specv_copy_bytes(dst, src, stream=None):
     n = src.numel() * src.element_size()
     st = _lib.specv_copy_bytes(_ptr(dst), _ptr(src), n, _stream(stream, src.device))
     _check(st, "specv_copy_bytes")
+
+
+def specv_read_bytes(src, sink=None, stream=None):
+    """Read-only stream of src (a multiple of 64 KiB) with pass 1's access
+    pattern; returns the per-wave XOR checksums (int32, bytes / 32768)."""
+    import torch
+    n = src.numel() * src.element_size()
+    if sink is None:
+        sink = torch.empty(n // 32768, dtype=torch.int32, device=src.device)
+    st = _lib.specv_read_bytes(_ptr(src), n, _ptr(sink), _stream(stream, src.device))
+    _check(st, "specv_read_bytes")
+    return sink
 
 
 # hipEventDisableSystemFence: the event only timestamps; recording it does not

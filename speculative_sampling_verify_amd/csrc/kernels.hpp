@@ -979,6 +979,47 @@ __global__ __launch_bounds__(kBlock) void k_philox(uint64_t seed, const uint32_t
   out[4 * i + 3] = w.w3;
 }
 
+// Read-only stream with pass 1's access pattern, for the read bandwidth the
+// part reaches with it: 64 KiB segments, each read by two sibling waves that
+// take alternate 4 KiB tiles with 16-byte non-temporal loads, the next tile
+// issued before the previous one is folded; every dword is XOR-folded into
+// one word per wave (so the loads are not dead).
+constexpr int64_t kProbeSegBytes = 65536;
+
+__global__ __launch_bounds__(kBlock) void k_read_probe(const u32x4* src, int64_t segments,
+                                                       uint32_t* sink) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t item = wave_uniform((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
+  if (item >= 2 * segments) return;
+  const u32x4* p = src + (item >> 1) * (kProbeSegBytes / 16);
+  const int sib = (int)(item & 1);
+  constexpr int kTiles = (int)(kProbeSegBytes / 4096 / 2);  // 8 per wave
+  auto load = [&](int t, u32x4 (&r)[4]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      r[u] = __builtin_nontemporal_load(p + (int64_t)(sib + 2 * t) * 256 + u * kWave + lane);
+  };
+  uint32_t acc = 0u;
+  auto fold = [&](const u32x4 (&r)[4]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc ^= r[u].x ^ r[u].y ^ r[u].z ^ r[u].w;
+  };
+  u32x4 a[4], b[4];
+  load(0, a);
+  for (int t = 0; t + 3 < kTiles; t += 2) {
+    load(t + 1, b);
+    fold(a);
+    load(t + 2, a);
+    fold(b);
+  }
+  load(kTiles - 1, b);
+  fold(a);
+  fold(b);
+#pragma unroll
+  for (int off = kWave / 2; off >= 1; off >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, off, kWave);
+  if (lane == 0) sink[item] = acc;
+}
+
 __global__ __launch_bounds__(kBlock) void k_copy(u32x4* dst, const u32x4* src, int64_t n16) {
   const int64_t stride = (int64_t)gridDim.x * kBlock;
   for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n16; i += stride)

@@ -1043,6 +1043,17 @@ specv_status_t specv_copy_bytes(void* dst, const void* src, size_t bytes, hipStr
   return launched();
 }
 
+specv_status_t specv_read_bytes(const void* src, size_t bytes, uint32_t* sink,
+                                hipStream_t stream) {
+  if (bytes == 0) return SPECV_OK;
+  if (!src || !sink || bytes % kProbeSegBytes != 0 || !aligned(src, 16) || !aligned(sink, 4))
+    return SPECV_ERR_INVALID_ARGUMENT;
+  const int64_t segments = (int64_t)(bytes / kProbeSegBytes);
+  hipLaunchKernelGGL(k_read_probe, dim3(blocks_for(2 * segments)), dim3(kBlock), 0, stream,
+                     static_cast<const u32x4*>(src), segments, sink);
+  return launched();
+}
+
 const char* specv_status_string(specv_status_t status) {
   switch (status) {
     case SPECV_OK: return "ok";

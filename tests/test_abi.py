@@ -78,6 +78,10 @@ def test_other_entry_points_validate():
     assert lib.specv_philox4x32_10(0, None, None, 0, None) == OK
     assert lib.specv_copy_bytes(FAKE, FAKE, 15, None) == INVALID
     assert lib.specv_copy_bytes(FAKE, FAKE, 0, None) == OK
+    assert lib.specv_read_bytes(FAKE, 65536 + 16, FAKE, None) == INVALID  # not whole segments
+    assert lib.specv_read_bytes(None, 65536, FAKE, None) == INVALID
+    assert lib.specv_read_bytes(FAKE, 65536, None, None) == INVALID
+    assert lib.specv_read_bytes(None, 0, None, None) == OK
     shp = shape()
     assert lib.specv_softmax_rows(ctypes.byref(shp), FAKE, FAKE, FAKE, FAKE, FAKE, -1, FAKE, FAKE,
                                   1 << 30, None) == INVALID
