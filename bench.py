@@ -71,6 +71,48 @@ def make_inputs(name):
     return getattr(synth, base)(**kw), desc
 
 
+def batch1_latency(torch, svx, dev, calls=200):
+    """The literal batch-1 call of the T5-XXL-like setting (one sequence,
+    gamma = 5, V = 32128, bf16, T = 1): microseconds per call for back-to-back
+    eager calls on one stream, and for replays of a HIP graph that captured
+    one call (launch overhead is most of it at this size)."""
+    import synth
+    x = synth.t5xxl_like(rounds=1)
+    d = svx.from_inputs(x, dev)
+    shape = svx._shape_of(d["target"], d["draft"], d["gamma"], x.max_gamma)
+    ws = svx.workspace_for(shape, dev)
+    out_n = torch.empty(1, dtype=torch.int32, device=dev)
+    out_next = torch.empty(1, dtype=torch.int32, device=dev)
+    s = torch.cuda.Stream(device=dev)
+
+    def call():
+        svx.specv_verify(d["target"], d["draft"], d["draft_tokens"], d["gamma"], d["temperature"],
+                         max_gamma=x.max_gamma, seed=x.seed, philox_row_offset=x.row_offset,
+                         out_n=out_n, out_next=out_next, workspace=ws, stream=s)
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(s):
+            for _ in range(20):
+                fn()
+            e0.record(s)
+            for _ in range(calls):
+                fn()
+            e1.record(s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / calls * 1e3
+
+    s.wait_stream(torch.cuda.current_stream(dev))
+    eager_us = timed(call)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call()
+    torch.cuda.synchronize()
+    graph_us = timed(g.replay)
+    return {"config": "1 sequence, gamma=5, V=32128, bf16, T=1 (one round of the T5-XXL-like "
+                      "setting)", "eager_us_per_call": eager_us, "graph_us_per_replay": graph_us}
+
+
 def cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -605,6 +647,8 @@ def main():
     rg = read_gbps(torch, svx, dev)
     result["read_probe_gbps"] = rg
     result["roofline"]["frac_of_read_probe"] = achieved / rg
+    if args.workload == "t5xxl_like" and args.lenience == "none":
+        result["batch1_latency"] = batch1_latency(torch, svx, dev)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on the host")
         result["cpu_baseline"] = cpu_baseline(x, n_host, next_host, lenience=args.lenience,
