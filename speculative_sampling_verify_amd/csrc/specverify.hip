@@ -33,6 +33,13 @@ constexpr size_t kAlign = 256;
 constexpr int64_t kK1ChunkBF16 = SPECV_K1_CHUNK_BF16;
 constexpr int64_t kK1ChunkF32 = SPECV_K1_CHUNK_F32;
 constexpr int64_t kMaxChunks1 = 16;                  // pass-1 chunks per row (at most)
+#ifndef SPECV_MIN_PASS1_WAVES
+#define SPECV_MIN_PASS1_WAVES 512
+#endif
+constexpr int64_t kMinPass1Waves = SPECV_MIN_PASS1_WAVES;  // two per compute unit
+#ifndef SPECV_MIN_WAVES_CHUNK_CAP
+#define SPECV_MIN_WAVES_CHUNK_CAP 4
+#endif
 constexpr int kDrawStep = kBlock * 8; // elements per workgroup scan step of the draw
 constexpr int64_t kTargetMassItems = SPECV_MASS_WAVES;  // pass-2 waves to aim for
 // Accept step, pass 2 and draw in one launch when a sequence's pass-2 waves fit
@@ -87,6 +94,16 @@ void make_plan(const specv_shape_t* s, Plan* p) {
   const int64_t per = (p->dt == kBF16) ? kK1ChunkBF16 : kK1ChunkF32;
   int64_t c1 = (p->V + per - 1) / per;
   if (c1 < 2 && p->V > SPECV_K1_TWO_CHUNKS_ABOVE) c1 = 2;
+  // a batch too small to fill the part (a few sequences) gets more, shorter
+  // chunks: at least kMinPass1Waves waves while a row has tiles to give
+  const int64_t rows = p->tt + p->td;
+  if (rows > 0 && rows * c1 < kMinPass1Waves) {
+    const int64_t want = (kMinPass1Waves + rows - 1) / rows;
+    const int64_t tiles = (p->V + 2047) / 2048;  // the fewest tiles of any path's tiling
+    int64_t cap = tiles < SPECV_MIN_WAVES_CHUNK_CAP ? tiles : SPECV_MIN_WAVES_CHUNK_CAP;
+    cap = cap > c1 ? cap : c1;
+    c1 = want < cap ? want : cap;
+  }
   c1 = c1 < 1 ? 1 : (c1 > kMaxChunks1 ? kMaxChunks1 : c1);
   p->chunks1 = (int)c1;
   // pass 2: enough chunks per sequence to give about kTargetMassItems waves
