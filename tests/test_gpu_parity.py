@@ -495,10 +495,13 @@ DIAG_CASES = [
     ("serving_b64", dict(batch=6), 64),              # T = 0.7, K at its maximum
     ("ragged_b256", dict(batch=10), 1),              # ragged gammas, 10 chunks
     ("large_vocab", dict(batch=8), 10),              # fp32, V = 256000, odd greedy, p == q rows
+    # long merged lists: 5 chunks x 64 (the 8-slot merge), 11 chunks x 64 (16 slots)
+    ("ragged_b256", dict(batch=4), 64),
+    ("large_vocab", dict(batch=4), 64),
 ]
 
 
-@pytest.mark.parametrize("name,kw,k", DIAG_CASES, ids=[c[0] for c in DIAG_CASES])
+@pytest.mark.parametrize("name,kw,k", DIAG_CASES, ids=["%s-k%d" % (c[0], c[2]) for c in DIAG_CASES])
 def test_diagnostics_parity(svx, name, kw, k):
     assert_diag_parity(name, make(name, **kw), k)
 
