@@ -432,7 +432,6 @@ def specv_copy_bytes(dst, src, stream=None):
 def specv_read_bytes(src, sink=None, stream=None):
     """Read-only stream of src (a multiple of 64 KiB) with pass 1's access
     pattern; returns the per-wave XOR checksums (int32, bytes / 32768)."""
-    import torch
     n = src.numel() * src.element_size()
     if sink is None:
         sink = torch.empty(n // 32768, dtype=torch.int32, device=src.device)
