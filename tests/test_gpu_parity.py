@@ -599,7 +599,7 @@ def random_case(seed):
     return pack(seqs, V, dtype)
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(96))
 def test_random_shapes_parity(svx, seed):
     x = random_case(seed)
     parity_case(svx, "random %d (V=%d %s B=%d max_gamma=%d)" % (seed, x.vocab, x.dtype, x.batch,
