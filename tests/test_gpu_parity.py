@@ -604,3 +604,13 @@ def test_random_shapes_parity(svx, seed):
     x = random_case(seed)
     parity_case(svx, "random %d (V=%d %s B=%d max_gamma=%d)" % (seed, x.vocab, x.dtype, x.batch,
                                                                x.max_gamma), x, repeat=False)
+
+
+@pytest.mark.parametrize("seed", range(32))
+def test_diagnostics_random_shapes(svx, seed):
+    # the random shapes above (ragged, masked, mixed greedy) with a random top-k
+    x = random_case(seed)
+    if x.total_draft_rows == 0:
+        pytest.skip("no draft positions")
+    k = int(np.random.default_rng(seed).integers(0, min(64, x.vocab) + 1))
+    assert_diag_parity("random %d" % seed, x, k)
