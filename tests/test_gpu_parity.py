@@ -614,3 +614,15 @@ def test_diagnostics_random_shapes(svx, seed):
         pytest.skip("no draft positions")
     k = int(np.random.default_rng(seed).integers(0, min(64, x.vocab) + 1))
     assert_diag_parity("random %d" % seed, x, k)
+
+
+@pytest.mark.parametrize("seed", range(32))
+def test_lenient_random_shapes(svx, seed):
+    # the random shapes above with a random lenience function and epsilon
+    x = random_case(seed)
+    rng = np.random.default_rng(7 * seed + 3)
+    kind = ["lin", "sq", "exp"][int(rng.integers(0, 3))]
+    eps = float(rng.choice([1.0, 0.9, 0.5, 0.2, 0.05, 0.01]))
+    got = run_gpu_lenient(svx, x, kind, eps)
+    orc = run_oracle(x, lenience=kind, epsilon=eps)
+    assert_parity("lenient random %d %s %g" % (seed, kind, eps), x, got, orc)
