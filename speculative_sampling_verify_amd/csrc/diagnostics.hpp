@@ -158,7 +158,7 @@ __device__ __forceinline__ float raw_elem(const typename Tile<DT, VEC>::Raw& r) 
 template <int DT, bool VEC, int G>
 __device__ __forceinline__ void diag_terms(const typename Tile<DT, VEC>::Raw& rd,
                                            const typename Tile<DT, VEC>::Raw& rt, float k,
-                                           float rkT, float rkD, float iT, float iD, float& sa,
+                                           float rkT, float rkD, float r, float iD, float& sa,
                                            float& ss, float& sA, float& mx) {
   float pa[8], ps[8], pA[8];
 #pragma unroll
@@ -178,12 +178,17 @@ __device__ __forceinline__ void diag_terms(const typename Tile<DT, VEC>::Raw& rd
     const float eD = __builtin_fmaf(zD, k, -rkD);
     const float tD = exp2_hw(eD);
     const float tT = exp2_hw(__builtin_fmaf(zT, k, -rkT));
-    pa[u] = fminf(tT * iT, tD * iD);
+    // min(p, q) = min(tT r, tD) / S^D with r = S^D / S^T: one product per
+    // element, the 1 / S^D once per group
+    pa[u] = fminf(tT * r, tD);
     ps[u] = tD;
-    pA[u] = (tD == 0.f) ? 0.f : tD * eD;  // masked tokens: 0 * -inf is 0 here
+    // a masked token (tD = 0, eD = -inf) must add 0: eD is clamped to the
+    // lowest finite float, which changes nothing where tD > 0 (eD is finite
+    // there) and turns 0 * -inf into -0
+    pA[u] = tD * fmaxf(eD, -3.40282347e38f);
     mx = fmaxf(mx, zD);
   }
-  sa = tree_sum(pa);
+  sa = tree_sum(pa) * iD;
   ss = tree_sum(ps);
   sA = tree_sum(pA);
 }
@@ -213,7 +218,7 @@ __global__ __launch_bounds__(kBlock) void k5_diag_pass(DiagArgs a) {
   if (!st_t.valid || !st_d.valid) return;
   const void* trow = static_cast<const char*>(a.target) + tr * a.V * esz;
   const void* drow = static_cast<const char*>(a.draft) + j * a.V * esz;
-  const float iT = sampling ? (float)(1.0 / st_t.s) : 0.f;
+  const float rTD = sampling ? (float)(st_d.s / st_t.s) : 0.f;
   const float iD = sampling ? (float)(1.0 / st_d.s) : 0.f;
   const int64_t tiles = (a.V + TL::EPI - 1) / TL::EPI;
   const int n_iter = (int)((tiles - c + a.chunks - 1) / a.chunks);
@@ -267,11 +272,11 @@ __global__ __launch_bounds__(kBlock) void k5_diag_pass(DiagArgs a) {
     float mx = ninf();
     if (sampling) {
       float ga[NG], gs[NG], gA[NG];
-      diag_terms<DT, VEC, 0>(rd, rt, k, st_t.rk, st_d.rk, iT, iD, ga[0], gs[0], gA[0], mx);
-      diag_terms<DT, VEC, 1>(rd, rt, k, st_t.rk, st_d.rk, iT, iD, ga[1], gs[1], gA[1], mx);
+      diag_terms<DT, VEC, 0>(rd, rt, k, st_t.rk, st_d.rk, rTD, iD, ga[0], gs[0], gA[0], mx);
+      diag_terms<DT, VEC, 1>(rd, rt, k, st_t.rk, st_d.rk, rTD, iD, ga[1], gs[1], gA[1], mx);
       if constexpr (NG == 4) {
-        diag_terms<DT, VEC, 2>(rd, rt, k, st_t.rk, st_d.rk, iT, iD, ga[2], gs[2], gA[2], mx);
-        diag_terms<DT, VEC, 3>(rd, rt, k, st_t.rk, st_d.rk, iT, iD, ga[3], gs[3], gA[3], mx);
+        diag_terms<DT, VEC, 2>(rd, rt, k, st_t.rk, st_d.rk, rTD, iD, ga[2], gs[2], gA[2], mx);
+        diag_terms<DT, VEC, 3>(rd, rt, k, st_t.rk, st_d.rk, rTD, iD, ga[3], gs[3], gA[3], mx);
       }
       sa += (double)tree_sum(ga);
       ss += (double)tree_sum(gs);
