@@ -488,6 +488,9 @@ def main():
     ap.add_argument("--cascade", action="store_true",
                     help="time the vertical cascade over three bigram tables instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-batch1", action="store_true",
+                    help="skip the batch-1 latency figure (its small launches of the same "
+                         "kernels would mix into a profiler's per-kernel averages)")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="run only a plain device copy of this many bytes (counter calibration)")
     args = ap.parse_args()
@@ -647,7 +650,7 @@ def main():
     rg = read_gbps(torch, svx, dev)
     result["read_probe_gbps"] = rg
     result["roofline"]["frac_of_read_probe"] = achieved / rg
-    if args.workload == "t5xxl_like" and args.lenience == "none":
+    if args.workload == "t5xxl_like" and args.lenience == "none" and not args.no_batch1:
         result["batch1_latency"] = batch1_latency(torch, svx, dev)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on the host")
