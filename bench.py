@@ -340,6 +340,8 @@ def bench_decode(args, torch, svx, dev):
     t_stop.record(stream)
     torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_stop) / K
+    # "gather": the row gather with the verify step's pass 1 folded in
+    # (k_dec_gather_stats); "verify": the accept step, pass 2 and the draw
     names = ("drafting", "gather", "verify", "append")
     stage_ms = {nm: float(np.mean([ev.elapsed_ms(si) for ev in evs])) for si, nm in
                 enumerate(names)}
@@ -360,7 +362,7 @@ def bench_decode(args, torch, svx, dev):
                                "%d rounds, T=1" % (B, V, g, R),
                    "batch": B, "vocab": V, "gamma": g, "rounds": R},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None, "kernel": "k_dec_gather",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None, "kernel": "k_dec_gather_stats",
                      "algorithmic_bytes_per_launch": gather_bytes,
                      "avg_launch_ms": stage_ms["gather"]},
         "stage_ms_last_round": stage_ms,
@@ -441,7 +443,7 @@ def bench_cascade(args, torch, svx, dev):
                                "f_sq eps=%g at the intermediate review, T=1" % (B, V, k1, k2, R, eps),
                    "batch": B, "vocab": V, "k1": k1, "k2": k2, "rounds": R},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None, "kernel": "k_dec_gather",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None, "kernel": "k_dec_gather_stats",
                      "algorithmic_bytes_per_launch": gather_bytes,
                      "avg_launch_ms": stage_ms["inner_gather"]},
         "stage_ms_last_round": stage_ms,

@@ -8,9 +8,11 @@
 //                 from softmax(draft row / T) by inverse CDF in index order
 //                 (u = word 0 of Philox(seed; row, i, 1)), or by argmax when
 //                 T = 0, and records which table row feeds each packed row;
-//   k_dec_gather  copies those table rows into the packed layout of the
-//                 verify step (what a model's output layer would write);
-//   the verify step (plan, pass 1, accept + pass 2, draw);
+//   k_dec_gather_stats  copies those table rows into the packed layout of
+//                 the verify step (what a model's output layer would write)
+//                 and forms the verify step's pass-1 statistics of each row
+//                 as it writes it (as an output layer's epilogue could);
+//   the rest of the verify step (accept + pass 2 + draw);
 //   k_dec_append  appends the n accepted drafts and the drawn token.
 // Within a lane the drafting scan holds 16 consecutive elements, so lane
 // order is index order and the walk follows the index-order CDF.
@@ -431,8 +433,8 @@ __global__ __launch_bounds__(kDecWaves * kWave) void k_dec_draft_wg(DecodeArgs a
   }
 }
 
-// Copies table rows into the packed verify layout: one wave per (packed row,
-// 16 KiB piece). Rows [0, n_t) are target rows, then n_d draft rows.
+// Where the rows of one round come from and go to: packed target rows
+// [0, n_t) and draft rows [0, n_d), row r copied from table row *_src[r].
 struct GatherArgs {
   const void* ttab;
   const void* dtab;
@@ -441,31 +443,58 @@ struct GatherArgs {
   void* tdst;
   void* ddst;
   int64_t row_bytes, n_t, n_d;
-  int32_t pieces;  // per row
 };
 
-constexpr int64_t kGatherPiece = 16384;
-
-template <bool VEC>
-__global__ __launch_bounds__(kBlock) void k_dec_gather(GatherArgs a) {
+// The gather with the verify step's pass 1 folded in: one wave per (packed
+// row, pass-1 chunk), the chunk's tiles as k1_row_stats takes them, each tile
+// stored to the packed row while its statistics are formed (chunk_pass with
+// STORE), so the verify step starts at the accept step. The partials are
+// those k1_row_stats would write from the packed rows, bit for bit. Rows
+// without statistics (draft rows of greedy sequences, invalid temperatures)
+// are only copied. The batch is uniform (gamma for every sequence): the first
+// workgroup also checks the gammas and sets the status word, as pass 1 does.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kBlock) void k_dec_gather_stats(GatherArgs g, RowStatsArgs a) {
+  using TL = Tile<DT, VEC>;
+  if (a.gamma && blockIdx.x == 0) {
+    bool bad = false;
+    for (int64_t b = threadIdx.x; b < a.B; b += blockDim.x) bad |= a.gamma[b] != a.uniform_g;
+    bad = __syncthreads_or(bad);
+    if (threadIdx.x == 0) a.status_out[0] = bad ? kLayoutError : 0u;
+  }
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t item = wave_uniform((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
-  if (item >= (a.n_t + a.n_d) * a.pieces) return;
-  const int64_t r = item / a.pieces;
-  const int64_t p = item - r * a.pieces;
-  const bool tgt = r < a.n_t;
-  const int64_t src_row = tgt ? a.trow_src[r] : a.drow_src[r - a.n_t];
-  const char* src = static_cast<const char*>(tgt ? a.ttab : a.dtab) + src_row * a.row_bytes;
-  char* dst = static_cast<char*>(tgt ? a.tdst : a.ddst) + (tgt ? r : r - a.n_t) * a.row_bytes;
-  const int64_t b0 = p * kGatherPiece;
-  const int64_t b1 = min(a.row_bytes, b0 + kGatherPiece);
-  if constexpr (VEC) {
-    for (int64_t o = b0 + (int64_t)lane * 16; o < b1; o += kWave * 16)
-      *reinterpret_cast<u32x4*>(dst + o) = *reinterpret_cast<const u32x4*>(src + o);
-  } else {
-    for (int64_t o = b0 + (int64_t)lane * 2; o < b1; o += kWave * 2)
-      *reinterpret_cast<uint16_t*>(dst + o) = *reinterpret_cast<const uint16_t*>(src + o);
+  if (item >= (a.total_t + a.total_d) * a.chunks) return;
+  const int64_t r = item / a.chunks;
+  const int c = (int)(item - r * a.chunks);
+  const bool is_draft = r >= a.total_t;
+  const int64_t j = is_draft ? r - a.total_t : r;
+  const int64_t src_row = is_draft ? g.drow_src[j] : g.trow_src[j];
+  const void* src = static_cast<const char*>(is_draft ? g.dtab : g.ttab) + src_row * g.row_bytes;
+  void* dst = static_cast<char*>(is_draft ? g.ddst : g.tdst) + j * g.row_bytes;
+  const int64_t tiles = (a.V + TL::EPI - 1) / TL::EPI;
+  const int n_iter = (int)((tiles - c + a.chunks - 1) / a.chunks);
+  typename TL::Raw first;
+  load_tile<DT, VEC>(src, a.V, c, lane, first);
+  const int64_t seq = is_draft ? j / a.uniform_g : j / (a.uniform_g + 1);
+  const float k = seq_scale(a.temperature[seq]);
+  const bool stats = is_draft ? (k > 0.f) : (k >= 0.f);
+  if (!stats) {
+    // copy only: the verify step reads no statistics of this row
+    for (int it = 0; it < n_iter; ++it) {
+      const int64_t t = (int64_t)c + (int64_t)it * a.chunks;
+      if (it > 0) load_tile<DT, VEC>(src, a.V, t, lane, first);
+      TL::store_raw(dst, t * TL::EPI, a.V, 0, lane, first);
+    }
+    return;
   }
+  RowPart out;
+  float lm;
+  if (k > 0.f)
+    out = chunk_pass<DT, VEC, true, false, true>(src, a.V, c, a.chunks, n_iter, k, lane, first, lm, dst);
+  else
+    out = chunk_pass<DT, VEC, false, true, true>(src, a.V, c, a.chunks, n_iter, 0.f, lane, first, lm, dst);
+  if (lane == 0) (is_draft ? a.dparts : a.tparts)[j * a.chunks + c] = out;
 }
 
 __global__ __launch_bounds__(kBlock) void k_dec_append(DecodeArgs a) {

@@ -135,6 +135,34 @@ struct Tile {
     }
   }
 
+  // Stores the raw tile of iteration `it` as load_raw read it (the same
+  // slots), skipping slots at or past e1; non-temporal 16-byte stores on the
+  // vector path.
+  __device__ static __forceinline__ void store_raw(void* row, int64_t e0, int64_t e1, int it,
+                                                   int lane, const Raw& r) {
+    if constexpr (VEC) {
+      u32x4* p = reinterpret_cast<u32x4*>(static_cast<char*>(row) + e0 * (DT == kBF16 ? 2 : 4));
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t vec = (int64_t)(it * 4 + u) * kWave + lane;
+        if (e0 + vec * VE < e1)
+          __builtin_nontemporal_store(u32x4{r.d[4 * u], r.d[4 * u + 1], r.d[4 * u + 2], r.d[4 * u + 3]},
+                                      p + vec);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NE; ++j) {
+        const int64_t idx = e0 + (int64_t)(it * NE + j) * kWave + lane;
+        if (idx < e1) {
+          if constexpr (DT == kBF16)
+            static_cast<uint16_t*>(row)[idx] = (uint16_t)(r.d[j] >> 16);
+          else
+            static_cast<uint32_t*>(row)[idx] = r.d[j];
+        }
+      }
+    }
+  }
+
   __device__ static __forceinline__ void load_raw(const void* row, int64_t e0, int64_t e1, int it,
                                                   int n_full, int lane, Raw& r) {
     if (it < n_full) load_raw<false>(row, e0, e1, it, lane, r);

@@ -197,10 +197,15 @@ __device__ __forceinline__ void load_tile(const void* row, int64_t V, int64_t t,
   else TL::template load_raw<true>(row, e0, V, 0, lane, r);
 }
 
-template <int DT, bool VEC, bool SAMPLING, bool WITH_ARG>
+//
+// With STORE, every tile is also written to `dst` (a row of the same length)
+// as it is processed: a producer that writes the rows computes their
+// statistics in the same pass.
+template <int DT, bool VEC, bool SAMPLING, bool WITH_ARG, bool STORE = false>
 __device__ __forceinline__ RowPart chunk_pass(const void* row, int64_t V, int c, int chunks,
                                               int n_iter, float k, int lane,
-                                              typename Tile<DT, VEC>::Raw& a, float& lane_max) {
+                                              typename Tile<DT, VEC>::Raw& a, float& lane_max,
+                                              void* dst = nullptr) {
   using TL = Tile<DT, VEC>;
   using Raw = typename TL::Raw;
   constexpr int NE = TL::NE;
@@ -210,6 +215,7 @@ __device__ __forceinline__ RowPart chunk_pass(const void* row, int64_t V, int c,
   bool bad = false;
   int best = -1;
   auto process = [&](const Raw& raw, int it) {
+    if constexpr (STORE) TL::store_raw(dst, ((int64_t)c + (int64_t)it * chunks) * TL::EPI, V, 0, lane, raw);
     float z[NE];
     TL::widen(raw, z);
     const float g = tile_max(z);

@@ -166,6 +166,10 @@ struct Call {
   hipEvent_t* events;
   int32_t lenience = kLenNone;
   float eps = 1.f;
+  // Pass 1 already done (uniform batch only): the pass-1 partials and the
+  // status word are in the workspace, written by a producer of the rows
+  // (k_dec_gather_stats), so the call starts at the accept step.
+  bool skip_pass1 = false;
 };
 
 specv_status_t check_common(const specv_shape_t* shape, const void* target, const void* draft,
@@ -366,6 +370,7 @@ specv_status_t run(const Call& c) {
   if ((c.inj_r == nullptr) != (c.inj_u == nullptr)) return SPECV_ERR_INVALID_ARGUMENT;
   const bool vec = vector_path(p, c.target, c.draft);
   const bool uniform = uniform_batch(p);
+  if (c.skip_pass1 && !uniform) return SPECV_ERR_INVALID_ARGUMENT;
   // A uniform batch has no plan launch: pass 1's first workgroup checks the
   // gammas and sets the status word.
   mark(c.events, 2 * SPECV_STAGE_PLAN, c.stream);
@@ -373,7 +378,8 @@ specv_status_t run(const Call& c) {
     return st;
   mark(c.events, 2 * SPECV_STAGE_PLAN + 1, c.stream);
   mark(c.events, 2 * SPECV_STAGE_ROWSTATS, c.stream);
-  if ((st = launch_row_stats(p, vec, c.target, c.draft, c.ws, c.stream, false, false, 0, nullptr,
+  if (!c.skip_pass1 &&
+      (st = launch_row_stats(p, vec, c.target, c.draft, c.ws, c.stream, false, false, 0, nullptr,
                              c.temperature, uniform, c.gamma)) != SPECV_OK)
     return st;
   mark(c.events, 2 * SPECV_STAGE_ROWSTATS + 1, c.stream);
@@ -669,6 +675,37 @@ specv_status_t specv_position_diagnostics(const specv_shape_t* shape, const void
   return SPECV_OK;
 }
 
+// The gather of one round with the verify step's pass 1 folded in: the
+// partials go to the verify workspace `vws` laid out by plan `vp`.
+specv_status_t launch_gather_stats(bool bf16, bool vec, const GatherArgs& ga, const Plan& vp,
+                                   void* vws, const float* temperature, const int32_t* gam,
+                                   hipStream_t stream) {
+  RowStatsArgs a{};
+  a.tparts = at<RowPart>(vws, vp.off_tparts);
+  a.dparts = at<RowPart>(vws, vp.off_dparts);
+  a.status = at<uint32_t>(vws, 0);
+  a.total_t = vp.tt;
+  a.total_d = vp.td;
+  a.V = vp.V;
+  a.B = (int32_t)vp.B;
+  a.chunks = vp.chunks1;
+  a.uniform_g = (int32_t)vp.max_gamma;
+  a.temperature = temperature;
+  a.gamma = gam;
+  a.status_out = at<uint32_t>(vws, 0);
+  const int64_t waves = (vp.tt + vp.td) * vp.chunks1;
+  if (waves == 0) return SPECV_OK;
+  const dim3 grid(blocks_for(waves)), block(kBlock);
+  if (bf16) {
+    if (vec) hipLaunchKernelGGL((k_dec_gather_stats<kBF16, true>), grid, block, 0, stream, ga, a);
+    else hipLaunchKernelGGL((k_dec_gather_stats<kBF16, false>), grid, block, 0, stream, ga, a);
+  } else {
+    if (vec) hipLaunchKernelGGL((k_dec_gather_stats<kF32, true>), grid, block, 0, stream, ga, a);
+    else hipLaunchKernelGGL((k_dec_gather_stats<kF32, false>), grid, block, 0, stream, ga, a);
+  }
+  return launched();
+}
+
 // Drafting of one round: a workgroup per sequence when its rows fit the
 // workgroup's registers (V <= 8192), else one wave per sequence streaming the row.
 specv_status_t launch_draft(bool bf16, bool vec, const DecodeArgs& a, int64_t B, hipStream_t stream) {
@@ -758,9 +795,7 @@ specv_status_t specv_decode_bigram(const specv_decode_shape_t* shape, const void
   ga.row_bytes = d.row_bytes;
   ga.n_t = B * (g + 1);
   ga.n_d = B * g;
-  ga.pieces = (int32_t)((d.row_bytes + kGatherPiece - 1) / kGatherPiece);
   const bool vec = d.row_bytes % 16 == 0 && aligned(target_table, 16) && aligned(draft_table, 16);
-  const int64_t gather_waves = (ga.n_t + ga.n_d) * ga.pieces;
   for (int64_t r = 0; r < R; ++r) {
     a.round = (int32_t)r;
     a.row_base = philox_row_offset + (uint64_t)(r * B);
@@ -770,14 +805,15 @@ specv_status_t specv_decode_bigram(const specv_decode_shape_t* shape, const void
     if ((st = launch_draft(shape->dtype == SPECV_BF16, vec, a, B, stream)) != SPECV_OK) return st;
     mark(ev, 2 * SPECV_STAGE_PLAN + 1, stream);
     mark(ev, 2 * SPECV_STAGE_ROWSTATS, stream);
-    if (vec) hipLaunchKernelGGL((k_dec_gather<true>), dim3(blocks_for(gather_waves)), block, 0, stream, ga);
-    else hipLaunchKernelGGL((k_dec_gather<false>), dim3(blocks_for(gather_waves)), block, 0, stream, ga);
-    if ((st = launched()) != SPECV_OK) return st;
+    if ((st = launch_gather_stats(shape->dtype == SPECV_BF16, vec, ga, d.vp, workspace, temperature,
+                                  a.gam, stream)) != SPECV_OK)
+      return st;
     mark(ev, 2 * SPECV_STAGE_ROWSTATS + 1, stream);
     mark(ev, 2 * SPECV_STAGE_ACCEPT_MASS, stream);
     Call c{&d.vshape, ga.tdst, ga.ddst, a.drafts, a.gam, temperature, seed, a.row_base, nullptr,
            nullptr, at<int32_t>(workspace, d.off_vn), at<int32_t>(workspace, d.off_vnext),
            workspace, d.vp.bytes, stream, nullptr};
+    c.skip_pass1 = true;
     if ((st = run(c)) != SPECV_OK) return st;
     mark(ev, 2 * SPECV_STAGE_ACCEPT_MASS + 1, stream);
     mark(ev, 2 * SPECV_STAGE_DRAW, stream);
@@ -888,7 +924,6 @@ specv_status_t specv_cascade_bigram(const specv_cascade_shape_t* shape, const vo
   ga.row_bytes = c.row_bytes;
   ga.n_t = B * (k2 + 1);
   ga.n_d = B * k2;
-  ga.pieces = (int32_t)((c.row_bytes + kGatherPiece - 1) / kGatherPiece);
   const bool vec = c.row_bytes % 16 == 0 && aligned(mid_table, 16) && aligned(small_table, 16);
   const dim3 block(kBlock);
   const unsigned seq_blocks = (unsigned)((B + kBlock - 1) / kBlock);
@@ -909,10 +944,9 @@ specv_status_t specv_cascade_bigram(const specv_cascade_shape_t* shape, const vo
       if ((st = launch_draft(bf16, vec, di, B, stream)) != SPECV_OK) return st;
       mark(ev, 2 * SPECV_STAGE_PLAN + 1, stream);
       mark(ev, 2 * SPECV_STAGE_ROWSTATS, stream);
-      const int64_t gw = (ga.n_t + ga.n_d) * ga.pieces;
-      if (vec) hipLaunchKernelGGL((k_dec_gather<true>), dim3(blocks_for(gw)), block, 0, stream, ga);
-      else hipLaunchKernelGGL((k_dec_gather<false>), dim3(blocks_for(gw)), block, 0, stream, ga);
-      if ((st = launched()) != SPECV_OK) return st;
+      if ((st = launch_gather_stats(bf16, vec, ga, c.pin, workspace, temperature,
+                                    at<int32_t>(workspace, c.off_igam), stream)) != SPECV_OK)
+        return st;
       mark(ev, 2 * SPECV_STAGE_ROWSTATS + 1, stream);
       mark(ev, 2 * SPECV_STAGE_ACCEPT_MASS, stream);
       Call ci{&c.vin, ga.tdst, ga.ddst, di.drafts, at<int32_t>(workspace, c.off_igam), temperature,
@@ -920,6 +954,7 @@ specv_status_t specv_cascade_bigram(const specv_cascade_shape_t* shape, const vo
               at<int32_t>(workspace, c.off_vnext), workspace, c.vbytes, stream, nullptr};
       ci.lenience = len_kind;
       ci.eps = epsilon;
+      ci.skip_pass1 = true;
       if ((st = run(ci)) != SPECV_OK) return st;
       mark(ev, 2 * SPECV_STAGE_ACCEPT_MASS + 1, stream);
       hipLaunchKernelGGL(k_cas_inner_append, dim3(seq_blocks), block, 0, stream, ca);
