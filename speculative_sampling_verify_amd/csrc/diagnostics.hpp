@@ -20,8 +20,8 @@
 // the best K to a small LDS buffer and cuts the buffer back to the best K by
 // rank counting whenever it fills; the cut also raises the bar that a key
 // must clear. The first bar is the K-th largest lane maximum of the chunk,
-// taken in pass 1. A tile is scanned only when some lane's tile maximum
-// reaches the bar.
+// taken in pass 1. A tile's group of 8 slots is scanned only when some
+// lane's maximum over the group reaches the bar.
 // k6_diag_merge (one wave per position) sums the chunks' partials and merges
 // their lists; probabilities of the selected tokens are 2^(z k - rk) / S in
 // float64, as the accept step computes p(x) and q(x).
@@ -199,6 +199,7 @@ __global__ __launch_bounds__(kBlock) void k5_diag_pass(DiagArgs a) {
   using Raw = typename TL::Raw;
   constexpr int NE = TL::NE;
   constexpr int NG = NE / 8;
+  static_assert(kDiagGroup == 8, "diag_terms and the scan share 8-slot groups");
   constexpr int64_t esz = (DT == kBF16) ? 2 : 4;
   __shared__ __attribute__((aligned(16))) uint64_t sbuf[kWavesPerBlock][kDiagCap];
   const int lane = threadIdx.x & (kWave - 1);
@@ -207,40 +208,59 @@ __global__ __launch_bounds__(kBlock) void k5_diag_pass(DiagArgs a) {
   if (item >= a.total_d * a.chunks) return;
   const int64_t j = item / a.chunks;
   const int c = (int)(item - j * a.chunks);
-  if (a.status[0] & kLayoutError) return;
-  const int64_t b = diag_seq(a, j);
-  const float k = diag_scale(a, j, b);
-  if (!(k >= 0.f)) return;  // invalid temperature: the merge reports NaN
-  const bool sampling = k > 0.f;
+  // The sequence of draft row j: arithmetic in a uniform batch, whose rows
+  // are in bounds whatever the gammas hold (the host checked the row
+  // totals); otherwise from the plan, which fills it only for a valid layout.
+  int64_t b;
+  if (a.uniform_g > 0) {
+    b = j / a.uniform_g;
+  } else {
+    const uint32_t st0 = a.status[0];
+    const int32_t bs = a.dseq[j];
+    if (st0 & kLayoutError) return;
+    b = bs;
+  }
   const int64_t tr = j + b;
-  const RowStat st_t = merge_row(a.tparts + tr * a.chunks, a.chunks, k, sampling);
-  const RowStat st_d = merge_row(a.dparts + j * a.chunks, a.chunks, k, sampling);
-  if (!st_t.valid || !st_d.valid) return;
   const void* trow = static_cast<const char*>(a.target) + tr * a.V * esz;
   const void* drow = static_cast<const char*>(a.draft) + j * a.V * esz;
+  const int64_t tiles = (a.V + TL::EPI - 1) / TL::EPI;
+  const int n_iter = (int)((tiles - c + a.chunks - 1) / a.chunks);  // >= 1: c < chunks <= tiles
+  auto tile_start = [&](int it) { return ((int64_t)c + (int64_t)it * a.chunks) * TL::EPI; };
+  auto fetch_row = [&](const void* row, int it, Raw& r) {
+    const int64_t e0 = tile_start(it);
+    if (e0 + TL::EPI <= a.V) TL::template load_raw<false>(row, e0, a.V, 0, lane, r);
+    else TL::template load_raw<true>(row, e0, a.V, 0, lane, r);
+  };
+  // The draft row's first tile and the row partials go out before anything
+  // that waits on memory; the target row's first tile once the temperature
+  // says the position samples.
+  Raw da, ta;
+  fetch_row(drow, 0, da);
+  RowPart qt[4], qd[4];
+  load_parts4(a.tparts + tr * a.chunks, a.chunks, qt);
+  load_parts4(a.dparts + j * a.chunks, a.chunks, qd);
+  const int K = a.K;
+  float thz = (K > 0) ? a.bar[j * a.chunks + c] : ninf();  // logit of th
+  const float k = diag_scale(a, j, b);
+  if (a.uniform_g > 0 && (a.status[0] & kLayoutError)) return;
+  if (!(k >= 0.f)) return;  // invalid temperature: the merge reports NaN
+  const bool sampling = k > 0.f;
+  if (sampling) fetch_row(trow, 0, ta);
+  const RowStat st_t = merge_row_from(qt, a.tparts + tr * a.chunks, a.chunks, k, sampling);
+  const RowStat st_d = merge_row_from(qd, a.dparts + j * a.chunks, a.chunks, k, sampling);
+  if (!st_t.valid || !st_d.valid) return;
   const float rTD = sampling ? (float)(st_d.s / st_t.s) : 0.f;
   const float iD = sampling ? (float)(1.0 / st_d.s) : 0.f;
-  const int64_t tiles = (a.V + TL::EPI - 1) / TL::EPI;
-  const int n_iter = (int)((tiles - c + a.chunks - 1) / a.chunks);
-  const int K = a.K;
   const int limit = (2 * K > kWave) ? 2 * K : kWave;
   double sa = 0.0, ss = 0.0, sA = 0.0;
   int count = 0;          // keys in the buffer
-  // The first bar comes from pass 1: the K-th largest lane maximum of this
-  // chunk, a logit with at least K logits of the chunk at or above it, so
-  // keys below its value cannot reach the best K.
-  float thz = (K > 0) ? a.bar[j * a.chunks + c] : ninf();  // logit of th
+  // The first bar (thz, loaded above) comes from pass 1: the K-th largest
+  // lane maximum of this chunk, a logit with at least K logits of the chunk
+  // at or above it, so keys below its value cannot reach the best K.
   uint64_t th = rank_key(thz, INT32_MAX);  // keys at or below th cannot reach the best K
-  auto tile_start = [&](int it) { return ((int64_t)c + (int64_t)it * a.chunks) * TL::EPI; };
   auto fetch = [&](int it, Raw& rd, Raw& rt) {
-    const int64_t e0 = tile_start(it);
-    const bool full = e0 + TL::EPI <= a.V;
-    if (full) TL::template load_raw<false>(drow, e0, a.V, 0, lane, rd);
-    else TL::template load_raw<true>(drow, e0, a.V, 0, lane, rd);
-    if (sampling) {
-      if (full) TL::template load_raw<false>(trow, e0, a.V, 0, lane, rt);
-      else TL::template load_raw<true>(trow, e0, a.V, 0, lane, rt);
-    }
+    fetch_row(drow, it, rd);
+    if (sampling) fetch_row(trow, it, rt);
   };
   // the top-k step of one slot group: one compare per slot against the bar's
   // logit, the exact key test only where some lane may hold a candidate
@@ -269,14 +289,16 @@ __global__ __launch_bounds__(kBlock) void k5_diag_pass(DiagArgs a) {
   };
   auto process = [&](const Raw& rd, const Raw& rt, int it) {
     const int64_t e0 = tile_start(it);
-    float mx = ninf();
+    float gm[NG];  // the lane's maximum draft logit in each 8-slot group
+#pragma unroll
+    for (int g = 0; g < NG; ++g) gm[g] = ninf();
     if (sampling) {
       float ga[NG], gs[NG], gA[NG];
-      diag_terms<DT, VEC, 0>(rd, rt, k, st_t.rk, st_d.rk, rTD, iD, ga[0], gs[0], gA[0], mx);
-      diag_terms<DT, VEC, 1>(rd, rt, k, st_t.rk, st_d.rk, rTD, iD, ga[1], gs[1], gA[1], mx);
+      diag_terms<DT, VEC, 0>(rd, rt, k, st_t.rk, st_d.rk, rTD, iD, ga[0], gs[0], gA[0], gm[0]);
+      diag_terms<DT, VEC, 1>(rd, rt, k, st_t.rk, st_d.rk, rTD, iD, ga[1], gs[1], gA[1], gm[1]);
       if constexpr (NG == 4) {
-        diag_terms<DT, VEC, 2>(rd, rt, k, st_t.rk, st_d.rk, rTD, iD, ga[2], gs[2], gA[2], mx);
-        diag_terms<DT, VEC, 3>(rd, rt, k, st_t.rk, st_d.rk, rTD, iD, ga[3], gs[3], gA[3], mx);
+        diag_terms<DT, VEC, 2>(rd, rt, k, st_t.rk, st_d.rk, rTD, iD, ga[2], gs[2], gA[2], gm[2]);
+        diag_terms<DT, VEC, 3>(rd, rt, k, st_t.rk, st_d.rk, rTD, iD, ga[3], gs[3], gA[3], gm[3]);
       }
       sa += (double)tree_sum(ga);
       ss += (double)tree_sum(gs);
@@ -284,21 +306,27 @@ __global__ __launch_bounds__(kBlock) void k5_diag_pass(DiagArgs a) {
     } else if (K > 0) {
       float z[NE];
       TL::widen(rd, z);
-      mx = tile_max(z);
+#pragma unroll
+      for (int q = 0; q < NE; ++q) gm[q / 8] = fmaxf(gm[q / 8], z[q]);
     }
     if (K == 0) return;
+    float mx = gm[0];
+#pragma unroll
+    for (int g = 1; g < NG; ++g) mx = fmaxf(mx, gm[g]);
     if (ballot(mx >= thz) == 0) return;
-    scan_group(rd, e0, std::integral_constant<int, 0>{});
-    scan_group(rd, e0, std::integral_constant<int, 1>{});
+    // a group is scanned only where some lane's group maximum reaches the
+    // bar (which may have risen since the tile's check)
+    if (ballot(gm[0] >= thz) != 0) scan_group(rd, e0, std::integral_constant<int, 0>{});
+    if (ballot(gm[1] >= thz) != 0) scan_group(rd, e0, std::integral_constant<int, 1>{});
     if constexpr (NE / kDiagGroup == 4) {
-      scan_group(rd, e0, std::integral_constant<int, 2>{});
-      scan_group(rd, e0, std::integral_constant<int, 3>{});
+      if (ballot(gm[2] >= thz) != 0) scan_group(rd, e0, std::integral_constant<int, 2>{});
+      if (ballot(gm[3] >= thz) != 0) scan_group(rd, e0, std::integral_constant<int, 3>{});
     }
   };
-  // single-buffered: one tile (both rows) in flight at a time per wave
-  Raw da, ta;
+  // single-buffered: one tile (both rows) in flight at a time per wave; the
+  // first one was issued above
   for (int it = 0; it < n_iter; ++it) {
-    fetch(it, da, ta);
+    if (it > 0) fetch(it, da, ta);
     process(da, ta, it);
   }
   const int64_t slot = j * a.chunks + c;
