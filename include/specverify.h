@@ -214,8 +214,9 @@ specv_status_t specv_position_diagnostics(const specv_shape_t* shape, const void
  * failed round on). Rows of the draft table used by greedy sequences are not
  * checked for NaN. `events`: NULL, or 2 * SPECV_NUM_STAGES events recorded
  * around the stages of the last round: drafting (SPECV_STAGE_PLAN slot), the
- * row gather (ROWSTATS slot), the whole verify step (ACCEPT_MASS slot) and
- * the append (DRAW slot). Argument errors as for specv_verify; the workspace
+ * row gather, which also forms the verify step's pass-1 statistics (ROWSTATS
+ * slot), the rest of the verify step (ACCEPT_MASS slot) and the append (DRAW
+ * slot). Argument errors as for specv_verify; the workspace
  * is specv_decode_workspace_bytes(shape) bytes, 256-byte aligned. */
 typedef struct {
   int32_t batch;   /* >= 0                               */
@@ -259,8 +260,9 @@ specv_status_t specv_decode_bigram(const specv_decode_shape_t* shape, const void
  * (k1 + 1)] and out_accepted the target review's n. Lenience and epsilon as
  * in specv_verify_lenient. `events`: NULL, or 2 * SPECV_NUM_STAGES events
  * recorded in the last outer round: around the first inner round's drafting
- * (SPECV_STAGE_PLAN slot), its row gather (ROWSTATS slot) and its review
- * (ACCEPT_MASS slot), and around the whole target review with its append
+ * (SPECV_STAGE_PLAN slot), its row gather with the review's pass 1
+ * (ROWSTATS slot) and the rest of its review (ACCEPT_MASS slot), and around
+ * the whole target review with its append
  * (DRAW slot). */
 typedef struct {
   int32_t batch;   /* >= 0                                    */
