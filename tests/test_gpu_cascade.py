@@ -146,3 +146,38 @@ def test_cascade_parity_streamed_rows(svx):
     start = np.random.default_rng(11).integers(0, 9000, B)
     assert_cascade_parity("bf16 V=9000 sq 0.5", svx, tabs, T, start, k1=3, k2=2, rounds=2,
                           lenience="sq", epsilon=0.5, seed=13)
+
+
+def random_cascade_case(seed):
+    """A seeded random cascade problem: V (aligned or not, up to past the
+    8192 elements a workgroup holds), dtype, batch, k1 0..6, k2 0..4, rounds,
+    lenience and epsilon, greedy and sampling temperatures with an occasional
+    NaN one, and an occasional start token outside [0, V)."""
+    rng = np.random.default_rng(7000 + seed)
+    V = int(rng.choice([1, 2, 7, 64, 100, 999, 1024, 2048, 8192, 8200,
+                        int(rng.integers(2, 2000))]))
+    B = int(rng.integers(1, 64 if V <= 2048 else 16))
+    tabs = tables(V, 8000 + seed, s_mid=float(rng.choice([0.2, 0.6, 1.5])),
+                  s_small=float(rng.choice([0.5, 1.4, 3.0])), scale=float(rng.choice([0.7, 1.5, 2.5])))
+    if rng.random() < 0.5:
+        tabs = [bf16(t) for t in tabs]
+    T = np.where(rng.random(B) < 0.3, 0.0, rng.uniform(0.3, 2.0, B)).astype(np.float32)
+    T[rng.random(B) < 0.03] = np.nan
+    start = rng.integers(0, V, B).astype(np.int32)
+    bad = rng.random(B) < 0.03
+    start[bad] = np.where(rng.random(int(bad.sum())) < 0.5, -1, V)
+    kind = ["none", "lin", "sq", "exp"][int(rng.integers(0, 4))]
+    eps = 1.0 if kind == "none" else float(rng.choice([1.0, 0.7, 0.3, 0.05]))
+    kw = dict(k1=int(rng.integers(0, 7)), k2=int(rng.integers(0, 5)), rounds=int(rng.integers(1, 4)),
+              lenience=kind, epsilon=eps, seed=int(rng.integers(0, 2**63)),
+              row_offset=int(rng.integers(0, 2**40)))
+    return tabs, T, start, kw
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_cascade_random_shapes(svx, seed):
+    tabs, T, start, kw = random_cascade_case(seed)
+    got, _ = assert_cascade_parity("random %d %s" % (seed, "bf16" if tabs[0].dtype == np.uint16
+                                                     else "fp32"), svx, tabs, T, start, **kw)
+    failed = np.isnan(T) | (start < 0) | (start >= tabs[0].shape[0])
+    assert (got["length"][failed] == -1).all()

@@ -138,3 +138,36 @@ def test_decode_gpu_sequence_law(svx):
     pv = stats.chisquare(obs, exp).pvalue
     log("[law] decode GPU joint of 3 tokens: p = %.4g" % pv)
     assert pv > 1e-4
+
+
+def random_decode_case(seed):
+    """A seeded random decode problem: V (aligned or not, from 1 up to past
+    the 8192 elements a drafting workgroup holds), dtype, batch, gamma 0..8,
+    rounds, greedy and sampling temperatures with an occasional NaN one, and
+    an occasional start token outside [0, V)."""
+    rng = np.random.default_rng(5000 + seed)
+    V = int(rng.choice([1, 2, 5, 63, 64, 65, 255, 1000, 2048, 2050, 8192, 8200,
+                        int(rng.integers(2, 2500))]))
+    B = int(rng.integers(1, 80 if V <= 2500 else 24))
+    gamma = int(rng.integers(0, 9))
+    rounds = int(rng.integers(1, 5))
+    t, d = tables(V, 6000 + seed, sigma=float(rng.choice([0.1, 0.7, 2.0])),
+                  scale=float(rng.choice([0.5, 1.5, 3.0])))
+    if rng.random() < 0.5:
+        t, d = to_bf16_bits(t), to_bf16_bits(d)
+    T = np.where(rng.random(B) < 0.3, 0.0, rng.uniform(0.3, 2.0, B)).astype(np.float32)
+    T[rng.random(B) < 0.03] = np.nan
+    start = rng.integers(0, V, B).astype(np.int32)
+    bad = rng.random(B) < 0.03
+    start[bad] = np.where(rng.random(int(bad.sum())) < 0.5, -1, V)
+    return t, d, T, start, gamma, rounds, int(rng.integers(0, 2**63)), int(rng.integers(0, 2**40))
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_decode_random_shapes(svx, seed):
+    t, d, T, start, gamma, rounds, s, off = random_decode_case(seed)
+    got, want = assert_decode_parity("random %d %s" % (seed, "bf16" if t.dtype == np.uint16 else
+                                                       "fp32"), svx, t, d, T, start, gamma,
+                                     rounds, seed=s, row_offset=off)
+    failed = np.isnan(T) | (start < 0) | (start >= t.shape[0])
+    assert (got["length"][failed] == -1).all()
