@@ -790,6 +790,7 @@ int oracle_cascade_bigram(int64_t batch, int64_t vocab, int64_t k1, int64_t k2, 
   char* itpack = (char*)malloc((size_t)(B * (k2 + 1)) * row_bytes + 1);
   char* idpack = (char*)malloc((size_t)(B * k2) * row_bytes + 1);
   int32_t* itok = (int32_t*)malloc((size_t)(B * k2 + 1) * 4);
+  int32_t* ipack = (int32_t*)malloc((size_t)(B * k2 + 1) * 4); /* packed inner draft tokens */
   int32_t* igam = (int32_t*)malloc((size_t)(B + 1) * 4);
   /* outer review buffers (fp32) */
   float* otpack = (float*)malloc((size_t)(B * (k1 + 1) * V + 1) * 4);
@@ -869,12 +870,12 @@ int oracle_cascade_bigram(int64_t batch, int64_t vocab, int64_t k1, int64_t k2, 
         for (int64_t i = 0; i < g; ++i) {
           memcpy(idpack + (size_t)(td + i) * row_bytes,
                  (const char*)m2tab + (size_t)ipr[b * (k2 + 1) + i] * row_bytes, row_bytes);
-          otok[td + i] = itok[b * k2 + i]; /* packed draft tokens (scratch use) */
+          ipack[td + i] = itok[b * k2 + i];
         }
         tt += g + 1;
         td += g;
       }
-      oracle_verify(B, V, k2, dtype, tt, td, itpack, idpack, otok, igam, temperature, seed, rbase,
+      oracle_verify(B, V, k2, dtype, tt, td, itpack, idpack, ipack, igam, temperature, seed, rbase,
                     lenience_kind, eps, NULL, NULL, n_out, next_out, NULL, vnear, NULL, NULL,
                     nthreads);
       for (int64_t b = 0; b < B; ++b) {
@@ -962,7 +963,7 @@ int oracle_cascade_bigram(int64_t batch, int64_t vocab, int64_t k1, int64_t k2, 
     }
   }
   for (int64_t b = 0; b < B; ++b) out_length[b] = failed[b] ? -1 : len[b];
-  free(itpack); free(idpack); free(itok); free(igam); free(otpack); free(odpack); free(otok);
+  free(itpack); free(idpack); free(itok); free(ipack); free(igam); free(otpack); free(odpack); free(otok);
   free(ogam); free(dtok); free(dprev); free(dbonus); free(dlen); free(cur); free(len);
   free(failed); free(near); free(vnear); free(dnear); free(n_out); free(next_out); free(ipr); free(z);
   free(p1); free(q2);

@@ -111,6 +111,16 @@ def test_cascade_parity_lossless_no_inner_drafts_and_bad_starts(svx):
     assert got["length"][7] == -1
 
 
+def test_cascade_parity_inner_drafts_past_k1(svx):
+    # k2 > k1: one inner round drafts past the k1 tokens the target reviews
+    tabs = [bf16(t) for t in tables(700, 14)]
+    B = 80
+    T = np.where(np.arange(B) % 5 == 0, 0.0, 1.1).astype(np.float32)
+    start = np.random.default_rng(15).integers(0, 700, B)
+    assert_cascade_parity("bf16 k1=2 k2=5 sq 0.4", svx, tabs, T, start, k1=2, k2=5, rounds=3,
+                          lenience="sq", epsilon=0.4, seed=17)
+
+
 def test_cascade_gpu_target_law(svx):
     tabs = tables(5, 0)
     B, c = 400_000, 2

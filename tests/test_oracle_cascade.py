@@ -42,10 +42,10 @@ def joint3_pvalue(t, res, c, T=1.0):
     return stats.chisquare(obs, exp).pvalue
 
 
-def run(kind, eps, mutant=False, B=300_000, c=2, seed=4, T=1.0):
+def run(kind, eps, mutant=False, B=300_000, c=2, seed=4, T=1.0, k1=3, k2=2):
     t, m, s = tables()
     res = oracle.cascade_bigram(t, m, s, np.full(B, T, np.float32), np.full(B, c, np.int32),
-                                k1=3, k2=2, rounds=3, lenience=kind, epsilon=eps, seed=seed,
+                                k1=k1, k2=k2, rounds=3, lenience=kind, epsilon=eps, seed=seed,
                                 mutant_q_is_p1=mutant)
     return t, res, c
 
@@ -56,6 +56,15 @@ def test_target_law_survives_a_lenient_intermediate_review(kind, eps):
     assert (res.length >= 3).all() and (res.length <= 3 * 4).all()
     assert ((res.accepted >= 0) & (res.accepted <= 3)).all()
     np.testing.assert_array_equal(res.length, (res.accepted + 1).sum(axis=1))
+    assert joint3_pvalue(t, res, c) > P_MIN
+
+
+def test_target_law_with_more_inner_drafts_than_the_target_reviews():
+    # k2 > k1: one inner round already drafts past the k1 tokens the target
+    # reviews; the excess is dropped and the law still holds
+    t, res, c = run("sq", 0.5, k1=1, k2=3, seed=6)
+    assert (res.length >= 3).all() and (res.length <= 3 * 2).all()
+    assert ((res.accepted >= 0) & (res.accepted <= 1)).all()
     assert joint3_pvalue(t, res, c) > P_MIN
 
 
