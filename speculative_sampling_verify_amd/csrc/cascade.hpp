@@ -112,6 +112,47 @@ __device__ __forceinline__ void cas_load8(const void* row, int64_t V, int64_t v0
   }
 }
 
+// The same eight elements as raw 32-bit words: bf16 pairs (element 2w in the
+// low half of word w) or fp32 values. The workgroup row builder holds its
+// rows this way (half the registers for bf16) and widens them in each pass.
+template <int DT>
+struct CasRaw {
+  static constexpr int W = (DT == kBF16) ? 4 : 8;
+  uint32_t w[W];
+  __device__ __forceinline__ float operator[](int j) const {
+    if constexpr (DT == kBF16) return (j & 1) ? bf16_hi(w[j / 2]) : bf16_lo(w[j / 2]);
+    else return __uint_as_float(w[j]);
+  }
+};
+
+template <int DT, bool VEC>
+__device__ __forceinline__ void cas_load8_raw(const void* row, int64_t V, int64_t v0, CasRaw<DT>& r) {
+  if constexpr (VEC && DT == kBF16) {
+    u32x4 q = {0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};
+    if (v0 < V) q = *reinterpret_cast<const u32x4*>(static_cast<const char*>(row) + v0 * 2);
+    r.w[0] = q.x; r.w[1] = q.y; r.w[2] = q.z; r.w[3] = q.w;
+  } else {
+    float z[8];
+    cas_load8<DT, VEC>(row, V, v0, z);
+#pragma unroll
+    for (int q = 0; q < CasRaw<DT>::W; ++q) {
+      if constexpr (DT == kBF16)
+        r.w[q] = (__float_as_uint(z[2 * q + 1]) & 0xffff0000u) | (__float_as_uint(z[2 * q]) >> 16);
+      else
+        r.w[q] = __float_as_uint(z[q]);
+    }
+  }
+}
+
+// Empty asm statements that the compiler must assume change the words, so
+// that a pass widens and exponentiates them again instead of keeping an
+// earlier pass's values alive (several times the registers).
+template <int DT>
+__device__ __forceinline__ void cas_opaque(CasRaw<DT>& r) {
+#pragma unroll
+  for (int u = 0; u < CasRaw<DT>::W; ++u) asm volatile("" : "+v"(r.w[u]));
+}
+
 template <bool VEC>
 __device__ __forceinline__ void cas_store8(float* row, int64_t V, int64_t v0, const float (&z)[8]) {
   if constexpr (VEC) {
@@ -282,7 +323,7 @@ struct CasLds {
   double s1[kCasWaves], s2[kCasWaves], beta[kCasWaves], rmass[kCasWaves];
 };
 
-template <int DT, bool VEC>
+template <int DT, bool VEC, int32_t KIND>
 __global__ __launch_bounds__(kCasWaves * kWave) void k_cas_outer_rows_wg(CascadeArgs a) {
   __shared__ CasLds sh;
   const int lane = threadIdx.x & (kWave - 1);
@@ -323,25 +364,28 @@ __global__ __launch_bounds__(kCasWaves * kWave) void k_cas_outer_rows_wg(Cascade
   }
   const void* r2 = static_cast<const char*>(a.m2tab) + (int64_t)pv * V * esz;
   const float k = temp_scale(T);
-  float z1[kCasSteps][8], z2[kCasSteps][8];
+  CasRaw<DT> z1[kCasSteps], z2[kCasSteps];
 #pragma unroll
   for (int q = 0; q < kCasSteps; ++q) {
     const int64_t st = w + (int64_t)q * kCasWaves;
     if (st < n_steps) {
-      cas_load8<DT, VEC>(r1, V, st * kStep + (int64_t)lane * 8, z1[q]);
-      cas_load8<DT, VEC>(r2, V, st * kStep + (int64_t)lane * 8, z2[q]);
+      cas_load8_raw<DT, VEC>(r1, V, st * kStep + (int64_t)lane * 8, z1[q]);
+      cas_load8_raw<DT, VEC>(r2, V, st * kStep + (int64_t)lane * 8, z2[q]);
     } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) z1[q][j] = z2[q][j] = ninf();
+      for (int u = 0; u < CasRaw<DT>::W; ++u)
+        z1[q].w[u] = z2[q].w[u] = (DT == kBF16) ? 0xff80ff80u : 0xff800000u;
     }
   }
   // 1. maxima
   float m1 = ninf(), m2 = ninf();
 #pragma unroll
-  for (int q = 0; q < kCasSteps; ++q) {
-    m1 = fmaxf(m1, tile_max(z1[q]));
-    m2 = fmaxf(m2, tile_max(z2[q]));
-  }
+  for (int q = 0; q < kCasSteps; ++q)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      m1 = fmaxf(m1, z1[q][j]);
+      m2 = fmaxf(m2, z2[q][j]);
+    }
   m1 = wave_max(m1);
   m2 = wave_max(m2);
   if (lane == 0) {
@@ -356,20 +400,26 @@ __global__ __launch_bounds__(kCasWaves * kWave) void k_cas_outer_rows_wg(Cascade
     M2 = fmaxf(M2, sh.m2[q]);
   }
   const float R1 = ref_point(M1, k), R2 = ref_point(M2, k);
-  // 2. weights in place and the row sums
+  // The weights 2^(fl32(z k - R)) of step q, formed the same way in each
+  // pass (so with the same values); one step's weights are live at a time.
+  auto weights = [&](int q, float (&e1)[8], float (&e2)[8]) {
+    cas_opaque(z1[q]);
+    cas_opaque(z2[q]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      e1[j] = exp2_hw(__builtin_fmaf(z1[q][j], k, -R1));
+      e2[j] = exp2_hw(__builtin_fmaf(z2[q][j], k, -R2));
+    }
+  };
+  // 2. the row sums
   double s1 = 0.0, s2 = 0.0;
 #pragma unroll
   for (int q = 0; q < kCasSteps; ++q) {
     float e1[8], e2[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      z1[q][j] = exp2_hw(__builtin_fmaf(z1[q][j], k, -R1));
-      z2[q][j] = exp2_hw(__builtin_fmaf(z2[q][j], k, -R2));
-      e1[j] = z1[q][j];
-      e2[j] = z2[q][j];
-    }
+    weights(q, e1, e2);
     s1 += (double)tree_sum(e1);
     s2 += (double)tree_sum(e2);
+    __builtin_amdgcn_sched_barrier(0);
   }
   s1 = wave_sum(s1);
   s2 = wave_sum(s2);
@@ -387,48 +437,55 @@ __global__ __launch_bounds__(kCasWaves * kWave) void k_cas_outer_rows_wg(Cascade
   const float i1 = (float)(1.0 / S1), i2 = (float)(1.0 / S2);
   const float inv = (a.lenience == kLenLin) ? (float)(1.0 / (double)a.eps)
                     : (a.lenience == kLenSq) ? (float)(1.0 / ((double)a.eps * (double)a.eps)) : 1.f;
-  // 3. beta and the residual mass
-  double beta = 0.0, rmass = 0.0;
-#pragma unroll
-  for (int q = 0; q < kCasSteps; ++q) {
-    float bb[8], rr[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float p1 = z1[q][j] * i1, q2 = z2[q][j] * i2;
-      bb[j] = fminf(q2, lenient32(p1, a.lenience, a.eps, inv));
-      rr[j] = fmaxf(p1 - q2, 0.f);
-    }
-    beta += (double)tree_sum(bb);
-    rmass += (double)tree_sum(rr);
-  }
-  beta = wave_sum(beta);
-  rmass = wave_sum(rmass);
-  if (lane == 0) {
-    sh.beta[w] = beta;
-    sh.rmass[w] = rmass;
-  }
-  __syncthreads();
-  double B = 0.0, Rm = 0.0;
-#pragma unroll
-  for (int q = 0; q < kCasWaves; ++q) {
-    B += sh.beta[q];
-    Rm += sh.rmass[q];
-  }
-  const float c = (Rm > 0.0) ? (float)((1.0 - B) / Rm) : 0.f;
   const float T_ln2 = (float)((double)T * 0.69314718055994530942);
-  // the row fl32(T ln Q)
+  // 3. beta and the residual mass, then the row fl32(T ln Q). The lenience
+  // kind (a.lenience) is the template's KIND, so each kind's arithmetic
+  // gets a register allocation of its own.
+  {
+    double beta = 0.0, rmass = 0.0;
 #pragma unroll
-  for (int q = 0; q < kCasSteps; ++q) {
-    const int64_t st = w + (int64_t)q * kCasWaves;
-    if (st >= n_steps) break;
-    float o[8];
+    for (int q = 0; q < kCasSteps; ++q) {
+      float e1[8], e2[8], bb[8], rr[8];
+      weights(q, e1, e2);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float p1 = z1[q][j] * i1, q2 = z2[q][j] * i2;
-      const float Q = fminf(q2, lenient32(p1, a.lenience, a.eps, inv)) + c * fmaxf(p1 - q2, 0.f);
-      o[j] = t_ln32(Q, T_ln2);
+      for (int j = 0; j < 8; ++j) {
+        const float p1 = e1[j] * i1, q2 = e2[j] * i2;
+        bb[j] = fminf(q2, lenient32(p1, KIND, a.eps, inv));
+        rr[j] = fmaxf(p1 - q2, 0.f);
+      }
+      beta += (double)tree_sum(bb);
+      rmass += (double)tree_sum(rr);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    cas_store8<VEC>(out, V, st * kStep + (int64_t)lane * 8, o);
+    beta = wave_sum(beta);
+    rmass = wave_sum(rmass);
+    if (lane == 0) {
+      sh.beta[w] = beta;
+      sh.rmass[w] = rmass;
+    }
+    __syncthreads();
+    double B = 0.0, Rm = 0.0;
+#pragma unroll
+    for (int q = 0; q < kCasWaves; ++q) {
+      B += sh.beta[q];
+      Rm += sh.rmass[q];
+    }
+    const float c = (Rm > 0.0) ? (float)((1.0 - B) / Rm) : 0.f;
+#pragma unroll
+    for (int q = 0; q < kCasSteps; ++q) {
+      const int64_t st = w + (int64_t)q * kCasWaves;
+      if (st >= n_steps) break;
+      float e1[8], e2[8], o[8];
+      weights(q, e1, e2);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float p1 = e1[j] * i1, q2 = e2[j] * i2;
+        const float Q = fminf(q2, lenient32(p1, KIND, a.eps, inv)) + c * fmaxf(p1 - q2, 0.f);
+        o[j] = t_ln32(Q, T_ln2);
+      }
+      cas_store8<VEC>(out, V, st * kStep + (int64_t)lane * 8, o);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 }
 

@@ -505,6 +505,17 @@ bool make_cascade_plan(const specv_cascade_shape_t* s, CascadePlan* c) {
   return true;
 }
 
+// The workgroup row builder is instantiated per lenience kind.
+template <int DT, bool VEC>
+void launch_cas_rows_wg(dim3 g, dim3 wg, hipStream_t stream, const CascadeArgs& ca) {
+  switch (ca.lenience) {
+    case kLenLin: hipLaunchKernelGGL((k_cas_outer_rows_wg<DT, VEC, kLenLin>), g, wg, 0, stream, ca); break;
+    case kLenSq: hipLaunchKernelGGL((k_cas_outer_rows_wg<DT, VEC, kLenSq>), g, wg, 0, stream, ca); break;
+    case kLenExp: hipLaunchKernelGGL((k_cas_outer_rows_wg<DT, VEC, kLenExp>), g, wg, 0, stream, ca); break;
+    default: hipLaunchKernelGGL((k_cas_outer_rows_wg<DT, VEC, kLenNone>), g, wg, 0, stream, ca); break;
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -970,11 +981,11 @@ specv_status_t specv_cascade_bigram(const specv_cascade_shape_t* shape, const vo
       // a workgroup per (sequence, position): both drafter rows stay in registers
       const dim3 g((unsigned)ow), wg(kCasWaves * kWave);
       if (bf16) {
-        if (ovec) hipLaunchKernelGGL((k_cas_outer_rows_wg<kBF16, true>), g, wg, 0, stream, ca);
-        else hipLaunchKernelGGL((k_cas_outer_rows_wg<kBF16, false>), g, wg, 0, stream, ca);
+        if (ovec) launch_cas_rows_wg<kBF16, true>(g, wg, stream, ca);
+        else launch_cas_rows_wg<kBF16, false>(g, wg, stream, ca);
       } else {
-        if (ovec) hipLaunchKernelGGL((k_cas_outer_rows_wg<kF32, true>), g, wg, 0, stream, ca);
-        else hipLaunchKernelGGL((k_cas_outer_rows_wg<kF32, false>), g, wg, 0, stream, ca);
+        if (ovec) launch_cas_rows_wg<kF32, true>(g, wg, stream, ca);
+        else launch_cas_rows_wg<kF32, false>(g, wg, stream, ca);
       }
     } else if (bf16) {
       if (ovec) hipLaunchKernelGGL((k_cas_outer_rows<kBF16, true>), dim3(blocks_for(ow)), block, 0, stream, ca);
