@@ -191,3 +191,15 @@ def test_cascade_random_shapes(svx, seed):
                                                      else "fp32"), svx, tabs, T, start, **kw)
     failed = np.isnan(T) | (start < 0) | (start >= tabs[0].shape[0])
     assert (got["length"][failed] == -1).all()
+
+
+def test_cascade_bench_launch_full_size(svx):
+    # the launch the cascade benchmark times: the benchmark's three bigram
+    # tables (V = 8192, bf16), 2048 sequences, k1 = 5, k2 = 3, 8 rounds, f_sq
+    # with eps = 0.5 at the intermediate review, T = 1
+    import synth
+    tabs = synth.bigram_tables(8192, small=True)
+    B = 2048
+    assert_cascade_parity("bench launch", svx, [tabs.target, tabs.draft, tabs.small],
+                          np.ones(B, np.float32), tabs.start(B), k1=5, k2=3, rounds=8,
+                          lenience="sq", epsilon=0.5, seed=0)

@@ -171,3 +171,13 @@ def test_decode_random_shapes(svx, seed):
                                      rounds, seed=s, row_offset=off)
     failed = np.isnan(T) | (start < 0) | (start >= t.shape[0])
     assert (got["length"][failed] == -1).all()
+
+
+def test_decode_bench_launch_full_size(svx):
+    # the launch the decode benchmark times: the benchmark's bigram tables
+    # (V = 8192, bf16), 2048 sequences, gamma = 5, 8 rounds, T = 1
+    import synth
+    tabs = synth.bigram_tables(8192)
+    B = 2048
+    assert_decode_parity("bench launch", svx, tabs.target, tabs.draft, np.ones(B, np.float32),
+                         tabs.start(B), gamma=5, rounds=8, seed=0)

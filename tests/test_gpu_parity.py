@@ -506,6 +506,12 @@ def test_diagnostics_parity(svx, name, kw, k):
     assert_diag_parity(name, make(name, **kw), k)
 
 
+def test_diagnostics_bench_launch_full_size(svx):
+    # the launch the diagnostics benchmark times: 2000 rounds of the T5-XXL-like
+    # shape (10,000 draft positions), top-16
+    assert_diag_parity("t5xxl_like_2000_rounds (bench launch)", synth.t5xxl_like(rounds=2000), 16)
+
+
 def test_diagnostics_edges(svx):
     rng = np.random.default_rng(8)
     # odd V (scalar loads), masked tails, ties, a NaN row, T = 0 and k = 0 / k = V
