@@ -399,6 +399,17 @@ def test_lenient_parity_t5xxl_like(svx, kind, eps):
     assert_parity("lenient %s %g" % (kind, eps), x, got, orc)
 
 
+def test_lenient_bench_launch_full_size(svx):
+    # the launch the lossy benchmark times: 2000 rounds of the T5-XXL-like
+    # shape with f_sq and eps = 0.5
+    x = synth.t5xxl_like(rounds=2000)
+    log("[case] lenient sq eps=0.5 t5xxl_like B=%d (bench launch)" % x.batch)
+    got = run_gpu_lenient(svx, x, "sq", 0.5)
+    orc = run_oracle(x, lenience="sq", epsilon=0.5)
+    assert got[2] == 0
+    assert_parity("lenient sq 0.5 bench launch", x, got, orc)
+
+
 def test_lenient_parity_mixed_greedy_fp32(svx):
     # fp32, odd sequences greedy (lenience must not touch them), V = 256000
     x = synth.large_vocab(batch=6)
