@@ -216,7 +216,7 @@ WORKLOADS = [
     ("tiny_cpu_10000_rounds", lambda: synth.tiny_cpu(rounds=10000)),
     ("tiny_cpu_greedy", lambda: synth.tiny_cpu(rounds=10000, greedy=True)),
     ("t5xxl_like_300_rounds", lambda: synth.t5xxl_like(rounds=300)),
-    ("t5xxl_like_greedy_300", lambda: synth.t5xxl_like(rounds=300, greedy=True)),
+    ("t5xxl_like_greedy_2000 (bench launch)", lambda: synth.t5xxl_like(rounds=2000, greedy=True)),
     ("serving_b64_full", lambda: synth.serving_b64()),
     ("ragged_b256_b48", lambda: synth.ragged_b256(batch=48)),
     ("large_vocab_b24", lambda: synth.large_vocab(batch=24, identical=2)),
