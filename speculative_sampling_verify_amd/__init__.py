@@ -480,7 +480,9 @@ class StageEvents:
         return float(ms.value)
 
     def __del__(self):
-        h = StageEvents._hip
+        # type(self), not the module global, which may already be gone at
+        # interpreter shutdown
+        h = getattr(type(self), "_hip", None)
         if h is not None:
             for ev in self.array:
                 if ev:
