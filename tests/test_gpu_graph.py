@@ -172,3 +172,36 @@ def test_graph_diagnostics(svx):
                                               inp["temperature"], k, max_gamma=x0.max_gamma)
 
     _replay_check("diagnostics", capture, eager, inputs, static)
+
+
+def test_graph_cascade(svx):
+    # a whole vertical-cascade call (inner drafting and lenient reviews, the
+    # target review's row builder and lossless review) captured once
+    print("[case] graph capture cascade", flush=True)
+    V, B = 700, 48
+    rng = np.random.default_rng(4)
+    t = (rng.standard_normal((V, V)) * 1.5).astype(np.float32)
+    tabs = [torch.from_numpy(synth.to_bf16_bits(a).view(np.int16)).cuda()
+            for a in (t, t + rng.standard_normal((V, V)).astype(np.float32) * 0.6,
+                      t + rng.standard_normal((V, V)).astype(np.float32) * 1.4)]
+    inputs = [{"T": torch.from_numpy(np.where(np.arange(B) % 4 == 0, 0.0, 0.7 + 0.3 * i)
+                                      .astype(np.float32)).cuda(),
+               "start": torch.from_numpy(rng.integers(0, V, B).astype(np.int32)).cuda()}
+              for i in range(3)]
+    static = {k: v.clone() for k, v in inputs[0].items()}
+    k1, k2, R = 3, 2, 2
+    shape = svx.SpecvCascadeShape(B, V, k1, k2, R, svx.SPECV_BF16)
+    ws = torch.empty(svx.specv_cascade_workspace_bytes(shape), dtype=torch.uint8, device="cuda")
+    out = {"tokens": torch.empty((B, R * (k1 + 1)), dtype=torch.int32, device="cuda"),
+           "length": torch.empty(B, dtype=torch.int32, device="cuda"),
+           "accepted": torch.empty((B, R), dtype=torch.int32, device="cuda")}
+    kw = dict(k1=k1, k2=k2, rounds=R, lenience="sq", epsilon=0.5, seed=9)
+
+    def capture(stream):
+        return svx.specv_cascade_bigram(*tabs, static["T"], static["start"], out=out,
+                                        workspace=ws, stream=stream, **kw)
+
+    def eager(inp):
+        return svx.specv_cascade_bigram(*tabs, inp["T"], inp["start"], **kw)
+
+    _replay_check("cascade", capture, eager, inputs, static)
