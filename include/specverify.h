@@ -91,7 +91,8 @@ typedef struct {
   int32_t vocab;               /* V >= 1                                     */
   int32_t max_gamma;           /* 0 <= max_gamma <= SPECV_MAX_GAMMA          */
   specv_dtype_t dtype;         /* dtype of both logit tensors                */
-  int64_t total_target_rows;   /* sum_b (gamma_b + 1) == total_draft_rows + B */
+  int64_t total_target_rows;   /* sum_b (gamma_b + 1) == total_draft_rows + B;
+                                  at most 2^29, and total_target_rows * V at most 2^40 */
   int64_t total_draft_rows;    /* sum_b gamma_b <= B * max_gamma             */
 } specv_shape_t;
 

@@ -75,6 +75,10 @@ bool shape_ok(const specv_shape_t* s) {
   if (s->total_draft_rows > (int64_t)s->batch * s->max_gamma) return false;
   // packed element offsets must fit int64 comfortably
   if (s->total_target_rows > ((int64_t)1 << 40) / s->vocab) return false;
+  // every launch grid stays below 2^31 workgroups (at most 2^30 rows of both
+  // kinds, a few chunks each; many chunks only where V, and so 2^40 / V, bound
+  // the rows)
+  if (s->total_target_rows > ((int64_t)1 << 29)) return false;
   return true;
 }
 
@@ -199,8 +203,12 @@ inline void mark(hipEvent_t* ev, int idx, hipStream_t s) {
   if (ev && ev[idx]) (void)hipEventRecord(ev[idx], s);
 }
 
+// Workgroups for `waves` waves. The shape checks keep every grid far below
+// 2^31 workgroups; a count past that gives 0, which the launch rejects,
+// rather than a truncated grid.
 inline unsigned blocks_for(int64_t waves) {
-  return (unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock);
+  const int64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
+  return blocks > 0x7fffffff ? 0u : (unsigned)blocks;
 }
 
 // A batch is uniform when its row totals equal B * (max_gamma + 1): with

@@ -48,6 +48,14 @@ def test_workspace_bytes():
     a = svx.specv_workspace_bytes(shape(B=64, V=128256, g=7))
     b = svx.specv_workspace_bytes(shape(B=128, V=128256, g=7))
     assert 0 < a < b
+    # row totals: at most 2^29 target rows (launch grids), rows * V at most 2^40
+    B = (1 << 29) // 8
+    assert svx.specv_workspace_bytes(shape(B=B, V=1, g=7)) > 0
+    assert svx.specv_workspace_bytes(shape(B=B + 1, V=1, g=7)) == 0
+    assert svx.specv_workspace_bytes(shape(B=1 << 20, V=1 << 20, g=0)) > 0
+    assert svx.specv_workspace_bytes(shape(B=(1 << 20) + 1, V=1 << 20, g=0)) == 0
+    assert svx.specv_decode_workspace_bytes(svx.SpecvDecodeShape(B + 1, 2, 7, 1, 1)) == 0
+    assert svx.specv_cascade_workspace_bytes(svx.SpecvCascadeShape(B + 1, 2, 7, 1, 1, 1)) == 0
 
 
 def call_verify(shp, ws=FAKE, ws_bytes=1 << 30, target=FAKE, draft=FAKE, out=FAKE):
