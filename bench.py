@@ -197,12 +197,18 @@ def cpu_baseline(x, gpu_n, gpu_next, budget_s=12.0, lenience="none", epsilon=1.0
                               "near_ties": int(res.near_tie.sum())}}
 
 
-def load_traffic(workload, sha):
+def load_traffic(workload, sha, config=None):
+    """HBM bytes per launch of a bench line's dominant kernel, from the
+    counter runs stored under profiles/, while the kernel sources still hash
+    to the value they were taken with (and, where given, the launch matches
+    the configuration they were taken on); else None."""
     f = ROOT / "profiles" / ("traffic_%s.json" % workload)
     if not f.exists():
         return None
     rec = json.loads(f.read_text())
     if rec.get("kernel_sha") != sha:
+        return None
+    if config is not None and rec.get("config") != config:
         return None
     return rec.get("traffic_bytes_per_launch")
 
@@ -291,7 +297,10 @@ def bench_diagnostics(args, torch, svx, dev):
         "config": {"workload": desc + "; per-position diagnostics, top-%d" % k, "batch": x.batch,
                    "vocab": x.vocab, "logits": x.dtype, "top_k": k},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": load_traffic("t5xxl_like_diag", kernel_sha(),
+                                             {"workload": args.workload, "batch": x.batch,
+                                              "top_k": k}),
                      "kernel": "k5_diag_pass", "algorithmic_bytes_per_launch": by["pass2"],
                      "avg_launch_ms": p2_ms},
         "step_gbps": (by["pass1"] + by["pass2"]) / (ms_step * 1e-3) / 1e9,
@@ -362,7 +371,10 @@ def bench_decode(args, torch, svx, dev):
                                "%d rounds, T=1" % (B, V, g, R),
                    "batch": B, "vocab": V, "gamma": g, "rounds": R},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None, "kernel": "k_dec_gather_stats",
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": load_traffic("decode_bigram", kernel_sha(),
+                                             {"batch": B, "vocab": V, "gamma": g, "rounds": R}),
+                     "kernel": "k_dec_gather_stats",
                      "algorithmic_bytes_per_launch": gather_bytes,
                      "avg_launch_ms": stage_ms["gather"]},
         "stage_ms_last_round": stage_ms,
@@ -443,7 +455,11 @@ def bench_cascade(args, torch, svx, dev):
                                "f_sq eps=%g at the intermediate review, T=1" % (B, V, k1, k2, R, eps),
                    "batch": B, "vocab": V, "k1": k1, "k2": k2, "rounds": R},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None, "kernel": "k_dec_gather_stats",
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": load_traffic("cascade_bigram", kernel_sha(),
+                                             {"batch": B, "vocab": V, "k1": k1, "k2": k2,
+                                              "rounds": R}),
+                     "kernel": "k_dec_gather_stats",
                      "algorithmic_bytes_per_launch": gather_bytes,
                      "avg_launch_ms": stage_ms["inner_gather"]},
         "stage_ms_last_round": stage_ms,
