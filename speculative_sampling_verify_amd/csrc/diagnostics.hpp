@@ -92,11 +92,12 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
                                         __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-// A wave's candidate buffer in LDS: kDiagGroup slots of a tile are appended
-// between two checks, and the buffer is cut back to the best K whenever it
-// holds more than max(2K, 64) keys, so it never exceeds kDiagCap.
+// A wave's candidate buffer in LDS: a slot's candidates (at most one per
+// lane) are appended, and the buffer is cut back to the best K as soon as it
+// holds more than max(2K, 64) keys, so it never exceeds kDiagCap. Scans go
+// in groups of kDiagGroup slots.
 constexpr int kDiagGroup = 8;
-constexpr int kDiagCap = 2 * kMaxTopK + kDiagGroup * kWave;
+constexpr int kDiagCap = 2 * kMaxTopK + kWave;
 constexpr int kDiagSlots = kDiagCap / kWave;
 
 // rank[s] += number of the keys buf[0..n) above mine[s], for s < ns: eight
@@ -276,16 +277,16 @@ __global__ __launch_bounds__(kBlock) void k5_diag_pass(DiagArgs a) {
       const uint64_t m = ballot(cand);                                      \
       if (cand) buf[count + lanes_below(m)] = key;                          \
       count += __popcll(m);                                                 \
+      if (count > limit) {                                                  \
+        count = keep_best(buf, count, K, lane);                             \
+        th = buf[K - 1];                                                    \
+        thz = key_value(th);                                                \
+      }                                                                     \
     }                                                                       \
   }
     SPECV_SCAN(0) SPECV_SCAN(1) SPECV_SCAN(2) SPECV_SCAN(3)
     SPECV_SCAN(4) SPECV_SCAN(5) SPECV_SCAN(6) SPECV_SCAN(7)
 #undef SPECV_SCAN
-    if (count > limit) {
-      count = keep_best(buf, count, K, lane);
-      th = buf[K - 1];
-      thz = key_value(th);
-    }
   };
   auto process = [&](const Raw& rd, const Raw& rt, int it) {
     const int64_t e0 = tile_start(it);
