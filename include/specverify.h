@@ -183,7 +183,9 @@ specv_status_t specv_verify_lenient(const specv_shape_t* shape, const void* targ
  * stages as in specv_verify_profiled; the stages here are the plan, pass 1
  * (row statistics of every target and draft row), pass 2 (SPECV_STAGE_
  * ACCEPT_MASS slot: the per-position sums and top-k lists) and the merge
- * (SPECV_STAGE_DRAW slot). */
+ * (SPECV_STAGE_DRAW slot; it shares pass 2's launch, and its events are
+ * recorded back to back, when a position has 1, 2 or 4 pass-1 chunks and
+ * chunks * top_k <= 64). */
 #define SPECV_MAX_TOP_K 64
 size_t specv_diagnostics_workspace_bytes(const specv_shape_t* shape, int32_t top_k);
 specv_status_t specv_position_diagnostics(const specv_shape_t* shape, const void* target_logits,

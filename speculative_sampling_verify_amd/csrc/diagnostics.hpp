@@ -194,19 +194,30 @@ __device__ __forceinline__ void diag_terms(const typename Tile<DT, VEC>::Raw& rd
   sA = tree_sum(pA);
 }
 
-template <int DT, bool VEC>
-__global__ __launch_bounds__(kBlock) void k5_diag_pass(DiagArgs a) {
+// What one (position, chunk) wave of pass 2 leaves for the merge of its
+// position: its fp64 sums, the keys it kept (best first, in its LDS buffer)
+// and the position's row statistics.
+struct DiagChunk {
+  double sa, ss, sA;
+  int count;
+  RowStat st_t, st_d;
+  float k;
+};
+
+// Pass 2 of work item `item` (position j = item / chunks, chunk c = item %
+// chunks), by one wave with the LDS buffer `buf`. Returns false, with nothing
+// written, for a position that the merge reports as NaN (layout error,
+// invalid temperature, unusable row). With STORE the wave writes its sums and
+// its list for the merge kernel; else it leaves them in `out` and `buf`.
+template <int DT, bool VEC, bool STORE>
+__device__ __forceinline__ bool diag_chunk(const DiagArgs& a, int64_t item, int lane,
+                                           uint64_t* buf, DiagChunk& out) {
   using TL = Tile<DT, VEC>;
   using Raw = typename TL::Raw;
   constexpr int NE = TL::NE;
   constexpr int NG = NE / 8;
   static_assert(kDiagGroup == 8, "diag_terms and the scan share 8-slot groups");
   constexpr int64_t esz = (DT == kBF16) ? 2 : 4;
-  __shared__ __attribute__((aligned(16))) uint64_t sbuf[kWavesPerBlock][kDiagCap];
-  const int lane = threadIdx.x & (kWave - 1);
-  uint64_t* buf = sbuf[threadIdx.x >> 6];
-  const int64_t item = wave_uniform((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
-  if (item >= a.total_d * a.chunks) return;
   const int64_t j = item / a.chunks;
   const int c = (int)(item - j * a.chunks);
   // The sequence of draft row j: arithmetic in a uniform batch, whose rows
@@ -218,7 +229,7 @@ __global__ __launch_bounds__(kBlock) void k5_diag_pass(DiagArgs a) {
   } else {
     const uint32_t st0 = a.status[0];
     const int32_t bs = a.dseq[j];
-    if (st0 & kLayoutError) return;
+    if (st0 & kLayoutError) return false;
     b = bs;
   }
   const int64_t tr = j + b;
@@ -243,13 +254,13 @@ __global__ __launch_bounds__(kBlock) void k5_diag_pass(DiagArgs a) {
   const int K = a.K;
   float thz = (K > 0) ? a.bar[j * a.chunks + c] : ninf();  // logit of th
   const float k = diag_scale(a, j, b);
-  if (a.uniform_g > 0 && (a.status[0] & kLayoutError)) return;
-  if (!(k >= 0.f)) return;  // invalid temperature: the merge reports NaN
+  if (a.uniform_g > 0 && (a.status[0] & kLayoutError)) return false;
+  if (!(k >= 0.f)) return false;  // invalid temperature: the merge reports NaN
   const bool sampling = k > 0.f;
   if (sampling) fetch_row(trow, 0, ta);
   const RowStat st_t = merge_row_from(qt, a.tparts + tr * a.chunks, a.chunks, k, sampling);
   const RowStat st_d = merge_row_from(qd, a.dparts + j * a.chunks, a.chunks, k, sampling);
-  if (!st_t.valid || !st_d.valid) return;
+  if (!st_t.valid || !st_d.valid) return false;
   const float rTD = sampling ? (float)(st_d.s / st_t.s) : 0.f;
   const float iD = sampling ? (float)(1.0 / st_d.s) : 0.f;
   const int limit = (2 * K > kWave) ? 2 * K : kWave;
@@ -336,14 +347,117 @@ __global__ __launch_bounds__(kBlock) void k5_diag_pass(DiagArgs a) {
     ss = wave_sum(ss);
     sA = wave_sum(sA);
   }
-  if (lane == 0) a.parts[slot] = DiagPart{sa, ss, sA};
-  if (K > 0) {
-    count = keep_best(buf, count, K, lane);
-    if (lane < K) {
+  if (K > 0) count = keep_best(buf, count, K, lane);
+  if constexpr (STORE) {
+    if (lane == 0) a.parts[slot] = DiagPart{sa, ss, sA};
+    if (K > 0 && lane < K) {
       const bool have = lane < count;
       const uint64_t key = have ? buf[lane] : 0ull;
       a.topz[slot * K + lane] = have ? key_value(key) : ninf();
       a.topi[slot * K + lane] = have ? key_index(key) : INT32_MAX;
+    }
+  } else {
+    out = DiagChunk{sa, ss, sA, count, st_t, st_d, k};
+  }
+  return true;
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kBlock) void k5_diag_pass(DiagArgs a) {
+  __shared__ __attribute__((aligned(16))) uint64_t sbuf[kWavesPerBlock][kDiagCap];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t item = wave_uniform((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
+  if (item >= a.total_d * a.chunks) return;
+  DiagChunk unused;
+  (void)diag_chunk<DT, VEC, true>(a, item, lane, sbuf[threadIdx.x >> 6], unused);
+}
+
+// Pass 2 and the merge in one launch, for 1, 2 or 4 chunks per position and
+// at most 64 NS keys in a position's lists: the chunk waves of a position are
+// then in one workgroup (item = 4 blockIdx + wave), leave their sums and kept
+// keys in LDS, and after a workgroup barrier the chunk-0 wave merges them
+// exactly as k6_diag_merge does from global memory (the same reductions in
+// the same order, so the same bits). Every wave of the workgroup reaches the
+// barrier: nothing returns before it.
+template <int DT, bool VEC, int NS>
+__global__ __launch_bounds__(kBlock) void k5_diag_pass_merge(DiagArgs a) {
+  __shared__ __attribute__((aligned(16))) uint64_t sbuf[kWavesPerBlock][kDiagCap];
+  __shared__ __attribute__((aligned(16))) uint64_t mbuf[kWavesPerBlock * kMaxTopK];
+  __shared__ DiagPart mpart[kWavesPerBlock];
+  __shared__ int mcount[kWavesPerBlock];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = (int)(threadIdx.x >> 6);
+  const int64_t item = wave_uniform((int64_t)blockIdx.x * kWavesPerBlock + w);
+  const bool in_range = item < a.total_d * a.chunks;
+  DiagChunk o{};
+  const bool valid = in_range && diag_chunk<DT, VEC, false>(a, item, lane, sbuf[w], o);
+  if (lane == 0) {
+    mpart[w] = valid ? DiagPart{o.sa, o.ss, o.sA} : DiagPart{0.0, 0.0, 0.0};
+    mcount[w] = valid ? o.count : 0;
+  }
+  __syncthreads();
+  const int C = a.chunks;
+  if (!in_range || w % C != 0) return;
+  const int64_t j = item / C;
+  const int K = a.K;
+  if (!valid) {
+    if (lane == 0) {
+      a.out_alpha[j] = __builtin_nan("");
+      a.out_entropy[j] = __builtin_nan("");
+    }
+    if (lane < K) {
+      a.out_index[j * K + lane] = -1;
+      a.out_prob[j * K + lane] = __builtin_nan("");
+    }
+    return;
+  }
+  const bool sampling = o.k > 0.f;
+  double alpha, entropy;
+  if (sampling) {
+    const DiagPart part = (lane < C) ? mpart[w + lane] : DiagPart{0.0, 0.0, 0.0};
+    alpha = wave_sum(part.alpha);
+    const double S = wave_sum(part.s), A = wave_sum(part.a);
+    entropy = log(S) - 0.69314718055994530942 * A / S;
+  } else {
+    alpha = (o.st_t.arg == o.st_d.arg) ? 1.0 : 0.0;
+    entropy = 0.0;
+  }
+  if (lane == 0) {
+    a.out_alpha[j] = alpha;
+    a.out_entropy[j] = entropy;
+  }
+  if (K == 0) return;
+  // the union of the chunk lists, chunk by chunk, empty places as key 0
+  const int n = C * K;
+  const int ns = (n + kWave - 1) / kWave;
+  const int stride = (n + 7) / 8 * 8;
+  uint64_t* mb = mbuf + (w / C) * stride;
+  uint64_t mine[NS];  // n <= 64 NS (checked at launch)
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int e = lane + s * kWave;
+    uint64_t key = 0ull;
+    if (s < ns && e < n) {
+      const int cc = e / K, l = e - cc * K;
+      if (l < mcount[w + cc]) key = sbuf[w + cc][l];
+      mb[e] = key;
+    }
+    mine[s] = key;
+  }
+  __builtin_amdgcn_wave_barrier();
+  int rank[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) rank[s] = 0;
+  count_above<NS>(mb, n, ns, mine, rank);
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    if (s < ns && mine[s] != 0ull && rank[s] < K) {
+      const float z = key_value(mine[s]);
+      double q;
+      if (sampling) q = exp2((double)z * (double)o.k - (double)o.st_d.rk) / o.st_d.s;
+      else q = (rank[s] == 0) ? 1.0 : 0.0;
+      a.out_index[j * K + rank[s]] = key_index(mine[s]);
+      a.out_prob[j * K + rank[s]] = q;
     }
   }
 }

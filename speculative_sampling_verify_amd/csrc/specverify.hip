@@ -666,8 +666,21 @@ specv_status_t specv_position_diagnostics(const specv_shape_t* shape, const void
   a.temperature = temperature;
   const dim3 grid(blocks_for(p.td * p.chunks1)), block(kBlock);
   mark(events, 2 * SPECV_STAGE_ACCEPT_MASS, stream);
+  // with 1, 2 or 4 chunks per position a workgroup holds whole positions, and
+  // for lists of at most 64 keys in all the merge runs in the pass-2 launch
+  // (its event pair then times nothing); longer lists rank faster in a launch
+  // of their own
+  const bool fused_merge = kWavesPerBlock % p.chunks1 == 0 && p.chunks1 * top_k <= kWave;
   if (p.td == 0) {
     // nothing to compute
+  } else if (fused_merge) {
+    if (p.dt == kBF16) {
+      if (vec) hipLaunchKernelGGL((k5_diag_pass_merge<kBF16, true, 1>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((k5_diag_pass_merge<kBF16, false, 1>), grid, block, 0, stream, a);
+    } else {
+      if (vec) hipLaunchKernelGGL((k5_diag_pass_merge<kF32, true, 1>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((k5_diag_pass_merge<kF32, false, 1>), grid, block, 0, stream, a);
+    }
   } else if (p.dt == kBF16) {
     if (vec) hipLaunchKernelGGL((k5_diag_pass<kBF16, true>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((k5_diag_pass<kBF16, false>), grid, block, 0, stream, a);
@@ -679,7 +692,7 @@ specv_status_t specv_position_diagnostics(const specv_shape_t* shape, const void
   mark(events, 2 * SPECV_STAGE_ACCEPT_MASS + 1, stream);
   mark(events, 2 * SPECV_STAGE_DRAW, stream);
   const size_t merge_lds = (size_t)kWavesPerBlock * ((p.chunks1 * top_k + 7) / 8 * 8) * 8;
-  if (p.td > 0) {
+  if (p.td > 0 && !fused_merge) {
     // 64-key slots per lane for the union of the chunk lists
     const int n = p.chunks1 * top_k, ns = (n + kWave - 1) / kWave;
     const dim3 mg(blocks_for(p.td));
