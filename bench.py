@@ -301,7 +301,8 @@ def bench_diagnostics(args, torch, svx, dev):
                      "traffic": load_traffic("t5xxl_like_diag", kernel_sha(),
                                              {"workload": args.workload, "batch": x.batch,
                                               "top_k": k}),
-                     "kernel": "k5_diag_pass", "algorithmic_bytes_per_launch": by["pass2"],
+                     "kernel": "k5_diag_pass (k5_diag_pass_merge when the merge shares its launch)",
+                     "algorithmic_bytes_per_launch": by["pass2"],
                      "avg_launch_ms": p2_ms},
         "step_gbps": (by["pass1"] + by["pass2"]) / (ms_step * 1e-3) / 1e9,
         "stage_ms_instrumented": stage_ms,
