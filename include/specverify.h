@@ -338,8 +338,11 @@ specv_status_t specv_softmax_rows(const specv_shape_t* shape, const void* target
 specv_status_t specv_philox4x32_10(uint64_t seed, const uint32_t* ctr, uint32_t* out, int64_t n,
                                    hipStream_t stream);
 
-/* Plain device copy of `bytes` bytes (16-byte aligned pointers): a
- * calibration kernel for memory counters and copy bandwidth. */
+/* Device copy of `bytes` bytes (16-byte aligned pointers, bytes a multiple
+ * of 16): whole 64 KiB segments with the read probe's tiled pattern (two
+ * sibling waves per segment on alternate 4 KiB tiles, non-temporal loads and
+ * stores), a shorter tail by a grid-stride copy. A calibration kernel for
+ * memory counters and copy bandwidth. */
 specv_status_t specv_copy_bytes(void* dst, const void* src, size_t bytes, hipStream_t stream);
 
 /* Read-only stream of `bytes` bytes at src (device, 16-byte aligned; bytes a

@@ -1119,12 +1119,24 @@ specv_status_t specv_copy_bytes(void* dst, const void* src, size_t bytes, hipStr
   if (bytes == 0) return SPECV_OK;
   if (!dst || !src || bytes % 16 != 0 || !aligned(dst, 16) || !aligned(src, 16))
     return SPECV_ERR_INVALID_ARGUMENT;
-  const int64_t n16 = (int64_t)(bytes / 16);
-  int64_t blocks = (n16 + kBlock - 1) / kBlock;
-  if (blocks > 256 * 64) blocks = 256 * 64;
-  hipLaunchKernelGGL(k_copy, dim3((unsigned)blocks), dim3(kBlock), 0, stream,
-                     static_cast<u32x4*>(dst), static_cast<const u32x4*>(src), n16);
-  return launched();
+  // whole 64 KiB segments with the tiled copy, a shorter tail grid-stride
+  const int64_t segments = (int64_t)(bytes / kProbeSegBytes);
+  const int64_t tail16 = (int64_t)(bytes % kProbeSegBytes) / 16;
+  u32x4* d = static_cast<u32x4*>(dst);
+  const u32x4* s = static_cast<const u32x4*>(src);
+  if (segments > 0) {
+    hipLaunchKernelGGL(k_copy_tiled, dim3(blocks_for(2 * segments)), dim3(kBlock), 0, stream, d, s,
+                       segments);
+    const specv_status_t st = launched();
+    if (st != SPECV_OK) return st;
+  }
+  if (tail16 > 0) {
+    const int64_t off = segments * (kProbeSegBytes / 16);
+    hipLaunchKernelGGL(k_copy, dim3((unsigned)((tail16 + kBlock - 1) / kBlock)), dim3(kBlock), 0,
+                       stream, d + off, s + off, tail16);
+    return launched();
+  }
+  return SPECV_OK;
 }
 
 specv_status_t specv_read_bytes(const void* src, size_t bytes, uint32_t* sink,

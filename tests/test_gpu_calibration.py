@@ -1,4 +1,4 @@
-"""The calibration kernels through the C ABI: the plain copy behind the
+"""The calibration kernels through the C ABI: the copy behind the
 memory-counter scale factors and the bandwidth figures, and the read probe
 (pass 1's access pattern, read only). Both must move exactly the bytes they
 are given: the copy reproduces its source, and the probe's per-wave XOR
@@ -20,9 +20,12 @@ def svx():
     return m
 
 
-def test_copy_bytes_exact(svx):
+@pytest.mark.parametrize("nbytes", [48, 3 * 65536 + 48, 4096 * 65536])
+def test_copy_bytes_exact(svx, nbytes):
+    # whole 64 KiB segments take the tiled copy, a shorter tail the grid-stride one
+    print("[case] copy %d bytes" % nbytes, flush=True)
     rng = np.random.default_rng(1)
-    src = rng.integers(0, 256, 3 * 65536 + 48, dtype=np.uint8)
+    src = rng.integers(0, 256, nbytes, dtype=np.uint8)
     s = torch.from_numpy(src).cuda()
     d = torch.zeros_like(s)
     svx.specv_copy_bytes(d, s)
