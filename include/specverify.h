@@ -229,6 +229,9 @@ typedef struct {
   specv_dtype_t dtype;
 } specv_decode_shape_t;
 
+/* Workspace bytes for a decode call; 0 for an invalid shape. Size limits:
+ * V * V and batch * rounds * (gamma + 1) at most 2^40, and the verify step
+ * of a round (batch * (gamma + 1) target rows of V) within specv_shape_t's. */
 size_t specv_decode_workspace_bytes(const specv_decode_shape_t* shape);
 specv_status_t specv_decode_bigram(const specv_decode_shape_t* shape, const void* target_table,
                                    const void* draft_table, const float* temperature,
@@ -276,6 +279,10 @@ typedef struct {
   specv_dtype_t dtype;
 } specv_cascade_shape_t;
 
+/* Workspace bytes for a cascade call; 0 for an invalid shape. Size limits:
+ * V * V and batch * rounds * (k1 + 1) at most 2^40, and both reviews
+ * (batch * (k1 + 1) and batch * (k2 + 1) target rows of V) within
+ * specv_shape_t's. */
 size_t specv_cascade_workspace_bytes(const specv_cascade_shape_t* shape);
 specv_status_t specv_cascade_bigram(const specv_cascade_shape_t* shape, const void* target_table,
                                     const void* mid_table, const void* small_table,

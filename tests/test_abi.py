@@ -103,3 +103,58 @@ def test_status_strings():
     for code in range(5):
         assert svx.specv_status_string(code)
     assert svx.specv_status_string(99) == "unknown status"
+
+
+def shape_valid(B, V, mg, dt, tt, td):
+    """The documented shape rules of specverify.h."""
+    return (B >= 0 and V >= 1 and 0 <= mg <= 63 and dt in (0, 1) and td >= 0 and tt >= 0
+            and tt == td + B and td <= B * mg and tt <= (1 << 29) and tt * V <= (1 << 40))
+
+
+def test_shape_rules_property():
+    # random descriptors, extremes included: the workspace query is nonzero exactly
+    # for the shapes the header allows, and the verify call rejects every other one
+    # before anything is enqueued (the fake pointers are never touched)
+    hyp = pytest.importorskip("hypothesis")
+    st = pytest.importorskip("hypothesis.strategies")
+    i32 = st.one_of(st.integers(-3, 70), st.integers(-(1 << 31), (1 << 31) - 1))
+    i64 = st.one_of(st.integers(-3, 300), st.integers(0, 1 << 41), st.integers(-(1 << 63), (1 << 63) - 1))
+
+    @hyp.settings(max_examples=3000, deadline=None, derandomize=True)
+    @hyp.given(B=i32, V=i32, mg=i32, dt=st.integers(-2, 3), td=i64, extra=st.integers(-2, 2),
+               exact=st.booleans())
+    def check(B, V, mg, dt, td, extra, exact):
+        tt = td + B if exact else td + B + extra
+        tt = max(-(1 << 63), min(tt, (1 << 63) - 1))
+        shp = svx.make_shape(B, V, mg, dt, tt, td)
+        n = svx.specv_workspace_bytes(shp)
+        if shape_valid(B, V, mg, dt, tt, td):
+            assert n >= 256
+        else:
+            assert n == 0
+            assert call_verify(shp) == INVALID
+
+    check()
+
+
+def test_decode_and_cascade_shape_rules_property():
+    hyp = pytest.importorskip("hypothesis")
+    st = pytest.importorskip("hypothesis.strategies")
+    i32 = st.one_of(st.integers(-3, 70), st.integers(-(1 << 31), (1 << 31) - 1))
+
+    @hyp.settings(max_examples=2000, deadline=None, derandomize=True)
+    @hyp.given(B=i32, V=i32, g=i32, k2=i32, R=i32, dt=st.integers(-1, 2))
+    def check(B, V, g, k2, R, dt):
+        nd = svx.specv_decode_workspace_bytes(svx.SpecvDecodeShape(B, V, g, R, dt))
+        ok = (B >= 0 and V >= 1 and 0 <= g <= 63 and R >= 0 and dt in (0, 1) and V * V <= (1 << 40)
+              and B * R * (g + 1) <= (1 << 40) and B * (g + 1) <= (1 << 29)
+              and B * (g + 1) * V <= (1 << 40))
+        assert (nd > 0) == ok, (B, V, g, R, dt, nd)
+        nc = svx.specv_cascade_workspace_bytes(svx.SpecvCascadeShape(B, V, g, k2, R, dt))
+        okc = (B >= 0 and V >= 1 and 0 <= g <= 63 and 0 <= k2 <= 63 and R >= 0 and dt in (0, 1)
+               and V * V <= (1 << 40) and B * R * (g + 1) <= (1 << 40)
+               and max(B * (g + 1), B * (k2 + 1)) <= (1 << 29)
+               and max(B * (g + 1), B * (k2 + 1)) * V <= (1 << 40))
+        assert (nc > 0) == okc, (B, V, g, k2, R, dt, nc)
+
+    check()
