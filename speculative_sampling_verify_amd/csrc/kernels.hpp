@@ -614,7 +614,7 @@ struct DrawArgs {
   double* sub;        // [B, nsub] weight mass of each 1024-element sub-block
   int32_t* out_next;
   int64_t V;
-  int32_t B, chunks3, chunk3_elems, nsub;
+  int32_t B, chunks3, nsub;
 };
 
 // Wave-level inclusive scan of a sequence's sub-block masses in passes of 64
@@ -798,14 +798,21 @@ __device__ __forceinline__ void chunk_masses(const DrawArgs& a, const Select& s,
   constexpr int64_t esz = (DT == kBF16) ? 2 : 4;
   const void* trow = static_cast<const char*>(a.target) + s.trow * a.V * esz;
   const void* drow = W.residual ? static_cast<const char*>(a.draft) + s.drow * a.V * esz : nullptr;
-  const int64_t e0 = (int64_t)c * a.chunk3_elems, e1 = min(a.V, e0 + a.chunk3_elems);
-  const int64_t n = e1 - e0;
-  const int n_full = (int)(n / TL::EPI), n_iter = (int)((n + TL::EPI - 1) / TL::EPI);
+  // the row's tiles interleaved over the sequence's pass-2 waves (wave c
+  // takes tiles c, c + chunks3, ...), so neighbouring waves read neighbouring
+  // tiles at about the same time, as in pass 1
+  const int64_t tiles = (a.V + TL::EPI - 1) / TL::EPI;
   typename TL::Raw rt, rd;
   float w[NE];
-  for (int it = 0; it < n_iter; ++it) {
-    TL::load_raw(trow, e0, e1, it, n_full, lane, rt);
-    if (W.residual) TL::load_raw(drow, e0, e1, it, n_full, lane, rd);
+  for (int64_t t = c; t < tiles; t += a.chunks3) {
+    const int64_t e0 = t * TL::EPI;
+    if (e0 + TL::EPI <= a.V) {
+      TL::template load_raw<false>(trow, e0, a.V, 0, lane, rt);
+      if (W.residual) TL::template load_raw<false>(drow, e0, a.V, 0, lane, rd);
+    } else {
+      TL::template load_raw<true>(trow, e0, a.V, 0, lane, rt);
+      if (W.residual) TL::template load_raw<true>(drow, e0, a.V, 0, lane, rd);
+    }
     if constexpr (VEC && DT == kBF16) {
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
@@ -823,7 +830,7 @@ __device__ __forceinline__ void chunk_masses(const DrawArgs& a, const Select& s,
 #pragma unroll
       for (int j = 0; j < PER; ++j) part[j] = w[h * PER + j];
       const double m = wave_sum((double)tree_sum(part));
-      const int64_t sb = (e0 + (int64_t)it * TL::EPI) / kSub + h;
+      const int64_t sb = e0 / kSub + h;
       if (lane == 0 && sb < a.nsub) out[sb] = m;
     }
   }

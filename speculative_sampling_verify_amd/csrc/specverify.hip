@@ -322,7 +322,6 @@ DrawArgs draw_args(const Plan& p, const Call& c) {
   a.V = p.V;
   a.B = (int32_t)p.B;
   a.chunks3 = p.chunks3;
-  a.chunk3_elems = p.chunk3_elems;
   a.nsub = (int32_t)p.nsub;
   return a;
 }
