@@ -193,7 +193,7 @@ def cpu_baseline(x, gpu_n, gpu_next, budget_s=12.0, lenience="none", epsilon=1.0
             "sample": "%d pass(es) over the step's %d sequences (%d target rows each pass), %.1f s"
                       % (passes, x.batch, x.total_target_rows, el),
             "parity_vs_gpu": {"sequences": int(x.batch), "mismatches": int(mism.sum()),
-                              "unexplained": int((mism & ~res.near_tie).sum()),
+                              "not_admitted": int((~res.admits(gpu_n, gpu_next)).sum()),
                               "near_ties": int(res.near_tie.sum())}}
 
 

@@ -47,7 +47,7 @@ def _load():
     lib.oracle_verify.restype = ctypes.c_int
     lib.oracle_verify.argtypes = [i64, i64, i64, ctypes.c_int, i64, i64, P, P, P, P, P,
                                   u64, u64, ctypes.c_int, ctypes.c_float,
-                                  P, P, P, P, P, P, P, P, ctypes.c_int]
+                                  P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_int]
     lib.oracle_position_diagnostics.restype = ctypes.c_int
     lib.oracle_position_diagnostics.argtypes = [i64, i64, ctypes.c_int, i64, i64, P, P, P, P, i64,
                                                 P, P, P, P]
@@ -102,6 +102,35 @@ class VerifyResult:
     ratio: np.ndarray      # [B, max_gamma] float64 f(p_i(x_i))/q_i(x_i) (NaN if not reached)
     resmass: np.ndarray    # [B] float64 total weight of the final draw (NaN if greedy)
     layout_ok: bool
+    # the accept margin (smallest |r_i - ratio_i| / ratio_i over the decisive
+    # positions) and the draw margin (distance of u * C to the nearer end of
+    # the drawn token's CDF interval, over C), each +inf where there is none
+    accept_margin: np.ndarray = None
+    draw_margin: np.ndarray = None
+    # tokens whose CDF interval meets [u C - 1e-6 C, u C + 1e-6 C]: the
+    # outcomes a computation with rounding below 1e-6 of C can reach (only
+    # next_token when the draw is not a near-tie)
+    tok_lo: np.ndarray = None
+    tok_hi: np.ndarray = None
+    # the outcome with the first near-tie accept decision reversed: n and its
+    # token window; alt_n = -2 where no accept decision is a near-tie
+    alt_n: np.ndarray = None
+    alt_lo: np.ndarray = None
+    alt_hi: np.ndarray = None
+    # the chance, over the uniforms, that a decisive one lands within its
+    # window (given the rows and the n reached): the expected share of
+    # sequences the rule flags
+    near_prob: np.ndarray = None
+
+    def admits(self, n, tok):
+        """Per sequence: (n, tok) is the oracle's outcome up to the near-tie
+        rule -- n exact and tok inside the draw window, or the outcome on the
+        other side of the first near-tie accept decision."""
+        n = np.asarray(n)
+        tok = np.asarray(tok)
+        primary = (n == self.n) & (tok >= self.tok_lo) & (tok <= self.tok_hi)
+        alt = (self.alt_n >= 0) & (n == self.alt_n) & (tok >= self.alt_lo) & (tok <= self.alt_hi)
+        return primary | alt
 
 
 def verify(target, draft, tokens, gamma, temperature, *, vocab, max_gamma, seed=0,
@@ -129,6 +158,10 @@ def verify(target, draft, tokens, gamma, temperature, *, vocab, max_gamma, seed=
     near = np.empty(B, np.uint8)
     ratio = np.full((B, max(max_gamma, 1)), np.nan, np.float64)
     resmass = np.full(B, np.nan, np.float64)
+    am = np.empty(B, np.float64)
+    dm = np.empty(B, np.float64)
+    win = np.empty((B, 5), np.int32)
+    nprob = np.empty(B, np.float64)
     if r is not None:
         r = np.ascontiguousarray(r, dtype=np.float32).reshape(B, max_gamma)
     if u is not None:
@@ -138,9 +171,12 @@ def verify(target, draft, tokens, gamma, temperature, *, vocab, max_gamma, seed=
                              int(seed), int(row_offset), LENIENCE[lenience],
                              float(np.float32(epsilon)), _ptr(r), _ptr(u), _ptr(out_n),
                              _ptr(out_next), _ptr(margin), _ptr(near), _ptr(ratio),
-                             _ptr(resmass), int(nthreads or default_threads()))
+                             _ptr(resmass), _ptr(am), _ptr(dm), _ptr(win), _ptr(nprob),
+                             int(nthreads or default_threads()))
     return VerifyResult(out_n, out_next, margin, near.astype(bool),
-                        ratio[:, :max_gamma], resmass, code == 0)
+                        ratio[:, :max_gamma], resmass, code == 0, am, dm,
+                        win[:, 0].copy(), win[:, 1].copy(), win[:, 2].copy(), win[:, 3].copy(),
+                        win[:, 4].copy(), nprob)
 
 
 @dataclass

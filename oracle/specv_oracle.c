@@ -220,8 +220,12 @@ typedef struct {
   const float* inj_u; /* [batch] or NULL: injected final-draw uniforms  */
   int32_t* out_n;
   int32_t* out_next;
-  double* out_margin;  /* [batch] or NULL */
-  uint8_t* out_near;   /* [batch] or NULL */
+  double* out_margin;  /* [batch] or NULL: min(accept margin, draw margin) */
+  uint8_t* out_near;   /* [batch] or NULL: margin < ORACLE_NEAR_TIE */
+  double* out_accept_margin; /* [batch] or NULL: smallest |r_i - ratio_i| / ratio_i, decisive i */
+  double* out_draw_margin;   /* [batch] or NULL: distance of u * C to the nearest CDF step / C */
+  int32_t* out_window;       /* [batch, 5] or NULL: tok_lo, tok_hi, alt_n, alt_lo, alt_hi */
+  double* out_near_prob;     /* [batch] or NULL: chance that the decisive uniforms fall in a window */
   double* out_ratio;   /* [batch * max_gamma] or NULL: f(p_i(x_i))/q_i(x_i) */
   double* out_resmass; /* [batch] or NULL: total weight of the final draw */
   const int64_t* toff;
@@ -238,58 +242,224 @@ typedef struct {
   double* w;  /* V   */
 } scratch_t;
 
-static void set_result(const job_t* J, int64_t b, int32_t n, int32_t next, double margin) {
-  J->out_n[b] = n;
-  J->out_next[b] = next;
+/* Outcome of one sequence: n, the token, the two margins and the windows.
+ * tok_lo..tok_hi are the tokens whose CDF interval meets [t - d, t + d], d =
+ * ORACLE_NEAR_TIE * C (only the drawn token when the draw is not a near-tie);
+ * alt_* is the outcome with the first near-tie accept decision reversed
+ * (alt_n = -2 when there is none). */
+typedef struct {
+  int64_t n, tok, tok_lo, tok_hi;
+  double accept_margin, draw_margin;
+  int64_t near_pos; /* first decisive position with accept margin < ORACLE_NEAR_TIE, or -1 */
+  double near_prob; /* probability over the uniforms that a decisive one lands in its window */
+} outcome_t;
+
+static void set_result(const job_t* J, int64_t b, const outcome_t* o, const outcome_t* alt) {
+  const double margin = o->accept_margin < o->draw_margin ? o->accept_margin : o->draw_margin;
+  J->out_n[b] = (int32_t)o->n;
+  J->out_next[b] = (int32_t)o->tok;
   if (J->out_margin) J->out_margin[b] = margin;
   if (J->out_near) J->out_near[b] = (uint8_t)(margin < ORACLE_NEAR_TIE);
+  if (J->out_accept_margin) J->out_accept_margin[b] = o->accept_margin;
+  if (J->out_draw_margin) J->out_draw_margin[b] = o->draw_margin;
+  if (J->out_near_prob) J->out_near_prob[b] = o->near_prob;
+  if (J->out_window) {
+    int32_t* w = J->out_window + 5 * b;
+    w[0] = (int32_t)o->tok_lo;
+    w[1] = (int32_t)o->tok_hi;
+    w[2] = alt ? (int32_t)alt->n : -2;
+    w[3] = alt ? (int32_t)alt->tok_lo : -2;
+    w[4] = alt ? (int32_t)alt->tok_hi : -2;
+  }
+}
+
+static void set_failed(const job_t* J, int64_t b) {
+  outcome_t o = {-1, -1, -1, -1, INFINITY, INFINITY, -1, 0.0};
+  set_result(J, b, &o, NULL);
+}
+
+static void set_greedy(const job_t* J, int64_t b, int64_t n, int64_t tok) {
+  outcome_t o = {n, tok, tok, tok, INFINITY, INFINITY, -1, 0.0};
+  set_result(J, b, &o, NULL);
 }
 
 /* Inverse-CDF draw in index order over weights w[0..V): the smallest v with
- * t <= C_v where t = u * C_{V-1}. Returns -1 when the total is 0. */
-static int64_t inverse_cdf(const double* w, int64_t V, double u, double* margin, double* total_out) {
+ * t <= C_v where t = u * C_{V-1}. Returns -1 when the total is 0. Also the
+ * draw margin (distance of t to the nearer end of the token's CDF interval,
+ * over the total) and the window [*lo, *hi] of tokens whose interval meets
+ * [t - d, t + d], d = ORACLE_NEAR_TIE * total. */
+static int64_t cdf_search(const double* w, int64_t V, double t) {
+  /* smallest v with t <= C_v; rounding past the last prefix gives the last
+   * token of positive weight */
+  double c = 0.0;
+  for (int64_t v = 0; v < V; ++v) {
+    c += w[v];
+    if (t <= c) return v;
+  }
+  for (int64_t v = V - 1; v >= 0; --v)
+    if (w[v] > 0.0) return v;
+  return -1;
+}
+
+static int64_t inverse_cdf(const double* w, int64_t V, double u, double* margin, double* total_out,
+                           int64_t* lo, int64_t* hi) {
   double total = 0.0;
   for (int64_t v = 0; v < V; ++v) total += w[v];
   if (total_out) *total_out = total;
   if (!(total > 0.0)) return -1;
-  double t = u * total;
+  const double t = u * total;
   double c = 0.0, prev = 0.0;
+  int64_t tok = -1;
   for (int64_t v = 0; v < V; ++v) {
     prev = c;
     c += w[v];
     if (t <= c) {
-      double lo = t - prev, hi = c - t;
-      *margin = (lo < hi ? lo : hi) / total;
-      return v;
+      const double below = t - prev, above = c - t;
+      *margin = (below < above ? below : above) / total;
+      tok = v;
+      break;
     }
   }
-  /* Unreachable in exact arithmetic (t <= total); rounding could leave t a
-   * hair above the last prefix: take the last token of positive weight. */
-  for (int64_t v = V - 1; v >= 0; --v)
-    if (w[v] > 0.0) {
-      *margin = 0.0;
-      return v;
+  if (tok < 0) {
+    /* Unreachable in exact arithmetic (t <= total); rounding could leave t a
+     * hair above the last prefix: take the last token of positive weight. */
+    tok = cdf_search(w, V, 2.0 * total);
+    *margin = 0.0;
+  }
+  if (lo && hi) {
+    const double d = ORACLE_NEAR_TIE * total;
+    /* the lower end stays above 0: a weight-0 prefix is never drawn (u > 0) */
+    const double tl = t - d > 0.0 ? t - d : 0x1p-1074;
+    *lo = cdf_search(w, V, tl);
+    *hi = cdf_search(w, V, t + d);
+    if (*lo > tok) *lo = tok;
+    if (*hi < tok) *hi = tok;
+  }
+  return tok;
+}
+
+/* The sampling step of one sequence whose rows are valid: the accept walk
+ * (Algorithm A.1 steps 5-7) and the final draw (steps 8-11). With flip >= 0
+ * the decision at position flip is reversed (used for the outcome on the
+ * other side of a near-tie); flip < 0 is the step itself. */
+static void sample_outcome(const job_t* J, int64_t b, scratch_t* S, int64_t flip, outcome_t* o) {
+  const int64_t V = J->vocab;
+  const int64_t g = J->gamma[b];
+  const double T = (double)J->temperature[b];
+  const int64_t t0 = J->toff[b], d0 = J->doff[b];
+  const uint64_t philox_row = J->row_offset + (uint64_t)b;
+  o->accept_margin = INFINITY;
+  o->draw_margin = INFINITY;
+  o->near_pos = -1;
+  o->near_prob = 0.0;
+
+  /* Accept walk: ratio_i = f(p_i(x_i), eps) / q_i(x_i); reject at the first
+   * i with r_i > ratio_i. */
+  int64_t n = g;
+  for (int64_t i = 0; i < g; ++i) {
+    const int32_t x = J->tokens[d0 + i];
+    double mp, sp, mq, sq;
+    load_row(J->target, J->dtype, V, t0 + i, S->z);
+    row_softmax(S->z, V, T, &mp, &sp, NULL);
+    const double p_x = exp((S->z[x] - mp) / T) / sp;
+    load_row(J->draft, J->dtype, V, d0 + i, S->zq);
+    row_softmax(S->zq, V, T, &mq, &sq, NULL);
+    const double q_x = exp((S->zq[x] - mq) / T) / sq;
+    const double ratio = (q_x == 0.0) ? INFINITY : lenience(p_x, J->lenience, J->eps) / q_x;
+    if (flip < 0 && J->out_ratio) J->out_ratio[b * J->max_gamma + i] = ratio;
+    double r;
+    if (J->inj_r)
+      r = (double)J->inj_r[b * J->max_gamma + i];
+    else
+      draw_uniforms(J->seed, philox_row, (uint32_t)i, &r, NULL);
+    if (isfinite(ratio)) {
+      const double mg = fabs(r - ratio) / ratio;
+      if (mg < o->accept_margin) o->accept_margin = mg;
+      if (mg < ORACLE_NEAR_TIE && o->near_pos < 0) o->near_pos = i;
+      /* r is uniform on (0, 1]: the window of relative half-width 1e-6
+       * around a ratio below 1 has that much chance */
+      if (ratio < 1.0) o->near_prob += 2.0 * ORACLE_NEAR_TIE * ratio;
     }
-  return -1;
+    int reject = r > ratio;
+    if (i == flip) reject = !reject;
+    if (reject) {
+      n = i;
+      break;
+    }
+  }
+  if (g_mutant == MUTANT_N_PLUS_ONE && n < g) n = n + 1;
+
+  /* Final draw. */
+  double u;
+  if (J->inj_u)
+    u = (double)J->inj_u[b];
+  else
+    draw_uniforms(J->seed, philox_row, (uint32_t)n, NULL, &u);
+
+  load_row(J->target, J->dtype, V, t0 + n, S->z);
+  row_softmax(S->z, V, T, NULL, NULL, S->p);
+  if (n < g && g_mutant != MUTANT_RESIDUAL_IS_P) {
+    load_row(J->draft, J->dtype, V, d0 + n, S->zq);
+    row_softmax(S->zq, V, T, NULL, NULL, S->q);
+    for (int64_t v = 0; v < V; ++v) {
+      double d = S->p[v] - S->q[v];
+      S->w[v] = d > 0.0 ? d : 0.0;
+    }
+    if (g_mutant == MUTANT_RESIDUAL_IS_Q)
+      for (int64_t v = 0; v < V; ++v) S->w[v] = S->q[v];
+  } else {
+    for (int64_t v = 0; v < V; ++v) S->w[v] = S->p[v];
+  }
+  double total = 0.0;
+  int64_t lo = -1, hi = -1;
+  int64_t tok = inverse_cdf(S->w, V, u, &o->draw_margin, &total, &lo, &hi);
+  if (tok < 0) {
+    /* The residual has no mass (p_n == q_n up to rounding): draw from p_n. */
+    tok = inverse_cdf(S->p, V, u, &o->draw_margin, &total, &lo, &hi);
+  } else if (n < g && total < ORACLE_NEAR_TIE) {
+    /* A residual this small is not resolved by fp32 weights: a computation
+     * in fp32 may find no mass at all and draw from p_n instead. */
+    o->draw_margin = 0.0;
+    lo = 0;
+    hi = V - 1;
+  }
+  if (flip < 0 && J->out_resmass) J->out_resmass[b] = total;
+  if (o->draw_margin == 0.0 && lo == 0 && hi == V - 1) {
+    o->near_prob += 1.0; /* a residual below the window: flagged whatever u is */
+  } else if (total > 0.0) {
+    /* u * C is uniform on (0, C]: the part of it within d = 1e-6 C of a step
+     * of the CDF, summed over the tokens' intervals */
+    const double* wd = (total > 0.0 && tok >= 0 && S->w[tok] > 0.0) ? S->w : S->p;
+    double tw = 0.0;
+    for (int64_t v = 0; v < V; ++v) tw += wd[v];
+    for (int64_t v = 0; v < V; ++v) {
+      const double f = wd[v] / tw;
+      o->near_prob += f < 2.0 * ORACLE_NEAR_TIE ? f : 2.0 * ORACLE_NEAR_TIE;
+    }
+  }
+  o->n = n;
+  o->tok = tok;
+  o->tok_lo = lo;
+  o->tok_hi = hi;
 }
 
 static void verify_sequence(const job_t* J, int64_t b, scratch_t* S) {
   const int64_t V = J->vocab;
   if (!J->layout_ok) {
-    set_result(J, b, -1, -1, INFINITY);
+    set_failed(J, b);
     return;
   }
   const int64_t g = J->gamma[b];
   const double T = (double)J->temperature[b];
   const int64_t t0 = J->toff[b], d0 = J->doff[b];
   if (isnan(T) || T < 0.0 || isinf(T)) {
-    set_result(J, b, -1, -1, INFINITY);
+    set_failed(J, b);
     return;
   }
   for (int64_t i = 0; i < g; ++i) {
     int32_t x = J->tokens[d0 + i];
     if (x < 0 || x >= V) {
-      set_result(J, b, -1, -1, INFINITY);
+      set_failed(J, b);
       return;
     }
   }
@@ -311,7 +481,7 @@ static void verify_sequence(const job_t* J, int64_t b, scratch_t* S) {
       if (i == n && next < 0) next = a;
     }
     if (first_bad >= 0) {
-      set_result(J, b, -1, -1, INFINITY);
+      set_failed(J, b);
       return;
     }
     if (g_mutant == MUTANT_N_PLUS_ONE && n < g) {
@@ -319,7 +489,7 @@ static void verify_sequence(const job_t* J, int64_t b, scratch_t* S) {
       load_row(J->target, J->dtype, V, t0 + n, S->z);
       next = row_argmax(S->z, V);
     }
-    set_result(J, b, (int32_t)n, (int32_t)next, INFINITY);
+    set_greedy(J, b, n, next);
     return;
   }
 
@@ -327,81 +497,26 @@ static void verify_sequence(const job_t* J, int64_t b, scratch_t* S) {
   for (int64_t i = 0; i <= g; ++i) {
     load_row(J->target, J->dtype, V, t0 + i, S->z);
     if (!row_is_valid(S->z, V)) {
-      set_result(J, b, -1, -1, INFINITY);
+      set_failed(J, b);
       return;
     }
   }
   for (int64_t i = 0; i < g; ++i) {
-    load_row(J->draft, J->dtype, V, d0 + i, S->z);
-    if (!row_is_valid(S->z, V)) {
-      set_result(J, b, -1, -1, INFINITY);
-      return;
-    }
-  }
-
-  const uint64_t philox_row = J->row_offset + (uint64_t)b;
-  double margin = INFINITY;
-
-  /* Accept walk (Algorithm A.1 steps 5-7): ratio_i = f(p_i(x_i), eps) /
-   * q_i(x_i), reject at the first i with r_i > ratio_i. */
-  int64_t n = g;
-  for (int64_t i = 0; i < g; ++i) {
-    const int32_t x = J->tokens[d0 + i];
-    double mp, sp, mq, sq;
-    load_row(J->target, J->dtype, V, t0 + i, S->z);
-    row_softmax(S->z, V, T, &mp, &sp, NULL);
-    const double p_x = exp((S->z[x] - mp) / T) / sp;
     load_row(J->draft, J->dtype, V, d0 + i, S->zq);
-    row_softmax(S->zq, V, T, &mq, &sq, NULL);
-    const double q_x = exp((S->zq[x] - mq) / T) / sq;
-    const double ratio = (q_x == 0.0) ? INFINITY : lenience(p_x, J->lenience, J->eps) / q_x;
-    if (J->out_ratio) J->out_ratio[b * J->max_gamma + i] = ratio;
-    double r;
-    if (J->inj_r)
-      r = (double)J->inj_r[b * J->max_gamma + i];
-    else
-      draw_uniforms(J->seed, philox_row, (uint32_t)i, &r, NULL);
-    if (isfinite(ratio)) {
-      double mg = fabs(r - ratio) / ratio;
-      if (mg < margin) margin = mg;
-    }
-    if (r > ratio) {
-      n = i;
-      break;
+    if (!row_is_valid(S->zq, V)) {
+      set_failed(J, b);
+      return;
     }
   }
-  if (g_mutant == MUTANT_N_PLUS_ONE && n < g) n = n + 1;
-
-  /* Final draw (Algorithm A.1 steps 8-11). */
-  double u;
-  if (J->inj_u)
-    u = (double)J->inj_u[b];
-  else
-    draw_uniforms(J->seed, philox_row, (uint32_t)n, NULL, &u);
-
-  load_row(J->target, J->dtype, V, t0 + n, S->z);
-  row_softmax(S->z, V, T, NULL, NULL, S->p);
-  if (n < g && g_mutant != MUTANT_RESIDUAL_IS_P) {
-    load_row(J->draft, J->dtype, V, d0 + n, S->zq);
-    row_softmax(S->zq, V, T, NULL, NULL, S->q);
-    for (int64_t v = 0; v < V; ++v) {
-      double d = S->p[v] - S->q[v];
-      S->w[v] = d > 0.0 ? d : 0.0;
-    }
-    if (g_mutant == MUTANT_RESIDUAL_IS_Q)
-      for (int64_t v = 0; v < V; ++v) S->w[v] = S->q[v];
+  outcome_t o, alt;
+  sample_outcome(J, b, S, -1, &o);
+  if (o.near_pos >= 0 && J->out_window) {
+    /* the other side of the first near-tie accept decision */
+    sample_outcome(J, b, S, o.near_pos, &alt);
+    set_result(J, b, &o, &alt);
   } else {
-    for (int64_t v = 0; v < V; ++v) S->w[v] = S->p[v];
+    set_result(J, b, &o, NULL);
   }
-  double draw_margin = INFINITY, total = 0.0;
-  int64_t tok = inverse_cdf(S->w, V, u, &draw_margin, &total);
-  if (tok < 0) {
-    /* The residual has no mass (p_n == q_n up to rounding): draw from p_n. */
-    tok = inverse_cdf(S->p, V, u, &draw_margin, &total);
-  }
-  if (J->out_resmass) J->out_resmass[b] = total;
-  if (draw_margin < margin) margin = draw_margin;
-  set_result(J, b, (int32_t)n, (int32_t)tok, margin);
 }
 
 typedef struct {
@@ -472,7 +587,8 @@ int oracle_verify(int64_t batch, int64_t vocab, int64_t max_gamma, int dtype,
                   int lenience_kind, float eps,
                   const float* inj_r, const float* inj_u, int32_t* out_n, int32_t* out_next,
                   double* out_margin, uint8_t* out_near, double* out_ratio, double* out_resmass,
-                  int nthreads) {
+                  double* out_accept_margin, double* out_draw_margin, int32_t* out_window,
+                  double* out_near_prob, int nthreads) {
   job_t J;
   memset(&J, 0, sizeof J);
   J.batch = batch; J.vocab = vocab; J.max_gamma = max_gamma; J.dtype = dtype;
@@ -483,6 +599,9 @@ int oracle_verify(int64_t batch, int64_t vocab, int64_t max_gamma, int dtype,
   J.inj_r = inj_r; J.inj_u = inj_u;
   J.out_n = out_n; J.out_next = out_next; J.out_margin = out_margin; J.out_near = out_near;
   J.out_ratio = out_ratio; J.out_resmass = out_resmass;
+  J.out_accept_margin = out_accept_margin; J.out_draw_margin = out_draw_margin;
+  J.out_window = out_window;
+  J.out_near_prob = out_near_prob;
   J.nthreads = nthreads;
   return run_job(&J);
 }
@@ -694,7 +813,7 @@ int oracle_decode_bigram(int64_t batch, int64_t vocab, int64_t gamma, int64_t ro
           uint32_t w[4];
           oracle_philox4x32_10(seed, ctr, w);
           double margin = INFINITY;
-          x = inverse_cdf(q, V, oracle_uniform24(w[0]), &margin, NULL);
+          x = inverse_cdf(q, V, oracle_uniform24(w[0]), &margin, NULL, NULL, NULL);
           if (x < 0) x = 0;
           if (margin < ORACLE_NEAR_TIE) dnear[b] = 1;
         }
@@ -704,7 +823,7 @@ int oracle_decode_bigram(int64_t batch, int64_t vocab, int64_t gamma, int64_t ro
     }
     oracle_verify(B, V, g, dtype, B * (g + 1), B * g, tpack, dpack, tokens, gam, temperature, seed,
                   row_offset + (uint64_t)(r * B), ORACLE_LENIENCE_NONE, 1.0f, NULL, NULL, n_out,
-                  next_out, NULL, vnear, NULL, NULL, nthreads);
+                  next_out, NULL, vnear, NULL, NULL, NULL, NULL, NULL, NULL, nthreads);
     for (int64_t b = 0; b < B; ++b) {
       if (!failed[b] && n_out[b] < 0) failed[b] = 1;
       if (failed[b]) {
@@ -730,6 +849,125 @@ int oracle_decode_bigram(int64_t batch, int64_t vocab, int64_t gamma, int64_t ro
 /* Vertical cascade with bigram "models".                              */
 /* ------------------------------------------------------------------ */
 
+/* The target's review of one sequence's cascade draft (outer round of the
+ * vertical cascade), in float64 throughout: Algorithm A.1 without lenience,
+ * with the target's rows p_i = softmax(ttab[prev_i] / T), prev_0 = the last
+ * token, prev_i = draft token i - 1, and at each drafted position the law the
+ * token was drawn from (see oracle_cascade_bigram): Q = min(q2, f(p1)) +
+ * (1 - beta) norm(max(0, p1 - q2)) for a token from an inner position below
+ * k2, Q = p1 for a token from the inner bonus position (p1, q2: the mid and
+ * small softmaxes after the token's predecessor). Accept x_i while
+ * r_i <= p_i(x_i) / Q_i(x_i); the final draw is from norm(max(0, p_n - Q_n)),
+ * or from p_k1 when all k1 are accepted. Greedy (T = 0): exact match with the
+ * target's argmax. Sets *n = -1 on an unusable target row; *near when a
+ * decisive uniform lies within the near-tie window. */
+typedef struct {
+  double* zt; /* V: target logits of one row */
+  double* zm; /* V */
+  double* p1; /* V */
+  double* q2; /* V */
+  double* pt; /* V: target probabilities */
+  double* Q;  /* V: law of the draft token */
+  double* w;  /* V */
+} review_scratch_t;
+
+static void cascade_law(int64_t V, int dtype, const void* m1tab, const void* m2tab, double T,
+                        int32_t prev, int bonus, int kind, double eps, int mutant_q_is_p1,
+                        review_scratch_t* S) {
+  load_row(m1tab, dtype, V, prev, S->zm);
+  row_softmax(S->zm, V, T, NULL, NULL, S->p1);
+  if (bonus || mutant_q_is_p1) {
+    for (int64_t v = 0; v < V; ++v) S->Q[v] = S->p1[v];
+    return;
+  }
+  load_row(m2tab, dtype, V, prev, S->zm);
+  row_softmax(S->zm, V, T, NULL, NULL, S->q2);
+  double beta = 0.0, rmass = 0.0;
+  for (int64_t v = 0; v < V; ++v) {
+    const double f = lenience(S->p1[v], kind, eps);
+    beta += S->q2[v] < f ? S->q2[v] : f;
+    const double d = S->p1[v] - S->q2[v];
+    rmass += d > 0.0 ? d : 0.0;
+  }
+  for (int64_t v = 0; v < V; ++v) {
+    const double f = lenience(S->p1[v], kind, eps);
+    double q = S->q2[v] < f ? S->q2[v] : f;
+    const double d = S->p1[v] - S->q2[v];
+    if (rmass > 0.0 && d > 0.0) q += (1.0 - beta) * d / rmass;
+    S->Q[v] = q;
+  }
+}
+
+static void cascade_review(int64_t V, int64_t k1, int dtype, const void* ttab, const void* m1tab,
+                           const void* m2tab, double T, int32_t start, const int32_t* dtok,
+                           const int32_t* dprev, const int8_t* dbonus, int kind, double eps,
+                           int mutant_q_is_p1, uint64_t seed, uint64_t philox_row, int32_t* n_out,
+                           int32_t* next_out, uint8_t* near, review_scratch_t* S) {
+  *near = 0;
+  /* every target row the review reads must be usable */
+  for (int64_t i = 0; i <= k1; ++i) {
+    const int32_t prev = i == 0 ? start : dtok[i - 1];
+    load_row(ttab, dtype, V, prev, S->zt);
+    if (!row_is_valid(S->zt, V)) {
+      *n_out = -1;
+      *next_out = -1;
+      return;
+    }
+  }
+  if (T == 0.0) {
+    int64_t n = k1;
+    for (int64_t i = 0; i < k1; ++i) {
+      load_row(ttab, dtype, V, i == 0 ? start : dtok[i - 1], S->zt);
+      if (dtok[i] != row_argmax(S->zt, V)) {
+        n = i;
+        break;
+      }
+    }
+    load_row(ttab, dtype, V, n == 0 ? start : dtok[n - 1], S->zt);
+    *n_out = (int32_t)n;
+    *next_out = (int32_t)row_argmax(S->zt, V);
+    return;
+  }
+  int64_t n = k1;
+  for (int64_t i = 0; i < k1; ++i) {
+    const int32_t x = dtok[i];
+    load_row(ttab, dtype, V, i == 0 ? start : dtok[i - 1], S->zt);
+    row_softmax(S->zt, V, T, NULL, NULL, S->pt);
+    cascade_law(V, dtype, m1tab, m2tab, T, dprev[i], dbonus[i], kind, eps, mutant_q_is_p1, S);
+    const double ratio = S->Q[x] == 0.0 ? INFINITY : S->pt[x] / S->Q[x];
+    double r;
+    draw_uniforms(seed, philox_row, (uint32_t)i, &r, NULL);
+    if (isfinite(ratio) && fabs(r - ratio) / ratio < ORACLE_NEAR_TIE) *near = 1;
+    if (r > ratio) {
+      n = i;
+      break;
+    }
+  }
+  double u;
+  draw_uniforms(seed, philox_row, (uint32_t)n, NULL, &u);
+  load_row(ttab, dtype, V, n == 0 ? start : dtok[n - 1], S->zt);
+  row_softmax(S->zt, V, T, NULL, NULL, S->pt);
+  if (n < k1) {
+    cascade_law(V, dtype, m1tab, m2tab, T, dprev[n], dbonus[n], kind, eps, mutant_q_is_p1, S);
+    for (int64_t v = 0; v < V; ++v) {
+      const double d = S->pt[v] - S->Q[v];
+      S->w[v] = d > 0.0 ? d : 0.0;
+    }
+  } else {
+    for (int64_t v = 0; v < V; ++v) S->w[v] = S->pt[v];
+  }
+  double margin = INFINITY, total = 0.0;
+  int64_t tok = inverse_cdf(S->w, V, u, &margin, &total, NULL, NULL);
+  if (tok < 0) {
+    tok = inverse_cdf(S->pt, V, u, &margin, &total, NULL, NULL);
+  } else if (n < k1 && total < ORACLE_NEAR_TIE) {
+    margin = 0.0; /* a residual below the window (see sample_outcome) */
+  }
+  if (margin < ORACLE_NEAR_TIE) *near = 1;
+  *n_out = (int32_t)n;
+  *next_out = (int32_t)tok;
+}
+
 /* CS Drafting's vertical cascade (Chen et al., "Cascade Speculative
  * Drafting for Even Faster LLM Inference", sections 3.1 and 3.4) over three
  * bigram tables: target t, intermediate drafter m1, smallest drafter m2.
@@ -748,9 +986,8 @@ int oracle_decode_bigram(int64_t batch, int64_t vocab, int64_t gamma, int64_t ro
  * With that Q the target review keeps the target's output law whatever the
  * inner lenience: the reading under which the paper's claim, that a target
  * review without lenience leaves the output law unchanged, holds exactly.
- * The outer review runs in fp32 on
- * target rows converted exactly from the table and draft rows
- * fl32(T * ln Q) (-inf where Q = 0), so that softmax(row / T) = Q.
+ * The target review computes p and Q in float64 from the tables
+ * (cascade_review): the ratio p(x)/Q(x) and the residual max(0, p - Q).
  * Greedy sequences (T = 0) use exact-match reviews throughout.
  * Philox rows: outer round r uses the block row_offset + r * (k1 + 1) *
  * batch (+ b), inner round j the block row_offset + (r * (k1 + 1) + 1 + j)
@@ -763,18 +1000,6 @@ int oracle_decode_bigram(int64_t batch, int64_t vocab, int64_t gamma, int64_t ro
  * round with a near-tie anywhere in it. mutant_q_is_p1 = 1 makes the target
  * review use p1 as the draft distribution at every position (a negative
  * control: wrong unless eps = 1). */
-static void table_row_f32(const void* tab, int dtype, int64_t V, int64_t row, float* out) {
-  if (dtype == ORACLE_BF16) {
-    const uint16_t* h = (const uint16_t*)tab + row * V;
-    for (int64_t v = 0; v < V; ++v) {
-      uint32_t w = (uint32_t)h[v] << 16;
-      memcpy(&out[v], &w, 4);
-    }
-  } else {
-    memcpy(out, (const float*)tab + row * V, (size_t)V * 4);
-  }
-}
-
 int oracle_cascade_bigram(int64_t batch, int64_t vocab, int64_t k1, int64_t k2, int64_t rounds,
                           int dtype, const void* ttab, const void* m1tab, const void* m2tab,
                           const float* temperature, const int32_t* start, int lenience_kind,
@@ -792,11 +1017,16 @@ int oracle_cascade_bigram(int64_t batch, int64_t vocab, int64_t k1, int64_t k2, 
   int32_t* itok = (int32_t*)malloc((size_t)(B * k2 + 1) * 4);
   int32_t* ipack = (int32_t*)malloc((size_t)(B * k2 + 1) * 4); /* packed inner draft tokens */
   int32_t* igam = (int32_t*)malloc((size_t)(B + 1) * 4);
-  /* outer review buffers (fp32) */
-  float* otpack = (float*)malloc((size_t)(B * (k1 + 1) * V + 1) * 4);
-  float* odpack = (float*)malloc((size_t)(B * k1 * V + 1) * 4);
-  int32_t* otok = (int32_t*)malloc((size_t)(B * k1 + 1) * 4);
-  int32_t* ogam = (int32_t*)malloc((size_t)(B + 1) * 4);
+  /* the target review's rows, float64 */
+  review_scratch_t rvs;
+  review_scratch_t* rv = &rvs;
+  rv->zt = (double*)malloc((size_t)V * 8);
+  rv->zm = (double*)malloc((size_t)V * 8);
+  rv->p1 = (double*)malloc((size_t)V * 8);
+  rv->q2 = (double*)malloc((size_t)V * 8);
+  rv->pt = (double*)malloc((size_t)V * 8);
+  rv->Q = (double*)malloc((size_t)V * 8);
+  rv->w = (double*)malloc((size_t)V * 8);
   /* per-sequence state */
   int32_t* dtok = (int32_t*)malloc((size_t)(B * dcap + 1) * 4);   /* draft tokens      */
   int32_t* dprev = (int32_t*)malloc((size_t)(B * dcap + 1) * 4);  /* their prev token  */
@@ -852,7 +1082,7 @@ int oracle_cascade_bigram(int64_t batch, int64_t vocab, int64_t k1, int64_t k2, 
             uint32_t w[4];
             oracle_philox4x32_10(seed, ctr, w);
             double margin = INFINITY;
-            x = inverse_cdf(q2, V, oracle_uniform24(w[0]), &margin, NULL);
+            x = inverse_cdf(q2, V, oracle_uniform24(w[0]), &margin, NULL, NULL, NULL);
             if (x < 0) x = 0;
             if (margin < ORACLE_NEAR_TIE) dnear[b] = 1;
           }
@@ -876,8 +1106,8 @@ int oracle_cascade_bigram(int64_t batch, int64_t vocab, int64_t k1, int64_t k2, 
         td += g;
       }
       oracle_verify(B, V, k2, dtype, tt, td, itpack, idpack, ipack, igam, temperature, seed, rbase,
-                    lenience_kind, eps, NULL, NULL, n_out, next_out, NULL, vnear, NULL, NULL,
-                    nthreads);
+                    lenience_kind, eps, NULL, NULL, n_out, next_out, NULL, vnear, NULL, NULL, NULL,
+                    NULL, NULL, NULL, nthreads);
       for (int64_t b = 0; b < B; ++b) {
         if (dlen[b] >= k1) continue; /* draft already complete: result unused */
         if (n_out[b] < 0) {
@@ -903,50 +1133,25 @@ int oracle_cascade_bigram(int64_t batch, int64_t vocab, int64_t k1, int64_t k2, 
         dlen[b] += n + 1;
       }
     }
-    /* the target review of the first k1 draft tokens */
+    /* the target review of the first k1 draft tokens, without lenience */
     const uint64_t obase = row_offset + (uint64_t)(r * (k1 + 1) * B);
     for (int64_t b = 0; b < B; ++b) {
-      ogam[b] = (int32_t)k1;
-      const double T = (double)temperature[b];
-      const int ok = !(isnan(T) || T < 0.0 || isinf(T));
-      for (int64_t i = 0; i <= k1; ++i) {
-        const int32_t prev = i == 0 ? cur[b] : dtok[b * dcap + i - 1];
-        table_row_f32(ttab, dtype, V, prev, otpack + (size_t)(b * (k1 + 1) + i) * V);
-        if (i == k1) break;
-        otok[b * k1 + i] = dtok[b * dcap + i];
-        float* out = odpack + (size_t)(b * k1 + i) * V;
-        if (!ok || T == 0.0 || failed[b]) {
-          for (int64_t v = 0; v < V; ++v) out[v] = 0.f;
-          continue;
-        }
-        const int32_t pv = dprev[b * dcap + i];
-        load_row(m1tab, dtype, V, pv, z);
-        row_softmax(z, V, T, NULL, NULL, p1);
-        if (dbonus[b * dcap + i] || mutant_q_is_p1) {
-          for (int64_t v = 0; v < V; ++v) out[v] = p1[v] > 0.0 ? (float)(T * log(p1[v])) : -INFINITY;
-          continue;
-        }
-        load_row(m2tab, dtype, V, pv, z);
-        row_softmax(z, V, T, NULL, NULL, q2);
-        double beta = 0.0, rmass = 0.0;
-        for (int64_t v = 0; v < V; ++v) {
-          const double f = lenience(p1[v], lenience_kind, (double)eps);
-          beta += q2[v] < f ? q2[v] : f;
-          const double d = p1[v] - q2[v];
-          rmass += d > 0.0 ? d : 0.0;
-        }
-        for (int64_t v = 0; v < V; ++v) {
-          const double f = lenience(p1[v], lenience_kind, (double)eps);
-          double Q = q2[v] < f ? q2[v] : f;
-          const double d = p1[v] - q2[v];
-          if (rmass > 0.0 && d > 0.0) Q += (1.0 - beta) * d / rmass;
-          out[v] = Q > 0.0 ? (float)(T * log(Q)) : -INFINITY;
-        }
+      vnear[b] = 0;
+      if (failed[b]) {
+        n_out[b] = -1;
+        continue;
       }
+      const double T = (double)temperature[b];
+      if (isnan(T) || T < 0.0 || isinf(T)) {
+        n_out[b] = -1;
+        next_out[b] = -1;
+        continue;
+      }
+      cascade_review(V, k1, dtype, ttab, m1tab, m2tab, T, cur[b], dtok + b * dcap,
+                     dprev + b * dcap, dbonus + b * dcap, lenience_kind, (double)eps,
+                     mutant_q_is_p1, seed, obase + (uint64_t)b, &n_out[b], &next_out[b],
+                     &vnear[b], rv);
     }
-    oracle_verify(B, V, k1, ORACLE_F32, B * (k1 + 1), B * k1, otpack, odpack, otok, ogam,
-                  temperature, seed, obase, ORACLE_LENIENCE_NONE, 1.0f, NULL, NULL, n_out,
-                  next_out, NULL, vnear, NULL, NULL, nthreads);
     for (int64_t b = 0; b < B; ++b) {
       if (!failed[b] && n_out[b] < 0) failed[b] = 1;
       if (failed[b]) {
@@ -963,8 +1168,9 @@ int oracle_cascade_bigram(int64_t batch, int64_t vocab, int64_t k1, int64_t k2, 
     }
   }
   for (int64_t b = 0; b < B; ++b) out_length[b] = failed[b] ? -1 : len[b];
-  free(itpack); free(idpack); free(itok); free(ipack); free(igam); free(otpack); free(odpack); free(otok);
-  free(ogam); free(dtok); free(dprev); free(dbonus); free(dlen); free(cur); free(len);
+  free(itpack); free(idpack); free(itok); free(ipack); free(igam);
+  free(rv->zt); free(rv->zm); free(rv->p1); free(rv->q2); free(rv->pt); free(rv->Q); free(rv->w);
+  free(dtok); free(dprev); free(dbonus); free(dlen); free(cur); free(len);
   free(failed); free(near); free(vnear); free(dnear); free(n_out); free(next_out); free(ipr); free(z);
   free(p1); free(q2);
   return 0;

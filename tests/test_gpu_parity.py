@@ -1,12 +1,17 @@
 """GPU parity: libspecverify (through its C ABI) against the CPU oracle on the
 same seeded inputs and the same Philox stream.
 
-Bar: accepted counts and emitted tokens are
-bit-exact on every sequence that is not a near-tie (a decisive uniform within
-1e-6 relative of its threshold or of an inverse-CDF boundary; the oracle
-flags them and they are counted); probabilities within 1e-5 absolute; row
-maxima and argmax exact; runs bit-identical run to run. Greedy sequences have
-no near-ties.
+Bar: accepted counts and emitted tokens are bit-exact on every sequence, with
+one allowance where a decisive uniform lies within 1e-6 of its boundary (the
+oracle's near-tie rule: r_i within 1e-6 relative of its accept threshold, or
+u * C within 1e-6 * C of a step of the final draw's CDF). There the GPU's
+outcome must still be one the oracle admits: n exact and the token inside the
+oracle's window of tokens on either side of the step, or, for a near-tie
+accept decision, the oracle's outcome with that one decision reversed. The
+number of flagged sequences must stay within its expectation (the oracle's
+per-sequence chance of a flag, summed) plus five standard deviations.
+Probabilities within 1e-5 absolute; row maxima and argmax exact; runs
+bit-identical run to run. Greedy sequences have no near-ties.
 """
 import numpy as np
 import pytest
@@ -52,20 +57,36 @@ def run_gpu(svx, x, r=None, u=None, seed=None, row_offset=None, max_gamma=None):
     return n.cpu().numpy(), nxt.cpu().numpy(), svx.read_status(ws)
 
 
+def flag_cap(orc):
+    """The most flagged sequences the rule allows: the expected count plus
+    five standard deviations (a sum of independent flags) and a few."""
+    e = float(orc.near_prob[orc.n >= 0].sum())
+    return e, e + 5.0 * np.sqrt(e) + 3.0
+
+
 def assert_parity(name, x, got, orc):
     n, nxt = got[0], got[1]
-    mism = (n != orc.n) | (nxt != orc.next_token)
-    bad = mism & ~orc.near_tie
-    log("[parity] %s: B=%d V=%d %s  mismatches=%d near_ties=%d unexplained=%d mean_tokens=%.4f"
-        % (name, x.batch, x.vocab, x.dtype, mism.sum(), orc.near_tie.sum(), bad.sum(),
+    exact = (n == orc.n) & (nxt == orc.next_token)
+    ok = orc.admits(n, nxt)
+    in_window = ~exact & (n == orc.n) & (nxt >= orc.tok_lo) & (nxt <= orc.tok_hi)
+    reversed_ = ~exact & ~in_window & ok
+    flagged = int(orc.near_tie.sum())
+    expect, cap = flag_cap(orc)
+    log("[parity] %s: B=%d V=%d %s  exact=%d in_draw_window=%d reversed_accept=%d failed=%d "
+        "flagged=%d (expected %.1f, cap %.1f) mean_tokens=%.4f"
+        % (name, x.batch, x.vocab, x.dtype, exact.sum(), in_window.sum(), reversed_.sum(),
+           (~ok).sum(), flagged, expect, cap,
            np.mean(orc.n[orc.n >= 0] + 1) if (orc.n >= 0).any() else 0.0))
-    if bad.any():
-        idx = np.flatnonzero(bad)[:10]
+    if not ok.all():
+        idx = np.flatnonzero(~ok)[:10]
         detail = [(int(i), int(n[i]), int(orc.n[i]), int(nxt[i]), int(orc.next_token[i]),
-                   float(orc.margin[i])) for i in idx]
-        raise AssertionError("%s: %d unexplained mismatches (b, n_gpu, n_orc, tok_gpu, tok_orc, "
-                             "margin): %s" % (name, bad.sum(), detail))
-    return int(mism.sum())
+                   int(orc.tok_lo[i]), int(orc.tok_hi[i]), int(orc.alt_n[i]),
+                   float(orc.accept_margin[i]), float(orc.draw_margin[i])) for i in idx]
+        raise AssertionError("%s: %d outcomes the oracle does not admit (b, n_gpu, n_orc, "
+                             "tok_gpu, tok_orc, window_lo, window_hi, alt_n, accept_margin, "
+                             "draw_margin): %s" % (name, (~ok).sum(), detail))
+    assert flagged <= cap, "%s: %d flagged sequences, expected %.1f" % (name, flagged, expect)
+    return int((~exact).sum())
 
 
 def parity_case(svx, name, x, repeat=True):
@@ -365,8 +386,7 @@ def test_gpu_output_law_chi_square(svx, rounds):
     log("[chi] first-token p-value %.4g" % pv)
     assert pv > 1e-4
     orc = run_oracle(x)
-    mism = ((n != orc.n) | (nxt != orc.next_token)) & ~orc.near_tie
-    assert mism.sum() == 0
+    assert_parity("chi-square set", x, (n, nxt), orc)
 
 
 # --------------------------------------------------- lossy verification
