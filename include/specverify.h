@@ -42,7 +42,8 @@
  * Asynchrony: every entry point that takes a stream only enqueues work on it
  * and returns; results are valid after the stream is synchronised. Nothing
  * allocates device memory: scratch space is the caller's workspace, sized by
- * specv_workspace_bytes(). Calls that share a workspace must not overlap.
+ * specv_workspace_bytes() (specv_verify_noalloc: a static array). Calls that
+ * share a workspace must not overlap.
  *
  * Errors:
  *   - argument errors (null pointers, sizes out of range, row totals that
@@ -77,7 +78,8 @@ typedef enum {
   SPECV_ERR_INVALID_ARGUMENT = 1,
   SPECV_ERR_WORKSPACE = 2,
   SPECV_ERR_HIP = 3,
-  SPECV_ERR_UNSUPPORTED = 4
+  SPECV_ERR_UNSUPPORTED = 4,
+  SPECV_ERR_SCRATCH_LIMIT = 5 /* specv_verify_noalloc: shape too large for its scratch */
 } specv_status_t;
 
 /* Device status word: uint32 at byte offset 0 of the workspace after a call. */
@@ -109,6 +111,30 @@ specv_status_t specv_verify(const specv_shape_t* shape, const void* target_logit
                             uint64_t seed, uint64_t philox_row_offset,
                             int32_t* out_n_accepted, int32_t* out_next_token,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): specv_verify
+ * with no workspace argument. Its scratch is a static device array of
+ * SPECV_NOALLOC_SCRATCH_BYTES per GPU, created with the library's code object
+ * on that GPU and held until the process ends; its address is looked up once
+ * per device (the current device, which must be the stream's). The call
+ * allocates nothing and frees nothing. A shape whose workspace
+ * (specv_workspace_bytes) exceeds SPECV_NOALLOC_SCRATCH_BYTES returns
+ * SPECV_ERR_SCRATCH_LIMIT before anything is enqueued. Every call on one GPU
+ * shares that GPU's array: calls that overlap on one GPU (other streams, other
+ * threads) race and must be serialised by the caller. The array keeps the
+ * last call's contents; nothing in it needs clearing (every call writes what
+ * it reads). out_status: NULL, or a device uint32 that receives the status
+ * word of specv_verify's workspace (byte offset 0) once the call's kernels
+ * have run, by one more small launch on `stream` (0 for an empty batch).
+ * Everything else as specv_verify. */
+#define SPECV_NOALLOC_SCRATCH_BYTES (16u << 20)
+specv_status_t specv_verify_noalloc(const specv_shape_t* shape, const void* target_logits,
+                                    const void* draft_logits, const int32_t* draft_tokens,
+                                    const int32_t* gamma_per_row, const float* temperature,
+                                    uint64_t seed, uint64_t philox_row_offset,
+                                    int32_t* out_n_accepted, int32_t* out_next_token,
+                                    uint32_t* out_status, hipStream_t stream);
 
 /* Same as specv_verify with the uniforms given instead of drawn: r is
  * [B, max_gamma] float32 (r_i of sequence b at r[b * max_gamma + i]) and u is

@@ -19,6 +19,8 @@ SPECV_F32, SPECV_BF16 = 0, 1
 SPECV_MAX_GAMMA = 63
 SPECV_DEV_SEQ_ERROR = 1
 SPECV_DEV_LAYOUT_ERROR = 2
+SPECV_ERR_SCRATCH_LIMIT = 5
+SPECV_NOALLOC_SCRATCH_BYTES = 16 << 20
 STAGES = ("plan", "row_stats", "accept_and_mass", "draw")
 LENIENCE = {"none": 0, "lin": 1, "sq": 2, "exp": 3}
 
@@ -53,6 +55,8 @@ _lib.specv_workspace_bytes.restype = _sz
 _lib.specv_workspace_bytes.argtypes = [_SHP]
 _lib.specv_verify.restype = ctypes.c_int
 _lib.specv_verify.argtypes = [_SHP, _P, _P, _P, _P, _P, _u64, _u64, _P, _P, _P, _sz, _P]
+_lib.specv_verify_noalloc.restype = ctypes.c_int
+_lib.specv_verify_noalloc.argtypes = [_SHP, _P, _P, _P, _P, _P, _u64, _u64, _P, _P, _P, _P]
 _lib.specv_verify_profiled.restype = ctypes.c_int
 _lib.specv_verify_profiled.argtypes = [_SHP, _P, _P, _P, _P, _P, _u64, _u64, _P, _P, _P, _sz, _P, _P]
 _lib.specv_verify_with_uniforms.restype = ctypes.c_int
@@ -88,7 +92,7 @@ _lib.specv_read_bytes.argtypes = [_P, _sz, _P, _P]
 _lib.specv_status_string.restype = ctypes.c_char_p
 _lib.specv_status_string.argtypes = [ctypes.c_int]
 
-EXPORTED = ("specv_workspace_bytes", "specv_verify", "specv_verify_profiled",
+EXPORTED = ("specv_workspace_bytes", "specv_verify", "specv_verify_noalloc", "specv_verify_profiled",
             "specv_verify_with_uniforms", "specv_verify_lenient",
             "specv_diagnostics_workspace_bytes", "specv_position_diagnostics",
             "specv_decode_workspace_bytes", "specv_decode_bigram",
@@ -196,6 +200,35 @@ def specv_verify(target, draft, draft_tokens, gamma, temperature, *, max_gamma=N
                            _ptr(out_n), _ptr(out_next), _ptr(workspace), workspace.numel(),
                            _stream(stream, target.device))
     _check(st, "specv_verify")
+    return out_n, out_next
+
+
+def specv_verify_noalloc(target, draft, draft_tokens, gamma, temperature, *, max_gamma=None,
+                         seed=0, philox_row_offset=0, out_n=None, out_next=None, out_status=None,
+                         stream=None):
+    """specv_verify with the library's static scratch instead of a workspace
+    (allocates nothing itself when the outputs are given); ``out_status`` is
+    an optional int32 [1] device tensor receiving the status word."""
+    device = target.device
+    gamma = gamma if gamma.dtype == torch.int32 else gamma.to(torch.int32)
+    if draft is None:
+        draft = target[:0]
+    if draft_tokens is None:
+        draft_tokens = torch.empty(0, dtype=torch.int32, device=device)
+    if max_gamma is None:
+        max_gamma = int(gamma.max().item()) if gamma.numel() else 0
+    shape = _shape_of(target, draft, gamma, max_gamma)
+    if out_n is None:
+        out_n = torch.empty(gamma.shape[0], dtype=torch.int32, device=device)
+    if out_next is None:
+        out_next = torch.empty(gamma.shape[0], dtype=torch.int32, device=device)
+    _check_tensors(device, target=target, draft=draft, tokens=draft_tokens, gamma=gamma,
+                   temperature=temperature, out_n=out_n, out_next=out_next, out_status=out_status)
+    st = _lib.specv_verify_noalloc(ctypes.byref(shape), _ptr(target), _ptr(draft),
+                                   _ptr(draft_tokens), _ptr(gamma), _ptr(temperature), int(seed),
+                                   int(philox_row_offset), _ptr(out_n), _ptr(out_next),
+                                   _ptr(out_status), _stream(stream, device))
+    _check(st, "specv_verify_noalloc")
     return out_n, out_next
 
 

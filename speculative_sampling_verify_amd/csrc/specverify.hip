@@ -5,6 +5,8 @@
 
 #include <stdint.h>
 
+#include <mutex>
+
 #include "cascade.hpp"
 #include "decode.hpp"
 #include "diagnostics.hpp"
@@ -523,6 +525,35 @@ void launch_cas_rows_wg(dim3 g, dim3 wg, hipStream_t stream, const CascadeArgs& 
   }
 }
 
+// The static scratch of specv_verify_noalloc: one array per GPU, held until
+// the process ends. Host code never uses the array's name as an address; the
+// device address comes from hipGetSymbolAddress, looked up once per device
+// with that device current.
+__device__ __align__(256) unsigned char scratch[SPECV_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_address[kMaxDevices] = {};
+
+specv_status_t scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SPECV_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_address[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SPECV_ERR_HIP;
+    g_scratch_address[dev] = p;
+  }
+  *out = g_scratch_address[dev];
+  return SPECV_OK;
+}
+
+// The status word of a no-allocation call, copied to the caller's output
+// (0 when the batch was empty and nothing ran).
+__global__ void k_copy_status(const uint32_t* status, uint32_t* out) {
+  if (threadIdx.x == 0) out[0] = status ? status[0] : 0u;
+}
+
 }  // namespace
 
 extern "C" {
@@ -544,6 +575,31 @@ specv_status_t specv_verify(const specv_shape_t* shape, const void* target_logit
          seed, philox_row_offset, nullptr, nullptr, out_n_accepted, out_next_token,
          workspace, workspace_bytes, stream, nullptr};
   return run(c);
+}
+
+specv_status_t specv_verify_noalloc(const specv_shape_t* shape, const void* target_logits,
+                                    const void* draft_logits, const int32_t* draft_tokens,
+                                    const int32_t* gamma_per_row, const float* temperature,
+                                    uint64_t seed, uint64_t philox_row_offset,
+                                    int32_t* out_n_accepted, int32_t* out_next_token,
+                                    uint32_t* out_status, hipStream_t stream) {
+  if (!shape_ok(shape)) return SPECV_ERR_INVALID_ARGUMENT;
+  Plan p;
+  make_plan(shape, &p);
+  if (p.bytes > (size_t)SPECV_NOALLOC_SCRATCH_BYTES) return SPECV_ERR_SCRATCH_LIMIT;
+  void* ws = nullptr;
+  specv_status_t st = SPECV_OK;
+  if (p.B > 0 && (st = scratch_address(&ws)) != SPECV_OK) return st;
+  Call c{shape, target_logits, draft_logits, draft_tokens, gamma_per_row, temperature,
+         seed, philox_row_offset, nullptr, nullptr, out_n_accepted, out_next_token,
+         ws, (size_t)SPECV_NOALLOC_SCRATCH_BYTES, stream, nullptr};
+  if ((st = run(c)) != SPECV_OK) return st;
+  if (out_status) {
+    hipLaunchKernelGGL(k_copy_status, dim3(1), dim3(64), 0, stream,
+                       p.B > 0 ? static_cast<const uint32_t*>(ws) : nullptr, out_status);
+    return launched();
+  }
+  return SPECV_OK;
 }
 
 specv_status_t specv_verify_profiled(const specv_shape_t* shape, const void* target_logits,
@@ -1156,6 +1212,8 @@ const char* specv_status_string(specv_status_t status) {
     case SPECV_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case SPECV_ERR_HIP: return "HIP launch failed";
     case SPECV_ERR_UNSUPPORTED: return "unsupported";
+    case SPECV_ERR_SCRATCH_LIMIT:
+      return "the call needs more scratch than specv_verify_noalloc's static buffer holds";
   }
   return "unknown status";
 }

@@ -39,6 +39,20 @@ def shape(B=4, V=1000, g=3, dt=1, tt=None, td=None):
     return svx.make_shape(B, V, g, dt, tt, td)
 
 
+def test_noalloc_scratch_limit_before_any_hip_call():
+    # the no-allocation entry point refuses a shape whose workspace exceeds its
+    # static scratch before it looks anything up (no GPU needed)
+    B, g = 1 << 20, 7
+    big = svx.make_shape(B, 2, g, 0, B * (g + 1), B * g)
+    assert svx.specv_workspace_bytes(big) > svx.SPECV_NOALLOC_SCRATCH_BYTES
+    st = svx._lib.specv_verify_noalloc(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0, FAKE,
+                                       FAKE, None, None)
+    assert st == 5
+    bad = svx.make_shape(4, 0, 1, 0, 8, 4)  # V = 0
+    assert svx._lib.specv_verify_noalloc(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0, FAKE,
+                                         FAKE, None, None) == INVALID
+
+
 def test_workspace_bytes():
     assert svx.specv_workspace_bytes(shape()) >= 256
     assert svx.specv_workspace_bytes(shape(B=0, td=0)) >= 256
