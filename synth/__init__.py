@@ -27,7 +27,8 @@ Workloads, each shaped after a setting on the pages:
 
 Generator: numpy PCG64 streams keyed by SeedSequence((workload seed, sequence,
 ...)), so every sequence is reproducible on its own and rows are generated in
-parallel threads. Storage: fp32 values are rounded to bf16 with
+parallel threads. Later rounds of a workload (`first` / `round_index`) use the
+streams of later global sequence numbers: fresh logits and draft tokens. Storage: fp32 values are rounded to bf16 with
 round-to-nearest-even where the workload is bf16.
 """
 from __future__ import annotations
@@ -149,9 +150,12 @@ def _open_uniform(rng, n):
     return (rng.integers(0, 1 << 52, n) + 0.5) / float(1 << 52)
 
 
-def _assemble(name, V, max_gamma, dtype, gammas, temps, row_fn, gen_seed, meta=None) -> Inputs:
+def _assemble(name, V, max_gamma, dtype, gammas, temps, row_fn, gen_seed, meta=None,
+              first: int = 0) -> Inputs:
     """Allocate the packed layout and fill sequence b's rows with
-    row_fn(b, rng) -> (target_f32 [g+1, V], draft_f32 [g, V], same_rows)."""
+    row_fn(b, rng) -> (target_f32 [g+1, V], draft_f32 [g, V], same_rows).
+    Sequence b draws from the streams of global sequence first + b, so a
+    batch that starts at `first` holds fresh sequences (a later round)."""
     gammas = np.asarray(gammas, dtype=np.int32)
     temps = np.asarray(temps, dtype=np.float32)
     B = gammas.shape[0]
@@ -163,7 +167,7 @@ def _assemble(name, V, max_gamma, dtype, gammas, temps, row_fn, gen_seed, meta=N
     tokens = np.empty(int(doff[-1]), np.int32)
 
     def fill(b):
-        rng = _rng(gen_seed, b)
+        rng = _rng(gen_seed, first + b)
         t32, d32, same = row_fn(b, rng)
         g = int(gammas[b])
         target[toff[b]:toff[b + 1]] = _stored(t32, dtype)
@@ -173,7 +177,8 @@ def _assemble(name, V, max_gamma, dtype, gammas, temps, row_fn, gen_seed, meta=N
             draft[doff[b]:doff[b + 1]] = _stored(d32, dtype)
         if g:
             tokens[doff[b]:doff[b + 1]] = gumbel_max_tokens(draft[doff[b]:doff[b + 1]], dtype,
-                                                            float(temps[b]), _rng(gen_seed, b, 1 << 20))
+                                                            float(temps[b]),
+                                                            _rng(gen_seed, first + b, 1 << 20))
 
     def fill_range(lo_hi):
         for b in range(*lo_hi):
@@ -189,7 +194,7 @@ def _assemble(name, V, max_gamma, dtype, gammas, temps, row_fn, gen_seed, meta=N
         with ThreadPoolExecutor(_threads()) as ex:
             list(ex.map(fill_range, ranges))
     return Inputs(name, V, max_gamma, dtype, target, draft, tokens, gammas, temps,
-                  meta=dict(meta or {}))
+                  meta=dict(meta or {}, first=first))
 
 
 def tiny_cpu(rounds: int = 10000, greedy: bool = False, vocab: int = 1000, gamma: int = 4,
@@ -204,7 +209,7 @@ def tiny_cpu(rounds: int = 10000, greedy: bool = False, vocab: int = 1000, gamma
 
 
 def t5xxl_like(rounds: int = 2000, greedy: bool = False, vocab: int = 32128, gamma: int = 5,
-               gen_seed: int = 2) -> Inputs:
+               gen_seed: int = 2, first: int = 0) -> Inputs:
     def rows(b, rng):
         t = (rng.standard_normal((gamma + 1, vocab), dtype=np.float32) * 3.0)
         for i in range(gamma + 1):
@@ -213,22 +218,29 @@ def t5xxl_like(rounds: int = 2000, greedy: bool = False, vocab: int = 32128, gam
         return t, d, False
     T = 0.0 if greedy else 1.0
     return _assemble("t5xxl_like", vocab, gamma, "bf16", [gamma] * rounds, [T] * rounds, rows,
-                     gen_seed, {"greedy": greedy})
+                     gen_seed, {"greedy": greedy}, first)
 
 
-def serving_b64(batch: int = 64, vocab: int = 128256, gamma: int = 7, gen_seed: int = 3) -> Inputs:
+def serving_b64(batch: int = 64, vocab: int = 128256, gamma: int = 7, gen_seed: int = 3,
+                round_index: int = 0) -> Inputs:
     def rows(b, rng):
         t = (-2.0 * np.log(-np.log(_open_uniform(rng, (gamma + 1) * vocab)))).astype(np.float32)
         t = t.reshape(gamma + 1, vocab)
         d = 0.8 * t[:gamma] + rng.standard_normal((gamma, vocab), dtype=np.float32) * 1.5
         return t, d.astype(np.float32), False
     return _assemble("serving_b64", vocab, gamma, "bf16", [gamma] * batch, [0.7] * batch, rows,
-                     gen_seed)
+                     gen_seed, None, round_index * batch)
+
+
+def _batch_rng(gen_seed: int, round_index: int) -> np.random.Generator:
+    # per-batch draws (gammas, spreads, which sequences repeat their rows);
+    # round 0 keeps the original stream
+    return _rng(gen_seed, 1 << 30) if round_index == 0 else _rng(gen_seed, 1 << 30, round_index)
 
 
 def ragged_b256(batch: int = 256, vocab: int = 152064, max_gamma: int = 16,
-                gen_seed: int = 4) -> Inputs:
-    brng = _rng(gen_seed, 1 << 30)
+                gen_seed: int = 4, round_index: int = 0) -> Inputs:
+    brng = _batch_rng(gen_seed, round_index)
     gammas = brng.integers(1, max_gamma + 1, batch).astype(np.int32)
     sigmas = brng.uniform(0.2, 3.0, batch)
 
@@ -238,15 +250,16 @@ def ragged_b256(batch: int = 256, vocab: int = 152064, max_gamma: int = 16,
         d = t[:g] + rng.standard_normal((g, vocab), dtype=np.float32) * np.float32(sigmas[b])
         return t, d, False
     return _assemble("ragged_b256", vocab, max_gamma, "bf16", gammas, [1.0] * batch, rows, gen_seed,
-                     {"sigma": sigmas})
+                     {"sigma": sigmas}, round_index * batch)
 
 
 def large_vocab(batch: int = 128, vocab: int = 256000, gamma: int = 8, gen_seed: int = 5,
-                identical: int | None = None) -> Inputs:
+                identical: int | None = None, round_index: int = 0) -> Inputs:
     temps = np.where(np.arange(batch) % 2 == 1, 0.0, 1.0).astype(np.float32)
     evens = np.arange(0, batch, 2)
     k = int(round(0.05 * batch)) if identical is None else identical
-    same = set(int(x) for x in _rng(gen_seed, 1 << 30).choice(evens, min(k, len(evens)), replace=False))
+    same = set(int(x) for x in _batch_rng(gen_seed, round_index).choice(evens, min(k, len(evens)),
+                                                                         replace=False))
 
     def rows(b, rng):
         t = rng.standard_normal((gamma + 1, vocab), dtype=np.float32) * 2.0
@@ -255,7 +268,7 @@ def large_vocab(batch: int = 128, vocab: int = 256000, gamma: int = 8, gen_seed:
         d = t[:gamma] + rng.standard_normal((gamma, vocab), dtype=np.float32) * 0.8
         return t, d, False
     return _assemble("large_vocab", vocab, gamma, "f32", [gamma] * batch, temps, rows, gen_seed,
-                     {"identical_sequences": sorted(same)})
+                     {"identical_sequences": sorted(same)}, round_index * batch)
 
 
 def chi_square_set(rounds: int = 1_000_000, vocab: int = 8, gamma: int = 4, gen_seed: int = 11,
