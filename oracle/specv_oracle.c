@@ -61,8 +61,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-#define ORACLE_F32 0
-#define ORACLE_BF16 1
+#include "specv_oracle.h"
 
 #define ORACLE_NEAR_TIE 1e-6
 
@@ -186,11 +185,6 @@ static void row_softmax(const double* z, int64_t V, double T, double* m_out, dou
 /* Lenience functions (DistillSpec section 4, lossy SD paragraph, and the
  * thresholds of Algorithm A.1): f is
  * increasing in p and decreasing in eps, and f(p, 1) = p for all three. */
-#define ORACLE_LENIENCE_NONE 0
-#define ORACLE_LENIENCE_LIN 1
-#define ORACLE_LENIENCE_SQ 2
-#define ORACLE_LENIENCE_EXP 3
-
 static double lenience(double p, int kind, double eps) {
   switch (kind) {
     case ORACLE_LENIENCE_LIN:

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
+#include <string.h>
 
 #include <mutex>
 
@@ -18,6 +19,29 @@ using namespace specv;
 namespace {
 
 constexpr size_t kAlign = 256;
+
+// Enum fields and arguments of the C ABI arrive from C and ctypes callers as
+// plain 32-bit integers, so any value may be there; reading a C++ enum object
+// that holds a value outside its enumerators' range is undefined, so checks
+// read the integer bits instead.
+template <typename E>
+int32_t enum_bits(const E& e) {
+  static_assert(sizeof(E) == sizeof(int32_t), "the C ABI's enums are 32-bit");
+  int32_t v;
+  memcpy(&v, &e, sizeof v);
+  return v;
+}
+
+bool dtype_ok(const specv_dtype_t& dt) {
+  const int32_t v = enum_bits(dt);
+  return v == SPECV_F32 || v == SPECV_BF16;
+}
+
+bool lenience_ok(const specv_lenience_t& l, float epsilon) {
+  const int32_t v = enum_bits(l);
+  if (v < SPECV_LENIENCE_NONE || v > SPECV_LENIENCE_EXP) return false;
+  return v == SPECV_LENIENCE_NONE || (epsilon > 0.f && epsilon <= 1.f);
+}
 // Tuning constants (measured on MI355X; see the design notes).
 #ifndef SPECV_K1_CHUNK_BF16
 #define SPECV_K1_CHUNK_BF16 32768
@@ -71,10 +95,11 @@ struct Plan {
 bool shape_ok(const specv_shape_t* s) {
   if (!s) return false;
   if (s->batch < 0 || s->vocab < 1 || s->max_gamma < 0 || s->max_gamma > SPECV_MAX_GAMMA) return false;
-  if (s->dtype != SPECV_F32 && s->dtype != SPECV_BF16) return false;
+  if (!dtype_ok(s->dtype)) return false;
   if (s->total_draft_rows < 0 || s->total_target_rows < 0) return false;
-  if (s->total_target_rows != s->total_draft_rows + s->batch) return false;
+  // draft rows bounded first (B * max_gamma < 2^37), so the sum cannot overflow
   if (s->total_draft_rows > (int64_t)s->batch * s->max_gamma) return false;
+  if (s->total_target_rows != s->total_draft_rows + s->batch) return false;
   // packed element offsets must fit int64 comfortably
   if (s->total_target_rows > ((int64_t)1 << 40) / s->vocab) return false;
   // every launch grid stays below 2^31 workgroups (at most 2^30 rows of both
@@ -414,10 +439,10 @@ bool decode_shape_ok(const specv_decode_shape_t* s) {
   if (!s) return false;
   if (s->batch < 0 || s->vocab < 1 || s->gamma < 0 || s->gamma > SPECV_MAX_GAMMA || s->rounds < 0)
     return false;
-  if (s->dtype != SPECV_F32 && s->dtype != SPECV_BF16) return false;
+  if (!dtype_ok(s->dtype)) return false;
   // the [V, V] tables and the token buffer must be addressable
   if ((int64_t)s->vocab * s->vocab > ((int64_t)1 << 40)) return false;
-  if ((int64_t)s->batch * s->rounds * (s->gamma + 1) > ((int64_t)1 << 40)) return false;
+  if ((int64_t)s->batch * s->rounds > ((int64_t)1 << 40) / (s->gamma + 1)) return false;  // no overflow
   return true;
 }
 
@@ -470,9 +495,9 @@ bool cascade_shape_ok(const specv_cascade_shape_t* s) {
   if (!s) return false;
   if (s->batch < 0 || s->vocab < 1 || s->rounds < 0) return false;
   if (s->k1 < 0 || s->k1 > SPECV_MAX_GAMMA || s->k2 < 0 || s->k2 > SPECV_MAX_GAMMA) return false;
-  if (s->dtype != SPECV_F32 && s->dtype != SPECV_BF16) return false;
+  if (!dtype_ok(s->dtype)) return false;
   if ((int64_t)s->vocab * s->vocab > ((int64_t)1 << 40)) return false;
-  if ((int64_t)s->batch * s->rounds * (s->k1 + 1) > ((int64_t)1 << 40)) return false;
+  if ((int64_t)s->batch * s->rounds > ((int64_t)1 << 40) / (s->k1 + 1)) return false;  // no overflow
   return true;
 }
 
@@ -639,10 +664,7 @@ specv_status_t specv_verify_lenient(const specv_shape_t* shape, const void* targ
                                     int32_t* out_n_accepted, int32_t* out_next_token,
                                     void* workspace, size_t workspace_bytes, hipStream_t stream,
                                     hipEvent_t* events) {
-  if ((int)lenience < SPECV_LENIENCE_NONE || (int)lenience > SPECV_LENIENCE_EXP)
-    return SPECV_ERR_INVALID_ARGUMENT;
-  if (lenience != SPECV_LENIENCE_NONE && !(epsilon > 0.f && epsilon <= 1.f))
-    return SPECV_ERR_INVALID_ARGUMENT;
+  if (!lenience_ok(lenience, epsilon)) return SPECV_ERR_INVALID_ARGUMENT;
   const bool need_r = shape && shape->max_gamma > 0 && shape->batch > 0;
   if (u ? (need_r && !r) : (r != nullptr)) return SPECV_ERR_INVALID_ARGUMENT;
   Call c{shape, target_logits, draft_logits, draft_tokens, gamma_per_row, temperature,
@@ -928,10 +950,7 @@ specv_status_t specv_cascade_bigram(const specv_cascade_shape_t* shape, const vo
                                     size_t workspace_bytes, hipStream_t stream,
                                     hipEvent_t* events) {
   if (!cascade_shape_ok(shape)) return SPECV_ERR_INVALID_ARGUMENT;
-  if ((int)lenience < SPECV_LENIENCE_NONE || (int)lenience > SPECV_LENIENCE_EXP)
-    return SPECV_ERR_INVALID_ARGUMENT;
-  if (lenience != SPECV_LENIENCE_NONE && !(epsilon > 0.f && epsilon <= 1.f))
-    return SPECV_ERR_INVALID_ARGUMENT;
+  if (!lenience_ok(lenience, epsilon)) return SPECV_ERR_INVALID_ARGUMENT;
   CascadePlan c;
   if (!make_cascade_plan(shape, &c)) return SPECV_ERR_INVALID_ARGUMENT;
   const int64_t B = shape->batch, k1 = shape->k1, k2 = shape->k2, R = shape->rounds;
@@ -1206,7 +1225,7 @@ specv_status_t specv_read_bytes(const void* src, size_t bytes, uint32_t* sink,
 }
 
 const char* specv_status_string(specv_status_t status) {
-  switch (status) {
+  switch (enum_bits(status)) {
     case SPECV_OK: return "ok";
     case SPECV_ERR_INVALID_ARGUMENT: return "invalid argument";
     case SPECV_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
