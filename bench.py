@@ -2,12 +2,17 @@
 
 One step = one specv_verify call (all stages: plan, pass-1 row statistics,
 accept, residual mass, draw) over one batch of synthetic input already
-resident in HBM. Default workload: the T5-XXL-like setting (gamma = 5,
-V = 32128, bf16 logits, T = 1) with 2,000 rounds batched as independent
-sequences into one call. Prints one JSON line.
+resident in HBM. The headline line is the largest single-GPU workload: the
+large-vocabulary setting (B = 128, gamma = 8, V = 256000, fp32 logits, T = 1
+and greedy mixed per sequence). Beside it, "per_config" times the other
+workloads the same way (the tiny CPU-checkable one with 10,000 rounds batched
+into one call, the T5-XXL-like one with 2,000 rounds batched, at T = 1 and
+greedy, batched serving and ragged lookahead), each with its step-level
+fraction of the HBM peak, its pass-1 kernel fraction, the stored counter
+traffic and its parity counts against the CPU oracle. Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                  [--lenience none|lin|sq|exp --epsilon E]
+                  [--lenience none|lin|sq|exp --epsilon E] [--no-per-config]
                   [--no-cpu-baseline] [--copy-calibration BYTES]
 
 With --lenience other than none, a step is one specv_verify_lenient call
@@ -38,6 +43,8 @@ HBM_PEAK_GBPS = 8000.0
 MALL_BYTES = 256 << 20
 WORKLOADS = {
     # name: (generator kwargs, description)
+    "tiny_cpu": (dict(rounds=10000), "tiny CPU-checkable: 10000 rounds x (gamma=4, V=1000, fp32), "
+                                     "T=1"),
     "t5xxl_like": (dict(rounds=2000), "T5-XXL-like: 2000 rounds x (gamma=5, V=32128, bf16), T=1"),
     "t5xxl_like_greedy": (dict(rounds=2000, greedy=True),
                           "T5-XXL-like greedy: 2000 rounds x (gamma=5, V=32128, bf16), T=0"),
@@ -45,6 +52,12 @@ WORKLOADS = {
     "ragged_b256": (dict(), "ragged lookahead: B=256, gamma_b~U{1..16}, V=152064, bf16, T=1"),
     "large_vocab": (dict(), "large vocab: B=128, gamma=8, V=256000, fp32, odd rows greedy"),
 }
+HEADLINE = "large_vocab"
+PER_CONFIG = ["tiny_cpu", "t5xxl_like", "t5xxl_like_greedy", "serving_b64", "ragged_b256"]
+# workloads held to 70% of the HBM peak at step level (pass-1 bytes over the
+# whole step's time)
+STEP_TARGET = 0.70
+TARGET_WORKLOADS = ("t5xxl_like", "serving_b64", "ragged_b256")
 KERNEL_SOURCES = ["speculative_sampling_verify_amd/csrc/kernels.hpp",
                   "speculative_sampling_verify_amd/csrc/diagnostics.hpp",
                   "speculative_sampling_verify_amd/csrc/decode.hpp",
@@ -113,14 +126,50 @@ def batch1_latency(torch, svx, dev, calls=200):
                       "setting)", "eager_us_per_call": eager_us, "graph_us_per_replay": graph_us}
 
 
-def cpu_model() -> str:
+def host_cpu() -> dict:
+    """What the host offers the CPU baseline: the full model string and the
+    family/model/stepping that identify the part, the logical CPUs the kernel
+    reports, those this process may run on, and the cgroup's CPU quota."""
+    info = {"model": "unknown", "family": None, "model_number": None, "stepping": None}
+    keys = {"model name": "model", "cpu family": "family", "model": "model_number",
+            "stepping": "stepping"}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            if not line.strip():
+                break  # the first processor's block is enough
+            k, _, v = line.partition(":")
+            k = k.strip()
+            if k in keys:
+                info[keys[k]] = v.strip()
     except OSError:
         pass
-    return "unknown"
+    info["logical_cpus"] = os.cpu_count()
+    try:
+        info["affinity_cpus"] = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        info["affinity_cpus"] = os.cpu_count()
+    quota = None
+    try:
+        q, period = open("/sys/fs/cgroup/cpu.max").read().split()[:2]
+        if q != "max":
+            quota = int(q) / int(period)
+    except (OSError, ValueError):
+        pass
+    info["cgroup_cpu_quota"] = quota
+    return info
+
+
+# the CPU share of one GPU on these hosts: worker pools stay within it
+CPU_SHARE = 16
+
+
+def baseline_threads(info) -> int:
+    """One oracle thread per hardware thread this process may use, within the
+    cgroup quota and the host's CPU share of one GPU."""
+    n = info["affinity_cpus"] or 1
+    if info["cgroup_cpu_quota"]:
+        n = min(n, max(1, int(info["cgroup_cpu_quota"])))
+    return max(1, min(n, CPU_SHARE))
 
 
 def copy_gbps(torch, svx, dev, nbytes=1 << 30):
@@ -167,7 +216,8 @@ def cpu_baseline(x, gpu_n, gpu_next, budget_s=12.0, lenience="none", epsilon=1.0
     """The oracle as it stands, on the host's cores, over repeated passes of
     the same step's sequences (bounded by a time budget)."""
     import oracle
-    threads = oracle.default_threads()
+    host = host_cpu()
+    threads = baseline_threads(host)
     t0 = time.perf_counter()
     passes, res = 0, None
     while True:
@@ -189,7 +239,12 @@ def cpu_baseline(x, gpu_n, gpu_next, budget_s=12.0, lenience="none", epsilon=1.0
                   lenience=lenience, epsilon=epsilon, nthreads=1)
     single = sub.total_target_rows / (time.perf_counter() - t1)
     return {"value": rows / el, "unit": "verified target rows/s", "cores": threads,
-            "kind": "oracle", "single_thread_value": single, "cpu_model": cpu_model(),
+            "kind": "oracle", "threads_used": threads, "single_thread_value": single,
+            "single_thread_sample": "%d sequences (%d target rows)" % (sub.batch,
+                                                                      sub.total_target_rows),
+            "host": host,
+            "threads_rule": "one per CPU this process may run on, within the cgroup quota "
+                            "and the %d-CPU share of one GPU" % CPU_SHARE,
             "sample": "%d pass(es) over the step's %d sequences (%d target rows each pass), %.1f s"
                       % (passes, x.batch, x.total_target_rows, el),
             "parity_vs_gpu": {"sequences": int(x.batch), "mismatches": int(mism.sum()),
@@ -488,12 +543,137 @@ def bench_cascade(args, torch, svx, dev):
     print(json.dumps(result), flush=True)
 
 
+def measure_verify(torch, svx, dev, x, K, W, lenience="none", epsilon=1.0):
+    """Time K verify steps of one workload after W warm-up steps.
+
+    Distinct copies of the inputs rotate so that the bytes read between
+    reuses of one copy exceed the 256 MB memory-attached last-level cache
+    several times over. In every EVENT_EVERY-th timed step the library
+    records one HIP event pair around its pass-1 kernel (k1_row_stats), on
+    the stream it launches on; the other steps run uninstrumented (an event
+    record costs several microseconds of stream time). Outside the timed
+    region: the same steps with no events, and with an event pair around
+    every stage."""
+    base = svx.from_inputs(x, dev)
+    set_bytes = sum(t.numel() * t.element_size() for t in (base["target"], base["draft"]))
+    n_sets = max(2, int(np.ceil(4 * MALL_BYTES / max(1, set_bytes))))
+    sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(n_sets - 1)]
+    shape = svx._shape_of(base["target"], base["draft"], base["gamma"], x.max_gamma)
+    ws = svx.workspace_for(shape, dev)
+    out_n = torch.empty(x.batch, dtype=torch.int32, device=dev)
+    out_next = torch.empty(x.batch, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, events=None):
+        s = sets[i % n_sets]
+        if lenience != "none":
+            svx.specv_verify_lenient(s["target"], s["draft"], s["draft_tokens"], s["gamma"],
+                                     s["temperature"], lenience, epsilon,
+                                     max_gamma=x.max_gamma, seed=x.seed,
+                                     philox_row_offset=x.row_offset, out_n=out_n,
+                                     out_next=out_next, workspace=ws, stream=stream,
+                                     events=events)
+        elif events is None:
+            svx.specv_verify(s["target"], s["draft"], s["draft_tokens"], s["gamma"],
+                             s["temperature"], max_gamma=x.max_gamma, seed=x.seed,
+                             philox_row_offset=x.row_offset, out_n=out_n, out_next=out_next,
+                             workspace=ws, stream=stream)
+        else:
+            svx.specv_verify_profiled(s["target"], s["draft"], s["draft_tokens"], s["gamma"],
+                                      s["temperature"], events, max_gamma=x.max_gamma,
+                                      seed=x.seed, philox_row_offset=x.row_offset, out_n=out_n,
+                                      out_next=out_next, workspace=ws, stream=stream)
+
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    EVENT_EVERY = 5
+    k1_stage = svx.STAGES.index("row_stats")
+    k1_events = {i: svx.StageEvents(stages=(k1_stage,)) for i in range(0, K, EVENT_EVERY)}
+    t_start, t_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(K):
+        step(i, k1_events.get(i))
+    t_stop.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_stop) / K
+    k1_ms = float(np.mean([ev.elapsed_ms(k1_stage) for ev in k1_events.values()]))
+    t_start.record(stream)
+    for i in range(K):
+        step(i)
+    t_stop.record(stream)
+    torch.cuda.synchronize()
+    ms_step_plain = t_start.elapsed_time(t_stop) / K
+    all_events = [svx.StageEvents() for _ in range(K)]
+    for i in range(K):
+        step(i, all_events[i])
+    torch.cuda.synchronize()
+    stage_ms = {name: float(np.mean([ev.elapsed_ms(si) for ev in all_events]))
+                for si, name in enumerate(svx.STAGES)}
+    res = {"ms_per_step": ms_step, "k1_ms": k1_ms, "timed_launches": len(k1_events),
+           "ms_per_step_plain": ms_step_plain, "stage_ms": stage_ms, "sets": n_sets,
+           "n": out_n.cpu().numpy(), "next": out_next.cpu().numpy()}
+    del sets, base, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def parity_counts(x, n, nxt):
+    """The launch's outcomes against the CPU oracle on the same inputs and
+    Philox stream: exact matches, outcomes inside the oracle's near-tie
+    windows, and the flagged count against its expectation."""
+    import oracle
+    orc = oracle.verify(x.target, x.draft, x.tokens, x.gamma, x.temperature, vocab=x.vocab,
+                        max_gamma=x.max_gamma, seed=x.seed, row_offset=x.row_offset,
+                        nthreads=baseline_threads(host_cpu()))
+    exact = (n == orc.n) & (nxt == orc.next_token)
+    admitted = orc.admits(n, nxt)
+    e = float(orc.near_prob[orc.n >= 0].sum())
+    return {"sequences": int(x.batch), "exact": int(exact.sum()),
+            "admitted_near_tie": int((admitted & ~exact).sum()),
+            "not_admitted": int((~admitted).sum()), "flagged": int(orc.near_tie.sum()),
+            "flag_expectation": e, "flag_cap": e + 5.0 * np.sqrt(e) + 3.0}
+
+
+def per_config(torch, svx, dev, args, sha):
+    """The other workloads, timed as the headline one, with parity counts."""
+    out = {}
+    for name in PER_CONFIG:
+        if name == args.workload:
+            continue
+        x, desc = make_inputs(name)
+        log("[bench] per-config %s: B=%d, target rows=%d" % (name, x.batch, x.total_target_rows))
+        m = measure_verify(torch, svx, dev, x, args.steps, args.warmup)
+        pass1 = x.pass1_bytes()
+        step_frac = pass1 / (m["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBPS
+        traffic = load_traffic(name, sha)
+        rec = {"workload": desc, "ms_per_step": m["ms_per_step"],
+               "verified_target_rows_per_s": x.total_target_rows / (m["ms_per_step"] * 1e-3),
+               "pass1_bytes": pass1, "step_frac_of_peak": step_frac,
+               "pass1_kernel_ms": m["k1_ms"],
+               "pass1_kernel_frac": pass1 / (m["k1_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+               "traffic_bytes": traffic,
+               "traffic_ratio": traffic / pass1 if traffic else None,
+               "ms_per_step_uninstrumented": m["ms_per_step_plain"],
+               "stage_ms_instrumented": m["stage_ms"],
+               "parity_vs_oracle": parity_counts(x, m["n"], m["next"])}
+        if name in TARGET_WORKLOADS:
+            rec["target_step_frac"] = STEP_TARGET
+            rec["target_ms_per_step"] = pass1 / (STEP_TARGET * HBM_PEAK_GBPS * 1e9) * 1e3
+            rec["meets_target"] = bool(step_frac >= STEP_TARGET)
+        out[name] = rec
+        log("[bench]   %.1f us/step, %.1f%% of peak at step level, pass 1 %.1f%%"
+            % (m["ms_per_step"] * 1e3, 100 * step_frac, 100 * rec["pass1_kernel_frac"]))
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="t5xxl_like", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
     ap.add_argument("--lenience", default="none", choices=["none", "lin", "sq", "exp"])
     ap.add_argument("--epsilon", type=float, default=1.0)
     ap.add_argument("--diagnostics", type=int, default=-1, metavar="K",
@@ -507,6 +687,8 @@ def main():
     ap.add_argument("--cascade", action="store_true",
                     help="time the vertical cascade over three bigram tables instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="time the selected workload only (no per-config figures)")
     ap.add_argument("--no-batch1", action="store_true",
                     help="skip the batch-1 latency figure (its small launches of the same "
                          "kernels would mix into a profiler's per-kernel averages)")
@@ -548,94 +730,28 @@ def main():
     if args.cascade:
         return bench_cascade(args, torch, svx, dev)
 
-    t_gen = time.perf_counter()
+    # the probes first: they bring the part to its sustained clocks before any
+    # step is timed, and give the context figures of the line
+    cg = copy_gbps(torch, svx, dev)
+    rg = read_gbps(torch, svx, dev)
+
     x, desc = make_inputs(args.workload)
-    log("[bench] generated %s in %.1f s (B=%d, target rows=%d, draft rows=%d)"
-        % (args.workload, time.perf_counter() - t_gen, x.batch, x.total_target_rows,
-           x.total_draft_rows))
-    base = svx.from_inputs(x, dev)
-    set_bytes = sum(t.numel() * t.element_size() for t in (base["target"], base["draft"]))
-    # distinct copies so that the bytes read between reuses of one set exceed
-    # the 256 MB memory-attached last-level cache several times over
-    n_sets = max(2, int(np.ceil(4 * MALL_BYTES / max(1, set_bytes))))
-    sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(n_sets - 1)]
-    shape = svx._shape_of(base["target"], base["draft"], base["gamma"], x.max_gamma)
-    ws = svx.workspace_for(shape, dev)
-    out_n = torch.empty(x.batch, dtype=torch.int32, device=dev)
-    out_next = torch.empty(x.batch, dtype=torch.int32, device=dev)
-    stream = torch.cuda.current_stream(dev)
-
-    def step(i, events=None):
-        s = sets[i % n_sets]
-        if args.lenience != "none":
-            svx.specv_verify_lenient(s["target"], s["draft"], s["draft_tokens"], s["gamma"],
-                                     s["temperature"], args.lenience, args.epsilon,
-                                     max_gamma=x.max_gamma, seed=x.seed,
-                                     philox_row_offset=x.row_offset, out_n=out_n,
-                                     out_next=out_next, workspace=ws, stream=stream,
-                                     events=events)
-        elif events is None:
-            svx.specv_verify(s["target"], s["draft"], s["draft_tokens"], s["gamma"],
-                             s["temperature"], max_gamma=x.max_gamma, seed=x.seed,
-                             philox_row_offset=x.row_offset, out_n=out_n, out_next=out_next,
-                             workspace=ws, stream=stream)
-        else:
-            svx.specv_verify_profiled(s["target"], s["draft"], s["draft_tokens"], s["gamma"],
-                                      s["temperature"], events, max_gamma=x.max_gamma,
-                                      seed=x.seed, philox_row_offset=x.row_offset, out_n=out_n,
-                                      out_next=out_next, workspace=ws, stream=stream)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    # Timed region: K steps. In every EVENT_EVERY-th step the library records
-    # one HIP event pair around its pass-1 kernel (k1_row_stats), on the
-    # stream it launches on; everything else runs uninstrumented (each event
-    # record costs several microseconds of stream time, so sampling keeps
-    # that cost out of the step time while the kernel is still timed live).
-    K = args.steps
-    EVENT_EVERY = 5
-    k1_stage = svx.STAGES.index("row_stats")
-    k1_events = {i: svx.StageEvents(stages=(k1_stage,)) for i in range(0, K, EVENT_EVERY)}
-    t_start, t_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for i in range(K):
-        step(i, k1_events.get(i))
-    t_stop.record(stream)
-    torch.cuda.synchronize()
-    ms_step = t_start.elapsed_time(t_stop) / K
-    k1_ms = float(np.mean([ev.elapsed_ms(k1_stage) for ev in k1_events.values()]))
-
-    # Diagnostics outside the timed region: the same steps with no events at
-    # all, and with an event pair around every stage.
-    t_start.record(stream)
-    for i in range(K):
-        step(i)
-    t_stop.record(stream)
-    torch.cuda.synchronize()
-    ms_step_plain = t_start.elapsed_time(t_stop) / K
-    all_events = [svx.StageEvents() for _ in range(K)]
-    for i in range(K):
-        step(i, all_events[i])
-    torch.cuda.synchronize()
-    stage_ms = {name: float(np.mean([ev.elapsed_ms(si) for ev in all_events]))
-                for si, name in enumerate(svx.STAGES)}
-
-    n_host = out_n.cpu().numpy()
-    next_host = out_next.cpu().numpy()
+    log("[bench] %s: B=%d, target rows=%d, draft rows=%d" % (args.workload, x.batch,
+                                                            x.total_target_rows,
+                                                            x.total_draft_rows))
+    m = measure_verify(torch, svx, dev, x, args.steps, args.warmup, args.lenience, args.epsilon)
     pass1 = x.pass1_bytes()
-    rows_per_step = x.total_target_rows
-    emitted = int(np.sum(n_host[n_host >= 0] + 1))
-    achieved = pass1 / (k1_ms * 1e-3) / 1e9
+    achieved = pass1 / (m["k1_ms"] * 1e-3) / 1e9
     sha = kernel_sha()
+    n_host, next_host = m["n"], m["next"]
+    emitted = int(np.sum(n_host[n_host >= 0] + 1))
+    ms_step = m["ms_per_step"]
     result = {
         "metric": METRIC,
-        "value": rows_per_step / (ms_step * 1e-3),
+        "value": x.total_target_rows / (ms_step * 1e-3),
         "unit": "verified target rows/s",
         "n_gpus": 1,
-        "steps": K,
+        "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
         "higher_is_better": True,
@@ -652,24 +768,24 @@ def main():
                      "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": load_traffic(args.workload, sha),
                      "kernel": "k1_row_stats", "algorithmic_bytes_per_launch": pass1,
-                     "avg_launch_ms": k1_ms, "timed_launches": len(k1_events)},
+                     "avg_launch_ms": m["k1_ms"], "timed_launches": m["timed_launches"],
+                     "frac_of_copy": achieved / cg, "frac_of_read_probe": achieved / rg},
         "step_gbps": pass1 / (ms_step * 1e-3) / 1e9,
         "step_frac_of_peak": pass1 / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-        "ms_per_step_uninstrumented": ms_step_plain,
-        "stage_ms_instrumented": stage_ms,
+        "ms_per_step_uninstrumented": m["ms_per_step_plain"],
+        "stage_ms_instrumented": m["stage_ms"],
         "emitted_tokens_per_s": emitted / (ms_step * 1e-3),
         "mean_tokens_per_sequence": emitted / x.batch,
         "sequences_per_s": x.batch / (ms_step * 1e-3),
-        "rotating_input_sets": n_sets,
+        "rotating_input_sets": m["sets"],
+        "copy_gbps": cg,
+        "read_probe_gbps": rg,
         "kernel_sha": sha,
     }
-    cg = copy_gbps(torch, svx, dev)
-    result["copy_gbps"] = cg
-    result["roofline"]["frac_of_copy"] = achieved / cg
-    rg = read_gbps(torch, svx, dev)
-    result["read_probe_gbps"] = rg
-    result["roofline"]["frac_of_read_probe"] = achieved / rg
-    if args.workload == "t5xxl_like" and args.lenience == "none" and not args.no_batch1:
+    if args.lenience == "none" and not args.no_per_config:
+        result["parity_vs_oracle"] = parity_counts(x, n_host, next_host)
+        result["per_config"] = per_config(torch, svx, dev, args, sha)
+    if args.lenience == "none" and not args.no_batch1:
         result["batch1_latency"] = batch1_latency(torch, svx, dev)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on the host")
