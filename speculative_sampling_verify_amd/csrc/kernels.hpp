@@ -172,7 +172,130 @@ struct RowStatsArgs {
   const float* temperature;  // temperature[row / (gamma (+1))], tk/dk unused)
   const int32_t* gamma;  // non-null (uniform batch): workgroup 0 also does the
   uint32_t* status_out;  // plan's check (every gamma == uniform_g) and sets the status word
+  // inline_plan (a ragged batch of at most kInlinePlanMax sequences, gamma
+  // non-null, uniform_g < 0): no plan launch. Workgroup 0 writes the packed
+  // row offsets toff/doff [B + 1] and the status word; every wave finds its
+  // row's sequence with a wave scan of the gammas (tk/dk unused).
+  int32_t inline_plan, max_gamma;
+  int64_t* toff;
+  int64_t* doff;
 };
+
+constexpr int kInlinePlanMax = 1024;      // largest ragged batch planned inside pass 1
+constexpr int kInlinePlanRun = kInlinePlanMax / kWave;  // sequences per lane in its scans
+
+// Workgroup-wide exclusive scan of one int64 per thread (kBlock threads);
+// returns the exclusive prefix and the total in *total.
+__device__ __forceinline__ int64_t block_exclusive_scan(int64_t v, int64_t* total) {
+  __shared__ int64_t wsum[kWavesPerBlock];
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  int64_t incl = v;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int64_t o = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += o;
+  }
+  if (lane == kWave - 1) wsum[wave] = incl;
+  __syncthreads();
+  int64_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kWavesPerBlock; ++w) {
+    before += (w < wave) ? wsum[w] : 0;
+    all += wsum[w];
+  }
+  *total = all;
+  return before + incl - v;
+}
+
+// The plan of a ragged batch of B <= kInlinePlanMax sequences, by workgroup 0
+// of pass 1 (every thread of it takes this branch): thread t owns sequences
+// [t P, t P + P), P = ceil(B / kBlock). Writes the packed row offsets
+// toff/doff (with the totals at index B) and the status word: layout error
+// when a gamma lies outside [0, max_gamma] or the totals differ from the
+// shape's, the same rule and offsets as k0_plan.
+__device__ void inline_plan_wg0(const RowStatsArgs& a) {
+  constexpr int R = kInlinePlanMax / kBlock;
+  const int per = (a.B + kBlock - 1) / kBlock;
+  const int lo = (int)threadIdx.x * per;
+  int32_t g[R];
+  int64_t st = 0, sd = 0;
+  bool bad = false;
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const int b = lo + i;
+    g[i] = (i < per && b < a.B) ? a.gamma[b] : 0;
+    bad |= (i < per && b < a.B) && (g[i] < 0 || g[i] > a.max_gamma);
+    const int64_t gg = g[i] < 0 ? 0 : g[i];
+    if (i < per && b < a.B) {
+      st += gg + 1;
+      sd += gg;
+    }
+  }
+  int64_t tot_t, tot_d;
+  int64_t t = block_exclusive_scan(st, &tot_t);
+  __syncthreads();  // the scan's LDS is reused by the second scan
+  int64_t d = block_exclusive_scan(sd, &tot_d);
+  bad = __syncthreads_or(bad);
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const int b = lo + i;
+    if (i < per && b < a.B) {
+      const int64_t gg = g[i] < 0 ? 0 : g[i];
+      a.toff[b] = t;
+      a.doff[b] = d;
+      t += gg + 1;
+      d += gg;
+    }
+  }
+  if (threadIdx.x == 0) {
+    a.toff[a.B] = tot_t;
+    a.doff[a.B] = tot_d;
+    const bool layout_bad = bad || tot_t != a.total_t || tot_d != a.total_d;
+    a.status_out[0] = layout_bad ? kLayoutError : 0u;
+  }
+}
+
+// The sequence that owns packed target row j (draft row j with `draft`) of a
+// ragged batch of B <= kInlinePlanMax sequences, by one wave: lane l counts
+// the rows of sequences [l P, l P + P), P = ceil(B / 64), a wave scan of the
+// counts finds the lane whose run holds row j, and that run is walked with
+// v_readlane. The counts follow k0_plan (a negative gamma counts as 0);
+// gammas are also capped at max_gamma here, which changes no valid batch and
+// keeps the sums small. A row past the total (only in a batch with a layout
+// error, which the accept step reports) maps to the last sequence.
+__device__ __forceinline__ int32_t row_sequence(const RowStatsArgs& a, int64_t j, bool draft,
+                                                int lane) {
+  constexpr int R = kInlinePlanRun;
+  const int per = (a.B + kWave - 1) / kWave;
+  const int lo = lane * per;
+  int32_t c[R];
+  int32_t sum = 0;
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const int b = lo + i;
+    int32_t g = (i < per && b < a.B) ? a.gamma[b] : -1;
+    g = g < 0 ? 0 : (g > a.max_gamma ? a.max_gamma : g);
+    c[i] = (i < per && b < a.B) ? g + (draft ? 0 : 1) : 0;
+    sum += c[i];
+  }
+  int32_t incl = sum;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int32_t o = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += o;
+  }
+  const uint64_t m = ballot((int64_t)incl > j);
+  if (!m) return a.B - 1;
+  const int L = first_lane(m);
+  int64_t cum = __builtin_amdgcn_readlane(incl - sum, L);
+  int found = -1;
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    cum += __builtin_amdgcn_readlane(c[i], L);
+    found = (found < 0 && cum > j) ? i : found;
+  }
+  return L * per + found;
+}
 
 // Pass-1 loop over one (row, chunk), double-buffered: the loads of tile it+1
 // are in flight while tile it is processed. A row is cut into tiles of EPI
@@ -290,7 +413,10 @@ __device__ __forceinline__ RowPart chunk_pass(const void* row, int64_t V, int c,
 template <int DT, bool VEC, bool WITH_ARG>
 __global__ __launch_bounds__(kBlock) void k1_row_stats(RowStatsArgs a) {
   using TL = Tile<DT, VEC>;
-  if (a.gamma && blockIdx.x == 0) {
+  if (a.inline_plan && blockIdx.x == 0) {
+    // A ragged batch's plan, in this launch (offsets read after it ends).
+    inline_plan_wg0(a);
+  } else if (a.gamma && blockIdx.x == 0) {
     // The uniform batch's plan, in this launch: offsets and row scales are
     // arithmetic, so only the gammas are checked and the status word is set
     // (read after this launch ends). The whole workgroup takes this branch
@@ -315,20 +441,32 @@ __global__ __launch_bounds__(kBlock) void k1_row_stats(RowStatsArgs a) {
   // Target rows are always read: tile c is in flight while the row's scale
   // and the status word are looked up. Draft rows are read only for sampling
   // sequences, so their scale comes first.
+  // With the plan inside this launch the scale takes two dependent loads
+  // (the gammas, then T_b): the first tile of a draft row is then requested
+  // before them too, at the cost of one unneeded tile per (row, chunk) of a
+  // greedy sequence.
   typename TL::Raw first;
   float k;
-  if (is_draft) {
+  if (is_draft && !a.inline_plan) {
     k = (a.uniform_g >= 0) ? seq_scale(a.temperature[j / a.uniform_g]) : a.dk[j];
     // greedy (or invalid) sequence: the verify step needs no draft row
     if (!(k > 0.f) && !(a.all_drafts && k == 0.f)) return;
     load_tile<DT, VEC>(row, a.V, c, lane, first);
   } else {
     load_tile<DT, VEC>(row, a.V, c, lane, first);
-    k = (a.uniform_g >= 0) ? seq_scale(a.temperature[j / (a.uniform_g + 1)]) : a.tk[j];
-    if (!(k >= 0.f)) return;  // invalid temperature: the accept step fails the sequence
+    if (a.inline_plan)
+      k = seq_scale(a.temperature[row_sequence(a, j, is_draft, lane)]);
+    else  // a target row (draft rows take this branch only with the inline plan)
+      k = (a.uniform_g >= 0) ? seq_scale(a.temperature[j / (a.uniform_g + 1)]) : a.tk[j];
+    if (is_draft) {
+      if (!(k > 0.f) && !(a.all_drafts && k == 0.f)) return;
+    } else if (!(k >= 0.f)) {
+      return;  // invalid temperature: the accept step fails the sequence
+    }
   }
-  // a uniform batch reads only arithmetic offsets: its rows are computed
-  // whatever the gammas hold, and the accept step reports a layout error
+  // a uniform batch reads only arithmetic offsets, and a batch planned in
+  // this launch only its gammas: their rows are computed whatever the gammas
+  // hold, and the accept step reports a layout error
   if (!a.gamma && (a.status[0] & kLayoutError)) return;
   RowPart out;
   float lm;

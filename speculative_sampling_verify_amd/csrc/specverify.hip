@@ -70,6 +70,9 @@ constexpr int kDrawStep = kBlock * 8; // elements per workgroup scan step of the
 constexpr int64_t kTargetMassItems = SPECV_MASS_WAVES;  // pass-2 waves to aim for
 // Accept step, pass 2 and draw in one launch when a sequence's pass-2 waves fit
 // one workgroup and its sub-block masses fit this much LDS.
+#ifndef SPECV_INLINE_PLAN
+#define SPECV_INLINE_PLAN 1  // ragged batches of at most 1024 sequences: no plan launch
+#endif
 #ifndef SPECV_FUSED_DRAW
 #define SPECV_FUSED_DRAW 1
 #endif
@@ -265,7 +268,7 @@ specv_status_t launch_row_stats(const Plan& p, bool vec, const void* target, con
                                 void* ws, hipStream_t st, bool with_argmax = false,
                                 bool all_drafts = false, int bar_k = 0, float* bar = nullptr,
                                 const float* temperature = nullptr, bool uniform = false,
-                                const int32_t* plan_gamma = nullptr) {
+                                const int32_t* plan_gamma = nullptr, bool inline_plan = false) {
   RowStatsArgs a;
   a.target = target;
   a.draft = draft;
@@ -284,8 +287,12 @@ specv_status_t launch_row_stats(const Plan& p, bool vec, const void* target, con
   a.bar = bar;
   a.uniform_g = uniform ? (int32_t)p.max_gamma : -1;
   a.temperature = temperature;
-  a.gamma = uniform ? plan_gamma : nullptr;
+  a.gamma = (uniform || inline_plan) ? plan_gamma : nullptr;
   a.status_out = at<uint32_t>(ws, 0);
+  a.inline_plan = inline_plan ? 1 : 0;
+  a.max_gamma = (int32_t)p.max_gamma;
+  a.toff = at<int64_t>(ws, p.off_toff);
+  a.doff = at<int64_t>(ws, p.off_doff);
   const int64_t waves = (p.tt + p.td) * p.chunks1;
   if (waves == 0) return SPECV_OK;
   const dim3 grid(blocks_for(waves)), block(kBlock);
@@ -406,15 +413,20 @@ specv_status_t run(const Call& c) {
   const bool uniform = uniform_batch(p);
   if (c.skip_pass1 && !uniform) return SPECV_ERR_INVALID_ARGUMENT;
   // A uniform batch has no plan launch: pass 1's first workgroup checks the
-  // gammas and sets the status word.
+  // gammas and sets the status word. Nor has a ragged batch of at most
+  // kInlinePlanMax sequences: pass 1's first workgroup writes its offsets and
+  // status word, and each pass-1 wave finds its row's sequence itself.
+  const bool inline_plan = !uniform && !c.skip_pass1 && SPECV_INLINE_PLAN &&
+                           p.B <= kInlinePlanMax;
   mark(c.events, 2 * SPECV_STAGE_PLAN, c.stream);
-  if (!uniform && (st = launch_plan(p, c.gamma, c.temperature, c.ws, c.stream)) != SPECV_OK)
+  if (!uniform && !inline_plan &&
+      (st = launch_plan(p, c.gamma, c.temperature, c.ws, c.stream)) != SPECV_OK)
     return st;
   mark(c.events, 2 * SPECV_STAGE_PLAN + 1, c.stream);
   mark(c.events, 2 * SPECV_STAGE_ROWSTATS, c.stream);
   if (!c.skip_pass1 &&
       (st = launch_row_stats(p, vec, c.target, c.draft, c.ws, c.stream, false, false, 0, nullptr,
-                             c.temperature, uniform, c.gamma)) != SPECV_OK)
+                             c.temperature, uniform, c.gamma, inline_plan)) != SPECV_OK)
     return st;
   mark(c.events, 2 * SPECV_STAGE_ROWSTATS + 1, c.stream);
   mark(c.events, 2 * SPECV_STAGE_ACCEPT_MASS, c.stream);

@@ -376,6 +376,68 @@ def test_layout_error_and_empty_batch(svx):
     assert e[0].numel() == 0
 
 
+def ragged_case(B, V, max_gamma, seed, dtype="f32"):
+    """A ragged batch of B sequences, gammas uniform in [0, max_gamma] (the
+    first one at max_gamma), every fifth sequence greedy, draft rows = target
+    rows + N(0, 1), draft tokens drawn from the draft rows."""
+    rng = np.random.default_rng(seed)
+    g = rng.integers(0, max_gamma + 1, size=B).astype(np.int32)
+    g[0] = max_gamma
+    T = np.where(np.arange(B) % 5 == 3, 0.0, 1.0).astype(np.float32)
+    toff = np.concatenate([[0], np.cumsum(g + 1)])
+    doff = np.concatenate([[0], np.cumsum(g)])
+    target = (rng.standard_normal((int(toff[-1]), V)) * 2).astype(np.float32)
+    seq = np.repeat(np.arange(B), g)
+    trow = toff[seq] + (np.arange(int(doff[-1])) - doff[seq])
+    draft = (target[trow] + rng.standard_normal((len(trow), V))).astype(np.float32)
+    Ts = np.where(T[seq] > 0, T[seq], 1.0)[:, None]
+    noise = np.where(T[seq][:, None] > 0, rng.gumbel(size=draft.shape), 0.0)
+    tokens = np.argmax(draft / Ts + noise, axis=1).astype(np.int32)
+    conv = synth.to_bf16_bits if dtype == "bf16" else (lambda a: a)
+    return synth.Inputs("ragged B=%d" % B, V, max_gamma, dtype, conv(target), conv(draft), tokens,
+                        g, T)
+
+
+@pytest.mark.parametrize("B", [1, 63, 64, 65, 700, 1024, 1025, 2500])
+def test_ragged_plan_in_pass1_and_planned(svx, B):
+    # ragged batches up to 1024 sequences are planned inside pass 1 (no plan
+    # launch), larger ones by their own plan launch: both against the oracle
+    x = ragged_case(B, 40 if B > 100 else 333, 7, seed=B, dtype="bf16" if B % 2 else "f32")
+    parity_case(svx, "ragged B=%d (%s plan)" % (B, "in-pass-1" if B <= 1024 else "launched"), x)
+
+
+@pytest.mark.parametrize("B", [5, 1024, 1100])
+def test_ragged_layout_errors(svx, B):
+    # a gamma above max_gamma, a negative gamma, and gammas whose sum differs
+    # from the row totals, all with totals the host accepts: the device sees
+    # them, in pass 1's plan (B <= 1024) or in the plan launch
+    base = ragged_case(B, 24, 4, seed=7 + B)
+    assert base.total_draft_rows < B * base.max_gamma  # not a uniform batch
+    cases = []
+    g = base.gamma.copy(); i = int(np.flatnonzero(g == 4)[0]); j = int(np.flatnonzero(g > 0)[-1])
+    if i != j:
+        g[i], g[j] = 5, g[j] - 1          # 5 > max_gamma, totals unchanged
+        cases.append(("gamma above max_gamma", g))
+    g = base.gamma.copy(); i = int(np.flatnonzero(g > 1)[0])
+    k = (i + 1) % B
+    g[k], g[i] = -1, g[i] + g[k] + 1      # a negative gamma
+    cases.append(("negative gamma", g))
+    g = base.gamma.copy(); g[int(np.flatnonzero(g < 4)[0])] += 1
+    cases.append(("gamma sum above the row total", g))
+    for what, gam in cases:
+        x = synth.Inputs(base.name, base.vocab, base.max_gamma, base.dtype, base.target, base.draft,
+                         base.tokens, gam.astype(np.int32), base.temperature)
+        log("[case] ragged B=%d layout error: %s" % (B, what))
+        n, nxt, st = run_gpu(svx, x)
+        orc = run_oracle(x)
+        assert not orc.layout_ok
+        assert (n == -1).all() and (nxt == -1).all() and st & svx.SPECV_DEV_LAYOUT_ERROR, what
+    # and the untouched batch is fine
+    n, nxt, st = run_gpu(svx, base)
+    assert not st & svx.SPECV_DEV_LAYOUT_ERROR
+    assert_parity("ragged B=%d" % B, base, (n, nxt), run_oracle(base))
+
+
 # ------------------------------------------------- statistics on the GPU
 
 @pytest.mark.parametrize("rounds", [1_000_000])
