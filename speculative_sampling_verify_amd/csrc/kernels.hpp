@@ -64,6 +64,8 @@ struct PlanArgs {
   float* tk;
   float* dk;
   int32_t* dseq;  // optional: the sequence of each draft row
+  int32_t* ttok;  // optional: for each target row, the packed index of its
+                  // draft token (-1 for a sequence's last row)
   uint32_t* status;
   int64_t total_t, total_d;
   int32_t B, max_gamma;
@@ -140,6 +142,8 @@ __global__ __launch_bounds__(1024) void k0_plan(PlanArgs a) {
     for (int64_t j = d; j < dend; ++j) a.dk[j] = kk;
     if (a.dseq)
       for (int64_t j = d; j < dend; ++j) a.dseq[j] = b;
+    if (a.ttok)
+      for (int64_t j = t; j < tend; ++j) a.ttok[j] = (j - t < gg) ? (int32_t)(d + (j - t)) : -1;
     t += gg + 1;
     d += gg;
   }
@@ -179,7 +183,52 @@ struct RowStatsArgs {
   int32_t inline_plan, max_gamma;
   int64_t* toff;
   int64_t* doff;
+  // tokens non-null: the chunk-0 wave of each sampling row that has a draft
+  // token x also reads the row's logit at x (the accept step's ratio needs
+  // it) and stores it to zx_t[j] / zx_d[j] before its chunk loop (so that
+  // nothing of it stays in registers across the loop: the kernel is at the
+  // scalar register limit). The token of target row j comes from arithmetic
+  // (uniform batch), the wave's own scan (inline plan) or ttok[j] (the plan
+  // launch's table).
+  const int32_t* tokens;
+  const int32_t* ttok;
+  float* zx_t;
+  float* zx_d;
 };
+
+// A 4-byte load from a wave-uniform, 4-byte-aligned address through the
+// scalar data cache (constant address space): the value lands in a scalar
+// register, so a wave can hold it across its chunk loop at no cost in vector
+// registers. Read-only data only.
+__device__ __forceinline__ uintptr_t uniform_address(uintptr_t addr) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)addr >> 32));
+  return ((uintptr_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint32_t scalar_load_u32(uintptr_t addr) {
+  return *reinterpret_cast<const __attribute__((address_space(4))) uint32_t*>(uniform_address(addr));
+}
+__device__ __forceinline__ float scalar_load_f32(const float* p) {
+  return __uint_as_float(scalar_load_u32(reinterpret_cast<uintptr_t>(p)));
+}
+
+// Logit x of a row (wave-uniform row and x) as the aligned 4-byte word that
+// holds it: an aligned word never crosses a page, so it is readable wherever
+// the element is. logit_of_word() takes the element's fp32 bits out of it
+// later (bf16: the high half when x sits at a byte offset of 2 within the
+// word), so that the load is only waited for where the value is used.
+template <int DT>
+__device__ __forceinline__ uint32_t logit_word(const void* row, int32_t x, bool* high) {
+  const uintptr_t addr = uniform_address(reinterpret_cast<uintptr_t>(
+      static_cast<const char*>(row) + (int64_t)x * (DT == kBF16 ? 2 : 4)));
+  *high = (addr & 2) != 0;
+  return scalar_load_u32(addr & ~(uintptr_t)3);
+}
+template <int DT>
+__device__ __forceinline__ uint32_t logit_of_word(uint32_t w, bool high) {
+  if constexpr (DT == kBF16) return high ? (w & 0xffff0000u) : (w << 16);
+  else return w;
+}
 
 constexpr int kInlinePlanMax = 1024;      // largest ragged batch planned inside pass 1
 constexpr int kInlinePlanRun = kInlinePlanMax / kWave;  // sequences per lane in its scans
@@ -261,10 +310,11 @@ __device__ void inline_plan_wg0(const RowStatsArgs& a) {
 // counts finds the lane whose run holds row j, and that run is walked with
 // v_readlane. The counts follow k0_plan (a negative gamma counts as 0);
 // gammas are also capped at max_gamma here, which changes no valid batch and
-// keeps the sums small. A row past the total (only in a batch with a layout
-// error, which the accept step reports) maps to the last sequence.
+// keeps the sums small. Also reports the sequence's first row and its row
+// count. A row past the total (only in a batch with a layout error, which
+// the accept step reports) maps to the last sequence, with first row -1.
 __device__ __forceinline__ int32_t row_sequence(const RowStatsArgs& a, int64_t j, bool draft,
-                                                int lane) {
+                                                int lane, int64_t* first_row, int32_t* n_rows) {
   constexpr int R = kInlinePlanRun;
   const int per = (a.B + kWave - 1) / kWave;
   const int lo = lane * per;
@@ -285,15 +335,28 @@ __device__ __forceinline__ int32_t row_sequence(const RowStatsArgs& a, int64_t j
     if (lane >= off) incl += o;
   }
   const uint64_t m = ballot((int64_t)incl > j);
-  if (!m) return a.B - 1;
+  if (!m) {
+    *first_row = -1;
+    *n_rows = 0;
+    return a.B - 1;
+  }
   const int L = first_lane(m);
   int64_t cum = __builtin_amdgcn_readlane(incl - sum, L);
   int found = -1;
+  int64_t start = 0;
+  int32_t cnt = 0;
 #pragma unroll
   for (int i = 0; i < R; ++i) {
-    cum += __builtin_amdgcn_readlane(c[i], L);
-    found = (found < 0 && cum > j) ? i : found;
+    const int32_t ci = __builtin_amdgcn_readlane(c[i], L);
+    if (found < 0 && cum + ci > j) {
+      found = i;
+      start = cum;
+      cnt = ci;
+    }
+    cum += ci;
   }
+  *first_row = start;
+  *n_rows = cnt;
   return L * per + found;
 }
 
@@ -447,35 +510,75 @@ __global__ __launch_bounds__(kBlock) void k1_row_stats(RowStatsArgs a) {
   // greedy sequence.
   typename TL::Raw first;
   float k;
+  // The row's draft token (packed index; -1 for a sequence's last target
+  // row), for the capture of its logit below. Scalar loads: the token, the
+  // temperature and the logit come from wave-uniform addresses.
+  int64_t tok = -1;
   if (is_draft && !a.inline_plan) {
-    k = (a.uniform_g >= 0) ? seq_scale(a.temperature[j / a.uniform_g]) : a.dk[j];
+    tok = j;
+    k = (a.uniform_g >= 0) ? seq_scale(scalar_load_f32(a.temperature + j / a.uniform_g))
+                           : scalar_load_f32(a.dk + j);
     // greedy (or invalid) sequence: the verify step needs no draft row
     if (!(k > 0.f) && !(a.all_drafts && k == 0.f)) return;
     load_tile<DT, VEC>(row, a.V, c, lane, first);
   } else {
     load_tile<DT, VEC>(row, a.V, c, lane, first);
-    if (a.inline_plan)
-      k = seq_scale(a.temperature[row_sequence(a, j, is_draft, lane)]);
-    else  // a target row (draft rows take this branch only with the inline plan)
-      k = (a.uniform_g >= 0) ? seq_scale(a.temperature[j / (a.uniform_g + 1)]) : a.tk[j];
+    if (a.inline_plan) {
+      int64_t first_row;
+      int32_t n_rows;
+      const int32_t sb = row_sequence(a, j, is_draft, lane, &first_row, &n_rows);
+      // target row i of sequence sb: its token is draft row doff + i, with
+      // doff = (the sequence's first target row) - sb; none for the last row
+      if (is_draft) tok = j;
+      else if (first_row >= 0 && j - first_row < n_rows - 1) tok = (first_row - sb) + (j - first_row);
+      k = seq_scale(scalar_load_f32(a.temperature + sb));
+    } else if (a.uniform_g >= 0) {  // a target row (draft rows: inline plan only)
+      const int64_t sb = j / (a.uniform_g + 1), i = j - sb * (a.uniform_g + 1);
+      tok = (i < a.uniform_g) ? sb * a.uniform_g + i : -1;
+      k = seq_scale(scalar_load_f32(a.temperature + sb));
+    } else {
+      if (a.ttok) tok = (int32_t)scalar_load_u32(reinterpret_cast<uintptr_t>(a.ttok + j));
+      k = scalar_load_f32(a.tk + j);
+    }
     if (is_draft) {
       if (!(k > 0.f) && !(a.all_drafts && k == 0.f)) return;
     } else if (!(k >= 0.f)) {
       return;  // invalid temperature: the accept step fails the sequence
     }
   }
+  // The draft token's logit for the accept step, by the row's chunk-0 wave,
+  // stored before the chunk loop: the first tile is in flight meanwhile, but
+  // the second is only requested once the two dependent scalar loads are
+  // back, so the host enables the capture only where chunks are long. A
+  // token outside [0, V) stores 0: the accept step fails that sequence
+  // without using it.
+  if (a.tokens && c == 0 && k > 0.f && tok >= 0 && tok < a.total_d) {
+    const int32_t x = (int32_t)scalar_load_u32(reinterpret_cast<uintptr_t>(a.tokens + tok));
+    uint32_t bits = 0u;
+    if (x >= 0 && (int64_t)x < a.V) {
+      bool high;
+      const uint32_t w = logit_word<DT>(row, x, &high);
+      bits = logit_of_word<DT>(w, high);
+    }
+    if (lane == 0) (is_draft ? a.zx_d : a.zx_t)[j] = __uint_as_float(bits);
+  }
   // a uniform batch reads only arithmetic offsets, and a batch planned in
   // this launch only its gammas: their rows are computed whatever the gammas
   // hold, and the accept step reports a layout error
   if (!a.gamma && (a.status[0] & kLayoutError)) return;
+  // outputs addressed before the chunk loop: fewer scalar registers live
+  // across it (the kernel is at the scalar register limit)
+  RowPart* const dst = (is_draft ? a.dparts : a.tparts) + j * a.chunks + c;
+  float* const bar_dst = (is_draft && a.bar_k > 0) ? a.bar + j * a.chunks + c : nullptr;
+  const int32_t bar_k = a.bar_k;
   RowPart out;
   float lm;
   if (k > 0.f)
     out = chunk_pass<DT, VEC, true, WITH_ARG>(row, a.V, c, a.chunks, n_iter, k, lane, first, lm);
   else
     out = chunk_pass<DT, VEC, false, true>(row, a.V, c, a.chunks, n_iter, 0.f, lane, first, lm);
-  if (lane == 0) (is_draft ? a.dparts : a.tparts)[j * a.chunks + c] = out;
-  if (is_draft && a.bar_k > 0) {
+  if (lane == 0) *dst = out;
+  if (bar_dst) {
     // The bar_k-th largest of the lanes' maxima: a logit of the chunk with
     // at least bar_k logits of the chunk at or above it (-inf when fewer
     // lanes hold a logit), for the top-k selection of the diagnostics.
@@ -485,7 +588,7 @@ __global__ __launch_bounds__(kBlock) void k1_row_stats(RowStatsArgs a) {
       const float o = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(lm), l));
       rank += (o > lm || (o == lm && l < lane)) ? 1 : 0;
     }
-    if (rank == a.bar_k - 1) a.bar[j * a.chunks + c] = lm;
+    if (rank == bar_k - 1) *bar_dst = lm;
   }
 }
 
@@ -577,6 +680,10 @@ struct AcceptArgs {
   int32_t lenience;  // kLen*; kLenNone is the lossless step
   float eps;         // lenience parameter in (0, 1)
   int32_t uniform_g;  // >= 0: uniform batch with this gamma (offsets arithmetic)
+  // non-null: the draft tokens' logits captured by pass 1, one per target /
+  // draft row; else the accept step reads them from the logit rows
+  const float* zx_t;
+  const float* zx_d;
 };
 
 // f(p, eps): p / eps, p / eps^2 or p^eps, in float64 (f(p, 1) = p; the host
@@ -619,11 +726,17 @@ __device__ Select accept_sequence(const AcceptArgs& a, int64_t b, int lane, bool
   const int64_t d0 = uni ? b * a.uniform_g : a.doff[b];
   RowPart tq[4], dq[4];
   int x = 0;
+  const bool captured = a.zx_t != nullptr;
+  float zT = 0.f, zD = 0.f;
   if (uni) {
     if (lane <= g) load_parts4(a.tparts + (t0 + lane) * a.chunks, a.chunks, tq);
     if (lane < g) {
       x = a.tokens[d0 + lane];
       load_parts4(a.dparts + (d0 + lane) * a.chunks, a.chunks, dq);
+      if (captured) {
+        zT = a.zx_t[t0 + lane];
+        zD = a.zx_d[d0 + lane];
+      }
     }
   }
   if (status & kLayoutError) return finish(-1, -1, false);
@@ -640,6 +753,10 @@ __device__ Select accept_sequence(const AcceptArgs& a, int64_t b, int lane, bool
   }
   if (lane < g) {
     if (!uni) x = a.tokens[d0 + lane];
+    if (!uni && captured) {
+      zT = a.zx_t[t0 + lane];
+      zD = a.zx_d[d0 + lane];
+    }
     bad |= (x < 0) || ((int64_t)x >= a.V);
     if (sampling) {
       if (!uni) load_parts4(a.dparts + (d0 + lane) * a.chunks, a.chunks, dq);
@@ -666,8 +783,10 @@ __device__ Select accept_sequence(const AcceptArgs& a, int64_t b, int lane, bool
   }
   bool rej = false;
   if (lane < g) {
-    const float zT = load_logit<DT>(a.target, (t0 + lane) * a.V + x);
-    const float zD = load_logit<DT>(a.draft, (d0 + lane) * a.V + x);
+    if (!captured) {
+      zT = load_logit<DT>(a.target, (t0 + lane) * a.V + x);
+      zD = load_logit<DT>(a.draft, (d0 + lane) * a.V + x);
+    }
     const double p = exp2((double)zT * (double)k - (double)st_t.rk) / st_t.s;
     const double q = exp2((double)zD * (double)k - (double)st_d.rk) / st_d.s;
     const double ratio = (q == 0.0) ? (double)pinf() : lenient(p, a.lenience, a.eps) / q;

@@ -73,6 +73,9 @@ constexpr int64_t kTargetMassItems = SPECV_MASS_WAVES;  // pass-2 waves to aim f
 #ifndef SPECV_INLINE_PLAN
 #define SPECV_INLINE_PLAN 1  // ragged batches of at most 1024 sequences: no plan launch
 #endif
+#ifndef SPECV_CAPTURE_MIN_CHUNK_BYTES
+#define SPECV_CAPTURE_MIN_CHUNK_BYTES 49152  // 0: never capture
+#endif
 #ifndef SPECV_FUSED_DRAW
 #define SPECV_FUSED_DRAW 1
 #endif
@@ -89,6 +92,7 @@ struct Plan {
   int64_t nsub;
   bool fused_draw;  // k3_accept_mass_draw instead of k3_accept_mass + k4_draw
   size_t off_toff, off_doff, off_tk, off_dk, off_tparts, off_dparts, off_sel, off_sub;
+  size_t off_ttok, off_zxt, off_zxd;  // draft-token index per target row; captured logits
   size_t bytes;
   // per-position diagnostics (after the verify layout)
   size_t off_dseq, off_bar, off_dgparts, off_topz, off_topi;
@@ -160,6 +164,9 @@ void make_plan(const specv_shape_t* s, Plan* p) {
   p->fused_draw = SPECV_FUSED_DRAW && p->chunks3 * kWave <= 1024 &&
                   (size_t)p->nsub * sizeof(double) <= kFusedDrawLds;
   p->off_sub = off; off = align_up(off + (size_t)p->B * p->nsub * sizeof(double));
+  p->off_ttok = off; off = align_up(off + (size_t)p->tt * 4);
+  p->off_zxt = off; off = align_up(off + (size_t)p->tt * 4);
+  p->off_zxd = off; off = align_up(off + (size_t)p->td * 4);
   p->bytes = off;
 }
 
@@ -246,7 +253,7 @@ inline unsigned blocks_for(int64_t waves) {
 bool uniform_batch(const Plan& p) { return p.B > 0 && p.tt == p.B * (p.max_gamma + 1); }
 
 specv_status_t launch_plan(const Plan& p, const int32_t* gamma, const float* temperature, void* ws,
-                           hipStream_t st, int32_t* dseq = nullptr) {
+                           hipStream_t st, int32_t* dseq = nullptr, int32_t* ttok = nullptr) {
   PlanArgs a;
   a.gamma = gamma;
   a.temperature = temperature;
@@ -255,6 +262,7 @@ specv_status_t launch_plan(const Plan& p, const int32_t* gamma, const float* tem
   a.tk = at<float>(ws, p.off_tk);
   a.dk = at<float>(ws, p.off_dk);
   a.dseq = dseq;
+  a.ttok = ttok;
   a.status = at<uint32_t>(ws, 0);
   a.total_t = p.tt;
   a.total_d = p.td;
@@ -268,7 +276,8 @@ specv_status_t launch_row_stats(const Plan& p, bool vec, const void* target, con
                                 void* ws, hipStream_t st, bool with_argmax = false,
                                 bool all_drafts = false, int bar_k = 0, float* bar = nullptr,
                                 const float* temperature = nullptr, bool uniform = false,
-                                const int32_t* plan_gamma = nullptr, bool inline_plan = false) {
+                                const int32_t* plan_gamma = nullptr, bool inline_plan = false,
+                                const int32_t* tokens = nullptr) {
   RowStatsArgs a;
   a.target = target;
   a.draft = draft;
@@ -293,6 +302,11 @@ specv_status_t launch_row_stats(const Plan& p, bool vec, const void* target, con
   a.max_gamma = (int32_t)p.max_gamma;
   a.toff = at<int64_t>(ws, p.off_toff);
   a.doff = at<int64_t>(ws, p.off_doff);
+  // tokens given: capture the draft tokens' logits for the accept step
+  a.tokens = tokens;
+  a.ttok = (tokens && !uniform && !inline_plan) ? at<int32_t>(ws, p.off_ttok) : nullptr;
+  a.zx_t = tokens ? at<float>(ws, p.off_zxt) : nullptr;
+  a.zx_d = tokens ? at<float>(ws, p.off_zxd) : nullptr;
   const int64_t waves = (p.tt + p.td) * p.chunks1;
   if (waves == 0) return SPECV_OK;
   const dim3 grid(blocks_for(waves)), block(kBlock);
@@ -315,6 +329,17 @@ specv_status_t launch_row_stats(const Plan& p, bool vec, const void* target, con
     }
   }
   return launched();
+}
+
+// Pass 1 of specv_verify captures the draft tokens' logits for the accept
+// step (one dependent memory round trip less there) when its chunks are long:
+// the capture delays each chunk-0 wave's second tile by about one round trip,
+// a small share of a chunk of SPECV_CAPTURE_MIN_CHUNK_BYTES or more (measured:
+// faster on the serving, ragged and large-vocabulary launches, slower on
+// the T5-XXL-like one with its 32 KiB chunks).
+bool capture_logits(const Plan& p) {
+  return p.td > 0 && SPECV_CAPTURE_MIN_CHUNK_BYTES > 0 &&
+         p.V * p.esz >= (int64_t)SPECV_CAPTURE_MIN_CHUNK_BYTES * p.chunks1;
 }
 
 AcceptArgs accept_args(const Plan& p, const Call& c) {
@@ -343,6 +368,9 @@ AcceptArgs accept_args(const Plan& p, const Call& c) {
   a.lenience = c.lenience;
   a.eps = c.eps;
   a.uniform_g = uniform_batch(p) ? (int32_t)p.max_gamma : -1;
+  const bool captured = !c.skip_pass1 && capture_logits(p);  // pass 1 of run() captured them
+  a.zx_t = captured ? at<float>(c.ws, p.off_zxt) : nullptr;
+  a.zx_d = captured ? at<float>(c.ws, p.off_zxd) : nullptr;
   return a;
 }
 
@@ -420,13 +448,15 @@ specv_status_t run(const Call& c) {
                            p.B <= kInlinePlanMax;
   mark(c.events, 2 * SPECV_STAGE_PLAN, c.stream);
   if (!uniform && !inline_plan &&
-      (st = launch_plan(p, c.gamma, c.temperature, c.ws, c.stream)) != SPECV_OK)
+      (st = launch_plan(p, c.gamma, c.temperature, c.ws, c.stream, nullptr,
+                        at<int32_t>(c.ws, p.off_ttok))) != SPECV_OK)
     return st;
   mark(c.events, 2 * SPECV_STAGE_PLAN + 1, c.stream);
   mark(c.events, 2 * SPECV_STAGE_ROWSTATS, c.stream);
   if (!c.skip_pass1 &&
       (st = launch_row_stats(p, vec, c.target, c.draft, c.ws, c.stream, false, false, 0, nullptr,
-                             c.temperature, uniform, c.gamma, inline_plan)) != SPECV_OK)
+                             c.temperature, uniform, c.gamma, inline_plan,
+                             capture_logits(p) ? c.tokens : nullptr)) != SPECV_OK)
     return st;
   mark(c.events, 2 * SPECV_STAGE_ROWSTATS + 1, c.stream);
   mark(c.events, 2 * SPECV_STAGE_ACCEPT_MASS, c.stream);

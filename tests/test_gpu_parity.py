@@ -438,6 +438,88 @@ def test_ragged_layout_errors(svx, B):
     assert_parity("ragged B=%d" % B, base, (n, nxt), run_oracle(base))
 
 
+def uniform_case(B, V, g, seed, dtype="bf16", errors=False):
+    """A uniform batch (every gamma = g): T = 1, every fifth sequence greedy,
+    every seventh at T = 0.7; draft rows = target rows + N(0, 1); tokens drawn
+    from the draft rows. With `errors`, a few sequences carry data errors
+    (NaN or +inf logits, a draft token outside [0, V), invalid
+    temperatures)."""
+    rng = np.random.default_rng(seed)
+    T = np.ones(B, np.float32)
+    T[3::5] = 0.0
+    T[6::7] = 0.7
+    target = (rng.standard_normal((B * (g + 1), V)) * 2).astype(np.float32)
+    trow = (np.arange(B * g) // g) * (g + 1) + np.arange(B * g) % g
+    draft = (target[trow] + rng.standard_normal((B * g, V))).astype(np.float32)
+    Ts = np.repeat(T, g)
+    noise = np.where(Ts[:, None] > 0, rng.gumbel(size=draft.shape), 0.0)
+    tokens = np.argmax(draft / np.where(Ts > 0, Ts, 1.0)[:, None] + noise, axis=1).astype(np.int32)
+    if errors:
+        target[1 * (g + 1) + 1, 7] = np.nan
+        target[2 * (g + 1) + g, 9] = np.inf      # the bonus row
+        draft[4 * g + 0, 3] = np.nan
+        tokens[8 * g + 1] = V
+        tokens[9 * g] = -1
+        T[10], T[11], T[12] = -1.0, np.nan, np.inf
+        target[13 * (g + 1) + 2, :] = -np.inf    # no finite logit (sequence 13 greedy)
+    conv = synth.to_bf16_bits if dtype == "bf16" else (lambda a: a)
+    return synth.Inputs("uniform B=%d" % B, V, g, dtype, conv(target), conv(draft), tokens,
+                        np.full(B, g, np.int32), T)
+
+
+@pytest.mark.parametrize("B,V,g,dtype", [(1024, 8192, 3, "bf16"), (1100, 8193, 2, "bf16"),
+                                         (1030, 4096, 5, "f32"), (1500, 5000, 1, "f32"),
+                                         (2048, 20000, 0, "bf16")])
+def test_large_uniform_batch_parity(svx, B, V, g, dtype):
+    # uniform batches of a thousand and more sequences (no plan launch, the
+    # draw in the accept step's launch): vector and scalar loads (rows not
+    # 16-byte multiples), bf16 and fp32, gamma 0..5, greedy and sampling mixed
+    x = uniform_case(B, V, g, seed=B + V, dtype=dtype)
+    parity_case(svx, "uniform B=%d V=%d gamma=%d %s" % (B, V, g, dtype), x)
+
+
+def test_large_uniform_batch_errors(svx):
+    x = uniform_case(1100, 8192, 3, seed=5, errors=True)
+    n, nxt, st = run_gpu(svx, x)
+    orc = run_oracle(x)
+    np.testing.assert_array_equal(n[:20], orc.n[:20])
+    assert list(n[[1, 2, 4, 8, 9, 10, 11, 12, 13]]) == [-1] * 9
+    assert st & svx.SPECV_DEV_SEQ_ERROR and not st & svx.SPECV_DEV_LAYOUT_ERROR
+    assert_parity("uniform batch with data errors", x, (n, nxt), orc)
+    # gammas that keep the row totals but differ from max_gamma: a layout
+    # error that pass 1's first workgroup finds
+    gam = x.gamma.copy()
+    gam[700], gam[900] = 4, 2
+    y = synth.Inputs(x.name, x.vocab, x.max_gamma, x.dtype, x.target, x.draft, x.tokens, gam,
+                     x.temperature)
+    n, nxt, st = run_gpu(svx, y)
+    assert not run_oracle(y).layout_ok
+    assert (n == -1).all() and (nxt == -1).all() and st == svx.SPECV_DEV_LAYOUT_ERROR
+    # and a clean batch after it in the same workspace shape
+    clean = uniform_case(1100, 8192, 3, seed=6)
+    got, _ = parity_case(svx, "uniform batch after a layout error", clean)
+    assert run_gpu(svx, clean)[2] == 0
+
+
+@pytest.mark.parametrize("case", ["uniform", "ragged in pass 1", "ragged planned"])
+def test_long_rows_capture_and_data_errors(svx, case):
+    # rows long enough (48 KiB or more per pass-1 chunk) that pass 1 also
+    # captures each draft token's logit for the accept step: uniform, ragged
+    # with the plan inside pass 1 and ragged with the plan launch (its token
+    # table), with data errors on the uniform batch (tokens outside [0, V),
+    # NaN/+inf logits, invalid temperatures)
+    if case == "uniform":
+        x = uniform_case(16, 65536, 3, seed=21, errors=True)
+    elif case == "ragged in pass 1":
+        x = ragged_case(40, 65536, 5, seed=22, dtype="bf16")
+    else:
+        x = ragged_case(1100, 49152, 3, seed=23, dtype="bf16")
+    got, orc = parity_case(svx, "long rows, %s (B=%d V=%d)" % (case, x.batch, x.vocab), x)
+    if case == "uniform":
+        assert list(got[0][[1, 2, 4, 8, 9, 10, 11, 12, 13]]) == [-1] * 9
+        assert got[2] & svx.SPECV_DEV_SEQ_ERROR
+
+
 # ------------------------------------------------- statistics on the GPU
 
 @pytest.mark.parametrize("rounds", [1_000_000])
