@@ -87,8 +87,10 @@ def make_inputs(name):
 def batch1_latency(torch, svx, dev, calls=200):
     """The literal batch-1 call of the T5-XXL-like setting (one sequence,
     gamma = 5, V = 32128, bf16, T = 1): microseconds per call for back-to-back
-    eager calls on one stream, and for replays of a HIP graph that captured
-    one call (launch overhead is most of it at this size)."""
+    eager calls on one stream, for replays of a HIP graph that captured one
+    call, and per call for replays of a graph that captured 16 calls in a row
+    (which separates the cost of launching a graph from that of its kernel
+    nodes; launch overhead is most of it at this size)."""
     import synth
     x = synth.t5xxl_like(rounds=1)
     d = svx.from_inputs(x, dev)
@@ -122,8 +124,15 @@ def batch1_latency(torch, svx, dev, calls=200):
         call()
     torch.cuda.synchronize()
     graph_us = timed(g.replay)
+    g16 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g16, stream=s):
+        for _ in range(16):
+            call()
+    torch.cuda.synchronize()
+    graph16_us = timed(g16.replay) / 16
     return {"config": "1 sequence, gamma=5, V=32128, bf16, T=1 (one round of the T5-XXL-like "
-                      "setting)", "eager_us_per_call": eager_us, "graph_us_per_replay": graph_us}
+                      "setting)", "eager_us_per_call": eager_us, "graph_us_per_replay": graph_us,
+            "graph_of_16_calls_us_per_call": graph16_us}
 
 
 def host_cpu() -> dict:
@@ -293,6 +302,7 @@ def diag_cpu_baseline(x, k, budget_s=12.0):
 
 
 def bench_diagnostics(args, torch, svx, dev):
+    cg = copy_gbps(torch, svx, dev)  # clocks settle; also the counters' calibration kernel
     t_gen = time.perf_counter()
     x, desc = make_inputs(args.workload)
     log("[bench] generated %s in %.1f s" % (args.workload, time.perf_counter() - t_gen))
@@ -362,6 +372,7 @@ def bench_diagnostics(args, torch, svx, dev):
         "step_gbps": (by["pass1"] + by["pass2"]) / (ms_step * 1e-3) / 1e9,
         "stage_ms_instrumented": stage_ms,
         "rotating_input_sets": n_sets,
+        "copy_gbps": cg,
         "kernel_sha": kernel_sha(),
     }
     if not args.no_cpu_baseline:
@@ -372,6 +383,7 @@ def bench_diagnostics(args, torch, svx, dev):
 
 def bench_decode(args, torch, svx, dev):
     import synth
+    cg = copy_gbps(torch, svx, dev)  # clocks settle; also the counters' calibration kernel
     V, B, g, R = args.decode_vocab, args.decode_batch, args.decode_gamma, args.decode_rounds
     t_gen = time.perf_counter()
     tabs = synth.bigram_tables(V)
@@ -435,6 +447,7 @@ def bench_decode(args, torch, svx, dev):
                      "avg_launch_ms": stage_ms["gather"]},
         "stage_ms_last_round": stage_ms,
         "tokens_per_round": tokens / (B * R),
+        "copy_gbps": cg,
         "kernel_sha": kernel_sha(),
     }
     if not args.no_cpu_baseline:
@@ -459,6 +472,7 @@ def bench_decode(args, torch, svx, dev):
 
 def bench_cascade(args, torch, svx, dev):
     import synth
+    cg = copy_gbps(torch, svx, dev)  # clocks settle; also the counters' calibration kernel
     V, B, R = args.decode_vocab, args.decode_batch, args.decode_rounds
     k1, k2, kind, eps = 5, 3, "sq", 0.5
     t_gen = time.perf_counter()
@@ -520,6 +534,7 @@ def bench_cascade(args, torch, svx, dev):
                      "avg_launch_ms": stage_ms["inner_gather"]},
         "stage_ms_last_round": stage_ms,
         "tokens_per_target_review": tokens / (B * R),
+        "copy_gbps": cg,
         "kernel_sha": kernel_sha(),
     }
     if not args.no_cpu_baseline:
