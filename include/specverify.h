@@ -321,10 +321,13 @@ specv_status_t specv_cascade_bigram(const specv_cascade_shape_t* shape, const vo
 
 /* Stages of one call, in launch order. A stage is one kernel, with two
  * exceptions whose event pairs are then recorded back to back and time
- * nothing: a uniform batch (every gamma_b == max_gamma) has no plan launch
- * (pass 1 checks the gammas), and the draw shares the launch of the accept
- * step and pass 2 when one workgroup holds a sequence's pass-2 waves (16
- * waves at most: 512 or more sequences, or V <= 32768). */
+ * nothing: there is no plan launch for a uniform batch (every gamma_b ==
+ * max_gamma; pass 1 checks the gammas) nor for a ragged batch of at most
+ * 1024 sequences (pass 1's first workgroup writes the offsets and checks the
+ * gammas, and each pass-1 wave finds its row's sequence itself), and the
+ * draw shares the launch of the accept step and pass 2 when one workgroup
+ * holds a sequence's pass-2 waves (16 waves at most: 512 or more sequences,
+ * or V <= 32768). */
 #define SPECV_STAGE_PLAN 0        /* offsets of the packed rows, per-row T scale */
 #define SPECV_STAGE_ROWSTATS 1    /* pass 1: max, sum of exp (argmax) per row    */
 #define SPECV_STAGE_ACCEPT_MASS 2 /* ratios, uniforms, n; pass 2 weight masses   */
