@@ -68,6 +68,9 @@ constexpr int64_t kMinPass1Waves = SPECV_MIN_PASS1_WAVES;  // two per compute un
 #endif
 constexpr int kDrawStep = kBlock * 8; // elements per workgroup scan step of the draw
 constexpr int64_t kTargetMassItems = SPECV_MASS_WAVES;  // pass-2 waves to aim for
+constexpr int64_t kMassStepsPerWave = 5;      // draw steps per wave of a one-workgroup split
+constexpr int64_t kFusedMinWaves = 2048;      // ... if it still gives this many waves in all
+constexpr int64_t kTargetUnfusedItems = 3072;  // else unfused waves to aim for
 // Accept step, pass 2 and draw in one launch when a sequence's pass-2 waves fit
 // one workgroup and its sub-block masses fit this much LDS.
 #ifndef SPECV_INLINE_PLAN
@@ -144,14 +147,35 @@ void make_plan(const specv_shape_t* s, Plan* p) {
   }
   c1 = c1 < 1 ? 1 : (c1 > kMaxChunks1 ? kMaxChunks1 : c1);
   p->chunks1 = (int)c1;
-  // pass 2: enough chunks per sequence to give about kTargetMassItems waves
-  int64_t c3 = (kTargetMassItems + p->B - 1) / (p->B > 0 ? p->B : 1);
+  // pass 2: enough chunks per sequence to give about kTargetMassItems waves.
+  // Where that needs more than the 16 waves one workgroup holds (so the draw
+  // takes a launch of its own), a split with about kMassStepsPerWave draw
+  // steps per wave that fits one workgroup is taken instead if it still gives
+  // kFusedMinWaves waves in all; else fewer, longer unfused chunks (about
+  // kTargetUnfusedItems waves). Swept on this part per workload.
+  const int64_t Bp = p->B > 0 ? p->B : 1;
   const int64_t max_c3 = (p->V + kDrawStep - 1) / kDrawStep;
-  c3 = c3 < 1 ? 1 : (c3 > max_c3 ? max_c3 : c3);
-  int64_t ch3 = (p->V + c3 - 1) / c3;
-  ch3 = (ch3 + kDrawStep - 1) / kDrawStep * kDrawStep;
+  auto chunks_for = [&](int64_t c3, int64_t* elems) {
+    c3 = c3 < 1 ? 1 : (c3 > max_c3 ? max_c3 : c3);
+    int64_t ch3 = (p->V + c3 - 1) / c3;
+    ch3 = (ch3 + kDrawStep - 1) / kDrawStep * kDrawStep;
+    *elems = ch3;
+    return (p->V + ch3 - 1) / ch3;
+  };
+  int64_t ch3;
+  int64_t c3 = chunks_for((kTargetMassItems + Bp - 1) / Bp, &ch3);
+  if (c3 * kWave > 1024) {
+    int64_t chf;
+    const int64_t cf = chunks_for((max_c3 + kMassStepsPerWave - 1) / kMassStepsPerWave, &chf);
+    if (cf * kWave <= 1024 && Bp * cf >= kFusedMinWaves) {
+      c3 = cf;
+      ch3 = chf;
+    } else {
+      c3 = chunks_for((kTargetUnfusedItems + Bp - 1) / Bp, &ch3);
+    }
+  }
   p->chunk3_elems = (int)ch3;
-  p->chunks3 = (int)((p->V + ch3 - 1) / ch3);
+  p->chunks3 = (int)c3;
   size_t off = kAlign;  // [0, 256): status word
   p->off_toff = off; off = align_up(off + (size_t)(p->B + 1) * 8);
   p->off_doff = off; off = align_up(off + (size_t)(p->B + 1) * 8);
