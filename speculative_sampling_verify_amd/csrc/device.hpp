@@ -101,6 +101,34 @@ struct Tile {
     }
   }
 
+  // Where element `off` (0 <= off < EPI) of a tile lands in the raw dwords
+  // load_raw reads, packed with the chunk iteration `it` that holds the tile:
+  // (it << 11) | (dword << 7) | (high half << 6) | lane. The element's fp32
+  // bits are that dword (fp32, or bf16 widened on load), or its high half or
+  // its low half shifted up (two bf16 per dword).
+  __device__ static __forceinline__ int32_t capture_code(int it, int off) {
+    int dw, hi = 0, ln;
+    if constexpr (VEC) {
+      const int vec = off / VE;
+      ln = vec % kWave;
+      const int u = vec / kWave, e = off % VE;
+      if constexpr (DT == kBF16) {
+        dw = u * 4 + e / 2;
+        hi = e & 1;
+      } else {
+        dw = u * 4 + e;
+      }
+    } else {
+      dw = off / kWave;
+      ln = off % kWave;
+    }
+    return (it << 11) | (dw << 7) | (hi << 6) | ln;
+  }
+  __device__ static __forceinline__ uint32_t bits_of(uint32_t w, int32_t cap) {
+    if constexpr (VEC && DT == kBF16) return ((cap >> 6) & 1) ? (w & 0xffff0000u) : (w << 16);
+    else return w;
+  }
+
   // Raw load of iteration `it`; slots at or past e1 read as -inf when MASK.
   template <bool MASK>
   __device__ static __forceinline__ void load_raw(const void* row, int64_t e0, int64_t e1, int it,

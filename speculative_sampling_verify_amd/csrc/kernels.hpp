@@ -30,7 +30,10 @@ namespace specv {
 
 // Statistics of one (row, chunk): s = sum over the chunk's elements of
 // 2^(fl32(z k - ref_point(m, k))) (sampling rows) or 0/NaN (greedy rows, NaN
-// flags a NaN/+inf logit); m = max; arg = lowest index attaining m.
+// flags a NaN/+inf logit); m = max; arg = lowest index attaining m. The
+// verify step needs no argmax of a sampling row: there, arg of the chunk
+// that holds the row's draft token carries that logit's fp32 bits instead,
+// and the other chunks' arg is not written.
 struct RowPart {
   double s;
   float m;
@@ -183,17 +186,15 @@ struct RowStatsArgs {
   int32_t inline_plan, max_gamma;
   int64_t* toff;
   int64_t* doff;
-  // tokens non-null: the chunk-0 wave of each sampling row that has a draft
-  // token x also reads the row's logit at x (the accept step's ratio needs
-  // it) and stores it to zx_t[j] / zx_d[j] before its chunk loop (so that
-  // nothing of it stays in registers across the loop: the kernel is at the
-  // scalar register limit). The token of target row j comes from arithmetic
-  // (uniform batch), the wave's own scan (inline plan) or ttok[j] (the plan
-  // launch's table).
+  // tokens non-null (the verify step, no argmax of sampling rows): each
+  // sampling row that has a draft token x records its logit z[x] (the accept
+  // step's ratio needs it) as it passes: the wave whose chunk holds x writes
+  // the float's bits to the arg field of its partial, which sampling rows do
+  // not otherwise use; the other chunks leave that field as it was. The token
+  // of target row j comes from arithmetic (uniform batch), the wave's own scan
+  // (inline plan) or ttok[j] (the plan launch's table).
   const int32_t* tokens;
   const int32_t* ttok;
-  float* zx_t;
-  float* zx_d;
 };
 
 // A 4-byte load from a wave-uniform, 4-byte-aligned address through the
@@ -210,24 +211,6 @@ __device__ __forceinline__ uint32_t scalar_load_u32(uintptr_t addr) {
 }
 __device__ __forceinline__ float scalar_load_f32(const float* p) {
   return __uint_as_float(scalar_load_u32(reinterpret_cast<uintptr_t>(p)));
-}
-
-// Logit x of a row (wave-uniform row and x) as the aligned 4-byte word that
-// holds it: an aligned word never crosses a page, so it is readable wherever
-// the element is. logit_of_word() takes the element's fp32 bits out of it
-// later (bf16: the high half when x sits at a byte offset of 2 within the
-// word), so that the load is only waited for where the value is used.
-template <int DT>
-__device__ __forceinline__ uint32_t logit_word(const void* row, int32_t x, bool* high) {
-  const uintptr_t addr = uniform_address(reinterpret_cast<uintptr_t>(
-      static_cast<const char*>(row) + (int64_t)x * (DT == kBF16 ? 2 : 4)));
-  *high = (addr & 2) != 0;
-  return scalar_load_u32(addr & ~(uintptr_t)3);
-}
-template <int DT>
-__device__ __forceinline__ uint32_t logit_of_word(uint32_t w, bool high) {
-  if constexpr (DT == kBF16) return high ? (w & 0xffff0000u) : (w << 16);
-  else return w;
 }
 
 constexpr int kInlinePlanMax = 1024;      // largest ragged batch planned inside pass 1
@@ -387,11 +370,18 @@ __device__ __forceinline__ void load_tile(const void* row, int64_t V, int64_t t,
 // With STORE, every tile is also written to `dst` (a row of the same length)
 // as it is processed: a producer that writes the rows computes their
 // statistics in the same pass.
+//
+// With cap >= 0 (Tile::capture_code of one element of the chunk), the lane
+// that holds that element stores its logit's fp32 bits to *cap_dst after the
+// loop. Every tile takes its candidate dword with a uniform-index register
+// move and keeps it when the tile is the element's: no branch in the loop (a
+// branch there made the compiler drain the tile in flight at each back edge).
 template <int DT, bool VEC, bool SAMPLING, bool WITH_ARG, bool STORE = false>
 __device__ __forceinline__ RowPart chunk_pass(const void* row, int64_t V, int c, int chunks,
                                               int n_iter, float k, int lane,
                                               typename Tile<DT, VEC>::Raw& a, float& lane_max,
-                                              void* dst = nullptr) {
+                                              void* dst = nullptr, int32_t cap = -1,
+                                              uint32_t* cap_dst = nullptr) {
   using TL = Tile<DT, VEC>;
   using Raw = typename TL::Raw;
   constexpr int NE = TL::NE;
@@ -400,8 +390,18 @@ __device__ __forceinline__ RowPart chunk_pass(const void* row, int64_t V, int c,
   double s = 0.0;
   bool bad = false;
   int best = -1;
+  uint32_t capv = 0u;
   auto process = [&](const Raw& raw, int it) {
     if constexpr (STORE) TL::store_raw(dst, ((int64_t)c + (int64_t)it * chunks) * TL::EPI, V, 0, lane, raw);
+    if constexpr (SAMPLING && !WITH_ARG && !STORE) {
+      static_assert(TL::RD == 16, "the capture indexes 16 raw dwords");
+      typedef uint32_t v16 __attribute__((ext_vector_type(16)));
+      v16 vv;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) vv[q] = raw.d[q];
+      const uint32_t w = vv[(cap >> 7) & 15];
+      capv = ((cap >> 11) == it) ? w : capv;
+    }
     float z[NE];
     TL::widen(raw, z);
     const float g = tile_max(z);
@@ -449,6 +449,9 @@ __device__ __forceinline__ RowPart chunk_pass(const void* row, int64_t V, int c,
     process(b, it + 1);
   }
   lane_max = m;
+  if constexpr (SAMPLING && !WITH_ARG && !STORE) {
+    if (cap >= 0 && lane == (cap & 63)) *cap_dst = TL::bits_of(capv, cap);
+  }
   // wave merge: maximum first, then one rescale per lane and a float64 sum
   const float M = wave_max(m);
   double S;
@@ -511,8 +514,8 @@ __global__ __launch_bounds__(kBlock) void k1_row_stats(RowStatsArgs a) {
   typename TL::Raw first;
   float k;
   // The row's draft token (packed index; -1 for a sequence's last target
-  // row), for the capture of its logit below. Scalar loads: the token, the
-  // temperature and the logit come from wave-uniform addresses.
+  // row), for the capture of its logit below. Scalar loads: the token and the
+  // temperature come from wave-uniform addresses.
   int64_t tok = -1;
   if (is_draft && !a.inline_plan) {
     tok = j;
@@ -546,21 +549,19 @@ __global__ __launch_bounds__(kBlock) void k1_row_stats(RowStatsArgs a) {
       return;  // invalid temperature: the accept step fails the sequence
     }
   }
-  // The draft token's logit for the accept step, by the row's chunk-0 wave,
-  // stored before the chunk loop: the first tile is in flight meanwhile, but
-  // the second is only requested once the two dependent scalar loads are
-  // back, so the host enables the capture only where chunks are long. A
-  // token outside [0, V) stores 0: the accept step fails that sequence
-  // without using it.
-  if (a.tokens && c == 0 && k > 0.f && tok >= 0 && tok < a.total_d) {
-    const int32_t x = (int32_t)scalar_load_u32(reinterpret_cast<uintptr_t>(a.tokens + tok));
-    uint32_t bits = 0u;
-    if (x >= 0 && (int64_t)x < a.V) {
-      bool high;
-      const uint32_t w = logit_word<DT>(row, x, &high);
-      bits = logit_of_word<DT>(w, high);
+  // The draft token's logit for the accept step: the wave whose chunk holds
+  // token x takes it from the tile in its registers (capture code below). A
+  // token outside [0, V) is recorded nowhere: the accept step fails that
+  // sequence without looking for it.
+  int32_t cap = -1;
+  if constexpr (!WITH_ARG) {
+    if (a.tokens && k > 0.f && tok >= 0 && tok < a.total_d) {
+      const int32_t x = (int32_t)scalar_load_u32(reinterpret_cast<uintptr_t>(a.tokens + tok));
+      if (x >= 0 && (int64_t)x < a.V) {
+        const int64_t t = x / TL::EPI;
+        if (t % a.chunks == c) cap = TL::capture_code((int)(t / a.chunks), (int)(x - t * TL::EPI));
+      }
     }
-    if (lane == 0) (is_draft ? a.zx_d : a.zx_t)[j] = __uint_as_float(bits);
   }
   // a uniform batch reads only arithmetic offsets, and a batch planned in
   // this launch only its gammas: their rows are computed whatever the gammas
@@ -573,11 +574,20 @@ __global__ __launch_bounds__(kBlock) void k1_row_stats(RowStatsArgs a) {
   const int32_t bar_k = a.bar_k;
   RowPart out;
   float lm;
+  const bool capturing = !WITH_ARG && a.tokens && k > 0.f;
   if (k > 0.f)
-    out = chunk_pass<DT, VEC, true, WITH_ARG>(row, a.V, c, a.chunks, n_iter, k, lane, first, lm);
+    out = chunk_pass<DT, VEC, true, WITH_ARG>(row, a.V, c, a.chunks, n_iter, k, lane, first, lm, nullptr,
+                                              cap, reinterpret_cast<uint32_t*>(&dst->arg));
   else
     out = chunk_pass<DT, VEC, false, true>(row, a.V, c, a.chunks, n_iter, 0.f, lane, first, lm);
-  if (lane == 0) *dst = out;
+  if (lane == 0) {
+    if (capturing) {  // the arg field is the capture's
+      dst->s = out.s;
+      dst->m = out.m;
+    } else {
+      *dst = out;
+    }
+  }
   if (bar_dst) {
     // The bar_k-th largest of the lanes' maxima: a logit of the chunk with
     // at least bar_k logits of the chunk at or above it (-inf when fewer
@@ -608,8 +618,12 @@ __device__ __forceinline__ void load_parts4(const RowPart* p, int chunks, RowPar
   for (int u = 0; u < 4; ++u) q[u] = (u < chunks) ? p[u] : RowPart{0.0, ninf(), INT32_MAX};
 }
 
+// Merge of a row's chunk partials, the first four given. With cx >= 0, *cap
+// also receives the arg field of chunk cx (the logit bits that pass 1
+// recorded there) as the loop passes it.
 __device__ __forceinline__ RowStat merge_row_from(const RowPart (&q0)[4], const RowPart* p,
-                                                  int chunks, float k, bool sampling) {
+                                                  int chunks, float k, bool sampling, int cx = -1,
+                                                  uint32_t* cap = nullptr) {
   // Chunks in order, four loads in flight at a time: a running maximum (the
   // lowest index attaining it gives the argmax), the running sum moved onto
   // the new maximum's reference when it grows, and each group's terms moved
@@ -624,6 +638,11 @@ __device__ __forceinline__ RowStat merge_row_from(const RowPart (&q0)[4], const 
 #pragma unroll
     for (int u = 0; u < 4; ++u)
       q[u] = (c0 == 0) ? q0[u] : (c0 + u < chunks) ? p[c0 + u] : RowPart{0.0, ninf(), INT32_MAX};
+    if (cx >= 0) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (c0 + u == cx) *cap = (uint32_t)q[u].arg;
+    }
     float mg = M;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -680,10 +699,10 @@ struct AcceptArgs {
   int32_t lenience;  // kLen*; kLenNone is the lossless step
   float eps;         // lenience parameter in (0, 1)
   int32_t uniform_g;  // >= 0: uniform batch with this gamma (offsets arithmetic)
-  // non-null: the draft tokens' logits captured by pass 1, one per target /
-  // draft row; else the accept step reads them from the logit rows
-  const float* zx_t;
-  const float* zx_d;
+  // > 0: pass 1 recorded each draft token's logit in the partial of the
+  // chunk that holds it, with tiles of 1 << cap_shift elements; 0: the
+  // accept step reads the logits from the rows
+  int32_t cap_shift;
 };
 
 // f(p, eps): p / eps, p / eps^2 or p^eps, in float64 (f(p, 1) = p; the host
@@ -726,17 +745,11 @@ __device__ Select accept_sequence(const AcceptArgs& a, int64_t b, int lane, bool
   const int64_t d0 = uni ? b * a.uniform_g : a.doff[b];
   RowPart tq[4], dq[4];
   int x = 0;
-  const bool captured = a.zx_t != nullptr;
-  float zT = 0.f, zD = 0.f;
   if (uni) {
     if (lane <= g) load_parts4(a.tparts + (t0 + lane) * a.chunks, a.chunks, tq);
     if (lane < g) {
       x = a.tokens[d0 + lane];
       load_parts4(a.dparts + (d0 + lane) * a.chunks, a.chunks, dq);
-      if (captured) {
-        zT = a.zx_t[t0 + lane];
-        zD = a.zx_d[d0 + lane];
-      }
     }
   }
   if (status & kLayoutError) return finish(-1, -1, false);
@@ -744,23 +757,28 @@ __device__ Select accept_sequence(const AcceptArgs& a, int64_t b, int lane, bool
   const bool sampling = (T > 0.f) && (T < pinf());
   if (!greedy && !sampling) return finish(-1, -1, true);
   const float k = sampling ? temp_scale(T) : 0.f;
+  if (!uni) {  // a valid layout: the offsets address the packed arrays
+    if (lane <= g) load_parts4(a.tparts + (t0 + lane) * a.chunks, a.chunks, tq);
+    if (lane < g) {
+      x = a.tokens[d0 + lane];
+      if (sampling) load_parts4(a.dparts + (d0 + lane) * a.chunks, a.chunks, dq);
+    }
+  }
+  // the chunk whose partial holds x's logit, where pass 1 recorded it
+  const bool captured = a.cap_shift > 0;
+  int cx = -1;
+  if (captured && sampling && lane < g && x >= 0 && (int64_t)x < a.V) cx = (x >> a.cap_shift) % a.chunks;
+  uint32_t zTb = 0u, zDb = 0u;
   RowStat st_t{}, st_d{};
   bool bad = false;
   if (lane <= g) {
-    if (!uni) load_parts4(a.tparts + (t0 + lane) * a.chunks, a.chunks, tq);
-    st_t = merge_row_from(tq, a.tparts + (t0 + lane) * a.chunks, a.chunks, k, sampling);
+    st_t = merge_row_from(tq, a.tparts + (t0 + lane) * a.chunks, a.chunks, k, sampling, cx, &zTb);
     bad |= !st_t.valid;
   }
   if (lane < g) {
-    if (!uni) x = a.tokens[d0 + lane];
-    if (!uni && captured) {
-      zT = a.zx_t[t0 + lane];
-      zD = a.zx_d[d0 + lane];
-    }
     bad |= (x < 0) || ((int64_t)x >= a.V);
     if (sampling) {
-      if (!uni) load_parts4(a.dparts + (d0 + lane) * a.chunks, a.chunks, dq);
-      st_d = merge_row_from(dq, a.dparts + (d0 + lane) * a.chunks, a.chunks, k, true);
+      st_d = merge_row_from(dq, a.dparts + (d0 + lane) * a.chunks, a.chunks, k, true, cx, &zDb);
       bad |= !st_d.valid;
     }
   }
@@ -783,7 +801,11 @@ __device__ Select accept_sequence(const AcceptArgs& a, int64_t b, int lane, bool
   }
   bool rej = false;
   if (lane < g) {
-    if (!captured) {
+    float zT, zD;
+    if (captured) {
+      zT = __uint_as_float(zTb);
+      zD = __uint_as_float(zDb);
+    } else {
       zT = load_logit<DT>(a.target, (t0 + lane) * a.V + x);
       zD = load_logit<DT>(a.draft, (d0 + lane) * a.V + x);
     }
@@ -903,6 +925,64 @@ __device__ int64_t wave_scan_subs(const double* sub, int64_t nsub, double t, int
   return -1;
 }
 
+// The same scan over masses held in registers: lane l holds entries l,
+// l + 64, ... of at most kSubRegs passes (nsub <= 64 kSubRegs), requested all
+// at once, so the draw waits for them once instead of once per 64-entry pass
+// of each of its two scans. One sweep keeps every pass's prefixes; they are
+// the same additions in the same order as wave_scan_subs, so the total and
+// the located entry have the same bits.
+constexpr int kSubRegs = 4;
+
+__device__ __forceinline__ bool subs_fit_regs(int64_t nsub) { return nsub <= (int64_t)kWave * kSubRegs; }
+
+__device__ __forceinline__ void load_subs(const double* sub, int64_t nsub, int lane, double (&v)[kSubRegs]) {
+#pragma unroll
+  for (int q = 0; q < kSubRegs; ++q) {
+    const int64_t i = (int64_t)q * kWave + lane;
+    v[q] = (i < nsub) ? sub[i] : 0.0;
+  }
+}
+
+struct SubPrefix {
+  double incl[kSubRegs], excl[kSubRegs];
+  double total;
+};
+
+__device__ __forceinline__ void scan_subs_regs(const double (&v)[kSubRegs], int64_t nsub, int lane,
+                                               SubPrefix& P) {
+  double carry = 0.0;
+#pragma unroll
+  for (int q = 0; q < kSubRegs; ++q) {
+    P.incl[q] = 0.0;
+    P.excl[q] = 0.0;
+    if ((int64_t)q * kWave < nsub) {
+      P.incl[q] = wave_inclusive_scan(v[q], lane) + carry;
+      const double prev = __shfl_up(P.incl[q], 1, kWave);
+      P.excl[q] = (lane == 0) ? carry : prev;
+      carry = __shfl(P.incl[q], kWave - 1, kWave);
+    }
+  }
+  P.total = carry;
+}
+
+// The first entry whose inclusive prefix reaches t, and its exclusive prefix.
+__device__ __forceinline__ int64_t find_sub_regs(const SubPrefix& P, int64_t nsub, double t, int lane,
+                                                 double* base) {
+#pragma unroll
+  for (int q = 0; q < kSubRegs; ++q) {
+    const int64_t i = (int64_t)q * kWave + lane;
+    if ((int64_t)q * kWave < nsub) {
+      const uint64_t m = ballot(i < nsub && P.incl[q] >= t);
+      if (m) {
+        const int L = first_lane(m);
+        *base = __shfl(P.excl[q], L, kWave);
+        return (int64_t)q * kWave + L;
+      }
+    }
+  }
+  return -1;
+}
+
 // Sixteen consecutive logits [lo, lo + 16) of a row as fp32 (slots at or past
 // V read -inf). Vector path: lo is a multiple of 16 elements and rows are
 // 16-byte aligned, so a lane's run is 2 (bf16) or 4 (fp32) aligned 16-byte
@@ -997,20 +1077,30 @@ __device__ int wave_draw(const void* trow, const void* drow, const Weights& W, i
 
 // The final draw of one sequence by one wave: picks the sub-block that holds
 // u * total from the pass-2 masses `sub` (global or LDS), then walks that
-// sub-block.
+// sub-block. Where subs_fit_regs(nsub), `v` holds the masses as load_subs
+// leaves them (the caller requests them early) and the scans run on it.
 template <int DT, bool VEC>
-__device__ int draw_token(const DrawArgs& a, const double* sub, const Select& s, int lane) {
+__device__ int draw_token(const DrawArgs& a, const double* sub, const double (&v)[kSubRegs],
+                          const Select& s, int lane) {
   constexpr int64_t esz = (DT == kBF16) ? 2 : 4;
   const void* trow = static_cast<const char*>(a.target) + s.trow * a.V * esz;
   const void* drow = (s.mode == kModeResidual) ? static_cast<const char*>(a.draft) + s.drow * a.V * esz : nullptr;
+  const bool regs = subs_fit_regs(a.nsub);
+  SubPrefix P;
   double total = 0.0;
-  wave_scan_subs(sub, a.nsub, -1.0, lane, nullptr, &total);
+  if (regs) {
+    scan_subs_regs(v, a.nsub, lane, P);
+    total = P.total;
+  } else {
+    wave_scan_subs(sub, a.nsub, -1.0, lane, nullptr, &total);
+  }
   int token = -1;
   if (total > 0.0) {
     const double t = s.u * total;  // u in (0, 1]: t <= total
     const Weights W = make_weights(s, false);
     double base = 0.0;
-    const int64_t sb = wave_scan_subs(sub, a.nsub, t, lane, &base, nullptr);
+    const int64_t sb = regs ? find_sub_regs(P, a.nsub, t, lane, &base)
+                            : wave_scan_subs(sub, a.nsub, t, lane, &base, nullptr);
     int64_t last = -1;
     if (sb >= 0) {
       token = wave_draw<DT, VEC>(trow, drow, W, a.V, sb, sb + 1, base, t, lane, nullptr, &last);
@@ -1112,9 +1202,12 @@ __global__ __launch_bounds__(kBlock) void k4_draw(DrawArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t b = wave_uniform((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
   if (b >= a.B) return;
+  // the masses are requested with the selection, before its mode is known
+  double v[kSubRegs];
+  if (subs_fit_regs(a.nsub)) load_subs(a.sub + b * a.nsub, a.nsub, lane, v);
   const Select s = a.sel[b];
   if (s.mode == kModeNone) return;
-  const int token = draw_token<DT, VEC>(a, a.sub + b * a.nsub, s, lane);
+  const int token = draw_token<DT, VEC>(a, a.sub + b * a.nsub, v, s, lane);
   if (lane == 0) a.out_next[b] = token;
 }
 
@@ -1137,7 +1230,9 @@ __global__ __launch_bounds__(1024) void k3_accept_mass_draw(AcceptArgs acc, Draw
   if (active) chunk_masses<DT, VEC>(a, s, c, lane, sub_lds);
   __syncthreads();
   if (active && c == 0) {
-    const int token = draw_token<DT, VEC>(a, sub_lds, s, lane);
+    double v[kSubRegs];
+    if (subs_fit_regs(a.nsub)) load_subs(sub_lds, a.nsub, lane, v);
+    const int token = draw_token<DT, VEC>(a, sub_lds, v, s, lane);
     if (lane == 0) a.out_next[b] = token;
   }
 }

@@ -76,8 +76,8 @@ constexpr int64_t kTargetUnfusedItems = 3072;  // else unfused waves to aim for
 #ifndef SPECV_INLINE_PLAN
 #define SPECV_INLINE_PLAN 1  // ragged batches of at most 1024 sequences: no plan launch
 #endif
-#ifndef SPECV_CAPTURE_MIN_CHUNK_BYTES
-#define SPECV_CAPTURE_MIN_CHUNK_BYTES 49152  // 0: never capture
+#ifndef SPECV_CAPTURE
+#define SPECV_CAPTURE 1  // 0: the accept step reads the draft tokens' logits from the rows
 #endif
 #ifndef SPECV_FUSED_DRAW
 #define SPECV_FUSED_DRAW 1
@@ -95,7 +95,7 @@ struct Plan {
   int64_t nsub;
   bool fused_draw;  // k3_accept_mass_draw instead of k3_accept_mass + k4_draw
   size_t off_toff, off_doff, off_tk, off_dk, off_tparts, off_dparts, off_sel, off_sub;
-  size_t off_ttok, off_zxt, off_zxd;  // draft-token index per target row; captured logits
+  size_t off_ttok;  // draft-token index per target row (the plan launch's table)
   size_t bytes;
   // per-position diagnostics (after the verify layout)
   size_t off_dseq, off_bar, off_dgparts, off_topz, off_topi;
@@ -189,8 +189,6 @@ void make_plan(const specv_shape_t* s, Plan* p) {
                   (size_t)p->nsub * sizeof(double) <= kFusedDrawLds;
   p->off_sub = off; off = align_up(off + (size_t)p->B * p->nsub * sizeof(double));
   p->off_ttok = off; off = align_up(off + (size_t)p->tt * 4);
-  p->off_zxt = off; off = align_up(off + (size_t)p->tt * 4);
-  p->off_zxd = off; off = align_up(off + (size_t)p->td * 4);
   p->bytes = off;
 }
 
@@ -329,8 +327,6 @@ specv_status_t launch_row_stats(const Plan& p, bool vec, const void* target, con
   // tokens given: capture the draft tokens' logits for the accept step
   a.tokens = tokens;
   a.ttok = (tokens && !uniform && !inline_plan) ? at<int32_t>(ws, p.off_ttok) : nullptr;
-  a.zx_t = tokens ? at<float>(ws, p.off_zxt) : nullptr;
-  a.zx_d = tokens ? at<float>(ws, p.off_zxd) : nullptr;
   const int64_t waves = (p.tt + p.td) * p.chunks1;
   if (waves == 0) return SPECV_OK;
   const dim3 grid(blocks_for(waves)), block(kBlock);
@@ -355,18 +351,22 @@ specv_status_t launch_row_stats(const Plan& p, bool vec, const void* target, con
   return launched();
 }
 
-// Pass 1 of specv_verify captures the draft tokens' logits for the accept
-// step (one dependent memory round trip less there) when its chunks are long:
-// the capture delays each chunk-0 wave's second tile by about one round trip,
-// a small share of a chunk of SPECV_CAPTURE_MIN_CHUNK_BYTES or more (measured:
-// faster on the serving, ragged and large-vocabulary launches, slower on
-// the T5-XXL-like one with its 32 KiB chunks).
-bool capture_logits(const Plan& p) {
-  return p.td > 0 && SPECV_CAPTURE_MIN_CHUNK_BYTES > 0 &&
-         p.V * p.esz >= (int64_t)SPECV_CAPTURE_MIN_CHUNK_BYTES * p.chunks1;
+// Pass 1 of specv_verify records the draft tokens' logits for the accept
+// step (one dependent memory round trip less at its head): the wave whose
+// chunk holds a token takes its logit from the tile in its registers, so
+// nothing is loaded for it.
+bool capture_logits(const Plan& p) { return p.td > 0 && SPECV_CAPTURE; }
+
+// log2 of pass 1's tile length (elements) on the path `vec` picks
+int tile_shift(const Plan& p, bool vec) {
+  const int epi = (p.dt == kBF16) ? (vec ? Tile<kBF16, true>::EPI : Tile<kBF16, false>::EPI)
+                                   : (vec ? Tile<kF32, true>::EPI : Tile<kF32, false>::EPI);
+  int sh = 0;
+  while ((1 << sh) < epi) ++sh;
+  return sh;
 }
 
-AcceptArgs accept_args(const Plan& p, const Call& c) {
+AcceptArgs accept_args(const Plan& p, const Call& c, bool vec) {
   AcceptArgs a;
   a.target = c.target;
   a.draft = c.draft;
@@ -392,9 +392,8 @@ AcceptArgs accept_args(const Plan& p, const Call& c) {
   a.lenience = c.lenience;
   a.eps = c.eps;
   a.uniform_g = uniform_batch(p) ? (int32_t)p.max_gamma : -1;
-  const bool captured = !c.skip_pass1 && capture_logits(p);  // pass 1 of run() captured them
-  a.zx_t = captured ? at<float>(c.ws, p.off_zxt) : nullptr;
-  a.zx_d = captured ? at<float>(c.ws, p.off_zxd) : nullptr;
+  const bool captured = !c.skip_pass1 && capture_logits(p);  // pass 1 of run() recorded them
+  a.cap_shift = captured ? tile_shift(p, vec) : 0;
   return a;
 }
 
@@ -413,7 +412,7 @@ DrawArgs draw_args(const Plan& p, const Call& c) {
 }
 
 specv_status_t launch_accept_mass(const Plan& p, bool vec, const Call& c) {
-  const AcceptArgs acc = accept_args(p, c);
+  const AcceptArgs acc = accept_args(p, c, vec);
   const DrawArgs a = draw_args(p, c);
   if (p.fused_draw) {
     // one workgroup per sequence, one wave per pass-2 chunk; masses in LDS

@@ -478,6 +478,17 @@ def test_large_uniform_batch_parity(svx, B, V, g, dtype):
     parity_case(svx, "uniform B=%d V=%d gamma=%d %s" % (B, V, g, dtype), x)
 
 
+@pytest.mark.parametrize("B,V,g,dtype", [(8, 262144, 3, "f32"), (8, 262145, 3, "bf16"),
+                                         (512, 270000, 0, "bf16")])
+def test_draw_scan_paths(svx, B, V, g, dtype):
+    # the draw's scans over the sub-block masses (1024 elements each): held
+    # in registers up to 256 sub-blocks (V <= 262144), read from memory past
+    # that; with the draw in its own launch (few sequences) and in the mass
+    # launch (one workgroup per sequence)
+    x = uniform_case(B, V, g, seed=V + g, dtype=dtype)
+    parity_case(svx, "draw scan B=%d V=%d gamma=%d %s" % (B, V, g, dtype), x)
+
+
 def test_large_uniform_batch_errors(svx):
     x = uniform_case(1100, 8192, 3, seed=5, errors=True)
     n, nxt, st = run_gpu(svx, x)
@@ -503,11 +514,11 @@ def test_large_uniform_batch_errors(svx):
 
 @pytest.mark.parametrize("case", ["uniform", "ragged in pass 1", "ragged planned"])
 def test_long_rows_capture_and_data_errors(svx, case):
-    # rows long enough (48 KiB or more per pass-1 chunk) that pass 1 also
-    # captures each draft token's logit for the accept step: uniform, ragged
-    # with the plan inside pass 1 and ragged with the plan launch (its token
-    # table), with data errors on the uniform batch (tokens outside [0, V),
-    # NaN/+inf logits, invalid temperatures)
+    # long rows (48 KiB or more per pass-1 chunk, many tiles per chunk) with
+    # each draft token's logit recorded by the pass-1 wave whose chunk holds
+    # it: uniform, ragged with the plan inside pass 1 and ragged with the
+    # plan launch (its token table), with data errors on the uniform batch
+    # (tokens outside [0, V), NaN/+inf logits, invalid temperatures)
     if case == "uniform":
         x = uniform_case(16, 65536, 3, seed=21, errors=True)
     elif case == "ragged in pass 1":
