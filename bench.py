@@ -9,7 +9,10 @@ workloads the same way (the tiny CPU-checkable one with 10,000 rounds batched
 into one call, the T5-XXL-like one with 2,000 rounds batched, at T = 1 and
 greedy, batched serving and ragged lookahead), each with its step-level
 fraction of the HBM peak, its pass-1 kernel fraction, the stored counter
-traffic and its parity counts against the CPU oracle. Prints one JSON line.
+traffic and its parity counts against the CPU oracle. Every workload also
+gets the time of one launch of the library's read probe over its pass-1
+bytes: what a single streaming read of that size takes on this part. Prints
+one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                   [--lenience none|lin|sq|exp --epsilon E] [--no-per-config]
@@ -561,6 +564,32 @@ def bench_cascade(args, torch, svx, dev):
     print(json.dumps(result), flush=True)
 
 
+def read_probe_ms(torch, svx, dev, nbytes, reps=15):
+    """Time per launch of the library's read probe over `nbytes` (rounded up
+    to 64 KiB), back to back over rotating buffers (at least 1 GiB between
+    re-reads of one buffer, as the verify step's inputs rotate): what one
+    streaming launch of a workload's pass-1 bytes takes on this part, launch
+    and ramp costs included. The median over `reps` rounds."""
+    n = -(-nbytes // 65536) * 65536
+    nbuf = max(2, -(-(1 << 30) // n))
+    bufs = [torch.empty(n, dtype=torch.uint8, device=dev).fill_(1) for _ in range(nbuf)]
+    sinks = [torch.empty(n // 32768, dtype=torch.int32, device=dev) for _ in range(nbuf)]
+    for i in range(2 * nbuf):
+        svx.specv_read_bytes(bufs[i % nbuf], sinks[i % nbuf])
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ts = []
+    for _ in range(reps):
+        s.record()
+        for i in range(nbuf):
+            svx.specv_read_bytes(bufs[i], sinks[i])
+        e.record()
+        torch.cuda.synchronize()
+        ts.append(s.elapsed_time(e) / nbuf)
+    del bufs, sinks
+    torch.cuda.empty_cache()
+    return float(np.median(ts))
+
+
 def settle_clocks(torch, svx, dev, launches=600, nbytes=512 << 20):
     """About 50 ms of sustained streaming (the library's read probe over 512
     MiB, back to back) right before a workload's warm-up: generating a
@@ -686,6 +715,7 @@ def per_config(torch, svx, dev, args, sha):
         pass1 = x.pass1_bytes()
         step_frac = pass1 / (m["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBPS
         traffic = load_traffic(name, sha)
+        probe = read_probe_ms(torch, svx, dev, pass1)
         rec = {"workload": desc, "ms_per_step": m["ms_per_step"],
                "verified_target_rows_per_s": x.total_target_rows / (m["ms_per_step"] * 1e-3),
                "pass1_bytes": pass1, "step_frac_of_peak": step_frac,
@@ -696,6 +726,9 @@ def per_config(torch, svx, dev, args, sha):
                "traffic_bytes": traffic,
                "traffic_ratio": traffic / pass1 if traffic else None,
                "ms_per_step_uninstrumented": m["ms_per_step_plain"],
+               "read_probe_same_bytes_ms": probe,
+               "step_frac_of_read_probe": probe / m["ms_per_step_plain"],
+               "pass1_frac_of_read_probe": probe / m["k1_ms"],
                "stage_ms_instrumented": m["stage_ms"],
                "parity_vs_oracle": parity_counts(x, m["n"], m["next"])}
         if name in TARGET_WORKLOADS:
@@ -703,8 +736,9 @@ def per_config(torch, svx, dev, args, sha):
             rec["target_ms_per_step"] = pass1 / (STEP_TARGET * HBM_PEAK_GBPS * 1e9) * 1e3
             rec["meets_target"] = bool(step_frac >= STEP_TARGET)
         out[name] = rec
-        log("[bench]   %.1f us/step, %.1f%% of peak at step level, pass 1 %.1f%%"
-            % (m["ms_per_step"] * 1e3, 100 * step_frac, 100 * rec["pass1_kernel_frac"]))
+        log("[bench]   %.1f us/step, %.1f%% of peak at step level, pass 1 %.1f%%; a read of the "
+            "pass-1 bytes alone takes %.1f us" % (m["ms_per_step"] * 1e3, 100 * step_frac,
+                                                  100 * rec["pass1_kernel_frac"], probe * 1e3))
     return out
 
 
@@ -783,6 +817,7 @@ def main():
     pass1 = x.pass1_bytes()
     achieved = pass1 / (m["k1_ms"] * 1e-3) / 1e9
     sha = kernel_sha()
+    probe = read_probe_ms(torch, svx, dev, pass1)
     n_host, next_host = m["n"], m["next"]
     emitted = int(np.sum(n_host[n_host >= 0] + 1))
     ms_step = m["ms_per_step"]
@@ -813,6 +848,9 @@ def main():
         "step_gbps": pass1 / (ms_step * 1e-3) / 1e9,
         "step_frac_of_peak": pass1 / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "ms_per_step_uninstrumented": m["ms_per_step_plain"],
+        "read_probe_same_bytes_ms": probe,
+        "step_frac_of_read_probe": probe / m["ms_per_step_plain"],
+        "pass1_frac_of_read_probe": probe / m["k1_ms"],
         "stage_ms_instrumented": m["stage_ms"],
         "emitted_tokens_per_s": emitted / (ms_step * 1e-3),
         "mean_tokens_per_sequence": emitted / x.batch,
