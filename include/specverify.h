@@ -37,7 +37,10 @@
  *   temperature    [B] float32: > 0 sampling, == 0 greedy
  *   out_n_accepted [B] int32, out_next_token [B] int32
  * Both logit tensors share one dtype (bf16 or fp32). -inf logits are legal
- * (masked tokens).
+ * (masked tokens), and so is any finite logit: masks with the most negative
+ * finite value work as -inf would. A sampling T_b must keep log2(e)/T_b, the
+ * fp32 scale of the logits, finite: T_b above about 4.2e-39 (exactly: the
+ * float64 quotient log2(e)/T_b below 2^128 - 2^103).
  *
  * Asynchrony: every entry point that takes a stream only enqueues work on it
  * and returns; results are valid after the stream is synchronised. Nothing
@@ -53,7 +56,8 @@
  *   - data errors found on the device give that sequence (-1, -1) and set a
  *     bit in the status word at byte offset 0 of the workspace: a gamma_b
  *     outside [0, max_gamma] or gammas that disagree with the row totals
- *     (every sequence gets (-1, -1)); T_b NaN, negative or +inf; a draft token
+ *     (every sequence gets (-1, -1)); T_b NaN, negative, +inf or too small for
+ *     the fp32 scale log2(e)/T_b; a draft token
  *     outside [0, V); a needed row with NaN or +inf or no finite logit
  *     (needed rows: all target rows; draft rows only of sampling sequences).
  */
@@ -197,7 +201,7 @@ specv_status_t specv_verify_lenient(const specv_shape_t* shape, const void* targ
  * zero-temperature limits of greedy verification: p and q one-hot at their
  * argmax, so alpha is 1 or 0, the entropy 0 and the top-1 probability 1.
  * A position whose target or draft row holds NaN or +inf or no finite logit,
- * or whose T_b is NaN, negative or +inf, gets NaN alpha and entropy, index
+ * or whose T_b is invalid (as for specv_verify), gets NaN alpha and entropy, index
  * -1 and probability NaN; after a layout error (as in specv_verify) every
  * position reads so, and the status bit is set. 0 <= top_k <= min(V,
  * SPECV_MAX_TOP_K); with top_k == 0 the top-k pointers may be NULL.

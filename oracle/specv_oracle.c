@@ -47,8 +47,9 @@
  *     residual mass is exactly 0 the weights fall back to p_n;
  *   - greedy argmax ties resolve to the lowest index, on the raw logits;
  *   - a sequence whose needed rows hold NaN or +inf, or hold no finite logit,
- *     or whose tokens fall outside [0, V), or whose T is NaN, negative or
- *     +inf, yields (n, token) = (-1, -1); a gamma outside [0, max_gamma], or
+ *     or whose tokens fall outside [0, V), or whose T is NaN, negative,
+ *     +inf or below the fp32 range of log2(e)/T (temperature_invalid),
+ *     yields (n, token) = (-1, -1); a gamma outside [0, max_gamma], or
  *     row totals that disagree with the gammas, make every sequence (-1, -1).
  *
  * Parity pins: see the test suite (Philox against rocRAND's implementation,
@@ -141,6 +142,17 @@ static void load_row(const void* base, int dtype, int64_t V, int64_t row, double
     const float* p = (const float*)base + row * V;
     for (int64_t v = 0; v < V; ++v) z[v] = (double)p[v];
   }
+}
+
+/* A temperature outside the step's domain: NaN, negative or +inf, or a
+ * positive T so small that the logit scale log2(e)/T is not a finite fp32
+ * number (T below about 4.2e-39). The second part is a stated limit of the
+ * library's fp32 arithmetic, not of the method; the test is exact: the
+ * quotient in float64 rounds to +inf in fp32 from 2^128 - 2^103 on. */
+static int temperature_invalid(double T) {
+  if (isnan(T) || T < 0.0 || isinf(T)) return 1;
+  if (T == 0.0) return 0;
+  return 1.4426950408889634074 / T >= 0x1.ffffffp127;
 }
 
 /* A row is usable when it has no NaN, no +inf and at least one finite value
@@ -446,7 +458,7 @@ static void verify_sequence(const job_t* J, int64_t b, scratch_t* S) {
   const int64_t g = J->gamma[b];
   const double T = (double)J->temperature[b];
   const int64_t t0 = J->toff[b], d0 = J->doff[b];
-  if (isnan(T) || T < 0.0 || isinf(T)) {
+  if (temperature_invalid(T)) {
     set_failed(J, b);
     return;
   }
@@ -687,8 +699,7 @@ int oracle_position_diagnostics(int64_t batch, int64_t vocab, int dtype, int64_t
       const int64_t j = d0 + i;
       load_row(target, dtype, V, t0 + i, zp);
       load_row(draft, dtype, V, d0 + i, zq);
-      const int ok = row_is_valid(zp, V) && row_is_valid(zq, V) && !isnan(T) && T >= 0.0 &&
-                     !isinf(T);
+      const int ok = row_is_valid(zp, V) && row_is_valid(zq, V) && !temperature_invalid(T);
       if (!ok) {
         out_alpha[j] = NAN;
         out_entropy[j] = NAN;
@@ -797,7 +808,7 @@ int oracle_decode_bigram(int64_t batch, int64_t vocab, int64_t gamma, int64_t ro
                row_bytes);
         load_row(dtab, dtype, V, prev, z);
         int64_t x = 0;
-        if (!row_is_valid(z, V) || isnan(T) || T < 0.0 || isinf(T)) {
+        if (!row_is_valid(z, V) || temperature_invalid(T)) {
           x = 0; /* verification reports the sequence */
         } else if (T == 0.0) {
           x = row_argmax(z, V);
@@ -1065,7 +1076,7 @@ int oracle_cascade_bigram(int64_t batch, int64_t vocab, int64_t k1, int64_t k2, 
           if (i == g) break;
           load_row(m2tab, dtype, V, prev, z);
           int64_t x = 0;
-          if (!row_is_valid(z, V) || isnan(T) || T < 0.0 || isinf(T)) {
+          if (!row_is_valid(z, V) || temperature_invalid(T)) {
             x = 0;
           } else if (T == 0.0) {
             x = row_argmax(z, V);
@@ -1136,7 +1147,7 @@ int oracle_cascade_bigram(int64_t batch, int64_t vocab, int64_t k1, int64_t k2, 
         continue;
       }
       const double T = (double)temperature[b];
-      if (isnan(T) || T < 0.0 || isinf(T)) {
+      if (temperature_invalid(T)) {
         n_out[b] = -1;
         next_out[b] = -1;
         continue;

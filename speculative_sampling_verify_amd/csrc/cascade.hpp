@@ -213,7 +213,7 @@ __global__ __launch_bounds__(kBlock) void k_cas_outer_rows(CascadeArgs a) {
   if (lane == 0) a.otok[b * a.k1 + i] = a.dtok[b * a.dcap + i];
   float* out = a.odpack + (b * a.k1 + i) * V;
   const float T = a.temperature[b];
-  const bool sampling = T > 0.f && T < pinf();
+  const bool sampling = sampling_temperature(T);
   if (!sampling || a.fail[b]) {
     const float zero[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int64_t v0 = (int64_t)lane * 8; v0 < V; v0 += kStep) cas_store8<VEC>(out, V, v0, zero);
@@ -231,33 +231,32 @@ __global__ __launch_bounds__(kBlock) void k_cas_outer_rows(CascadeArgs a) {
   }
   const void* r2 = static_cast<const char*>(a.m2tab) + (int64_t)pv * V * esz;
   const float k = temp_scale(T);
-  // pass 1: per-lane online max and sum of 2^(z k - rk) for both rows
-  float m1 = ninf(), m2 = ninf(), rk1 = 0.f, rk2 = 0.f;
+  // pass 1: per-lane online max and sum of 2^((z - max) k) for both rows
+  float m1 = ninf(), m2 = ninf();
   double s1 = 0.0, s2 = 0.0;
-  auto online = [&](const float (&z)[8], float& m, float& rk, double& s) {
+  auto online = [&](const float (&z)[8], float& m, double& s) {
     const float g = tile_max(z);
     if (!(g > ninf())) return;
     const float mn = fmaxf(m, g);
-    const float rkn = ref_point(mn, k);
-    const float sc = (m == ninf()) ? 0.f : exp2_hw(rk - rkn);
+    const float sc = rescale32(m, mn, k);
+    const float ref = ref_logit(mn);
     float e[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) e[j] = exp2_hw(__builtin_fmaf(z[j], k, -rkn));
+    for (int j = 0; j < 8; ++j) e[j] = exp2_hw(term_exp(z[j], ref, k));
     s = __builtin_fma(s, (double)sc, (double)tree_sum(e));
     m = mn;
-    rk = rkn;
   };
   for (int64_t v0 = (int64_t)lane * 8; v0 < V; v0 += kStep) {
     float z1[8], z2[8];
     cas_load8<DT, VEC>(r1, V, v0, z1);
     cas_load8<DT, VEC>(r2, V, v0, z2);
-    online(z1, m1, rk1, s1);
-    online(z2, m2, rk2, s2);
+    online(z1, m1, s1);
+    online(z2, m2, s2);
   }
   const float M1 = wave_max(m1), M2 = wave_max(m2);
-  const float R1 = ref_point(M1, k), R2 = ref_point(M2, k);
-  const double S1 = wave_sum((m1 == ninf()) ? 0.0 : s1 * exp2((double)(m1 * k) - (double)R1));
-  const double S2 = wave_sum((m2 == ninf()) ? 0.0 : s2 * exp2((double)(m2 * k) - (double)R2));
+  const float R1 = ref_logit(M1), R2 = ref_logit(M2);
+  const double S1 = wave_sum((m1 == ninf()) ? 0.0 : s1 * exp2(((double)m1 - (double)R1) * (double)k));
+  const double S2 = wave_sum((m2 == ninf()) ? 0.0 : s2 * exp2(((double)m2 - (double)R2) * (double)k));
   // Passes 2 and 3 work per element in fp32 (p1 and q2 come from fp32
   // terms already) and add in fp64 per lane: the rows are fp32, and the
   // error stays near 1e-7 relative.
@@ -265,8 +264,8 @@ __global__ __launch_bounds__(kBlock) void k_cas_outer_rows(CascadeArgs a) {
   const float inv = (a.lenience == kLenLin) ? (float)(1.0 / (double)a.eps)
                     : (a.lenience == kLenSq) ? (float)(1.0 / ((double)a.eps * (double)a.eps)) : 1.f;
   auto probs = [&](float z1, float z2, float& p1, float& q2) {
-    p1 = exp2_hw(__builtin_fmaf(z1, k, -R1)) * i1;
-    q2 = exp2_hw(__builtin_fmaf(z2, k, -R2)) * i2;
+    p1 = exp2_hw(term_exp(z1, R1, k)) * i1;
+    q2 = exp2_hw(term_exp(z2, R2, k)) * i2;
   };
   // pass 2: beta = sum min(q2, f(p1)) and the residual mass sum max(0, p1 - q2)
   double beta = 0.0, rmass = 0.0;
@@ -309,7 +308,7 @@ __global__ __launch_bounds__(kBlock) void k_cas_outer_rows(CascadeArgs a) {
 // both drafter rows in registers, so each row is read once and each weight
 // formed once; the passes exchange per-wave results through LDS:
 //   1. the rows' maxima M1, M2;
-//   2. the weights 2^(fl32(z k - rk(M))) in place, and S1, S2 (per-lane fp32
+//   2. the weights 2^(fl32(fl32(z - M) k)) in place, and S1, S2 (per-lane fp32
 //      tree sums of eight, fp64 lane and wave sums, the waves added in order);
 //   3. beta and the residual mass from p1 = t1 fl32(1/S1), q2 = t2 fl32(1/S2);
 // then each wave writes its steps of fl32(T ln Q). Every early return depends
@@ -349,7 +348,7 @@ __global__ __launch_bounds__(kCasWaves * kWave) void k_cas_outer_rows_wg(Cascade
   if (threadIdx.x == 0) a.otok[b * a.k1 + i] = a.dtok[b * a.dcap + i];
   float* out = a.odpack + (b * a.k1 + i) * V;
   const float T = a.temperature[b];
-  const bool sampling = T > 0.f && T < pinf();
+  const bool sampling = sampling_temperature(T);
   if (!sampling || a.fail[b]) {
     const float zero[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int64_t st = w; st < n_steps; st += kCasWaves)
@@ -399,16 +398,16 @@ __global__ __launch_bounds__(kCasWaves * kWave) void k_cas_outer_rows_wg(Cascade
     M1 = fmaxf(M1, sh.m1[q]);
     M2 = fmaxf(M2, sh.m2[q]);
   }
-  const float R1 = ref_point(M1, k), R2 = ref_point(M2, k);
-  // The weights 2^(fl32(z k - R)) of step q, formed the same way in each
+  const float R1 = ref_logit(M1), R2 = ref_logit(M2);
+  // The weights 2^(fl32(fl32(z - R) k)) of step q, formed the same way in each
   // pass (so with the same values); one step's weights are live at a time.
   auto weights = [&](int q, float (&e1)[8], float (&e2)[8]) {
     cas_opaque(z1[q]);
     cas_opaque(z2[q]);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      e1[j] = exp2_hw(__builtin_fmaf(z1[q][j], k, -R1));
-      e2[j] = exp2_hw(__builtin_fmaf(z2[q][j], k, -R2));
+      e1[j] = exp2_hw(term_exp(z1[q][j], R1, k));
+      e2[j] = exp2_hw(term_exp(z2[q][j], R2, k));
     }
   };
   // 2. the row sums

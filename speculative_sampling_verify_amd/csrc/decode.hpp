@@ -101,7 +101,7 @@ __device__ __forceinline__ void dec_load(const void* row, int64_t V, int64_t e0,
 constexpr int kDecBatch = 8;
 
 // One draw from softmax(row * k) (k = log2(e)/T), or the argmax for k == 0.
-// Pass 1: per-lane online (max, sum of 2^(z k - rk)) over the row, merged
+// Pass 1: per-lane online (max, sum of 2^((z - max) k)) over the row, merged
 // across the wave (fp64 sum). Pass 2 walks the tiles in order: a tile's
 // per-lane fp32 tree sums are scanned in fp64 across the wave; the first
 // tile whose running total reaches u * S holds the token, the first lane
@@ -121,7 +121,7 @@ __device__ int dec_sample_row(const void* row, int64_t V, float k, double u, int
       }
     }
   };
-  float m = ninf(), rk = 0.f;
+  float m = ninf();
   double s = 0.0;
   int64_t arg = INT32_MAX;
   for (int64_t t0 = 0; t0 < n_tiles; t0 += kDecBatch) {
@@ -138,14 +138,13 @@ __device__ int dec_sample_row(const void* row, int64_t V, float k, double u, int
           }
       } else if (g > ninf()) {
         const float mn = fmaxf(m, g);
-        const float rkn = ref_point(mn, k);
-        const float sc = (m == ninf()) ? 0.f : exp2_hw(rk - rkn);
+        const float sc = rescale32(m, mn, k);
+        const float ref = ref_logit(mn);
         float e[kDecPL];
 #pragma unroll
-        for (int j = 0; j < kDecPL; ++j) e[j] = exp2_hw(__builtin_fmaf(z[b][j], k, -rkn));
+        for (int j = 0; j < kDecPL; ++j) e[j] = exp2_hw(term_exp(z[b][j], ref, k));
         s = __builtin_fma(s, (double)sc, (double)tree_sum(e));
         m = mn;
-        rk = rkn;
       }
     }
   }
@@ -154,8 +153,8 @@ __device__ int dec_sample_row(const void* row, int64_t V, float k, double u, int
     const int best = wave_min((m == M && arg < INT32_MAX) ? (int)arg : INT32_MAX);
     return best == INT32_MAX ? 0 : best;
   }
-  const float rkM = ref_point(M, k);
-  const double S = wave_sum((m == ninf()) ? 0.0 : s * exp2((double)(m * k) - (double)rkM));
+  const float refM = ref_logit(M);
+  const double S = wave_sum((m == ninf()) ? 0.0 : s * exp2(((double)m - (double)refM) * (double)k));
   const double target = u * S;
   double C = 0.0;
   for (int64_t t0 = 0; t0 < n_tiles; t0 += kDecBatch) {
@@ -166,7 +165,7 @@ __device__ int dec_sample_row(const void* row, int64_t V, float k, double u, int
       float w[kDecPL], tw[kDecPL];
 #pragma unroll
       for (int j = 0; j < kDecPL; ++j) {
-        w[j] = exp2_hw(__builtin_fmaf(z[b][j], k, -rkM));
+        w[j] = exp2_hw(term_exp(z[b][j], refM, k));
         tw[j] = w[j];
       }
       const float ls = tree_sum(tw);
@@ -207,7 +206,7 @@ __global__ __launch_bounds__(kBlock) void k_dec_draft(DecodeArgs a) {
   const int64_t b = wave_uniform((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
   if (b >= a.B) return;
   const float T = a.temperature[b];
-  const bool sampling = T > 0.f && T < pinf();
+  const bool sampling = sampling_temperature(T);
   const bool greedy = T == 0.f;
   const float k = sampling ? temp_scale(T) : 0.f;
   const uint64_t prow = a.row_base + (uint64_t)b;
@@ -239,7 +238,7 @@ __global__ __launch_bounds__(kBlock) void k_dec_draft(DecodeArgs a) {
 // so a drafted token costs one row load and three LDS exchanges:
 //   1. each wave's maximum (and its lowest index attaining it); greedy
 //      sequences take the row's argmax from these and stop here;
-//   2. weights 2^(fl32(z k - rk(M))) against the row maximum M, per-lane fp32
+//   2. weights 2^(fl32(fl32(z - M) k)) against the row maximum M, per-lane fp32
 //      tree sums per tile, a wave inclusive scan per tile (fp64) whose last
 //      lane is the tile's mass, and the wave's segment mass (its tiles'
 //      masses added in order); S = the segment masses added in wave order;
@@ -307,7 +306,7 @@ __device__ int wg_sample_row(const void* row, int64_t V, float k, double u, int 
     return best == INT32_MAX ? 0 : best;
   }
   // 2. weights, tile scans and segment masses
-  const float rkM = ref_point(M, k);
+  const float refM = ref_logit(M);
   float ls[kDecTPW];
   double incl[kDecTPW];
   double seg = 0.0;
@@ -316,7 +315,7 @@ __device__ int wg_sample_row(const void* row, int64_t V, float k, double u, int 
     float tw[kDecPL];
 #pragma unroll
     for (int j = 0; j < kDecPL; ++j) {
-      z[t][j] = exp2_hw(__builtin_fmaf(z[t][j], k, -rkM));  // the weight, in place
+      z[t][j] = exp2_hw(term_exp(z[t][j], refM, k));  // the weight, in place
       tw[j] = z[t][j];
     }
     ls[t] = tree_sum(tw);
@@ -406,7 +405,7 @@ __global__ __launch_bounds__(kDecWaves * kWave) void k_dec_draft_wg(DecodeArgs a
   const int w = (int)(threadIdx.x >> 6);
   const int64_t b = blockIdx.x;
   const float T = a.temperature[b];
-  const bool sampling = T > 0.f && T < pinf();
+  const bool sampling = sampling_temperature(T);
   const bool greedy = T == 0.f;
   const float k = sampling ? temp_scale(T) : 0.f;
   const uint64_t prow = a.row_base + (uint64_t)b;

@@ -36,27 +36,39 @@ __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2
 
 // log2(e) / T in fp32: exp((z - m) / T) = 2^((z - m) * k). Every kernel that
 // evaluates a softmax at temperature T derives k through this one function.
+// It overflows to +inf for T below about 4.2e-39, which the callers treat as
+// an invalid temperature.
 __device__ __forceinline__ float temp_scale(float T) {
   return (float)(1.4426950408889634074 / (double)T);
 }
 
-// Reference point of a row or chunk with maximum m: rk = fl32(m * k), or 0
-// for an all-masked (-inf) span. Terms are 2^(fl32(z k - rk)), so the same
-// rk appears in a row's sum and in every probability taken from it, and its
-// rounding cancels between them.
-__device__ __forceinline__ float ref_point(float m, float k) { return (m == ninf()) ? 0.f : m * k; }
-
-// Factor that moves a sum taken relative to maximum m onto the reference of
-// maximum mn >= m; 0 for an all-masked sum (keeps NaN payloads: NaN * 0).
-__device__ __forceinline__ double rescale64(float m, float mn, float k) {
-  if (m == ninf()) return 0.0;
-  return exp2((double)(m * k) - (double)ref_point(mn, k));
+// A sampling temperature: T > 0, finite, and log2(e)/T finite in fp32.
+__device__ __forceinline__ bool sampling_temperature(float T) {
+  return T > 0.f && T < pinf() && temp_scale(T) < pinf();
 }
 
-// The same factor from v_exp_f32 (within 1 ulp; exactly 1 when m == mn).
+// Per-sequence scale: k = log2(e)/T for a sampling temperature, 0 for a
+// greedy sequence (T = 0), -1 for an invalid temperature.
+__device__ __forceinline__ float seq_scale(float T) {
+  return sampling_temperature(T) ? temp_scale(T) : (T == 0.f ? 0.f : -1.f);
+}
+
+// Reference logit of a row or span with maximum m: m itself, or 0 for an
+// all-masked (-inf) span. Terms are 2^(fl32(fl32(z - ref) k)) (term_exp):
+// the maximum's term is exactly 1 and none overflows, at any finite logits
+// and any finite k (a difference that overflows to -inf gives 0). A
+// reference m * k instead would carry that product's rounding error into
+// every term, which overflows the exponent range once |m k| passes 2^31
+// (logits masked with the most negative finite value, tiny T).
+__device__ __forceinline__ float ref_logit(float m) { return (m == ninf()) ? 0.f : m; }
+__device__ __forceinline__ float term_exp(float z, float ref, float k) { return (z - ref) * k; }
+
+// Factor that moves a sum taken relative to maximum m onto the reference of
+// maximum mn >= m, from v_exp_f32 (within 1 ulp; exactly 1 when m == mn); 0
+// for an all-masked sum (keeps NaN payloads: NaN * 0).
 __device__ __forceinline__ float rescale32(float m, float mn, float k) {
   if (m == ninf()) return 0.f;
-  return exp2_hw(m * k - ref_point(mn, k));
+  return exp2_hw(term_exp(m, ref_logit(mn), k));
 }
 
 template <int DT>

@@ -11,7 +11,8 @@
 // interleaved tiles as pass 1 -- and accumulates per element, in fp32 terms
 // and fp64 lane sums:
 //   min(t^T_v / S^T, t^D_v / S^D),   t^D_v,   t^D_v * e^D_v,
-// with t = 2^e, e = fl32(z k - rk) exactly as in pass 1. Since
+// with t = 2^e, e = fl32(fl32(z - M) k) exactly as in pass 1 (M the row's
+// maximum). Since
 // q_v = t^D_v / S and ln q_v = e^D_v ln 2 - ln S,
 //   entropy = ln S - ln 2 * (sum_v t^D_v e^D_v) / S,   S = sum_v t^D_v.
 // Top-k: q is monotone in the logit, so the list is selected on raw logits,
@@ -23,7 +24,7 @@
 // taken in pass 1. A tile's group of 8 slots is scanned only when some
 // lane's maximum over the group reaches the bar.
 // k6_diag_merge (one wave per position) sums the chunks' partials and merges
-// their lists; probabilities of the selected tokens are 2^(z k - rk) / S in
+// their lists; probabilities of the selected tokens are 2^((z - M) k) / S in
 // float64, as the accept step computes p(x) and q(x).
 #pragma once
 
@@ -159,7 +160,7 @@ __device__ __forceinline__ float raw_elem(const typename Tile<DT, VEC>::Raw& r) 
 template <int DT, bool VEC, int G>
 __device__ __forceinline__ void diag_terms(const typename Tile<DT, VEC>::Raw& rd,
                                            const typename Tile<DT, VEC>::Raw& rt, float k,
-                                           float rkT, float rkD, float r, float iD, float& sa,
+                                           float refT, float refD, float r, float iD, float& sa,
                                            float& ss, float& sA, float& mx) {
   float pa[8], ps[8], pA[8];
 #pragma unroll
@@ -176,9 +177,9 @@ __device__ __forceinline__ void diag_terms(const typename Tile<DT, VEC>::Raw& rd
       SPECV_SLOT(4) SPECV_SLOT(5) SPECV_SLOT(6) SPECV_SLOT(7)
 #undef SPECV_SLOT
     }
-    const float eD = __builtin_fmaf(zD, k, -rkD);
+    const float eD = term_exp(zD, refD, k);
     const float tD = exp2_hw(eD);
-    const float tT = exp2_hw(__builtin_fmaf(zT, k, -rkT));
+    const float tT = exp2_hw(term_exp(zT, refT, k));
     // min(p, q) = min(tT r, tD) / S^D with r = S^D / S^T: one product per
     // element, the 1 / S^D once per group
     pa[u] = fminf(tT * r, tD);
@@ -306,11 +307,11 @@ __device__ __forceinline__ bool diag_chunk(const DiagArgs& a, int64_t item, int 
     for (int g = 0; g < NG; ++g) gm[g] = ninf();
     if (sampling) {
       float ga[NG], gs[NG], gA[NG];
-      diag_terms<DT, VEC, 0>(rd, rt, k, st_t.rk, st_d.rk, rTD, iD, ga[0], gs[0], gA[0], gm[0]);
-      diag_terms<DT, VEC, 1>(rd, rt, k, st_t.rk, st_d.rk, rTD, iD, ga[1], gs[1], gA[1], gm[1]);
+      diag_terms<DT, VEC, 0>(rd, rt, k, st_t.ref, st_d.ref, rTD, iD, ga[0], gs[0], gA[0], gm[0]);
+      diag_terms<DT, VEC, 1>(rd, rt, k, st_t.ref, st_d.ref, rTD, iD, ga[1], gs[1], gA[1], gm[1]);
       if constexpr (NG == 4) {
-        diag_terms<DT, VEC, 2>(rd, rt, k, st_t.rk, st_d.rk, rTD, iD, ga[2], gs[2], gA[2], gm[2]);
-        diag_terms<DT, VEC, 3>(rd, rt, k, st_t.rk, st_d.rk, rTD, iD, ga[3], gs[3], gA[3], gm[3]);
+        diag_terms<DT, VEC, 2>(rd, rt, k, st_t.ref, st_d.ref, rTD, iD, ga[2], gs[2], gA[2], gm[2]);
+        diag_terms<DT, VEC, 3>(rd, rt, k, st_t.ref, st_d.ref, rTD, iD, ga[3], gs[3], gA[3], gm[3]);
       }
       sa += (double)tree_sum(ga);
       ss += (double)tree_sum(gs);
@@ -454,7 +455,7 @@ __global__ __launch_bounds__(kBlock) void k5_diag_pass_merge(DiagArgs a) {
     if (s < ns && mine[s] != 0ull && rank[s] < K) {
       const float z = key_value(mine[s]);
       double q;
-      if (sampling) q = exp2((double)z * (double)o.k - (double)o.st_d.rk) / o.st_d.s;
+      if (sampling) q = exp2(((double)z - (double)o.st_d.ref) * (double)o.k) / o.st_d.s;
       else q = (rank[s] == 0) ? 1.0 : 0.0;
       a.out_index[j * K + rank[s]] = key_index(mine[s]);
       a.out_prob[j * K + rank[s]] = q;
@@ -552,7 +553,7 @@ __global__ __launch_bounds__(kBlock) void k6_diag_merge(DiagArgs a) {
     if (s < ns && mine[s] != 0ull && rank[s] < K) {
       const float z = key_value(mine[s]);
       double q;
-      if (sampling) q = exp2((double)z * (double)k - (double)st_d.rk) / st_d.s;
+      if (sampling) q = exp2(((double)z - (double)st_d.ref) * (double)k) / st_d.s;
       else q = (rank[s] == 0) ? 1.0 : 0.0;
       a.out_index[j * K + rank[s]] = key_index(mine[s]);
       a.out_prob[j * K + rank[s]] = q;

@@ -8,7 +8,7 @@
 //                  gammas and initialises the status word instead.
 //   k1_row_stats   pass 1, the HBM-bound hot loop: every needed logit row is
 //                  streamed once with 16-byte non-temporal loads; each wave
-//                  owns one (row, chunk) and keeps (max, sum of 2^(z k - rk),
+//                  owns one (row, chunk) and keeps (max, sum of 2^((z - max) k),
 //                  argmax) in registers, reduced across the wave by shuffles.
 //   k3_accept_mass the accept step (one wave per sequence, one lane per draft
 //                  position: merge the chunk statistics, gather p_i(x_i) and
@@ -29,7 +29,7 @@
 namespace specv {
 
 // Statistics of one (row, chunk): s = sum over the chunk's elements of
-// 2^(fl32(z k - ref_point(m, k))) (sampling rows) or 0/NaN (greedy rows, NaN
+// 2^(fl32(fl32(z - ref_logit(m)) k)) (sampling rows) or 0/NaN (greedy rows, NaN
 // flags a NaN/+inf logit); m = max; arg = lowest index attaining m. The
 // verify step needs no argmax of a sampling row: there, arg of the chunk
 // that holds the row's draft token carries that logit's fp32 bits instead,
@@ -51,7 +51,7 @@ struct Select {
   int64_t trow;  // target row (packed index) of the draw
   int64_t drow;  // draft row for the residual, else -1
   float k;       // log2(e) / T
-  float rkT, rkD;
+  float refT, refD;  // reference logits (row maxima) of the selected rows
   int32_t pad;
   double sT, sD;
   double u;
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(1024) void k0_plan(PlanArgs a) {
     sd += gg;
     if (b - lo < kPlanKeep) {
       keep_g[b - lo] = g;
-      keep_k[b - lo] = (T > 0.f && T < pinf()) ? temp_scale(T) : (T == 0.f ? 0.f : -1.f);
+      keep_k[b - lo] = seq_scale(T);
     }
   }
   // workgroup exclusive scan of (st, sd): waves, then the 16 wave totals
@@ -135,7 +135,7 @@ __global__ __launch_bounds__(1024) void k0_plan(PlanArgs a) {
     } else {
       g = a.gamma[b];
       const float T = a.temperature[b];
-      kk = (T > 0.f && T < pinf()) ? temp_scale(T) : (T == 0.f ? 0.f : -1.f);
+      kk = seq_scale(T);
     }
     const int64_t gg = g < 0 ? 0 : g;
     a.toff[b] = t;
@@ -154,12 +154,6 @@ __global__ __launch_bounds__(1024) void k0_plan(PlanArgs a) {
     a.toff[a.B] = tot_t;
     a.doff[a.B] = tot_d;
   }
-}
-
-// Per-sequence temperature scale as k0_plan writes it per row: log2(e)/T for
-// a sampling sequence, 0 for a greedy one, -1 for an invalid temperature.
-__device__ __forceinline__ float seq_scale(float T) {
-  return (T > 0.f && T < pinf()) ? temp_scale(T) : (T == 0.f ? 0.f : -1.f);
 }
 
 struct RowStatsArgs {
@@ -386,7 +380,7 @@ __device__ __forceinline__ RowPart chunk_pass(const void* row, int64_t V, int c,
   using Raw = typename TL::Raw;
   constexpr int NE = TL::NE;
   constexpr bool ARG = WITH_ARG || !SAMPLING;
-  float m = ninf(), rk = 0.f;
+  float m = ninf();
   double s = 0.0;
   bool bad = false;
   int best = -1;
@@ -408,15 +402,14 @@ __device__ __forceinline__ RowPart chunk_pass(const void* row, int64_t V, int c,
     if constexpr (ARG) best = (g > m) ? it : best;
     if constexpr (SAMPLING) {
       const float mn = fmaxf(m, g);
-      const float rkn = ref_point(mn, k);
-      const float sc = (m == ninf()) ? 0.f : exp2_hw(rk - rkn);
+      const float sc = rescale32(m, mn, k);
+      const float ref = ref_logit(mn);
       float e[NE];
 #pragma unroll
-      for (int j = 0; j < NE; ++j) e[j] = exp2_hw(__builtin_fmaf(z[j], k, -rkn));
+      for (int j = 0; j < NE; ++j) e[j] = exp2_hw(term_exp(z[j], ref, k));
       const float acc = tree_sum(e);
       s = __builtin_fma(s, (double)sc, (double)acc);
       m = mn;
-      rk = rkn;
     } else {
 #pragma unroll
       for (int j = 0; j < NE; ++j) bad |= !(z[j] < pinf());
@@ -456,7 +449,7 @@ __device__ __forceinline__ RowPart chunk_pass(const void* row, int64_t V, int c,
   const float M = wave_max(m);
   double S;
   if constexpr (SAMPLING) {
-    const double f = (m == ninf()) ? 0.0 : exp2((double)(m * k) - (double)ref_point(M, k));
+    const double f = (m == ninf()) ? 0.0 : exp2(((double)m - (double)ref_logit(M)) * (double)k);
     S = wave_sum(s * f);
   } else {
     S = (ballot(bad) != 0) ? __builtin_nan("") : 0.0;
@@ -604,9 +597,9 @@ __global__ __launch_bounds__(kBlock) void k1_row_stats(RowStatsArgs a) {
 
 // Per-row merge of the chunk statistics.
 struct RowStat {
-  double s;    // sum of 2^(fl32(z k - rk)) over the row (sampling), 0/NaN (greedy)
+  double s;    // sum of 2^(fl32(fl32(z - ref) k)) over the row (sampling), 0/NaN (greedy)
   float m;     // row max
-  float rk;    // ref_point(m, k)
+  float ref;   // ref_logit(m)
   int32_t arg; // lowest index attaining m
   bool valid;  // no NaN/+inf and at least one finite logit
 };
@@ -665,7 +658,7 @@ __device__ __forceinline__ RowStat merge_row_from(const RowPart (&q0)[4], const 
   RowStat st;
   st.s = S;
   st.m = M;
-  st.rk = ref_point(M, k);
+  st.ref = ref_logit(M);
   st.arg = arg;
   st.valid = (M > ninf()) && (M < pinf()) && !__builtin_isnan(S);
   return st;
@@ -754,7 +747,7 @@ __device__ Select accept_sequence(const AcceptArgs& a, int64_t b, int lane, bool
   }
   if (status & kLayoutError) return finish(-1, -1, false);
   const bool greedy = (T == 0.f);
-  const bool sampling = (T > 0.f) && (T < pinf());
+  const bool sampling = sampling_temperature(T);
   if (!greedy && !sampling) return finish(-1, -1, true);
   const float k = sampling ? temp_scale(T) : 0.f;
   if (!uni) {  // a valid layout: the offsets address the packed arrays
@@ -809,8 +802,8 @@ __device__ Select accept_sequence(const AcceptArgs& a, int64_t b, int lane, bool
       zT = load_logit<DT>(a.target, (t0 + lane) * a.V + x);
       zD = load_logit<DT>(a.draft, (d0 + lane) * a.V + x);
     }
-    const double p = exp2((double)zT * (double)k - (double)st_t.rk) / st_t.s;
-    const double q = exp2((double)zD * (double)k - (double)st_d.rk) / st_d.s;
+    const double p = exp2(((double)zT - (double)st_t.ref) * (double)k) / st_t.s;
+    const double q = exp2(((double)zD - (double)st_d.ref) * (double)k) / st_d.s;
     const double ratio = (q == 0.0) ? (double)pinf() : lenient(p, a.lenience, a.eps) / q;
     rej = r > ratio;
   }
@@ -821,8 +814,8 @@ __device__ Select accept_sequence(const AcceptArgs& a, int64_t b, int lane, bool
   s.trow = t0 + n;
   s.drow = (n < g) ? d0 + n : -1;
   s.k = k;
-  s.rkT = __shfl(st_t.rk, n, kWave);
-  s.rkD = __shfl(st_d.rk, n, kWave);
+  s.refT = __shfl(st_t.ref, n, kWave);
+  s.refD = __shfl(st_d.ref, n, kWave);
   s.pad = 0;
   s.sT = __shfl(st_t.s, n, kWave);
   s.sD = __shfl(st_d.s, n, kWave);
@@ -852,8 +845,8 @@ __device__ __forceinline__ Select uniform_select(const Select& s) {
   u.trow = wave_uniform(s.trow);
   u.drow = wave_uniform(s.drow);
   u.k = uniform_f32(s.k);
-  u.rkT = uniform_f32(s.rkT);
-  u.rkD = uniform_f32(s.rkD);
+  u.refT = uniform_f32(s.refT);
+  u.refD = uniform_f32(s.refD);
   u.pad = 0;
   u.sT = uniform_f64(s.sT);
   u.sD = uniform_f64(s.sD);
@@ -861,14 +854,17 @@ __device__ __forceinline__ Select uniform_select(const Select& s) {
   return u;
 }
 
-// Weight of one token in the final draw: max(0, p - q) or p, in fp32.
+// Weight of one token in the final draw: max(0, p - q) or p, in fp32:
+// p = 2^(fl32(fl32(z - M) k)) * fl32(1/S). (With log2(1/S) folded into the
+// exponent instead, the exponent of a likely token sits near -log2 S, where
+// fp32 resolves only about 2^-19: ten times the error of the product form.)
 struct Weights {
-  float k, rkT, rkD, iT, iD;
+  float k, refT, refD, iT, iD;
   bool residual;
   __device__ __forceinline__ float operator()(float zT, float zD) const {
-    const float pT = exp2_hw(__builtin_fmaf(zT, k, -rkT)) * iT;
+    const float pT = exp2_hw(term_exp(zT, refT, k)) * iT;
     if (!residual) return pT;
-    const float pD = exp2_hw(__builtin_fmaf(zD, k, -rkD)) * iD;
+    const float pD = exp2_hw(term_exp(zD, refD, k)) * iD;
     return fmaxf(pT - pD, 0.f);
   }
 };
@@ -876,8 +872,8 @@ struct Weights {
 __device__ __forceinline__ Weights make_weights(const Select& s, bool force_bonus) {
   Weights w;
   w.k = s.k;
-  w.rkT = s.rkT;
-  w.rkD = s.rkD;
+  w.refT = s.refT;
+  w.refD = s.refD;
   w.iT = (float)(1.0 / s.sT);
   w.iD = (float)(1.0 / s.sD);
   w.residual = (s.mode == kModeResidual) && !force_bonus;
@@ -1281,9 +1277,8 @@ __global__ __launch_bounds__(kBlock) void k_merge_rows(MergeArgs a) {
   const float k = sampling ? kk : 0.f;
   const RowStat st = merge_row((is_draft ? a.dparts : a.tparts) + j * a.chunks, a.chunks, k, sampling);
   om[j] = st.m;
-  // re-reference the sum from fl32(m k) to m k exactly: sum 2^((z - m) k)
-  os[j] = sampling ? (st.valid ? st.s * exp2((double)st.rk - (double)st.m * (double)k) : __builtin_nan(""))
-                   : (st.valid ? 0.0 : __builtin_nan(""));
+  // the sum is taken relative to m: sum 2^((z - m) k)
+  os[j] = sampling ? (st.valid ? st.s : __builtin_nan("")) : (st.valid ? 0.0 : __builtin_nan(""));
   oa[j] = st.arg;
 }
 
@@ -1300,8 +1295,8 @@ struct ProbArgs {
   int32_t B, chunks;
 };
 
-// grid (element chunks of 2048, rows): p_v = 2^(fl32(z k - rk)) * fl32(1/S),
-// the same arithmetic as the final draw's weights.
+// grid (element chunks of 2048, rows): p_v = 2^(fl32(fl32(z - m) k)) *
+// fl32(1/S), the same arithmetic as the final draw's weights.
 template <int DT>
 __global__ __launch_bounds__(kBlock) void k_softmax_rows(ProbArgs a) {
   const int64_t k_row = blockIdx.y;
@@ -1321,7 +1316,7 @@ __global__ __launch_bounds__(kBlock) void k_softmax_rows(ProbArgs a) {
   Select s{};
   s.mode = kModeBonus;
   s.k = k;
-  s.rkT = st.rk;
+  s.refT = st.ref;
   s.sT = st.s;
   const Weights W = make_weights(s, true);
   constexpr int64_t esz = (DT == kBF16) ? 2 : 4;

@@ -478,6 +478,78 @@ def test_large_uniform_batch_parity(svx, B, V, g, dtype):
     parity_case(svx, "uniform B=%d V=%d gamma=%d %s" % (B, V, g, dtype), x)
 
 
+BF16_LOWEST = -3.3895313892515355e38  # the most negative finite bf16 (0xff7f)
+
+
+def range_case(kind, dtype, seed, B=48, V=3000, g=4):
+    """Logits at the ends of the floating-point range (uniform batch, every
+    fourth sequence greedy, V = 3000: several pass-1 tiles per row):
+    - "lowest_mask": a random half of each sequence's vocabulary masked with
+      the dtype's most negative finite value instead of -inf (what
+      torch.finfo(dtype).min masking produces), the same tokens in its
+      target and draft rows;
+    - "minus_1e30_mask": the same with -1e30;
+    - "huge": logits of magnitude about 1e12 (nearly one-hot rows);
+    - "offset": logits + 1e9 (quantised to multiples of 64 in fp32: ties);
+    - "tiny_T": T = 1e-30 for the sampling sequences (nearly one-hot);
+    - "huge_T": T = 3e38 (nearly uniform; log2(e)/T is an fp32 subnormal);
+    - "denormal_T": T = 1e-40, where log2(e)/T overflows fp32: outside the
+      stated domain, a data error on both sides.
+    Draft tokens are drawn from the draft rows, so masked tokens are never
+    drafted."""
+    rng = np.random.default_rng(seed)
+    T = np.where(np.arange(B) % 4 == 3, 0.0, np.where(np.arange(B) % 4 == 1, 0.7, 1.0)).astype(np.float32)
+    rows_t = B * (g + 1)
+    target = (rng.standard_normal((rows_t, V)) * 2).astype(np.float32)
+    trow = (np.arange(B * g) // g) * (g + 1) + np.arange(B * g) % g
+    draft = (target[trow] + rng.standard_normal((B * g, V))).astype(np.float32)
+    if kind in ("lowest_mask", "minus_1e30_mask"):
+        low = {"lowest_mask": BF16_LOWEST if dtype == "bf16" else np.finfo(np.float32).min,
+               "minus_1e30_mask": -1e30}[kind]
+        mask = rng.random((B, V)) < 0.5
+        target[mask[np.arange(rows_t) // (g + 1)]] = low
+        draft[mask[np.arange(B * g) // g]] = low
+    elif kind == "huge":
+        target *= np.float32(1e12)
+        draft *= np.float32(1e12)
+    elif kind == "offset":
+        target += np.float32(1e9)
+        draft += np.float32(1e9)
+    elif kind == "tiny_T":
+        T = np.where(T > 0, np.float32(1e-30), T).astype(np.float32)
+    elif kind == "huge_T":
+        T = np.where(T > 0, np.float32(3e38), T).astype(np.float32)
+    elif kind == "denormal_T":  # log2(e)/T overflows fp32: outside the domain
+        T = np.where(T > 0, np.float32(1e-40), T).astype(np.float32)
+    Ts = np.repeat(T, g).astype(np.float64)
+    Ts = np.where(Ts < 1e-38, 0.0, Ts)  # drafting at an invalid T: argmax
+    z = draft.astype(np.float64) / np.where(Ts > 0, Ts, 1.0)[:, None]
+    noise = np.where(Ts[:, None] > 0, rng.gumbel(size=draft.shape), 0.0)
+    tokens = np.argmax(z + noise, axis=1).astype(np.int32)
+    conv = synth.to_bf16_bits if dtype == "bf16" else (lambda a: a)
+    return synth.Inputs("range %s" % kind, V, g, dtype, conv(target), conv(draft), tokens,
+                        np.full(B, g, np.int32), T)
+
+
+@pytest.mark.parametrize("kind", ["lowest_mask", "minus_1e30_mask", "huge", "offset", "tiny_T",
+                                  "huge_T", "denormal_T"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_extreme_logit_ranges(svx, kind, dtype):
+    # the softmax of a row at any finite logits and temperature: masks with
+    # the most negative finite value, logits of magnitude 1e12, a large common
+    # offset, T = 1e-30 and T = 3e38 all give the oracle's outcomes, with no
+    # sequence reported as a data error; T = 1e-40 fails every sampling
+    # sequence on both sides
+    x = range_case(kind, dtype, seed=len(kind) * 7 + (dtype == "bf16"))
+    got, orc = parity_case(svx, "range %s %s" % (kind, dtype), x)
+    if kind == "denormal_T":
+        sampling = x.temperature > 0
+        assert (orc.n[sampling] == -1).all() and (orc.n[~sampling] >= 0).all()
+        assert got[2] & svx.SPECV_DEV_SEQ_ERROR
+    else:
+        assert (orc.n >= 0).all() and (got[0] >= 0).all() and got[2] == 0
+
+
 @pytest.mark.parametrize("B,V,g,dtype", [(8, 262144, 3, "f32"), (8, 262145, 3, "bf16"),
                                          (512, 270000, 0, "bf16")])
 def test_draw_scan_paths(svx, B, V, g, dtype):

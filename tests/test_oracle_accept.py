@@ -137,6 +137,42 @@ def test_data_errors_give_sentinels():
     assert res.n[0] >= 0 and res.n[9] >= 0
 
 
+def test_temperature_domain():
+    # sampling needs log2(e)/T finite in fp32: T = 1e-38 (scale 1.44e38) and
+    # T = 3e38 are valid, T = 1e-39 (scale 1.44e39 > FLT_MAX) and the
+    # smallest subnormal are not; T = 0 stays greedy
+    V = 4
+    good = one_step(V, [range(4), range(4)], [[0, 1]], [0])
+    Ts = [1e-38, 3e38, 1e-39, float(np.float32(1.4e-45)), 0.0]
+    res = run_oracle(pack([dict(good, T=T) for T in Ts], V))
+    assert list(res.n >= 0) == [True, True, False, False, True]
+
+
+def test_tiny_temperature_reaches_the_greedy_limit():
+    # As T -> 0 each softmax becomes one-hot at its row's maximum, so with
+    # unique maxima the sampling step at T = 1e-30 (a valid temperature)
+    # gives the greedy outcome for drafts drawn at that T (the draft rows'
+    # argmax): accept while x_i == argmax p_i, then emit argmax p_n, since
+    # the residual max(0, p_n - q_n) is one-hot there too.
+    rng = np.random.default_rng(3)
+    V, g, B = 50, 4, 40
+    seqs = []
+    for _ in range(B):
+        t = rng.permutation(V * (g + 1)).reshape(g + 1, V).astype(np.float32)  # unique values
+        d = t[:g].copy()
+        flip = rng.random(g) < 0.4  # some drafts disagree with the target's argmax
+        for i in np.flatnonzero(flip):
+            d[i] = rng.permutation(V).astype(np.float32)
+        tokens = [int(np.argmax(d[i])) for i in range(g)]
+        seqs.append({"target": t, "draft": d, "tokens": tokens, "T": 1e-30})
+    x = pack(seqs, V)
+    hot = run_oracle(x, seed=5)
+    greedy = run_oracle(pack([dict(s_, T=0.0) for s_ in seqs], V), seed=5)
+    np.testing.assert_array_equal(hot.n, greedy.n)
+    np.testing.assert_array_equal(hot.next_token, greedy.next_token)
+    assert (hot.n < g).any() and (hot.n == g).any()
+
+
 def test_layout_errors_poison_every_sequence():
     V = 4
     good = one_step(V, [range(4), range(4)], [[0, 1]], [0])
