@@ -160,7 +160,7 @@ __device__ __forceinline__ float raw_elem(const typename Tile<DT, VEC>::Raw& r) 
 template <int DT, bool VEC, int G>
 __device__ __forceinline__ void diag_terms(const typename Tile<DT, VEC>::Raw& rd,
                                            const typename Tile<DT, VEC>::Raw& rt, float k,
-                                           float refT, float refD, float r, float iD, float& sa,
+                                           float refT, float refD, float lr, float iD, float& sa,
                                            float& ss, float& sA, float& mx) {
   float pa[8], ps[8], pA[8];
 #pragma unroll
@@ -179,10 +179,11 @@ __device__ __forceinline__ void diag_terms(const typename Tile<DT, VEC>::Raw& rd
     }
     const float eD = term_exp(zD, refD, k);
     const float tD = exp2_hw(eD);
-    const float tT = exp2_hw(term_exp(zT, refT, k));
-    // min(p, q) = min(tT r, tD) / S^D with r = S^D / S^T: one product per
-    // element, the 1 / S^D once per group
-    pa[u] = fminf(tT * r, tD);
+    // min(p, q) = min(tT r, tD) / S^D with r = S^D / S^T, tT r formed as
+    // 2^(fl32(z - M) k + log2 r) in one fma (log2 r is of order 1, so the
+    // exponent keeps its resolution); the 1 / S^D once per group
+    const float tTr = exp2_hw(__builtin_fmaf(zT - refT, k, lr));
+    pa[u] = fminf(tTr, tD);
     ps[u] = tD;
     // a masked token (tD = 0, eD = -inf) must add 0: eD is clamped to the
     // lowest finite float, which changes nothing where tD > 0 (eD is finite
@@ -262,7 +263,7 @@ __device__ __forceinline__ bool diag_chunk(const DiagArgs& a, int64_t item, int 
   const RowStat st_t = merge_row_from(qt, a.tparts + tr * a.chunks, a.chunks, k, sampling);
   const RowStat st_d = merge_row_from(qd, a.dparts + j * a.chunks, a.chunks, k, sampling);
   if (!st_t.valid || !st_d.valid) return false;
-  const float rTD = sampling ? (float)(st_d.s / st_t.s) : 0.f;
+  const float lTD = sampling ? (float)log2(st_d.s / st_t.s) : 0.f;  // log2 (S^D / S^T)
   const float iD = sampling ? (float)(1.0 / st_d.s) : 0.f;
   const int limit = (2 * K > kWave) ? 2 * K : kWave;
   double sa = 0.0, ss = 0.0, sA = 0.0;
@@ -307,11 +308,11 @@ __device__ __forceinline__ bool diag_chunk(const DiagArgs& a, int64_t item, int 
     for (int g = 0; g < NG; ++g) gm[g] = ninf();
     if (sampling) {
       float ga[NG], gs[NG], gA[NG];
-      diag_terms<DT, VEC, 0>(rd, rt, k, st_t.ref, st_d.ref, rTD, iD, ga[0], gs[0], gA[0], gm[0]);
-      diag_terms<DT, VEC, 1>(rd, rt, k, st_t.ref, st_d.ref, rTD, iD, ga[1], gs[1], gA[1], gm[1]);
+      diag_terms<DT, VEC, 0>(rd, rt, k, st_t.ref, st_d.ref, lTD, iD, ga[0], gs[0], gA[0], gm[0]);
+      diag_terms<DT, VEC, 1>(rd, rt, k, st_t.ref, st_d.ref, lTD, iD, ga[1], gs[1], gA[1], gm[1]);
       if constexpr (NG == 4) {
-        diag_terms<DT, VEC, 2>(rd, rt, k, st_t.ref, st_d.ref, rTD, iD, ga[2], gs[2], gA[2], gm[2]);
-        diag_terms<DT, VEC, 3>(rd, rt, k, st_t.ref, st_d.ref, rTD, iD, ga[3], gs[3], gA[3], gm[3]);
+        diag_terms<DT, VEC, 2>(rd, rt, k, st_t.ref, st_d.ref, lTD, iD, ga[2], gs[2], gA[2], gm[2]);
+        diag_terms<DT, VEC, 3>(rd, rt, k, st_t.ref, st_d.ref, lTD, iD, ga[3], gs[3], gA[3], gm[3]);
       }
       sa += (double)tree_sum(ga);
       ss += (double)tree_sum(gs);

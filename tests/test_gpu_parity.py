@@ -812,6 +812,16 @@ def test_diagnostics_heavy_ties(svx):
         assert_diag_parity("heavy ties", x, k)
 
 
+@pytest.mark.parametrize("kind", ["lowest_mask", "minus_1e30_mask", "huge", "tiny_T"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_diagnostics_extreme_ranges(svx, kind, dtype):
+    # alpha, entropy and top-16 at the ends of the range: masks with the most
+    # negative finite value (their q is 0 and adds nothing to the entropy),
+    # logits of magnitude 1e12 and T = 1e-30 (one-hot rows)
+    x = range_case(kind, dtype, seed=len(kind) * 11 + (dtype == "bf16"), B=16)
+    assert_diag_parity("range %s %s" % (kind, dtype), x, 16)
+
+
 def test_diagnostics_argument_errors(svx):
     x = synth.tiny_cpu(rounds=4, vocab=32)
     for k in (-1, 33, 65):
