@@ -121,6 +121,32 @@ def test_cascade_parity_inner_drafts_past_k1(svx):
                           lenience="sq", epsilon=0.4, seed=17)
 
 
+BF16_LOWEST = -3.3895313892515355e38  # the most negative finite bf16 (0xff7f)
+
+
+@pytest.mark.parametrize("kind", ["lowest_mask", "tiny_T"])
+def test_cascade_parity_extreme_ranges(svx, kind):
+    # the three tables mask half the vocabulary with the most negative finite
+    # bf16 (never generated), or T = 1e-30 (every draw one-hot)
+    V, B = 2048, 64
+    tabs = list(tables(V, 41, scale=2.0))
+    rng = np.random.default_rng(42)
+    T = np.where(np.arange(B) % 4 == 0, 0.0, 0.9).astype(np.float32)
+    ok = np.arange(V)
+    if kind == "lowest_mask":
+        cols = rng.random(V) < 0.5
+        for t in tabs:
+            t[:, cols] = BF16_LOWEST
+        ok = np.flatnonzero(~cols)
+    else:
+        T = np.where(T > 0, np.float32(1e-30), T).astype(np.float32)
+    got, want = assert_cascade_parity(kind, svx, [bf16(t) for t in tabs], T, rng.choice(ok, B),
+                                      k1=3, k2=2, rounds=3, lenience="sq", epsilon=0.5, seed=9)
+    assert (want.length > 0).all() and (got["length"] > 0).all()
+    if kind == "lowest_mask":
+        assert np.isin(got["tokens"][got["tokens"] >= 0], ok).all()
+
+
 def test_cascade_gpu_target_law(svx):
     tabs = tables(5, 0)
     B, c = 400_000, 2

@@ -125,6 +125,36 @@ def test_decode_parity_streamed_rows(svx):
                          rng.integers(0, 9000, B), gamma=4, rounds=3, seed=21)
 
 
+BF16_LOWEST = -3.3895313892515355e38  # the most negative finite bf16 (0xff7f)
+
+
+@pytest.mark.parametrize("kind,dtype", [("lowest_mask", "bf16"), ("lowest_mask", "f32"),
+                                        ("tiny_T", "bf16")])
+def test_decode_parity_extreme_ranges(svx, kind, dtype):
+    # tables whose rows mask half the vocabulary with the dtype's most
+    # negative finite value (those tokens are never generated), or T = 1e-30
+    # (drafting and verification one-hot at the row maxima)
+    V, B = 2048, 64
+    t, d = tables(V, 31, sigma=1.0, scale=2.0)
+    rng = np.random.default_rng(32)
+    T = np.where(np.arange(B) % 4 == 0, 0.0, 1.0).astype(np.float32)
+    ok = np.arange(V)
+    if kind == "lowest_mask":
+        cols = rng.random(V) < 0.5
+        low = BF16_LOWEST if dtype == "bf16" else np.finfo(np.float32).min
+        t[:, cols] = low
+        d[:, cols] = low
+        ok = np.flatnonzero(~cols)
+    else:
+        T = np.where(T > 0, np.float32(1e-30), T).astype(np.float32)
+    conv = to_bf16_bits if dtype == "bf16" else (lambda a: a)
+    got, want = assert_decode_parity("%s %s" % (kind, dtype), svx, conv(t), conv(d), T,
+                                     rng.choice(ok, B), gamma=4, rounds=4, seed=33)
+    assert (want.length > 0).all() and (got["length"] > 0).all()
+    if kind == "lowest_mask":
+        assert np.isin(got["tokens"][got["tokens"] >= 0], ok).all()
+
+
 def test_decode_gpu_sequence_law(svx):
     # the GPU loop's own output: joint of the first three tokens vs the chain
     t, d = tables(5, 0)
