@@ -24,6 +24,8 @@
 //                  boundary, orders the masses before the draw).
 #pragma once
 
+#include <type_traits>
+
 #include "device.hpp"
 
 namespace specv {
@@ -854,29 +856,56 @@ __device__ __forceinline__ Select uniform_select(const Select& s) {
   return u;
 }
 
-// Weight of one token in the final draw: max(0, p - q) or p, in fp32:
-// p = 2^(fl32(fl32(z - M) k)) * fl32(1/S). (With log2(1/S) folded into the
-// exponent instead, the exponent of a likely token sits near -log2 S, where
-// fp32 resolves only about 2^-19: ten times the error of the product form.)
+// Weight of one token in the final draw: max(0, p - q) or p, in fp32. Two
+// forms of p = 2^((z - M) k) / S (M the row maximum), equal to fp32
+// rounding:
+//   exact (any logits): 2^(fl32(fl32(z - M) k)) * fl32(1/S);
+//   FMA, where |fl32(M k)| < 2^24 (every realistic row): 2^(fl32(z k - r)) * c
+//     with r = fl32(M k) and c = fl32(2^-e / S), e = M k - r exactly (one
+//     fma): the terms' common factor 2^e (|e| <= 1 there) is divided out.
+// The form is chosen once per sequence (weights_fma: both rows of a
+// residual) and serves both the masses and the draw's walk, so they agree
+// bit for bit. With log2(1/S) folded into the exponent instead, a likely
+// token's exponent sits near -log2 S, where fp32 resolves only about 2^-19:
+// ten times the error of the product form.
+template <bool FMA>
 struct Weights {
-  float k, refT, refD, iT, iD;
+  float k, aT, aD, cT, cD;  // aT = M (exact form) or r (FMA form); cT the multiplier
   bool residual;
   __device__ __forceinline__ float operator()(float zT, float zD) const {
-    const float pT = exp2_hw(term_exp(zT, refT, k)) * iT;
+    const float pT = exp2_hw(FMA ? __builtin_fmaf(zT, k, -aT) : term_exp(zT, aT, k)) * cT;
     if (!residual) return pT;
-    const float pD = exp2_hw(term_exp(zD, refD, k)) * iD;
+    const float pD = exp2_hw(FMA ? __builtin_fmaf(zD, k, -aD) : term_exp(zD, aD, k)) * cD;
     return fmaxf(pT - pD, 0.f);
   }
 };
 
-__device__ __forceinline__ Weights make_weights(const Select& s, bool force_bonus) {
-  Weights w;
+__device__ __forceinline__ bool residual_weights(const Select& s, bool force_bonus) {
+  return (s.mode == kModeResidual) && !force_bonus;
+}
+
+__device__ __forceinline__ bool weights_fma(const Select& s, bool force_bonus) {
+  constexpr float kLim = 16777216.f;  // 2^24: |M k - fl32(M k)| <= 1 below it
+  return fabsf(s.refT * s.k) < kLim && (!residual_weights(s, force_bonus) || fabsf(s.refD * s.k) < kLim);
+}
+
+template <bool FMA>
+__device__ __forceinline__ Weights<FMA> make_weights(const Select& s, bool force_bonus) {
+  Weights<FMA> w;
   w.k = s.k;
-  w.refT = s.refT;
-  w.refD = s.refD;
-  w.iT = (float)(1.0 / s.sT);
-  w.iD = (float)(1.0 / s.sD);
-  w.residual = (s.mode == kModeResidual) && !force_bonus;
+  w.residual = residual_weights(s, force_bonus);
+  if constexpr (FMA) {
+    w.aT = s.refT * s.k;
+    w.aD = s.refD * s.k;
+    const float eT = __builtin_fmaf(s.refT, s.k, -w.aT), eD = __builtin_fmaf(s.refD, s.k, -w.aD);
+    w.cT = (float)((double)exp2_hw(-eT) / s.sT);
+    w.cD = (float)((double)exp2_hw(-eD) / s.sD);
+  } else {
+    w.aT = s.refT;
+    w.aD = s.refD;
+    w.cT = (float)(1.0 / s.sT);
+    w.cD = (float)(1.0 / s.sD);
+  }
   return w;
 }
 
@@ -1014,8 +1043,8 @@ __device__ __forceinline__ void load16(const void* row, int64_t lo, int64_t V, f
 // reaches t, and that lane walks its 16 weights. Returns the token, or -1 if
 // t is not reached (with t < 0: always), the final prefix in *total and the
 // last element of positive weight in *last.
-template <int DT, bool VEC>
-__device__ int wave_draw(const void* trow, const void* drow, const Weights& W, int64_t V,
+template <int DT, bool VEC, class WT>
+__device__ int wave_draw(const void* trow, const void* drow, const WT& W, int64_t V,
                          int64_t sb0, int64_t sb1, double carry, double t, int lane,
                          double* total, int64_t* last) {
   int64_t lastpos = -1;
@@ -1093,29 +1122,38 @@ __device__ int draw_token(const DrawArgs& a, const double* sub, const double (&v
   int token = -1;
   if (total > 0.0) {
     const double t = s.u * total;  // u in (0, 1]: t <= total
-    const Weights W = make_weights(s, false);
     double base = 0.0;
     const int64_t sb = regs ? find_sub_regs(P, a.nsub, t, lane, &base)
                             : wave_scan_subs(sub, a.nsub, t, lane, &base, nullptr);
-    int64_t last = -1;
-    if (sb >= 0) {
-      token = wave_draw<DT, VEC>(trow, drow, W, a.V, sb, sb + 1, base, t, lane, nullptr, &last);
-      if (token < 0) token = (int)last;
-    }
-    for (int64_t q = a.nsub - 1; token < 0 && q >= 0; --q) {
-      // rounding left t past every prefix: the last token of positive weight
-      if (!(sub[q] > 0.0)) continue;
-      wave_draw<DT, VEC>(trow, drow, W, a.V, q, q + 1, 0.0, -1.0, lane, nullptr, &last);
-      token = (int)last;
-    }
+    auto walk = [&](auto fma) {
+      const Weights<decltype(fma)::value> W = make_weights<decltype(fma)::value>(s, false);
+      int tok = -1;
+      int64_t last = -1;
+      if (sb >= 0) {
+        tok = wave_draw<DT, VEC>(trow, drow, W, a.V, sb, sb + 1, base, t, lane, nullptr, &last);
+        if (tok < 0) tok = (int)last;
+      }
+      for (int64_t q = a.nsub - 1; tok < 0 && q >= 0; --q) {
+        // rounding left t past every prefix: the last token of positive weight
+        if (!(sub[q] > 0.0)) continue;
+        wave_draw<DT, VEC>(trow, drow, W, a.V, q, q + 1, 0.0, -1.0, lane, nullptr, &last);
+        tok = (int)last;
+      }
+      return tok;
+    };
+    token = weights_fma(s, false) ? walk(std::true_type{}) : walk(std::false_type{});
   } else {
     // The residual has no mass in fp32 (p_n == q_n to rounding): draw from p_n.
-    const Weights W = make_weights(s, true);
-    double tot = 0.0;
-    int64_t last = -1;
-    wave_draw<DT, VEC>(trow, nullptr, W, a.V, 0, a.nsub, 0.0, -1.0, lane, &tot, &last);
-    token = wave_draw<DT, VEC>(trow, nullptr, W, a.V, 0, a.nsub, 0.0, s.u * tot, lane, nullptr, nullptr);
-    if (token < 0) token = (int)last;
+    auto walk = [&](auto fma) {
+      const Weights<decltype(fma)::value> W = make_weights<decltype(fma)::value>(s, true);
+      double tot = 0.0;
+      int64_t last = -1;
+      wave_draw<DT, VEC>(trow, nullptr, W, a.V, 0, a.nsub, 0.0, -1.0, lane, &tot, &last);
+      const int tok = wave_draw<DT, VEC>(trow, nullptr, W, a.V, 0, a.nsub, 0.0, s.u * tot, lane,
+                                         nullptr, nullptr);
+      return (tok < 0) ? (int)last : tok;
+    };
+    token = weights_fma(s, true) ? walk(std::true_type{}) : walk(std::false_type{});
   }
   return token;
 }
@@ -1130,14 +1168,14 @@ __device__ int draw_token(const DrawArgs& a, const double* sub, const double (&v
 // Pass 2 over chunk c of the selected row pair of one sequence: the weight
 // mass of every 1024-element sub-block of the chunk, stored to out[sub-block]
 // (global memory or LDS).
-template <int DT, bool VEC>
-__device__ __forceinline__ void chunk_masses(const DrawArgs& a, const Select& s, int c, int lane,
-                                             double* out) {
+template <int DT, bool VEC, bool FMA>
+__device__ __forceinline__ void chunk_masses_w(const DrawArgs& a, const Select& s, int c, int lane,
+                                               double* out) {
   using TL = Tile<DT, VEC>;
   constexpr int NE = TL::NE;
   constexpr int SUBS = TL::EPI / kSub;  // sub-blocks per tile (1 or 2)
   constexpr int PER = NE / SUBS;        // slots per lane per sub-block
-  const Weights W = make_weights(s, false);
+  const Weights<FMA> W = make_weights<FMA>(s, false);
   constexpr int64_t esz = (DT == kBF16) ? 2 : 4;
   const void* trow = static_cast<const char*>(a.target) + s.trow * a.V * esz;
   const void* drow = W.residual ? static_cast<const char*>(a.draft) + s.drow * a.V * esz : nullptr;
@@ -1177,6 +1215,14 @@ __device__ __forceinline__ void chunk_masses(const DrawArgs& a, const Select& s,
       if (lane == 0 && sb < a.nsub) out[sb] = m;
     }
   }
+}
+
+// The weights' form is the same for the whole sequence (weights_fma).
+template <int DT, bool VEC>
+__device__ __forceinline__ void chunk_masses(const DrawArgs& a, const Select& s, int c, int lane,
+                                             double* out) {
+  if (weights_fma(s, false)) chunk_masses_w<DT, VEC, true>(a, s, c, lane, out);
+  else chunk_masses_w<DT, VEC, false>(a, s, c, lane, out);
 }
 
 template <int DT, bool VEC>
@@ -1318,14 +1364,18 @@ __global__ __launch_bounds__(kBlock) void k_softmax_rows(ProbArgs a) {
   s.k = k;
   s.refT = st.ref;
   s.sT = st.s;
-  const Weights W = make_weights(s, true);
   constexpr int64_t esz = (DT == kBF16) ? 2 : 4;
   const void* row = static_cast<const char*>(is_draft ? a.draft : a.target) + j * a.V * esz;
   const int64_t v0 = (int64_t)blockIdx.x * 2048;
-  for (int q = threadIdx.x; q < 2048; q += kBlock) {
-    const int64_t v = v0 + q;
-    if (v < a.V) a.out[k_row * a.V + v] = W(load_logit<DT>(row, v), 0.f);
-  }
+  auto fill = [&](auto fma) {
+    const Weights<decltype(fma)::value> W = make_weights<decltype(fma)::value>(s, true);
+    for (int q = threadIdx.x; q < 2048; q += kBlock) {
+      const int64_t v = v0 + q;
+      if (v < a.V) a.out[k_row * a.V + v] = W(load_logit<DT>(row, v), 0.f);
+    }
+  };
+  if (weights_fma(s, true)) fill(std::true_type{});
+  else fill(std::false_type{});
 }
 
 __global__ __launch_bounds__(kBlock) void k_philox(uint64_t seed, const uint32_t* ctr,
