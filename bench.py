@@ -9,7 +9,8 @@ workloads the same way (the tiny CPU-checkable one with 10,000 rounds batched
 into one call, the T5-XXL-like one with 2,000 rounds batched, at T = 1 and
 greedy, batched serving and ragged lookahead), each with its step-level
 fraction of the HBM peak, its pass-1 kernel fraction, the stored counter
-traffic and its parity counts against the CPU oracle. Every workload also
+traffic, its parity counts against the CPU oracle and its tokens per round
+against the pages' closed form at its acceptance rates. Every workload also
 gets the time of one launch of the library's read probe over its pass-1
 bytes: what a single streaming read of that size takes on this part. Prints
 one JSON line.
@@ -703,6 +704,45 @@ def parity_counts(x, n, nxt):
             "flag_expectation": e, "flag_cap": e + 5.0 * np.sqrt(e) + 3.0}
 
 
+def tokens_vs_closed_form(torch, svx, dev, x, n):
+    """Emitted tokens per sequence against the closed form of the pages: with
+    per-position acceptance rates alpha_j = sum_v min(p_j, q_j) (the
+    library's diagnostics on the same inputs, outside the timed region), a
+    round emits tau = sum_{k=0}^{gamma} prod_{j<k} alpha_j tokens on average,
+    which is (1 - alpha^(gamma+1)) / (1 - alpha) when every alpha_j is alpha.
+    The inputs draw each draft token from its draft row, so acceptances are
+    independent Bernoulli(alpha_j) across the batch's positions and the
+    observed mean should sit within a few standard errors of the mean tau."""
+    d = svx.from_inputs(x, dev)
+    out = svx.specv_position_diagnostics(d["target"], d["draft"], d["gamma"], d["temperature"], 0,
+                                         max_gamma=x.max_gamma)
+    alpha = out["alpha"].cpu().numpy()
+    del d, out
+    torch.cuda.empty_cache()
+    doff = np.concatenate([[0], np.cumsum(x.gamma)])
+    taus, vars_, obs = [], [], []
+    for b in range(x.batch):
+        a = alpha[doff[b]:doff[b + 1]]
+        if n[b] < 0 or np.isnan(a).any():
+            continue
+        reach = np.concatenate([[1.0], np.cumprod(a)])  # P(round reaches position k)
+        pk = reach[:-1] * (1.0 - a)                     # P(n = k), k < gamma
+        pk = np.concatenate([pk, reach[-1:]])           # P(n = gamma)
+        k = np.arange(len(pk)) + 1.0                    # tokens emitted
+        mu = float((pk * k).sum())
+        taus.append(mu)
+        vars_.append(float((pk * k * k).sum()) - mu * mu)
+        obs.append(float(n[b] + 1))
+    cnt = len(obs)
+    mean_obs, mean_tau = float(np.mean(obs)), float(np.mean(taus))
+    se = float(np.sqrt(np.sum(vars_))) / cnt
+    return {"sequences": cnt, "observed_tokens_per_sequence": mean_obs,
+            "closed_form_tokens_per_sequence": mean_tau,
+            "mean_acceptance_rate": float(np.nanmean(alpha)),
+            "standard_error": se,
+            "z": (mean_obs - mean_tau) / se if se > 0 else 0.0}
+
+
 def per_config(torch, svx, dev, args, sha):
     """The other workloads, timed as the headline one, with parity counts."""
     out = {}
@@ -730,6 +770,7 @@ def per_config(torch, svx, dev, args, sha):
                "step_frac_of_read_probe": probe / m["ms_per_step_plain"],
                "pass1_frac_of_read_probe": probe / m["k1_ms"],
                "stage_ms_instrumented": m["stage_ms"],
+               "tokens_vs_closed_form": tokens_vs_closed_form(torch, svx, dev, x, m["n"]),
                "parity_vs_oracle": parity_counts(x, m["n"], m["next"])}
         if name in TARGET_WORKLOADS:
             rec["target_step_frac"] = STEP_TARGET
@@ -861,6 +902,7 @@ def main():
         "kernel_sha": sha,
     }
     if args.lenience == "none" and not args.no_per_config:
+        result["tokens_vs_closed_form"] = tokens_vs_closed_form(torch, svx, dev, x, n_host)
         result["parity_vs_oracle"] = parity_counts(x, n_host, next_host)
         result["per_config"] = per_config(torch, svx, dev, args, sha)
     if args.lenience == "none" and not args.no_batch1:
