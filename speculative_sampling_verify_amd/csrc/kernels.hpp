@@ -2,20 +2,25 @@
 //
 // The step (DistillSpec, Appendix A.3, Algorithm A.1, lenience 1) runs as:
 //   k0_plan        offsets of the packed ragged rows, row -> sequence maps,
-//                  layout validation; initialises the status word. Not
-//                  launched for a uniform batch (every gamma equal), whose
-//                  offsets are arithmetic: k1's first workgroup checks the
-//                  gammas and initialises the status word instead.
+//                  layout validation; initialises the status word. Launched
+//                  only for ragged batches of more than 1024 sequences: a
+//                  uniform batch (every gamma equal) has arithmetic offsets,
+//                  and k1's first workgroup checks its gammas; a smaller
+//                  ragged batch is planned by k1's first workgroup, and each
+//                  pass-1 wave finds its row's sequence with a wave scan.
 //   k1_row_stats   pass 1, the HBM-bound hot loop: every needed logit row is
 //                  streamed once with 16-byte non-temporal loads; each wave
 //                  owns one (row, chunk) and keeps (max, sum of 2^((z - max) k),
-//                  argmax) in registers, reduced across the wave by shuffles.
+//                  argmax) in registers, reduced across the wave by shuffles;
+//                  the wave whose chunk holds a row's draft token also
+//                  records that logit for the accept step.
 //   k3_accept_mass the accept step (one wave per sequence, one lane per draft
-//                  position: merge the chunk statistics, gather p_i(x_i) and
-//                  q_i(x_i), draw r_i from Philox, first rejection by ballot;
-//                  greedy sequences finish here) fused with pass 2 over the
-//                  one selected row pair of each sampling sequence: weight
-//                  mass max(0, p - q) or p per 1024-element sub-block.
+//                  position: merge the chunk statistics, p_i(x_i) and
+//                  q_i(x_i) from the recorded logits, r_i from Philox, first
+//                  rejection by ballot; greedy sequences finish here) fused
+//                  with pass 2 over the one selected row pair of each
+//                  sampling sequence: weight mass max(0, p - q) or p per
+//                  1024-element sub-block.
 //   k4_draw        one wave per sampling sequence picks the sub-block that
 //                  holds u * total and a wave prefix scan inside it finds the
 //                  token (inverse CDF in index order).
