@@ -704,14 +704,46 @@ def parity_counts(x, n, nxt):
             "flag_expectation": e, "flag_cap": e + 5.0 * np.sqrt(e) + 3.0}
 
 
+def closed_form_tokens(alpha, gamma, n):
+    """Tokens per round against the closed form, from per-position acceptance
+    rates `alpha` (packed by sequence, gamma[b] each) and observed n per
+    sequence (-1 for a failed one). A round reaches position k with
+    probability prod_{j<k} alpha_j, so it emits tau = sum_{k=0}^{gamma}
+    prod_{j<k} alpha_j tokens on average ((1 - alpha^(gamma+1)) / (1 - alpha)
+    for equal alpha); with independent acceptances, n + 1 has the law
+    P(n = k) = prod_{j<k} alpha_j (1 - alpha_k) for k < gamma and
+    P(n = gamma) = prod_j alpha_j, whose variance gives the standard error of
+    the batch mean."""
+    doff = np.concatenate([[0], np.cumsum(gamma)])
+    taus, vars_, obs = [], [], []
+    for b in range(len(gamma)):
+        a = np.asarray(alpha[doff[b]:doff[b + 1]], np.float64)
+        if n[b] < 0 or np.isnan(a).any():
+            continue
+        reach = np.concatenate([[1.0], np.cumprod(a)])  # P(round reaches position k)
+        pk = np.concatenate([reach[:-1] * (1.0 - a), reach[-1:]])  # P(n = k)
+        k = np.arange(len(pk)) + 1.0                    # tokens emitted
+        mu = float((pk * k).sum())
+        taus.append(mu)
+        vars_.append(max(0.0, float((pk * k * k).sum()) - mu * mu))
+        obs.append(float(n[b] + 1))
+    cnt = len(obs)
+    if cnt == 0:
+        return {"sequences": 0}
+    mean_obs, mean_tau = float(np.mean(obs)), float(np.mean(taus))
+    se = float(np.sqrt(np.sum(vars_))) / cnt
+    return {"sequences": cnt, "observed_tokens_per_sequence": mean_obs,
+            "closed_form_tokens_per_sequence": mean_tau,
+            "mean_acceptance_rate": float(np.nanmean(np.asarray(alpha, np.float64))),
+            "standard_error": se,
+            "z": (mean_obs - mean_tau) / se if se > 0 else 0.0}
+
+
 def tokens_vs_closed_form(torch, svx, dev, x, n):
-    """Emitted tokens per sequence against the closed form of the pages: with
-    per-position acceptance rates alpha_j = sum_v min(p_j, q_j) (the
-    library's diagnostics on the same inputs, outside the timed region), a
-    round emits tau = sum_{k=0}^{gamma} prod_{j<k} alpha_j tokens on average,
-    which is (1 - alpha^(gamma+1)) / (1 - alpha) when every alpha_j is alpha.
-    The inputs draw each draft token from its draft row, so acceptances are
-    independent Bernoulli(alpha_j) across the batch's positions and the
+    """closed_form_tokens with each draft position's acceptance rate
+    alpha_j = sum_v min(p_j, q_j) from the library's diagnostics on the same
+    inputs (outside the timed region). The inputs draw each draft token from
+    its draft row, so acceptances are independent Bernoulli(alpha_j) and the
     observed mean should sit within a few standard errors of the mean tau."""
     d = svx.from_inputs(x, dev)
     out = svx.specv_position_diagnostics(d["target"], d["draft"], d["gamma"], d["temperature"], 0,
@@ -719,28 +751,7 @@ def tokens_vs_closed_form(torch, svx, dev, x, n):
     alpha = out["alpha"].cpu().numpy()
     del d, out
     torch.cuda.empty_cache()
-    doff = np.concatenate([[0], np.cumsum(x.gamma)])
-    taus, vars_, obs = [], [], []
-    for b in range(x.batch):
-        a = alpha[doff[b]:doff[b + 1]]
-        if n[b] < 0 or np.isnan(a).any():
-            continue
-        reach = np.concatenate([[1.0], np.cumprod(a)])  # P(round reaches position k)
-        pk = reach[:-1] * (1.0 - a)                     # P(n = k), k < gamma
-        pk = np.concatenate([pk, reach[-1:]])           # P(n = gamma)
-        k = np.arange(len(pk)) + 1.0                    # tokens emitted
-        mu = float((pk * k).sum())
-        taus.append(mu)
-        vars_.append(float((pk * k * k).sum()) - mu * mu)
-        obs.append(float(n[b] + 1))
-    cnt = len(obs)
-    mean_obs, mean_tau = float(np.mean(obs)), float(np.mean(taus))
-    se = float(np.sqrt(np.sum(vars_))) / cnt
-    return {"sequences": cnt, "observed_tokens_per_sequence": mean_obs,
-            "closed_form_tokens_per_sequence": mean_tau,
-            "mean_acceptance_rate": float(np.nanmean(alpha)),
-            "standard_error": se,
-            "z": (mean_obs - mean_tau) / se if se > 0 else 0.0}
+    return closed_form_tokens(alpha, x.gamma, n)
 
 
 def per_config(torch, svx, dev, args, sha):
