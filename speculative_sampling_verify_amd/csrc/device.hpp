@@ -209,6 +209,27 @@ struct Tile {
     else load_raw<true>(row, e0, e1, it, lane, r);
   }
 
+  // The raw tile of a row of V <= EPI elements (vector path, so V is a
+  // multiple of VE) with no branch around a load: a vector past the row's end
+  // loads the row's last vector again and reads as -inf, the values
+  // load_raw<true> gives it.
+  __device__ static __forceinline__ void load_only_tile(const void* row, int64_t V, int lane, Raw& r) {
+    static_assert(VEC, "vector path only");
+    const u32x4* p = static_cast<const u32x4*>(row);
+    constexpr uint32_t kNegInf = (DT == kBF16) ? 0xff80ff80u : 0xff800000u;  // -inf
+    const int last = (int)(V / VE) - 1;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int vec = u * kWave + lane;
+      const u32x4 q = __builtin_nontemporal_load(p + (vec < last ? vec : last));
+      const bool past = vec > last;
+      r.d[4 * u + 0] = past ? kNegInf : q.x;
+      r.d[4 * u + 1] = past ? kNegInf : q.y;
+      r.d[4 * u + 2] = past ? kNegInf : q.z;
+      r.d[4 * u + 3] = past ? kNegInf : q.w;
+    }
+  }
+
   __device__ static __forceinline__ void widen(const Raw& r, float (&z)[NE]) {
     if constexpr (VEC && DT == kBF16) {
 #pragma unroll

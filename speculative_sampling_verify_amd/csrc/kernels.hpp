@@ -377,7 +377,11 @@ __device__ __forceinline__ void load_tile(const void* row, int64_t V, int64_t t,
 // loop. Every tile takes its candidate dword with a uniform-index register
 // move and keeps it when the tile is the element's: no branch in the loop (a
 // branch there made the compiler drain the tile in flight at each back edge).
-template <int DT, bool VEC, bool SAMPLING, bool WITH_ARG, bool STORE = false>
+//
+// With ONE, `a` is the row's only tile (n_iter == 1, chunks == 1) and the
+// argmax reads it from the registers instead of loading it again: the same
+// values, so the same result.
+template <int DT, bool VEC, bool SAMPLING, bool WITH_ARG, bool STORE = false, bool ONE = false>
 __device__ __forceinline__ RowPart chunk_pass(const void* row, int64_t V, int c, int chunks,
                                               int n_iter, float k, int lane,
                                               typename Tile<DT, VEC>::Raw& a, float& lane_max,
@@ -426,7 +430,9 @@ __device__ __forceinline__ RowPart chunk_pass(const void* row, int64_t V, int c,
   auto tile_of = [&](int it) { return (int64_t)c + (int64_t)it * chunks; };
   Raw b;
   int it = 0;
-  if constexpr (DT == kBF16) {
+  if constexpr (ONE) {
+    process(a, 0);
+  } else if constexpr (DT == kBF16) {
     // Only a chunk's last tile can be partial (it is the row's last tile).
     // This loop loads full tiles only, with no branch around the loads: each
     // step issues one tile and then works on the one before it, so the
@@ -441,12 +447,14 @@ __device__ __forceinline__ RowPart chunk_pass(const void* row, int64_t V, int c,
       process(b, it + 1);
     }
   }
-  for (; it < n_iter; it += 2) {
-    if (it + 1 < n_iter) load_tile<DT, VEC>(row, V, tile_of(it + 1), lane, b);
-    process(a, it);
-    if (it + 1 >= n_iter) break;
-    if (it + 2 < n_iter) load_tile<DT, VEC>(row, V, tile_of(it + 2), lane, a);
-    process(b, it + 1);
+  if constexpr (!ONE) {
+    for (; it < n_iter; it += 2) {
+      if (it + 1 < n_iter) load_tile<DT, VEC>(row, V, tile_of(it + 1), lane, b);
+      process(a, it);
+      if (it + 1 >= n_iter) break;
+      if (it + 2 < n_iter) load_tile<DT, VEC>(row, V, tile_of(it + 2), lane, a);
+      process(b, it + 1);
+    }
   }
   lane_max = m;
   if constexpr (SAMPLING && !WITH_ARG && !STORE) {
@@ -466,7 +474,8 @@ __device__ __forceinline__ RowPart chunk_pass(const void* row, int64_t V, int c,
     if (best >= 0 && m == M) {
       const int64_t e0 = tile_of(best) * TL::EPI;
       float z[NE];
-      TL::template load<true>(row, e0, V, 0, lane, z);
+      if constexpr (ONE) TL::widen(a, z);
+      else TL::template load<true>(row, e0, V, 0, lane, z);
 #pragma unroll
       for (int j = NE - 1; j >= 0; --j)
         if (z[j] == m) arg = (int)TL::index(e0, 0, lane, j);
@@ -599,6 +608,123 @@ __global__ __launch_bounds__(kBlock) void k1_row_stats(RowStatsArgs a) {
       rank += (o > lm || (o == lm && l < lane)) ? 1 : 0;
     }
     if (rank == bar_k - 1) *bar_dst = lm;
+  }
+}
+
+// Pass 1 for rows of one tile (vector path, V <= EPI, so one chunk per row)
+// in a uniform or planned batch, without the diagnostics' extras: each wave
+// takes R consecutive rows (target rows, then draft rows, numbered as
+// k1_row_stats numbers them) and keeps the next row's tile in flight while it
+// works on the current one. With one such row per wave, a wave's only load
+// had returned before its reductions began, so nothing of its own was in
+// flight during them. A row that is not read (the draft row of a greedy
+// sequence, a row with an invalid temperature, one past the last row) loads
+// the first target row's tile instead, so that no load sits under a branch,
+// and writes nothing. Each row gets the statistics k1_row_stats gives it,
+// bit for bit: the same chunk_pass on the same tile.
+template <int DT, int R>
+__global__ __launch_bounds__(kBlock) void k1_short_rows(RowStatsArgs a) {
+  static_assert(R >= 2 && R % 2 == 0, "rows per wave: a positive even number");
+  using TL = Tile<DT, true>;
+  using Raw = typename TL::Raw;
+  if (a.gamma && blockIdx.x == 0) {
+    // the uniform batch's check of its gammas, as in k1_row_stats
+    bool bad = false;
+    for (int64_t b = threadIdx.x; b < a.B; b += blockDim.x) bad |= a.gamma[b] != a.uniform_g;
+    bad = __syncthreads_or(bad);
+    if (threadIdx.x == 0) a.status_out[0] = bad ? kLayoutError : 0u;
+  }
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t r0 = wave_uniform(((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6)) * R);
+  const int64_t rows = a.total_t + a.total_d;
+  if (r0 >= rows) return;
+  if (!a.gamma && (a.status[0] & kLayoutError)) return;
+  constexpr int64_t esz = (DT == kBF16) ? 2 : 4;
+  struct Row {
+    const void* row;
+    RowPart* dst;  // nullptr: the row is not read
+    float k;
+    int32_t cap;
+  };
+  // The row's logits, scale and capture code, found as k1_row_stats finds
+  // them (scalar loads only).
+  auto row_of = [&](int64_t r) {
+    Row w{a.target, nullptr, 0.f, -1};
+    if (r >= rows) return w;
+    const bool is_draft = r >= a.total_t;
+    const int64_t j = is_draft ? r - a.total_t : r;
+    int64_t tok = -1;
+    float k;
+    if (a.uniform_g >= 0) {
+      int64_t sb;
+      if (is_draft) {
+        sb = j / a.uniform_g;
+        tok = j;
+      } else {
+        sb = j / (a.uniform_g + 1);
+        const int64_t i = j - sb * (a.uniform_g + 1);
+        tok = (i < a.uniform_g) ? sb * a.uniform_g + i : -1;
+      }
+      k = seq_scale(scalar_load_f32(a.temperature + sb));
+    } else if (is_draft) {
+      tok = j;
+      k = scalar_load_f32(a.dk + j);
+    } else {
+      if (a.ttok) tok = (int32_t)scalar_load_u32(reinterpret_cast<uintptr_t>(a.ttok + j));
+      k = scalar_load_f32(a.tk + j);
+    }
+    // greedy or invalid sequences need no draft row; an invalid temperature
+    // needs no target row either (the accept step fails the sequence)
+    const bool read = is_draft ? (k > 0.f || (a.all_drafts && k == 0.f)) : (k >= 0.f);
+    if (!read) return w;
+    w.row = static_cast<const char*>(is_draft ? a.draft : a.target) + j * a.V * esz;
+    w.dst = (is_draft ? a.dparts : a.tparts) + j;
+    w.k = k;
+    if (a.tokens && k > 0.f && tok >= 0 && tok < a.total_d) {
+      const int32_t x = (int32_t)scalar_load_u32(reinterpret_cast<uintptr_t>(a.tokens + tok));
+      if (x >= 0 && (int64_t)x < a.V) w.cap = TL::capture_code(0, x);
+    }
+    return w;
+  };
+  auto work = [&](const Row& w, Raw& t) {
+    if (!w.dst) {
+      // Unused tile: its loads are waited for here all the same. A path that
+      // left them outstanding made the compiler wait, after the join, for
+      // the next row's tile too before it reused these registers.
+#pragma unroll
+      for (int q = 0; q < TL::RD; ++q) asm volatile("" ::"v"(t.d[q]));
+      return;
+    }
+    RowPart out;
+    float lm;
+    const bool sampling = w.k > 0.f;
+    if (sampling)
+      out = chunk_pass<DT, true, true, false, false, true>(w.row, a.V, 0, 1, 1, w.k, lane, t, lm, nullptr,
+                                                           w.cap, reinterpret_cast<uint32_t*>(&w.dst->arg));
+    else
+      out = chunk_pass<DT, true, false, true, false, true>(w.row, a.V, 0, 1, 1, 0.f, lane, t, lm);
+    if (lane == 0) {
+      if (sampling && a.tokens) {  // the arg field is the capture's
+        w.dst->s = out.s;
+        w.dst->m = out.m;
+      } else {
+        *w.dst = out;
+      }
+    }
+  };
+  Raw ta, tb;
+  Row wa = row_of(r0);
+  TL::load_only_tile(wa.row, a.V, lane, ta);
+#pragma unroll
+  for (int i = 0; i < R; i += 2) {
+    const Row wb = row_of(r0 + i + 1);
+    TL::load_only_tile(wb.row, a.V, lane, tb);
+    work(wa, ta);
+    if (i + 2 < R) {
+      wa = row_of(r0 + i + 2);
+      TL::load_only_tile(wa.row, a.V, lane, ta);
+    }
+    work(wb, tb);
   }
 }
 

@@ -82,6 +82,9 @@ constexpr int64_t kTargetUnfusedItems = 3072;  // else unfused waves to aim for
 #ifndef SPECV_FUSED_DRAW
 #define SPECV_FUSED_DRAW 1
 #endif
+#ifndef SPECV_SHORT_ROWS
+#define SPECV_SHORT_ROWS 2  // rows per pass-1 wave for rows of one tile (0: one row per wave)
+#endif
 constexpr size_t kFusedDrawLds = 64 * 1024;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -329,6 +332,16 @@ specv_status_t launch_row_stats(const Plan& p, bool vec, const void* target, con
   a.ttok = (tokens && !uniform && !inline_plan) ? at<int32_t>(ws, p.off_ttok) : nullptr;
   const int64_t waves = (p.tt + p.td) * p.chunks1;
   if (waves == 0) return SPECV_OK;
+  // rows of one tile: several rows per wave, the next one's tile in flight
+  const int64_t epi = (p.dt == kBF16) ? Tile<kBF16, true>::EPI : Tile<kF32, true>::EPI;
+  if (SPECV_SHORT_ROWS > 0 && vec && p.chunks1 == 1 && p.V <= epi && !with_argmax && !all_drafts &&
+      bar_k == 0 && !inline_plan) {
+    constexpr int R = SPECV_SHORT_ROWS > 0 ? SPECV_SHORT_ROWS : 2;
+    const dim3 grid(blocks_for((p.tt + p.td + R - 1) / R)), block(kBlock);
+    if (p.dt == kBF16) hipLaunchKernelGGL((k1_short_rows<kBF16, R>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k1_short_rows<kF32, R>), grid, block, 0, st, a);
+    return launched();
+  }
   const dim3 grid(blocks_for(waves)), block(kBlock);
   // specv_verify needs no argmax of sampling rows; the diagnostics export does
   if (with_argmax) {

@@ -675,6 +675,20 @@ def test_lenient_parity_mixed_greedy_fp32(svx):
     np.testing.assert_array_equal(got[1][greedy], base[1][greedy])
 
 
+@pytest.mark.parametrize("kind", ["lowest_mask", "huge", "offset", "tiny_T", "huge_T"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_lenient_extreme_logit_ranges(svx, kind, dtype):
+    # the lossy acceptance reads the same max-relative probabilities as the
+    # lossless one: at the ends of the range it still gives the oracle's
+    # outcomes, with no sequence reported as a data error
+    x = range_case(kind, dtype, seed=len(kind) * 13 + (dtype == "bf16"))
+    log("[case] lenient sq 0.3 range %s %s B=%d" % (kind, dtype, x.batch))
+    got = run_gpu_lenient(svx, x, "sq", 0.3)
+    orc = run_oracle(x, lenience="sq", epsilon=0.3)
+    assert got[2] == 0 and (orc.n >= 0).all()
+    assert_parity("lenient sq 0.3 range %s %s" % (kind, dtype), x, got, orc)
+
+
 @pytest.mark.parametrize("kind", ["none", "lin", "sq", "exp"])
 def test_lenient_eps_one_equals_lossless(svx, kind):
     x = synth.tiny_cpu(rounds=512)
