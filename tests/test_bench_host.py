@@ -1,5 +1,5 @@
-"""Host-side arithmetic of bench.py (no GPU): the tokens-per-round figure
-against the closed form of the pages."""
+"""Host-side logic of bench.py (no GPU): the tokens-per-round figure against
+the closed form of the pages, and the pass-1 kernel a launch's line names."""
 import itertools
 import sys
 from pathlib import Path
@@ -48,3 +48,17 @@ def test_closed_form_greedy_and_failed_sequences():
     assert r["sequences"] == 2
     assert r["closed_form_tokens_per_sequence"] == pytest.approx((3 + 1) / 2)
     assert r["standard_error"] == 0.0 and r["z"] == 0.0
+
+
+@pytest.mark.parametrize("vocab,size,gamma,kernel", [
+    (1000, 4, [4] * 16, "k1_short_rows"),          # the tiny fp32 workload's rows: 4000 B
+    (1024, 4, [4] * 16, "k1_short_rows"),          # exactly one 4 KiB tile
+    (1025, 4, [4] * 16, "k1_row_stats"),           # two tiles
+    (2048, 2, [3] * 16, "k1_short_rows"),          # one bf16 tile
+    (2044, 2, [3] * 16, "k1_row_stats"),           # 4088 B: not a multiple of 16 bytes
+    (32128, 2, [5] * 16, "k1_row_stats"),          # the T5-XXL-like rows
+    (1000, 4, [1, 2] * 8, "k1_row_stats"),         # ragged, planned inside pass 1
+    (1000, 4, [1, 2] * 600, "k1_short_rows"),      # ragged past 1024 sequences: plan launch
+])
+def test_pass1_kernel_of_a_launch(vocab, size, gamma, kernel):
+    assert bench.pass1_kernel(vocab, size, np.array(gamma, np.int32)) == kernel
