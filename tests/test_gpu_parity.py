@@ -478,6 +478,24 @@ def test_large_uniform_batch_parity(svx, B, V, g, dtype):
     parity_case(svx, "uniform B=%d V=%d gamma=%d %s" % (B, V, g, dtype), x)
 
 
+@pytest.mark.parametrize("B,V,g,dtype,errors", [
+    (333, 1024, 4, "f32", True),   # 2,997 rows: the last wave's second row is past the end
+    (257, 2048, 2, "bf16", True),  # one bf16 tile per row
+    (64, 1020, 5, "f32", False),   # 4,080-byte rows: the last vectors of each lane masked
+    (100, 4, 3, "f32", False),     # 16-byte rows: one vector per row
+    (101, 8, 1, "bf16", False),    # 16-byte bf16 rows
+])
+def test_short_row_pass1(svx, B, V, g, dtype, errors):
+    # rows of one 4 KiB tile: two rows per pass-1 wave, with greedy sequences'
+    # draft rows and invalid temperatures' rows skipped (their loads go to the
+    # first target row), NaN / +inf / all -inf rows and bad tokens
+    x = uniform_case(B, V, g, seed=B * 7 + V, dtype=dtype, errors=errors)
+    got, orc = parity_case(svx, "short rows B=%d V=%d gamma=%d %s%s" % (
+        B, V, g, dtype, " errors" if errors else ""), x)
+    if errors:
+        assert got[2] & svx.SPECV_DEV_SEQ_ERROR
+
+
 BF16_LOWEST = -3.3895313892515355e38  # the most negative finite bf16 (0xff7f)
 
 
