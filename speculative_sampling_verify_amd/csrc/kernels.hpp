@@ -14,6 +14,9 @@
 //                  argmax) in registers, reduced across the wave by shuffles;
 //                  the wave whose chunk holds a row's draft token also
 //                  records that logit for the accept step.
+//   k1_short_rows  pass 1 for rows of one 4 KiB tile (uniform and plan-launch
+//                  batches): two rows per wave, the second row's tile in
+//                  flight while the first is reduced; the same statistics.
 //   k3_accept_mass the accept step (one wave per sequence, one lane per draft
 //                  position: merge the chunk statistics, p_i(x_i) and
 //                  q_i(x_i) from the recorded logits, r_i from Philox, first
