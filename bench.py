@@ -472,18 +472,20 @@ def bench_decode(args, torch, svx, dev):
     if not args.no_cpu_baseline:
         import oracle
         log("[bench] timing the CPU oracle's decode loop on the host")
+        threads = baseline_threads(host_cpu())
         nb, el, res = 8, 0.0, None
         while True:
             t0 = time.perf_counter()
             res = oracle.decode_bigram(tabs.target, tabs.draft, np.ones(nb, np.float32),
-                                       tabs.start(nb), gamma=g, rounds=R, seed=0)
+                                       tabs.start(nb), gamma=g, rounds=R, seed=0,
+                                       nthreads=threads)
             el = time.perf_counter() - t0
             if el >= 5.0 or nb >= B:
                 break
             nb = min(B, nb * 2)
         gen = int(res.length[res.length > 0].sum())
         result["cpu_baseline"] = {"value": gen / el, "unit": "generated tokens/s",
-                                  "cores": oracle.default_threads(), "kind": "oracle",
+                                  "cores": threads, "kind": "oracle",
                                   "sample": "%d sequences x %d rounds (%d tokens), %.1f s"
                                             % (nb, R, gen, el)}
     print(json.dumps(result), flush=True)
@@ -560,19 +562,20 @@ def bench_cascade(args, torch, svx, dev):
     if not args.no_cpu_baseline:
         import oracle
         log("[bench] timing the CPU oracle's cascade on the host")
+        threads = baseline_threads(host_cpu())
         nb = 8
         while True:
             t0 = time.perf_counter()
             res = oracle.cascade_bigram(tabs.target, tabs.draft, tabs.small, np.ones(nb, np.float32),
                                         tabs.start(nb), k1=k1, k2=k2, rounds=R, lenience=kind,
-                                        epsilon=eps)
+                                        epsilon=eps, nthreads=threads)
             el = time.perf_counter() - t0
             if el >= 5.0 or nb >= B:
                 break
             nb = min(B, nb * 2)
         gen = int(res.length[res.length > 0].sum())
         result["cpu_baseline"] = {"value": gen / el, "unit": "generated tokens/s",
-                                  "cores": oracle.default_threads(), "kind": "oracle",
+                                  "cores": threads, "kind": "oracle",
                                   "sample": "%d sequences x %d rounds (%d tokens), %.1f s"
                                             % (nb, R, gen, el)}
     print(json.dumps(result), flush=True)
