@@ -1053,6 +1053,9 @@ struct DrawArgs {
   int32_t* out_next;
   int64_t V;
   int32_t B, chunks3, nsub;
+  // k3_accept_mass_draw with one wave and one sub-block per sequence: the
+  // launch's LDS also holds the wave's weights (16 bytes after the mass)
+  int32_t weights_in_lds;
 };
 
 // Wave-level inclusive scan of a sequence's sub-block masses in passes of 64
@@ -1177,23 +1180,24 @@ __device__ __forceinline__ void load16(const void* row, int64_t lo, int64_t V, f
 // reaches t, and that lane walks its 16 weights. Returns the token, or -1 if
 // t is not reached (with t < 0: always), the final prefix in *total and the
 // last element of positive weight in *last.
-template <int DT, bool VEC, class WT>
-__device__ int wave_draw(const void* trow, const void* drow, const WT& W, int64_t V,
-                         int64_t sb0, int64_t sb1, double carry, double t, int lane,
-                         double* total, int64_t* last) {
+//
+// `weights(sb, lo, w)` gives the lane's sixteen weights of sub-block sb,
+// elements [lo, lo + 16): from the rows (wave_draw) or from where the masses'
+// pass left them (wave_draw_from).
+template <class SRC>
+__device__ int wave_draw_src(const SRC& weights, int64_t sb0, int64_t sb1, double carry, double t,
+                             int lane, double* total, int64_t* last) {
   int64_t lastpos = -1;
   for (int64_t sb = sb0; sb < sb1; ++sb) {
     const int64_t lo = sb * kSub + (int64_t)lane * 16;
-    float w[16], zt[16], zd[16];
-    load16<DT, VEC>(trow, lo, V, zt);
-    if (W.residual) load16<DT, VEC>(drow, lo, V, zd);
+    float w[16];
+    weights(sb, lo, w);
     // positions within the lane's run are kept as 0..15 (not as 64-bit
     // element indices): it halves the registers the walk needs
     double ls = 0.0;
     int lastj = -1;  // last slot of positive weight in this lane's run
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      w[j] = W(zt[j], W.residual ? zd[j] : 0.f);
       lastj = (w[j] > 0.f) ? j : lastj;
       ls += (double)w[j];
     }
@@ -1234,13 +1238,47 @@ __device__ int wave_draw(const void* trow, const void* drow, const WT& W, int64_
   return -1;
 }
 
+// The walk with the weights formed from the selected rows.
+template <int DT, bool VEC, class WT>
+__device__ int wave_draw(const void* trow, const void* drow, const WT& W, int64_t V,
+                         int64_t sb0, int64_t sb1, double carry, double t, int lane,
+                         double* total, int64_t* last) {
+  auto from_rows = [&](int64_t, int64_t lo, float (&w)[16]) {
+    float zt[16], zd[16];
+    load16<DT, VEC>(trow, lo, V, zt);
+    if (W.residual) load16<DT, VEC>(drow, lo, V, zd);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) w[j] = W(zt[j], W.residual ? zd[j] : 0.f);
+  };
+  return wave_draw_src(from_rows, sb0, sb1, carry, t, lane, total, last);
+}
+
+// The walk over sub-block 0 with the weights the masses' pass stored in LDS
+// at their element indices (`wl[e]` = the weight of element e < kSub): the
+// same values wave_draw would form again from the rows.
+__device__ __forceinline__ int wave_draw_from(const float* wl, double carry, double t, int lane,
+                                              int64_t* last) {
+  auto from_lds = [&](int64_t, int64_t lo, float (&w)[16]) {
+    const float4* p = reinterpret_cast<const float4*>(wl + lo);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float4 q = p[u];
+      w[4 * u + 0] = q.x;
+      w[4 * u + 1] = q.y;
+      w[4 * u + 2] = q.z;
+      w[4 * u + 3] = q.w;
+    }
+  };
+  return wave_draw_src(from_lds, 0, 1, carry, t, lane, nullptr, last);
+}
+
 // The final draw of one sequence by one wave: picks the sub-block that holds
 // u * total from the pass-2 masses `sub` (global or LDS), then walks that
 // sub-block. Where subs_fit_regs(nsub), `v` holds the masses as load_subs
 // leaves them (the caller requests them early) and the scans run on it.
 template <int DT, bool VEC>
 __device__ int draw_token(const DrawArgs& a, const double* sub, const double (&v)[kSubRegs],
-                          const Select& s, int lane) {
+                          const Select& s, int lane, const float* wl = nullptr) {
   constexpr int64_t esz = (DT == kBF16) ? 2 : 4;
   const void* trow = static_cast<const char*>(a.target) + s.trow * a.V * esz;
   const void* drow = (s.mode == kModeResidual) ? static_cast<const char*>(a.draft) + s.drow * a.V * esz : nullptr;
@@ -1263,14 +1301,17 @@ __device__ int draw_token(const DrawArgs& a, const double* sub, const double (&v
       const Weights<decltype(fma)::value> W = make_weights<decltype(fma)::value>(s, false);
       int tok = -1;
       int64_t last = -1;
+      // wl (one sub-block): the residual weights the masses' pass left in LDS
       if (sb >= 0) {
-        tok = wave_draw<DT, VEC>(trow, drow, W, a.V, sb, sb + 1, base, t, lane, nullptr, &last);
+        tok = wl ? wave_draw_from(wl, base, t, lane, &last)
+                 : wave_draw<DT, VEC>(trow, drow, W, a.V, sb, sb + 1, base, t, lane, nullptr, &last);
         if (tok < 0) tok = (int)last;
       }
       for (int64_t q = a.nsub - 1; tok < 0 && q >= 0; --q) {
         // rounding left t past every prefix: the last token of positive weight
         if (!(sub[q] > 0.0)) continue;
-        wave_draw<DT, VEC>(trow, drow, W, a.V, q, q + 1, 0.0, -1.0, lane, nullptr, &last);
+        if (wl) wave_draw_from(wl, 0.0, -1.0, lane, &last);
+        else wave_draw<DT, VEC>(trow, drow, W, a.V, q, q + 1, 0.0, -1.0, lane, nullptr, &last);
         tok = (int)last;
       }
       return tok;
@@ -1302,9 +1343,12 @@ __device__ int draw_token(const DrawArgs& a, const double* sub, const double (&v
 // Pass 2 over chunk c of the selected row pair of one sequence: the weight
 // mass of every 1024-element sub-block of the chunk, stored to out[sub-block]
 // (global memory or LDS).
+//
+// With wsave (a row of one sub-block), the weights of sub-block 0 are also
+// stored there at their element indices, for the draw's walk.
 template <int DT, bool VEC, bool FMA>
 __device__ __forceinline__ void chunk_masses_w(const DrawArgs& a, const Select& s, int c, int lane,
-                                               double* out) {
+                                               double* out, float* wsave) {
   using TL = Tile<DT, VEC>;
   constexpr int NE = TL::NE;
   constexpr int SUBS = TL::EPI / kSub;  // sub-blocks per tile (1 or 2)
@@ -1339,6 +1383,10 @@ __device__ __forceinline__ void chunk_masses_w(const DrawArgs& a, const Select& 
       for (int q = 0; q < NE; ++q)
         w[q] = W(__uint_as_float(rt.d[q]), W.residual ? __uint_as_float(rd.d[q]) : 0.f);
     }
+    if (wsave && e0 == 0) {
+#pragma unroll
+      for (int j = 0; j < PER; ++j) wsave[TL::index(0, 0, lane, j)] = w[j];
+    }
 #pragma unroll
     for (int h = 0; h < SUBS; ++h) {
       float part[PER];
@@ -1354,9 +1402,9 @@ __device__ __forceinline__ void chunk_masses_w(const DrawArgs& a, const Select& 
 // The weights' form is the same for the whole sequence (weights_fma).
 template <int DT, bool VEC>
 __device__ __forceinline__ void chunk_masses(const DrawArgs& a, const Select& s, int c, int lane,
-                                             double* out) {
-  if (weights_fma(s, false)) chunk_masses_w<DT, VEC, true>(a, s, c, lane, out);
-  else chunk_masses_w<DT, VEC, false>(a, s, c, lane, out);
+                                             double* out, float* wsave = nullptr) {
+  if (weights_fma(s, false)) chunk_masses_w<DT, VEC, true>(a, s, c, lane, out, wsave);
+  else chunk_masses_w<DT, VEC, false>(a, s, c, lane, out, wsave);
 }
 
 template <int DT, bool VEC>
@@ -1403,12 +1451,16 @@ __global__ __launch_bounds__(1024) void k3_accept_mass_draw(AcceptArgs acc, Draw
   const int64_t b = blockIdx.x;
   const Select s = uniform_select(accept_sequence<DT>(acc, b, lane, c == 0));
   const bool active = s.mode != kModeNone;
-  if (active) chunk_masses<DT, VEC>(a, s, c, lane, sub_lds);
+  // one wave and one sub-block: the wave keeps its weights in LDS (after the
+  // mass, 16 bytes on) and the draw walks them instead of forming them again
+  // from the rows
+  float* const wl = a.weights_in_lds ? reinterpret_cast<float*>(sub_lds + 2) : nullptr;
+  if (active) chunk_masses<DT, VEC>(a, s, c, lane, sub_lds, wl);
   __syncthreads();
   if (active && c == 0) {
     double v[kSubRegs];
     if (subs_fit_regs(a.nsub)) load_subs(sub_lds, a.nsub, lane, v);
-    const int token = draw_token<DT, VEC>(a, sub_lds, v, s, lane);
+    const int token = draw_token<DT, VEC>(a, sub_lds, v, s, lane, wl);
     if (lane == 0) a.out_next[b] = token;
   }
 }

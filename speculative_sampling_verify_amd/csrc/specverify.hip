@@ -82,6 +82,9 @@ constexpr int64_t kTargetUnfusedItems = 3072;  // else unfused waves to aim for
 #ifndef SPECV_FUSED_DRAW
 #define SPECV_FUSED_DRAW 1
 #endif
+#ifndef SPECV_DRAW_FROM_LDS
+#define SPECV_DRAW_FROM_LDS 1  // one wave, one sub-block: the draw walks the weights left in LDS
+#endif
 #ifndef SPECV_SHORT_ROWS
 #define SPECV_SHORT_ROWS 2  // rows per pass-1 wave for rows of one tile (0: one row per wave)
 #endif
@@ -421,6 +424,7 @@ DrawArgs draw_args(const Plan& p, const Call& c) {
   a.B = (int32_t)p.B;
   a.chunks3 = p.chunks3;
   a.nsub = (int32_t)p.nsub;
+  a.weights_in_lds = (p.fused_draw && p.chunks3 == 1 && p.nsub == 1 && SPECV_DRAW_FROM_LDS) ? 1 : 0;
   return a;
 }
 
@@ -430,7 +434,9 @@ specv_status_t launch_accept_mass(const Plan& p, bool vec, const Call& c) {
   if (p.fused_draw) {
     // one workgroup per sequence, one wave per pass-2 chunk; masses in LDS
     const dim3 grid((unsigned)p.B), block((unsigned)(p.chunks3 * kWave));
-    const size_t lds = (size_t)p.nsub * sizeof(double);
+    // one wave and one sub-block: the draw's weights stay in LDS too
+    const size_t lds = a.weights_in_lds ? 2 * sizeof(double) + kSub * sizeof(float)
+                                        : (size_t)p.nsub * sizeof(double);
     if (p.dt == kBF16) {
       if (vec) hipLaunchKernelGGL((k3_accept_mass_draw<kBF16, true>), grid, block, lds, c.stream, acc, a);
       else hipLaunchKernelGGL((k3_accept_mass_draw<kBF16, false>), grid, block, lds, c.stream, acc, a);
