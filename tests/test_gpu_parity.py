@@ -496,6 +496,55 @@ def test_short_row_pass1(svx, B, V, g, dtype, errors):
         assert got[2] & svx.SPECV_DEV_SEQ_ERROR
 
 
+def short_rows_random_case(seed):
+    """A seeded random batch of short rows (up to one 4 KiB tile, mostly
+    16-byte multiples): uniform, or ragged past 1024 sequences (the plan
+    launch); gamma 0..16, greedy, sampling and an occasional invalid
+    temperature, masked tokens, draft tokens drawn from the draft rows."""
+    rng = np.random.default_rng(50000 + seed)
+    dtype = "bf16" if rng.random() < 0.5 else "f32"
+    vec = 8 if dtype == "bf16" else 4
+    vmax = 2048 if dtype == "bf16" else 1024
+    V = (int(rng.integers(1, vmax // vec + 1)) * vec if rng.random() < 0.85
+         else int(rng.integers(1, vmax + 1)))
+    ragged = rng.random() < 0.25
+    g = int(rng.integers(0, 17))
+    bmax = max(1, min(3000, 12_000_000 // max(1, (2 * g + 1) * V)))
+    B = int(rng.integers(1025, 1400)) if ragged and bmax >= 1025 else int(rng.integers(1, bmax + 1))
+    gam = rng.integers(0, g + 1, size=B).astype(np.int32) if ragged else np.full(B, g, np.int32)
+    gam[0] = g
+    T = np.where(rng.random(B) < 0.2, 0.0, rng.uniform(0.3, 2.0, B)).astype(np.float32)
+    if rng.random() < 0.2:
+        T[rng.integers(0, B)] = -1.0
+    toff = np.concatenate([[0], np.cumsum(gam + 1)])
+    doff = np.concatenate([[0], np.cumsum(gam)])
+    target = (rng.standard_normal((int(toff[-1]), V)) * float(rng.choice([0.5, 2.0, 4.0]))).astype(np.float32)
+    seq = np.repeat(np.arange(B), gam)
+    trow = toff[seq] + (np.arange(int(doff[-1])) - doff[seq])
+    draft = (target[trow] + rng.standard_normal((len(trow), V)) * float(rng.choice([0.1, 1.0]))).astype(np.float32)
+    if V > 4 and rng.random() < 0.3:
+        cols = rng.choice(V, size=V // 4, replace=False)
+        target[:, cols] = -np.inf
+        draft[:, cols[: len(cols) // 2]] = -np.inf
+    Ts = np.where(T[seq] > 0, T[seq], 1.0)[:, None]
+    z = np.where(np.isfinite(draft), draft / Ts, -np.inf)
+    noise = np.where(T[seq][:, None] > 0, rng.gumbel(size=draft.shape), 0.0)
+    tokens = np.argmax(z + noise, axis=1).astype(np.int32)
+    conv = synth.to_bf16_bits if dtype == "bf16" else (lambda a: a)
+    return synth.Inputs("short rows random %d" % seed, V, g, dtype, conv(target), conv(draft), tokens,
+                        gam, T)
+
+
+@pytest.mark.parametrize("seed", range(32))
+def test_short_rows_random(svx, seed):
+    # short rows at random shapes: pass 1 two rows per wave, pass 2 one wave
+    # per sequence (weights left in LDS for the draw where V <= 1024)
+    x = short_rows_random_case(seed)
+    parity_case(svx, "short rows random %d (V=%d %s B=%d gamma<=%d %s)" % (
+        seed, x.vocab, x.dtype, x.batch, x.max_gamma,
+        "ragged" if (x.gamma != x.gamma[0]).any() else "uniform"), x, repeat=False)
+
+
 BF16_LOWEST = -3.3895313892515355e38  # the most negative finite bf16 (0xff7f)
 
 
