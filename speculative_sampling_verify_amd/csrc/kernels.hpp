@@ -29,7 +29,9 @@
 //                  token (inverse CDF in index order).
 //   k3_accept_mass_draw  both of the last two in one launch when a sequence's
 //                  pass-2 waves fit one workgroup (a barrier, not a kernel
-//                  boundary, orders the masses before the draw).
+//                  boundary, orders the masses before the draw); with one
+//                  wave and one sub-block per sequence the draw walks the
+//                  weights that wave left in LDS.
 #pragma once
 
 #include <type_traits>
@@ -618,13 +620,13 @@ __global__ __launch_bounds__(kBlock) void k1_row_stats(RowStatsArgs a) {
 // in a uniform or planned batch, without the diagnostics' extras: each wave
 // takes R consecutive rows (target rows, then draft rows, numbered as
 // k1_row_stats numbers them) and keeps the next row's tile in flight while it
-// works on the current one. With one such row per wave, a wave's only load
-// had returned before its reductions began, so nothing of its own was in
-// flight during them. A row that is not read (the draft row of a greedy
-// sequence, a row with an invalid temperature, one past the last row) loads
-// the first target row's tile instead, so that no load sits under a branch,
-// and writes nothing. Each row gets the statistics k1_row_stats gives it,
-// bit for bit: the same chunk_pass on the same tile.
+// works on the current one (with one such row per wave, a wave would have
+// nothing of its own in flight during its reductions). A row that is not
+// read (the draft row of a greedy sequence, a row with an invalid
+// temperature, one past the last row) loads the first target row's tile
+// instead, so that no load sits under a branch, and writes nothing. Each row
+// gets the statistics k1_row_stats gives it, bit for bit: the same
+// chunk_pass on the same tile.
 template <int DT, int R>
 __global__ __launch_bounds__(kBlock) void k1_short_rows(RowStatsArgs a) {
   static_assert(R >= 2 && R % 2 == 0, "rows per wave: a positive even number");
