@@ -545,6 +545,47 @@ def test_short_rows_random(svx, seed):
         "ragged" if (x.gamma != x.gamma[0]).any() else "uniform"), x, repeat=False)
 
 
+@pytest.mark.parametrize("V,g,dtype,K", [(32128, 5, "bf16", 16), (1000, 4, "f32", 64),
+                                         (256000, 8, "f32", 4)])
+def test_logits_past_4_gib(svx, V, g, dtype, K):
+    # byte offsets past 32 bits: a uniform batch just long enough that the
+    # last K sequences' target and draft rows start beyond 4 GiB (5-10 GB of
+    # logits on the device). Those K hold random rows (every fifth greedy)
+    # and are checked against the oracle at their own Philox rows; the others
+    # hold zero logits (p = q uniform: every draft accepted, the token drawn
+    # from p) and are checked for that.
+    row_bytes = V * (2 if dtype == "bf16" else 4)
+    b0 = 2**32 // (g * row_bytes) + 1
+    B = b0 + K
+    assert b0 * g * row_bytes > 2**32
+    xs = uniform_case(K, V, g, seed=V + K, dtype=dtype)
+    d = svx.from_inputs(xs)
+    el = torch.int16 if dtype == "bf16" else torch.float32
+    log("[case] logits past 4 GiB: V=%d gamma=%d %s B=%d (%.1f GB), random sequences %d.." % (
+        V, g, dtype, B, B * (2 * g + 1) * row_bytes / 1e9, b0))
+    target = torch.zeros((B * (g + 1), V), dtype=el, device="cuda")
+    draft = torch.zeros((B * g, V), dtype=el, device="cuda")
+    target[b0 * (g + 1):] = d["target"]
+    draft[b0 * g:] = d["draft"]
+    tokens = torch.zeros(B * g, dtype=torch.int32, device="cuda")
+    tokens[b0 * g:] = d["draft_tokens"]
+    gamma = torch.full((B,), g, dtype=torch.int32, device="cuda")
+    temp = torch.ones(B, dtype=torch.float32, device="cuda")
+    temp[b0:] = d["temperature"]
+    ws = svx.workspace_for(svx._shape_of(target, draft, gamma, g), "cuda")
+    P = 12345
+    n, nxt = svx.specv_verify(target, draft, tokens, gamma, temp, max_gamma=g, seed=xs.seed,
+                              philox_row_offset=P, workspace=ws)
+    torch.cuda.synchronize()
+    n, nxt, st = n.cpu().numpy(), nxt.cpu().numpy(), svx.read_status(ws)
+    del target, draft
+    torch.cuda.empty_cache()
+    assert st == 0
+    assert (n[:b0] == g).all() and (nxt[:b0] >= 0).all() and (nxt[:b0] < V).all()
+    orc = run_oracle(xs, row_offset=P + b0)
+    assert_parity("past 4 GiB V=%d %s" % (V, dtype), xs, (n[b0:], nxt[b0:], st), orc)
+
+
 BF16_LOWEST = -3.3895313892515355e38  # the most negative finite bf16 (0xff7f)
 
 
