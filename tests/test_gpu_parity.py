@@ -578,12 +578,27 @@ def test_logits_past_4_gib(svx, V, g, dtype, K):
                               philox_row_offset=P, workspace=ws)
     torch.cuda.synchronize()
     n, nxt, st = n.cpu().numpy(), nxt.cpu().numpy(), svx.read_status(ws)
+    # the diagnostics on the same rows: the last K * g positions against the
+    # oracle, the zero rows' alpha = 1 and entropy = ln V
+    dg = svx.specv_position_diagnostics(target, draft, gamma, temp, 16, max_gamma=g)
+    torch.cuda.synchronize()
+    dg = {name: t.cpu().numpy() for name, t in dg.items()}
     del target, draft
     torch.cuda.empty_cache()
     assert st == 0
     assert (n[:b0] == g).all() and (nxt[:b0] >= 0).all() and (nxt[:b0] < V).all()
     orc = run_oracle(xs, row_offset=P + b0)
     assert_parity("past 4 GiB V=%d %s" % (V, dtype), xs, (n[b0:], nxt[b0:], st), orc)
+    want = oracle.position_diagnostics(xs.target, xs.draft, xs.gamma, xs.temperature, vocab=V,
+                                       top_k=16)
+    q0 = b0 * g
+    nan = np.isnan(want.alpha)
+    np.testing.assert_array_equal(np.isnan(dg["alpha"][q0:]), nan)
+    assert np.abs(dg["alpha"][q0:][~nan] - want.alpha[~nan]).max(initial=0) <= DIAG_ALPHA_TOL
+    assert np.abs(dg["entropy"][q0:][~nan] - want.entropy[~nan]).max(initial=0) <= DIAG_ENTROPY_TOL
+    np.testing.assert_array_equal(dg["topk_index"][q0:], want.topk_index)
+    assert np.abs(dg["alpha"][:q0] - 1.0).max() <= DIAG_ALPHA_TOL
+    assert np.abs(dg["entropy"][:q0] - np.log(V)).max() <= DIAG_ENTROPY_TOL
 
 
 BF16_LOWEST = -3.3895313892515355e38  # the most negative finite bf16 (0xff7f)
