@@ -1439,19 +1439,32 @@ __global__ __launch_bounds__(kBlock) void k4_draw(DrawArgs a) {
 
 // Accept step, pass 2 and the final draw in one launch, one workgroup per
 // sequence with one wave per pass-2 chunk (blockDim = 64 * chunks3, at most
-// 1024). Every wave runs the same accept step (wave 0 stores it), takes the
-// masses of its chunk into LDS, and after the workgroup barrier wave 0 draws
-// from them: the barrier replaces the kernel boundary of the two-launch form,
-// and the arithmetic is the same, so both forms give the same bits. Every
-// wave reaches the barrier: the accept step's outcome is the same in all of
-// them, and nothing returns before it.
+// 1024). Wave 0 runs the accept step and, with several waves, leaves the
+// selection in LDS for the others (a few sequences' workgroups are alone on
+// their compute units, where copies of the accept step in every wave would
+// share the SIMDs); every wave takes the masses of its chunk into LDS, and
+// after the workgroup barrier wave 0 draws from them: the barrier replaces
+// the kernel boundary of the two-launch form, and the arithmetic is the
+// same, so both forms give the same bits. Every wave reaches both barriers:
+// nothing returns before them.
 template <int DT, bool VEC>
 __global__ __launch_bounds__(1024) void k3_accept_mass_draw(AcceptArgs acc, DrawArgs a) {
   extern __shared__ double sub_lds[];  // [nsub] masses of the sequence's sub-blocks
+  __shared__ Select sel_lds;
   const int lane = threadIdx.x & (kWave - 1);
   const int c = (int)(threadIdx.x >> 6);
   const int64_t b = blockIdx.x;
-  const Select s = uniform_select(accept_sequence<DT>(acc, b, lane, c == 0));
+  Select s;
+  if (blockDim.x == kWave) {
+    s = uniform_select(accept_sequence<DT>(acc, b, lane, true));
+  } else {
+    if (c == 0) {
+      const Select s0 = accept_sequence<DT>(acc, b, lane, true);
+      if (lane == 0) sel_lds = s0;
+    }
+    __syncthreads();
+    s = uniform_select(sel_lds);
+  }
   const bool active = s.mode != kModeNone;
   // one wave and one sub-block: the wave keeps its weights in LDS (after the
   // mass, 16 bytes on) and the draw walks them instead of forming them again
