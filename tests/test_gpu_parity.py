@@ -601,6 +601,35 @@ def test_logits_past_4_gib(svx, V, g, dtype, K):
     assert np.abs(dg["entropy"][:q0] - np.log(V)).max() <= DIAG_ENTROPY_TOL
 
 
+def test_concurrent_streams(svx):
+    # two streams (default priority), each with its own inputs and workspace
+    # (a T5-XXL-like batch and a batch of one-tile fp32 rows), calls enqueued
+    # alternately: every call returns what the same call returns alone, so
+    # the library keeps no state between calls but the caller's workspace
+    xa = synth.t5xxl_like(rounds=64)
+    xb = uniform_case(300, 1000, 4, seed=3, dtype="f32")
+    ref = [run_gpu(svx, xa), run_gpu(svx, xb)]
+    log("[case] concurrent streams: B=%d V=%d and B=%d V=%d" % (xa.batch, xa.vocab, xb.batch, xb.vocab))
+    calls = []
+    for x in (xa, xb):
+        d = svx.from_inputs(x)
+        ws = svx.workspace_for(svx._shape_of(d["target"], d["draft"], d["gamma"], x.max_gamma), "cuda")
+        calls.append((x, d, ws, torch.cuda.Stream()))
+    torch.cuda.synchronize()
+    outs = []
+    for i in range(8):
+        for k, (x, d, ws, st) in enumerate(calls):
+            with torch.cuda.stream(st):
+                n, nxt = svx.specv_verify(d["target"], d["draft"], d["draft_tokens"], d["gamma"],
+                                          d["temperature"], max_gamma=x.max_gamma, seed=x.seed,
+                                          philox_row_offset=x.row_offset, workspace=ws, stream=st)
+            outs.append((k, n, nxt))
+    torch.cuda.synchronize()
+    for k, n, nxt in outs:
+        np.testing.assert_array_equal(n.cpu().numpy(), ref[k][0])
+        np.testing.assert_array_equal(nxt.cpu().numpy(), ref[k][1])
+
+
 BF16_LOWEST = -3.3895313892515355e38  # the most negative finite bf16 (0xff7f)
 
 
