@@ -535,6 +535,18 @@ def short_rows_random_case(seed):
                         gam, T)
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_short_rows_random_lenient(svx, seed):
+    # the lossy step on the random short-row batches (each lenience function)
+    x = short_rows_random_case(100 + seed)
+    kind, eps = [("lin", 0.5), ("sq", 0.3), ("exp", 0.2), ("lin", 0.05)][seed % 4]
+    log("[case] short rows random %d lenient %s %g (V=%d %s B=%d)" % (100 + seed, kind, eps, x.vocab,
+                                                                     x.dtype, x.batch))
+    got = run_gpu_lenient(svx, x, kind, eps)
+    orc = run_oracle(x, lenience=kind, epsilon=eps)
+    assert_parity("short rows random %d lenient %s %g" % (100 + seed, kind, eps), x, got, orc)
+
+
 @pytest.mark.parametrize("seed", range(32))
 def test_short_rows_random(svx, seed):
     # short rows at random shapes: pass 1 two rows per wave, pass 2 one wave

@@ -76,6 +76,13 @@ def test_noalloc_smaller_second_call_and_status(svx):
     check("t5xxl_like 8 rounds", svx, synth.t5xxl_like(rounds=8))
 
 
+def test_noalloc_short_rows(svx):
+    # rows of one tile (two per pass-1 wave) and one-wave draws from the
+    # weights in LDS, sampling and then greedy, the second call smaller
+    check("tiny_cpu 3000 rounds", svx, synth.tiny_cpu(rounds=3000))
+    check("tiny_cpu 500 rounds greedy", svx, synth.tiny_cpu(rounds=500, greedy=True))
+
+
 def test_noalloc_rejects_shapes_beyond_its_scratch(svx):
     # 2^20 sequences of gamma 7 need far more than the static scratch: the call
     # is refused before anything is enqueued (no tensor is read)
