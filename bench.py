@@ -81,6 +81,31 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def pass2_bytes(vocab, bytes_per_logit, gamma, temperature, n) -> int:
+    """Bytes the second pass must read, from the step's outcomes: for each
+    sampling sequence the step did not fail, the selected target row when
+    every draft was accepted, else the selected target and draft rows (the
+    residual's two rows); nothing for greedy and failed sequences."""
+    g = np.asarray(gamma, np.int64)
+    n = np.asarray(n, np.int64)
+    sampling = (np.asarray(temperature) > 0) & (n >= 0)
+    rows = np.where(n < g, 2, 1)
+    return int(rows[sampling].sum()) * int(vocab) * int(bytes_per_logit)
+
+
+def second_pass_fields(torch, svx, dev, x, m) -> dict:
+    """The second pass against a read of its own bytes: its algorithmic bytes
+    (pass2_bytes of the timed outcomes), one read-probe launch over that many
+    bytes, and the rest of the step after pass 1 (the uninstrumented step
+    time less the pass-1 kernel's event average: accept step, second pass,
+    draw and the launch gap)."""
+    p2 = pass2_bytes(x.vocab, x.bytes_per_logit, x.gamma, x.temperature, m["n"])
+    probe = read_probe_ms(torch, svx, dev, p2) if p2 > 0 else None
+    rest = m["ms_per_step_plain"] - m["k1_ms"]
+    return {"pass2_bytes": p2, "pass2_read_probe_ms": probe, "rest_of_step_ms": rest,
+            "rest_frac_of_pass2_read_probe": (probe / rest) if probe and rest > 0 else None}
+
+
 def pass1_kernel(vocab, bytes_per_logit, gamma) -> str:
     """The pass-1 kernel of a verify launch: rows of one 4 KiB tile (a
     multiple of 16 bytes) take k1_short_rows in a uniform batch or a ragged
@@ -797,6 +822,7 @@ def per_config(torch, svx, dev, args, sha):
                "step_frac_of_read_probe": probe / m["ms_per_step_plain"],
                "pass1_frac_of_read_probe": probe / m["k1_ms"],
                "stage_ms_instrumented": m["stage_ms"],
+               **second_pass_fields(torch, svx, dev, x, m),
                "tokens_vs_closed_form": tokens_vs_closed_form(torch, svx, dev, x, m["n"]),
                "parity_vs_oracle": parity_counts(x, m["n"], m["next"])}
         if name in TARGET_WORKLOADS:
@@ -921,6 +947,7 @@ def main():
         "step_frac_of_read_probe": probe / m["ms_per_step_plain"],
         "pass1_frac_of_read_probe": probe / m["k1_ms"],
         "stage_ms_instrumented": m["stage_ms"],
+        **second_pass_fields(torch, svx, dev, x, m),
         "emitted_tokens_per_s": emitted / (ms_step * 1e-3),
         "mean_tokens_per_sequence": emitted / x.batch,
         "sequences_per_s": x.batch / (ms_step * 1e-3),

@@ -62,3 +62,15 @@ def test_closed_form_greedy_and_failed_sequences():
 ])
 def test_pass1_kernel_of_a_launch(vocab, size, gamma, kernel):
     assert bench.pass1_kernel(vocab, size, np.array(gamma, np.int32)) == kernel
+
+
+def test_pass2_bytes_counts_the_selected_rows():
+    # gamma 3, V 10, fp32: a residual reads two rows, a bonus one, greedy and
+    # failed sequences none
+    g = np.array([3, 3, 3, 3, 3, 0], np.int32)
+    T = np.array([1.0, 1.0, 0.0, 0.7, 1.0, 1.0], np.float32)
+    n = np.array([0, 3, 1, 2, -1, 0], np.int32)
+    # seq 0: residual (2 rows); 1: bonus (1); 2: greedy (0); 3: residual (2);
+    # 4: failed (0); 5: gamma 0, every draft accepted: bonus (1)
+    assert bench.pass2_bytes(10, 4, g, T, n) == (2 + 1 + 2 + 1) * 10 * 4
+    assert bench.pass2_bytes(10, 2, g[:0], T[:0], n[:0]) == 0
