@@ -12,8 +12,9 @@ fraction of the HBM peak, its pass-1 kernel fraction, the stored counter
 traffic, its parity counts against the CPU oracle and its tokens per round
 against the pages' closed form at its acceptance rates. Every workload also
 gets the time of one launch of the library's read probe over its pass-1
-bytes: what a single streaming read of that size takes on this part. Prints
-one JSON line.
+bytes: what a single streaming read of that size takes on this part; and the
+same for its second pass's bytes (the selected rows, from the outcomes),
+beside the rest of the step after pass 1. Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                   [--lenience none|lin|sq|exp --epsilon E] [--no-per-config]
